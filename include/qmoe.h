@@ -1,0 +1,230 @@
+/*
+ * qmoe.h -- C ABI of the routed int4 Mixture-of-Experts layer for AMD MI355X (gfx950).
+ *
+ * Sources of the operations (the pages the library implements):
+ *   [TF-struct] TurboFieldfare post on discuss.pytorch.kr, section "TurboFieldfare의
+ *               전문가 스트리밍 구조" (expert-streaming structure): each layer has 128
+ *               routed experts, 8 chosen per token, plus a shared expert added without a
+ *               routing weight; the router listing (scale-free RMS norm, scaling by
+ *               router_scale / sqrt(hidden), 8-bit affine projection to per-expert
+ *               logits, top-8, softmax over the kept logits, times per_expert_scale);
+ *               cb2 combines the routed branches by router weight with the shared branch
+ *               and the residual; prompts are prefilled in chunks of at most 128 tokens,
+ *               so one expert read serves every row routed to it.
+ *   [TF-mem]    same post, section "TurboFieldfare가 메모리를 아끼는 방식": MLX affine
+ *               4-bit weights with one bf16 scale and one bf16 bias per 64 weights; only
+ *               the router projection is 8-bit.
+ *   [TF-inst]   same post, section "TurboFieldfare의 스트리밍 설치 방식": quantised values
+ *               are copied with a layout change only, never dequantised and requantised.
+ *   [SW-mem]    Swiftlet article on tech.utomolab.com, section "같은 모델을 왜 이렇게 적은
+ *               메모리로 돌릴 수 있나": routed experts stored as fixed-stride blocks so that
+ *               fetching one expert is a single read; 512 experts/top-10, 256/top-8.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensor pointers are DEVICE pointers owned by the caller, unless stated otherwise.
+ *    Descriptor structs (qmoe_dims, qmoe_router, qmoe_layer) live in HOST memory and are
+ *    read during the call only.  The library never allocates device memory; scratch
+ *    space comes from a caller-provided device workspace (see qmoe_workspace_bytes).
+ *  - Every compute call is enqueued asynchronously on the caller's hipStream_t (NULL is
+ *    the default stream).  No call synchronises or copies device->host, so every call
+ *    can be captured into a HIP graph.  Nothing is cleared with memset.
+ *  - bf16 values travel as uint16_t bit patterns.  Matrices are row-major.
+ *  - Status: every int-returning entry returns QMOE_OK (0) or a negative QMOE_ERR_*.
+ *    On error nothing is enqueued and qmoe_last_error() returns a thread-local message.
+ *    Arguments are validated on the host before any device call, so argument errors are
+ *    reported on machines without a GPU too.
+ *  - Calls keep no state between invocations (apart from the workspace contents, which
+ *    belong to the call using them); calls on different streams may run concurrently if
+ *    they use different workspaces and outputs.  Outputs must not alias inputs.
+ *  - T = 0 (no tokens) is a valid no-op that returns QMOE_OK.
+ *  - Shape limits: hidden, inter and shared_inter are multiples of 64; hidden <= 8192,
+ *    inter and shared_inter <= 4096 (so that one workgroup stages a block of activations in
+ *    LDS); group == 64; 1 <= top_k <= min(n_experts, 32); 1 <= n_experts <= 1024;
+ *    T <= 65536 per call.  Store base pointers and strides are 256-byte aligned.
+ *
+ * Quantised formats (canonical, as the pages describe them)
+ * ---------------------------------------------------------
+ *  int4 matrix [R, K]: codes uint8 [R, K/2], element 2m in the LOW nibble of byte m,
+ *  scale and bias bf16 [R, K/64]; value = scale[r, c/64] * code[r, c] + bias[r, c/64]
+ *  with unsigned codes 0..15.  int8 router [E, H]: codes uint8 [E, H] (0..255), scale and
+ *  bias bf16 [E, H/64], value = s * q + b.
+ *  An expert is gate [I, H], up [I, H] and down [H, I] int4 matrices (SwiGLU:
+ *  h = silu(x gate^T) * (x up^T), y = h down^T, silu(z) = z / (1 + exp(-z))).
+ */
+#ifndef QMOE_H
+#define QMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *qmoe_stream_t; /* the caller's hipStream_t */
+
+enum {
+    QMOE_OK = 0,
+    QMOE_ERR_ARG = -1,       /* null pointer, bad enum/flag, aliasing outputs */
+    QMOE_ERR_SHAPE = -2,     /* a dimension outside the limits above */
+    QMOE_ERR_WORKSPACE = -3, /* workspace null or smaller than qmoe_workspace_bytes */
+    QMOE_ERR_ARCH = -4,      /* current device is not gfx950 */
+    QMOE_ERR_HIP = -5        /* a HIP runtime call or kernel launch failed */
+};
+
+/* Layer dimensions. group must be 64. shared_inter = 0 means the layer has no shared expert. */
+typedef struct {
+    int32_t hidden;        /* H */
+    int32_t n_experts;     /* E */
+    int32_t top_k;         /* k */
+    int32_t inter;         /* I, routed expert width */
+    int32_t shared_inter;  /* Is, shared expert width (0: none) */
+    int32_t group;         /* 64 */
+} qmoe_dims;
+
+/* Router weights of one layer [TF-struct] router listing, [TF-mem] 8-bit projection. */
+typedef struct {
+    const uint8_t *codes;            /* [E, H] uint8 codes */
+    const uint16_t *scales;          /* [E, H/64] bf16 */
+    const uint16_t *biases;          /* [E, H/64] bf16 */
+    const float *router_scale;       /* [H] fp32 multiplier after the norm, or NULL for all ones */
+    const float *per_expert_scale;   /* [E] fp32, multiplies the softmax weights */
+    const float *logit_bias;         /* [E] fp32 added to the logits before top-k, or NULL */
+} qmoe_router;
+
+/* One layer: router + packed expert store (qmoe_pack_expert layout) + optional shared block. */
+typedef struct {
+    qmoe_dims d;
+    qmoe_router r;
+    const void *experts;     /* base of E blocks, block e at experts + e * expert_stride */
+    size_t expert_stride;    /* >= qmoe_expert_stride(&d, d.inter), multiple of 256 */
+    const void *shared;      /* one block packed with inter = shared_inter, or NULL */
+} qmoe_layer;
+
+/* ---------------------------------------------------------------- host-only queries */
+
+/* Library ABI version (major*10000 + minor*100 + patch). */
+int qmoe_version(void);
+
+/* Thread-local text of the last error (empty string if none). Never NULL. */
+const char *qmoe_last_error(void);
+
+/* Bytes of one packed expert block of width `inter` (4 KiB-rounded), 0 on invalid dims.
+ * [SW-mem]: experts are fixed-stride blocks, so expert e starts at base + e * stride. */
+size_t qmoe_expert_stride(const qmoe_dims *d, int32_t inter);
+
+/* Workspace bytes needed by qmoe_router_topk / qmoe_bucket / qmoe_expert_ffn /
+ * qmoe_layer_forward for calls with up to max_tokens tokens (0 on invalid dims).  The
+ * workspace is device memory owned by the caller.  Its first 128 KiB hold completion counters
+ * that must be zero when a call starts: initialise a new workspace once with
+ * qmoe_workspace_init (or a zero fill); every call returns the counters it used to zero
+ * before it completes, so later calls need no re-initialisation.  Calls that share one
+ * workspace must be ordered (same stream, or synchronised). */
+size_t qmoe_workspace_bytes(const qmoe_dims *d, int32_t max_tokens);
+
+/* Zero the counter area (the first 128 KiB, or all of a smaller workspace) with a kernel
+ * on `stream` (graph-capturable). */
+int qmoe_workspace_init(void *ws, size_t ws_bytes, qmoe_stream_t stream);
+
+/* ---------------------------------------------------------------- expert store */
+
+/* Copy one expert from the canonical int4 arrays (gate/up [inter, H], down [H, inter], see the
+ * format above; all device pointers) into `dst_block` (device, qmoe_expert_stride bytes,
+ * 256-byte aligned) in the store's tiled order.  Layout change only: every code, scale and
+ * bias bit is copied, nothing is dequantised or requantised [TF-inst].  `inter` is d->inter
+ * for a routed expert or d->shared_inter for the shared block. */
+int qmoe_pack_expert(const qmoe_dims *d, int32_t inter,
+                     const uint8_t *gate_q, const uint16_t *gate_s, const uint16_t *gate_b,
+                     const uint8_t *up_q, const uint16_t *up_s, const uint16_t *up_b,
+                     const uint8_t *down_q, const uint16_t *down_s, const uint16_t *down_b,
+                     void *dst_block, qmoe_stream_t stream);
+
+/* Exact inverse of qmoe_pack_expert: canonical arrays back from a packed block. */
+int qmoe_unpack_expert(const qmoe_dims *d, int32_t inter, const void *src_block,
+                       uint8_t *gate_q, uint16_t *gate_s, uint16_t *gate_b,
+                       uint8_t *up_q, uint16_t *up_s, uint16_t *up_b,
+                       uint8_t *down_q, uint16_t *down_s, uint16_t *down_b,
+                       qmoe_stream_t stream);
+
+/* ---------------------------------------------------------------- the four steps */
+
+/* Step 1, router [TF-struct] router listing.  For each token t of x [T, H] (bf16):
+ *   u = x / sqrt(mean(x^2) + 1e-6) * router_scale / sqrt(H)   (fp32)
+ *   logit_e = sum_h (s*q+b)[e,h] * u_h + logit_bias_e          (fp32 accumulate)
+ *   topk_idx[t, :] = the k largest logits, descending; equal logits -> lower expert index
+ *   topk_w[t, j] = softmax over the k kept logits, times per_expert_scale[topk_idx[t, j]]
+ * Outputs: topk_idx int32 [T, k], topk_w fp32 [T, k], logits fp32 [T, E] (optional, may be
+ * NULL).  ws: device workspace of qmoe_workspace_bytes(d, T) bytes. */
+int qmoe_router_topk(const qmoe_dims *d, const qmoe_router *r, const uint16_t *x, int32_t T,
+                     int32_t *topk_idx, float *topk_w, float *logits_or_null,
+                     void *ws, size_t ws_bytes, qmoe_stream_t stream);
+
+/* Step 2, bucketing: one expert read serves every row routed to it [TF-struct] (chunked
+ * prefill).  Groups the T*k assignments (flat id f = t*k + j, expert topk_idx[f]) by expert:
+ *   counts [E]      rows per expert
+ *   offsets [E+1]   exclusive prefix sum of counts (offsets[E] = T*k)
+ *   sorted [T*k]    flat ids grouped by ascending expert, ascending flat id within an expert
+ *   active [E]      the experts with a non-zero count, ascending (first *n_active entries valid)
+ *   n_active [1]    number of active experts
+ * Deterministic (bit-identical across runs).  Expert ids must lie in [0, E); behaviour is
+ * undefined otherwise.  With T = 0 the outputs are still written (all counts zero) and
+ * topk_idx may be NULL.  ws is not used and may be NULL. */
+int qmoe_bucket(const qmoe_dims *d, const int32_t *topk_idx, int32_t T,
+                int32_t *counts, int32_t *offsets, int32_t *sorted, int32_t *active,
+                int32_t *n_active, void *ws, size_t ws_bytes, qmoe_stream_t stream);
+
+/* Step 3, expert FFN over the bucketed assignments [TF-struct], weights in the packed store
+ * (int4 codes decoded in registers, never written out [TF-mem]).  For every assignment f
+ * (flat id, expert e = topk_idx[f], token t = f / k):
+ *   y[f, :] = down_e( silu(gate_e(x_t)) * up_e(x_t) )       fp32 [T*k, H]
+ * and, if the layer has a shared block and y_shared_or_null != NULL, for every token
+ *   y_shared[t, :] = shared FFN of x_t                        fp32 [T, H]
+ * offsets/sorted/active/n_active come from qmoe_bucket (device pointers). */
+int qmoe_expert_ffn(const qmoe_layer *L, const uint16_t *x, int32_t T,
+                    const int32_t *offsets, const int32_t *sorted, const int32_t *active,
+                    const int32_t *n_active, float *y, float *y_shared_or_null,
+                    void *ws, size_t ws_bytes, qmoe_stream_t stream);
+
+/* Step 4, combine (cb2 of [TF-struct] up to the residual add):
+ *   out[t, :] = bf16_rne( x[t] + y_shared[t] + sum_j topk_w[t, j] * y[t*k + j] )
+ * summed in fp32 in the order j = 0..k-1, then the shared branch, then the residual.
+ * y_shared may be NULL (no shared expert); out_f32_or_null receives the fp32 sum. */
+int qmoe_combine(const qmoe_dims *d, const uint16_t *x, const float *y, const float *topk_w,
+                 const float *y_shared_or_null, int32_t T, uint16_t *out,
+                 float *out_f32_or_null, qmoe_stream_t stream);
+
+/* The whole layer (steps 1-4) as three kernels with no host round trip:
+ *   kernel 1: router logits, then (last workgroup) top-k, softmax and bucketing, while other
+ *             workgroups of the same launch run the shared expert's gate/up projection;
+ *   kernel 2: routed gate/up projection + SwiGLU over the buckets;
+ *   kernel 3: routed and shared down projection; the last workgroup of each output row tile
+ *             adds the router-weighted routed rows, the shared row and the residual.
+ * out: bf16 [T, H]; out_f32_or_null: fp32 [T, H]; topk_idx_or_null / topk_w_or_null receive
+ * the routing ([T, k]).  Results equal qmoe_router_topk -> qmoe_bucket -> qmoe_expert_ffn ->
+ * qmoe_combine up to fp32 summation order.  T may exceed 128; callers that follow the pages'
+ * chunked prefill pass chunks of at most 128 tokens. */
+int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16_t *out,
+                       float *out_f32_or_null, int32_t *topk_idx_or_null,
+                       float *topk_w_or_null, void *ws, size_t ws_bytes,
+                       qmoe_stream_t stream);
+
+/* ---------------------------------------------------------------- timing helpers */
+
+/* Thin wrappers over HIP events so that callers can time individual kernels of
+ * qmoe_layer_forward on the stream they run on.  qmoe_set_profile_events(start, stop)
+ * makes subsequent qmoe_layer_forward calls on this thread record `start` right before and
+ * `stop` right after their routed gate/up kernel (pass NULL, NULL to stop).  Events are
+ * created with qmoe_event_create and read with qmoe_event_elapsed_ms (which synchronises on
+ * `stop`). */
+int qmoe_event_create(void **event_out);
+int qmoe_event_destroy(void *event);
+int qmoe_event_record(void *event, qmoe_stream_t stream);
+int qmoe_event_elapsed_ms(void *start, void *stop, float *ms_out);
+int qmoe_set_profile_events(void *start, void *stop);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMOE_H */

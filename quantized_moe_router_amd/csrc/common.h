@@ -1,0 +1,74 @@
+// Device helpers shared by the qmoe kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define QMOE_DEV __device__ __forceinline__
+
+typedef __bf16 qmoe_bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t qmoe_u32x4 __attribute__((ext_vector_type(4)));
+
+namespace qmoe {
+
+constexpr int WAVE = 64;
+constexpr int GROUP = 64;          // quantisation group (weights per scale/bias pair)
+constexpr int KSTEP_BYTES = 1152;  // one k-step of a 32-row tile: 1024 B codes + 128 B scale|bias
+constexpr int TILE_ROWS = 32;      // rows per store tile
+constexpr int MAX_TOPK = 32;
+constexpr int MAX_EXPERTS = 1024;
+constexpr int CHUNK_TOKENS = 128;  // layer_forward processes at most this many tokens per pass
+
+// ---------------------------------------------------------------- bf16 <-> fp32
+QMOE_DEV float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
+QMOE_DEV float bf16hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+QMOE_DEV float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+// round to nearest even (finite inputs)
+QMOE_DEV uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// D = a.lo*b.lo + a.hi*b.hi + c  (bf16 pairs, fp32 accumulate)
+QMOE_DEV float dot2bf(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(qmoe_bf16x2, a),
+                                         __builtin_bit_cast(qmoe_bf16x2, b), c, false);
+}
+
+// ---------------------------------------------------------------- int4 decode
+// A packed 32-bit word of the store holds 8 codes of consecutive elements e0..e7 with
+// element 2i in nibble i and element 2i+1 in nibble i+4 (i = 0..3).  OR-ing a nibble into
+// the mantissa of bf16 128.0 (0x4300) gives the exact bf16 value 128 + q, so one AND-OR
+// turns two codes into a bf16 pair (128+q_2i, 128+q_2i+1) aligned with the activation pair
+// (x_2i, x_2i+1).  The dot products therefore sum (128 + q) * x; callers subtract
+// 128 * sum(x) through the group bias term.
+constexpr uint32_t MAGIC2 = 0x43004300u;
+QMOE_DEV uint32_t nib_pair(uint32_t w, int i) { return ((w >> (4 * i)) & 0x000F000Fu) | MAGIC2; }
+
+// sum over 32 elements of (128 + q_j) * x_j; w: 4 packed words, x: 16 bf16 pairs
+QMOE_DEV float dot32_q4_bf16(const uint32_t w[4], const uint32_t x[16]) {
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    a0 = dot2bf(nib_pair(w[d], 0), x[4 * d + 0], a0);
+    a1 = dot2bf(nib_pair(w[d], 1), x[4 * d + 1], a1);
+    a0 = dot2bf(nib_pair(w[d], 2), x[4 * d + 2], a0);
+    a1 = dot2bf(nib_pair(w[d], 3), x[4 * d + 3], a1);
+  }
+  return a0 + a1;
+}
+
+// ---------------------------------------------------------------- wave reductions
+QMOE_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  return v;
+}
+QMOE_DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  return v;
+}
+
+QMOE_DEV float silu(float z) { return z / (1.0f + expf(-z)); }
+
+}  // namespace qmoe

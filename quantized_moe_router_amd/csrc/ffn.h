@@ -1,0 +1,329 @@
+// Expert FFN kernels over the packed store: SwiGLU gate/up projection and down projection
+// with int4 codes decoded in registers (never written out), and the router-weighted combine
+// with the shared expert and the residual (TurboFieldfare post, sections "TurboFieldfare의
+// 전문가 스트리밍 구조" and "TurboFieldfare가 메모리를 아끼는 방식").
+//
+// Math of one k-step (64 inputs = one group with scale s and bias b) of one row:
+//   sum_j (s q_j + b) x_j = s * sum_j (128 + q_j) x_j + (b - 128 s) * sum_j x_j
+// The first sum comes from bf16 dot products of exact (128 + q) operands with exact bf16
+// activations; the activation group sums are staged once per token.  Accumulation is fp32.
+// The down projection's input h is fp32; it is carried as hi + lo bf16 parts
+// (hi = bf16(h), lo = bf16(h - hi)), so its products keep ~16 significant bits.
+#pragma once
+#include "common.h"
+#include "store.h"
+
+namespace qmoe {
+
+struct FfnArgs {
+  const uint8_t *experts;     // routed blocks
+  size_t stride;
+  const uint8_t *shared;      // shared block or null
+  int H, I, Is, k, T;
+  const uint16_t *x;          // [T, H] bf16
+  const int32_t *offsets, *sorted, *active, *n_active;
+  int n_slots;                // routed slots in the grid (>= n_active)
+  uint16_t *hr_hi, *hr_lo;    // routed h [T*k, I] in bucket order
+  uint16_t *hs_hi, *hs_lo;    // shared h [T, Is]
+  float *y;                   // routed y [T*k, H] by flat id
+  float *y_sh;                // shared y [T, H] or null
+  // fused combine (down kernel of the layer path); out == null -> no combine
+  const float *topk_w;        // [T, k]
+  uint16_t *out;              // [T, H] bf16
+  float *out_f32;             // [T, H] or null
+  unsigned *cnt_tile;         // [H/32] completion counters
+  int gu_shared_only;         // gate/up launch covers only the shared expert's tiles
+};
+
+template <int MB>
+struct TokList {
+  int tok[MB];   // token index of each row of the block
+  int hpos[MB];  // row of h (and, for the down kernel, the source row of h)
+  int ypos[MB];  // row of y to write (down kernel)
+};
+
+// Resolve the rows handled by a workgroup of slot `slot` (routed) or the shared slot.
+struct SlotRows {
+  const uint8_t *blk;
+  int m;       // number of rows
+  int beg;     // first bucket position (routed) / 0 (shared)
+  bool shared;
+};
+
+QMOE_DEV bool slot_rows(const FfnArgs &a, int slot, bool shared, SlotRows &r) {
+  if (shared) {
+    r.blk = a.shared; r.m = a.T; r.beg = 0; r.shared = true;
+    return true;
+  }
+  if (slot >= *a.n_active) return false;
+  const int e = a.active[slot];
+  r.blk = a.experts + (size_t)e * a.stride;
+  r.beg = a.offsets[e];
+  r.m = a.offsets[e + 1] - r.beg;
+  r.shared = false;
+  return r.m > 0;
+}
+
+// ---------------------------------------------------------------- gate/up tile
+// LDS: x [MB][H] bf16, xs [MB][H/32] fp32, red [W][MB][32] fp32
+template <int W, int MB>
+QMOE_DEV size_t gu_lds_bytes(int H) {
+  return (size_t)MB * H * 2 + (size_t)MB * (H / 32) * 4 + (size_t)W * MB * 32 * 4;
+}
+
+template <int W, int MB>
+QMOE_DEV void gu_tile(const FfnArgs &a, const SlotRows &sr, int tile, char *smem) {
+  const int H = a.H;
+  const int I = sr.shared ? a.Is : a.I;
+  const int KS = H / GROUP;
+  const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
+  const int rr = lane % 32, half = lane / 32;
+  uint16_t *xl = (uint16_t *)smem;                              // [MB][H]
+  float *xs = (float *)(smem + (size_t)MB * H * 2);              // [MB][H/32]
+  float *red = xs + MB * (H / 32);                               // [W][MB][32]
+  const uint8_t *tbase = sr.blk + (size_t)tile * KS * KSTEP_BYTES;
+  const int ks0 = (KS * wv) / W, ks1 = (KS * (wv + 1)) / W;
+  for (int r0 = 0; r0 < sr.m; r0 += MB) {
+    const int mb = min(MB, sr.m - r0);
+    // stage activations and their 32-element sums
+    const int n8 = H / 8;
+    for (int c = tid; c < MB * n8; c += W * WAVE) {
+      const int i = c / n8, cc = c % n8;
+      if (i < mb) {
+        const int t = sr.shared ? (r0 + i) : (a.sorted[sr.beg + r0 + i] / a.k);
+        const qmoe_u32x4 v = *(const qmoe_u32x4 *)(a.x + (size_t)t * H + 8 * cc);
+        *(qmoe_u32x4 *)(xl + (size_t)i * H + 8 * cc) = v;
+        float p = bf16lo(v.x) + bf16hi(v.x) + bf16lo(v.y) + bf16hi(v.y) + bf16lo(v.z) +
+                  bf16hi(v.z) + bf16lo(v.w) + bf16hi(v.w);
+        p += __shfl_xor(p, 1, WAVE);
+        p += __shfl_xor(p, 2, WAVE);
+        if ((cc & 3) == 0) xs[i * (H / 32) + cc / 4] = p;
+      }
+    }
+    __syncthreads();
+    float acc[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) acc[i] = 0.f;
+    for (int ks = ks0; ks < ks1; ++ks) {
+      const uint8_t *kb = tbase + (size_t)ks * KSTEP_BYTES;
+      const qmoe_u32x4 cv = *(const qmoe_u32x4 *)(kb + lane * 16);
+      const uint32_t sb = *(const uint32_t *)(kb + 1024 + rr * 4);
+      const uint32_t w4[4] = {cv.x, cv.y, cv.z, cv.w};
+      const float s = bf16lo(sb), b = bf16hi(sb);
+      const float bb = fmaf(-128.f, s, b);
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        if (i < mb) {
+          const uint32_t *xp = (const uint32_t *)(xl + (size_t)i * H + ks * GROUP + half * 32);
+          uint32_t xv[16];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const qmoe_u32x4 t4 = *(const qmoe_u32x4 *)(xp + 4 * q);
+            xv[4 * q] = t4.x; xv[4 * q + 1] = t4.y; xv[4 * q + 2] = t4.z; xv[4 * q + 3] = t4.w;
+          }
+          const float d = dot32_q4_bf16(w4, xv);
+          acc[i] = fmaf(s, d, acc[i]);
+          acc[i] = fmaf(bb, xs[i * (H / 32) + ks * 2 + half], acc[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const float tot = acc[i] + __shfl_xor(acc[i], 32, WAVE);
+      if (half == 0) red[(wv * MB + i) * 32 + rr] = tot;
+    }
+    __syncthreads();
+    for (int o = tid; o < mb * 16; o += W * WAVE) {
+      const int i = o / 16, r = o % 16;
+      float g = 0.f, u = 0.f;
+      for (int w = 0; w < W; ++w) {
+        g += red[(w * MB + i) * 32 + r];
+        u += red[(w * MB + i) * 32 + 16 + r];
+      }
+      const float h = silu(g) * u;
+      const uint32_t hi = f32_to_bf16_bits(h);
+      const uint32_t lo = f32_to_bf16_bits(h - __uint_as_float(hi << 16));
+      const size_t row = sr.shared ? (size_t)(r0 + i) : (size_t)(sr.beg + r0 + i);
+      uint16_t *dh = sr.shared ? a.hs_hi : a.hr_hi;
+      uint16_t *dl = sr.shared ? a.hs_lo : a.hr_lo;
+      dh[row * I + 16 * tile + r] = (uint16_t)hi;
+      dl[row * I + 16 * tile + r] = (uint16_t)lo;
+    }
+    __syncthreads();
+  }
+}
+
+// grid.x = n_slots * (I/16) routed tiles, then Is/16 shared tiles (if a.shared)
+template <int W, int MB>
+__global__ void __launch_bounds__(W * WAVE) gu_kernel(FfnArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const int tiles_r = a.I / 16;
+  const int n_routed = a.gu_shared_only ? 0 : a.n_slots * tiles_r;
+  int bid = blockIdx.x;
+  SlotRows sr;
+  int tile;
+  if (bid < n_routed) {
+    if (!slot_rows(a, bid / tiles_r, false, sr)) return;
+    tile = bid % tiles_r;
+  } else {
+    slot_rows(a, 0, true, sr);
+    tile = bid - n_routed;
+  }
+  gu_tile<W, MB>(a, sr, tile, smem);
+}
+
+// ---------------------------------------------------------------- down tile
+// LDS: h hi [MB][K] bf16, h lo [MB][K] bf16, hsum [MB][K/32] fp32, red [W][MB][32] fp32
+template <int W, int MB>
+QMOE_DEV size_t d_lds_bytes(int K) {
+  return (size_t)MB * K * 4 + (size_t)MB * (K / 32) * 4 + (size_t)W * MB * 32 * 4;
+}
+
+template <int W, int MB>
+QMOE_DEV void d_tile(const FfnArgs &a, const SlotRows &sr, int tile, char *smem) {
+  const int H = a.H;
+  const int K = sr.shared ? a.Is : a.I;
+  const int KS = K / GROUP;
+  const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
+  const int rr = lane % 32, half = lane / 32;
+  uint16_t *hh = (uint16_t *)smem;                              // [MB][K]
+  uint16_t *hl = hh + (size_t)MB * K;                           // [MB][K]
+  float *hs = (float *)(hl + (size_t)MB * K);                   // [MB][K/32]
+  float *red = hs + MB * (K / 32);                              // [W][MB][32]
+  const BlockGeom geo = block_geom(H, K);
+  const uint8_t *tbase = sr.blk + geo.gu_bytes + (size_t)tile * KS * KSTEP_BYTES;
+  const int ks0 = (KS * wv) / W, ks1 = (KS * (wv + 1)) / W;
+  const uint16_t *src_hi = sr.shared ? a.hs_hi : a.hr_hi;
+  const uint16_t *src_lo = sr.shared ? a.hs_lo : a.hr_lo;
+  for (int r0 = 0; r0 < sr.m; r0 += MB) {
+    const int mb = min(MB, sr.m - r0);
+    const int n8 = K / 8;
+    for (int c = tid; c < MB * n8; c += W * WAVE) {
+      const int i = c / n8, cc = c % n8;
+      if (i < mb) {
+        const size_t row = (size_t)(sr.beg + r0 + i);
+        const qmoe_u32x4 vh = *(const qmoe_u32x4 *)(src_hi + row * K + 8 * cc);
+        const qmoe_u32x4 vl = *(const qmoe_u32x4 *)(src_lo + row * K + 8 * cc);
+        *(qmoe_u32x4 *)(hh + (size_t)i * K + 8 * cc) = vh;
+        *(qmoe_u32x4 *)(hl + (size_t)i * K + 8 * cc) = vl;
+        float p = (bf16lo(vh.x) + bf16lo(vl.x)) + (bf16hi(vh.x) + bf16hi(vl.x)) +
+                  (bf16lo(vh.y) + bf16lo(vl.y)) + (bf16hi(vh.y) + bf16hi(vl.y)) +
+                  (bf16lo(vh.z) + bf16lo(vl.z)) + (bf16hi(vh.z) + bf16hi(vl.z)) +
+                  (bf16lo(vh.w) + bf16lo(vl.w)) + (bf16hi(vh.w) + bf16hi(vl.w));
+        p += __shfl_xor(p, 1, WAVE);
+        p += __shfl_xor(p, 2, WAVE);
+        if ((cc & 3) == 0) hs[i * (K / 32) + cc / 4] = p;
+      }
+    }
+    __syncthreads();
+    float acc[MB];
+#pragma unroll
+    for (int i = 0; i < MB; ++i) acc[i] = 0.f;
+    for (int ks = ks0; ks < ks1; ++ks) {
+      const uint8_t *kb = tbase + (size_t)ks * KSTEP_BYTES;
+      const qmoe_u32x4 cv = *(const qmoe_u32x4 *)(kb + lane * 16);
+      const uint32_t sb = *(const uint32_t *)(kb + 1024 + rr * 4);
+      const uint32_t w4[4] = {cv.x, cv.y, cv.z, cv.w};
+      const float s = bf16lo(sb), b = bf16hi(sb);
+      const float bb = fmaf(-128.f, s, b);
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        if (i < mb) {
+          const size_t off = (size_t)i * K + ks * GROUP + half * 32;
+          uint32_t xh[16], xlo[16];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const qmoe_u32x4 th = *(const qmoe_u32x4 *)((const uint32_t *)(hh + off) + 4 * q);
+            const qmoe_u32x4 tl = *(const qmoe_u32x4 *)((const uint32_t *)(hl + off) + 4 * q);
+            xh[4 * q] = th.x; xh[4 * q + 1] = th.y; xh[4 * q + 2] = th.z; xh[4 * q + 3] = th.w;
+            xlo[4 * q] = tl.x; xlo[4 * q + 1] = tl.y; xlo[4 * q + 2] = tl.z; xlo[4 * q + 3] = tl.w;
+          }
+          const float d = dot32_q4_bf16(w4, xh) + dot32_q4_bf16(w4, xlo);
+          acc[i] = fmaf(s, d, acc[i]);
+          acc[i] = fmaf(bb, hs[i * (K / 32) + ks * 2 + half], acc[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const float tot = acc[i] + __shfl_xor(acc[i], 32, WAVE);
+      if (half == 0) red[(wv * MB + i) * 32 + rr] = tot;
+    }
+    __syncthreads();
+    for (int o = tid; o < mb * 32; o += W * WAVE) {
+      const int i = o / 32, r = o % 32;
+      float yv = 0.f;
+      for (int w = 0; w < W; ++w) yv += red[(w * MB + i) * 32 + r];
+      size_t yrow;
+      float *dst;
+      if (sr.shared) { yrow = (size_t)(r0 + i); dst = a.y_sh; }
+      else           { yrow = (size_t)a.sorted[sr.beg + r0 + i]; dst = a.y; }
+      dst[yrow * H + 32 * tile + r] = yv;
+    }
+    __syncthreads();
+  }
+}
+
+// combine of one 32-row tile for every token (fused into the down kernel of the layer path)
+QMOE_DEV void combine_tile(const FfnArgs &a, int tile) {
+  const int H = a.H;
+  for (int o = threadIdx.x; o < a.T * 32; o += blockDim.x) {
+    const int t = o / 32, col = 32 * tile + o % 32;
+    float acc = 0.f;
+    for (int j = 0; j < a.k; ++j)
+      acc = fmaf(a.topk_w[(size_t)t * a.k + j], a.y[((size_t)t * a.k + j) * H + col], acc);
+    if (a.y_sh) acc += a.y_sh[(size_t)t * H + col];
+    acc += bf16_to_f32(a.x[(size_t)t * H + col]);
+    a.out[(size_t)t * H + col] = (uint16_t)f32_to_bf16_bits(acc);
+    if (a.out_f32) a.out_f32[(size_t)t * H + col] = acc;
+  }
+}
+
+// grid = (H/32 tiles, n_slots routed slots + 1 shared slot if a.shared && a.y_sh)
+template <int W, int MB>
+__global__ void __launch_bounds__(W * WAVE) d_kernel(FfnArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const int tile = blockIdx.x;
+  const int slot = blockIdx.y;
+  SlotRows sr;
+  const bool shared = slot >= a.n_slots;
+  if (slot_rows(a, slot, shared, sr)) d_tile<W, MB>(a, sr, tile, smem);
+  if (a.out == nullptr) return;
+  // the last workgroup of this row tile adds routed rows, shared row and residual
+  __shared__ int last;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) last = (atomicAdd(&a.cnt_tile[tile], 1u) == gridDim.y - 1);
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  combine_tile(a, tile);
+  if (threadIdx.x == 0) a.cnt_tile[tile] = 0u;
+}
+
+// ---------------------------------------------------------------- standalone combine
+// out[t, :] = bf16( sum_j w[t,j] y[t*k+j, :] + y_sh[t, :] + x[t, :] ), fp32, j ascending
+__global__ void __launch_bounds__(256) combine_kernel(const uint16_t *x, const float *y,
+                                                      const float *w, const float *y_sh,
+                                                      int T, int H, int k, uint16_t *out,
+                                                      float *out_f32) {
+  const size_t n = (size_t)T * H;
+  for (size_t o = (size_t)blockIdx.x * blockDim.x + threadIdx.x; o < n;
+       o += (size_t)gridDim.x * blockDim.x) {
+    const size_t t = o / H, col = o % H;
+    float acc = 0.f;
+    for (int j = 0; j < k; ++j) acc = fmaf(w[t * k + j], y[(t * k + j) * H + col], acc);
+    if (y_sh) acc += y_sh[o];
+    acc += bf16_to_f32(x[o]);
+    out[o] = (uint16_t)f32_to_bf16_bits(acc);
+    if (out_f32) out_f32[o] = acc;
+  }
+}
+
+__global__ void zero_kernel(uint32_t *p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0u;
+}
+
+}  // namespace qmoe

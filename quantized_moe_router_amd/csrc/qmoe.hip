@@ -1,0 +1,519 @@
+// Host side of the qmoe C ABI: argument validation, workspace layout and kernel launches.
+// Every entry point validates its arguments on the host before touching the device, returns
+// a status code and never lets a C++ exception cross the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "qmoe.h"
+#include "common.h"
+#include "store.h"
+#include "router.h"
+#include "ffn.h"
+
+using namespace qmoe;
+
+namespace {
+
+constexpr int VERSION = 100;               // 0.1.0
+constexpr size_t COUNTER_BYTES = 128 * 1024;
+constexpr int GU_W = 4, GU_MB = 8;
+constexpr int D_W = 4, D_MB = 8;
+constexpr int MAX_T = 65536;
+
+thread_local std::string g_err;
+thread_local hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return QMOE_OK;
+}
+
+#define QMOE_HIP(call)                                                                  \
+  do {                                                                                  \
+    hipError_t e_ = (call);                                                             \
+    if (e_ != hipSuccess) return fail(QMOE_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+#define QMOE_LAUNCHED()                                                                 \
+  do {                                                                                  \
+    hipError_t e_ = hipGetLastError();                                                  \
+    if (e_ != hipSuccess) return fail(QMOE_ERR_HIP, "kernel launch: %s", hipGetErrorString(e_)); \
+  } while (0)
+
+inline bool mult64(int v) { return v > 0 && v % 64 == 0; }
+
+int check_dims(const qmoe_dims *d) {
+  if (!d) return fail(QMOE_ERR_ARG, "dims is NULL");
+  if (d->group != GROUP) return fail(QMOE_ERR_SHAPE, "group must be 64 (got %d)", d->group);
+  if (!mult64(d->hidden) || d->hidden > 8192)
+    return fail(QMOE_ERR_SHAPE, "hidden must be a positive multiple of 64 <= 8192 (got %d)", d->hidden);
+  if (!mult64(d->inter) || d->inter > 4096)
+    return fail(QMOE_ERR_SHAPE, "inter must be a positive multiple of 64 <= 4096 (got %d)", d->inter);
+  if (d->shared_inter != 0 && (!mult64(d->shared_inter) || d->shared_inter > 4096))
+    return fail(QMOE_ERR_SHAPE, "shared_inter must be 0 or a multiple of 64 <= 4096 (got %d)",
+                d->shared_inter);
+  if (d->n_experts < 1 || d->n_experts > MAX_EXPERTS)
+    return fail(QMOE_ERR_SHAPE, "n_experts must be in [1, %d] (got %d)", MAX_EXPERTS, d->n_experts);
+  if (d->top_k < 1 || d->top_k > MAX_TOPK || d->top_k > d->n_experts)
+    return fail(QMOE_ERR_SHAPE, "top_k must be in [1, min(n_experts, 32)] (got %d)", d->top_k);
+  return QMOE_OK;
+}
+
+int check_T(int32_t T) {
+  if (T < 0 || T > MAX_T) return fail(QMOE_ERR_SHAPE, "T must be in [0, %d] (got %d)", MAX_T, T);
+  return QMOE_OK;
+}
+
+inline bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Current device must be gfx950.  Cached per device ordinal.
+int check_arch() {
+  static std::mutex mu;
+  static int state[64] = {0};  // 0 unknown, 1 ok, 2 bad
+  int dev = 0;
+  QMOE_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return fail(QMOE_ERR_ARCH, "device ordinal %d out of range", dev);
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    if (state[dev] == 0) {
+      hipDeviceProp_t prop;
+      hipError_t e = hipGetDeviceProperties(&prop, dev);
+      if (e != hipSuccess) return fail(QMOE_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+      state[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+      if (state[dev] == 2)
+        return fail(QMOE_ERR_ARCH, "device %d is %s, this library is built for gfx950", dev,
+                    prop.gcnArchName);
+    }
+  }
+  if (state[dev] != 1) return fail(QMOE_ERR_ARCH, "device %d is not gfx950", dev);
+  return QMOE_OK;
+}
+
+inline size_t al(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct WsLayout {
+  size_t cnt, logits, tidx, tw, counts, offsets, sorted, active, nact;
+  size_t hr_hi, hr_lo, hs_hi, hs_lo, y, ysh, total;
+};
+
+WsLayout ws_layout(const qmoe_dims *d, int Tmax) {
+  WsLayout w;
+  const size_t T = (size_t)Tmax, k = d->top_k, E = d->n_experts, H = d->hidden;
+  const size_t Tc = std::min<size_t>(T, CHUNK_TOKENS);
+  size_t o = 0;
+  w.cnt = o; o += COUNTER_BYTES;
+  w.logits = o; o += al(T * E * 4);
+  w.tidx = o; o += al(T * k * 4);
+  w.tw = o; o += al(T * k * 4);
+  w.counts = o; o += al(E * 4);
+  w.offsets = o; o += al((E + 1) * 4);
+  w.sorted = o; o += al(T * k * 4);
+  w.active = o; o += al(E * 4);
+  w.nact = o; o += al(4);
+  w.hr_hi = o; o += al(T * k * d->inter * 2);
+  w.hr_lo = o; o += al(T * k * d->inter * 2);
+  w.hs_hi = o; o += al(T * (size_t)d->shared_inter * 2);
+  w.hs_lo = o; o += al(T * (size_t)d->shared_inter * 2);
+  w.y = o; o += al(Tc * k * H * 4);
+  w.ysh = o; o += al(Tc * H * 4);
+  w.total = o;
+  return w;
+}
+
+template <class T>
+inline T *at(void *ws, size_t off) { return (T *)((char *)ws + off); }
+
+int check_ws(const qmoe_dims *d, int T, void *ws, size_t ws_bytes) {
+  if (!ws) return fail(QMOE_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(QMOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const size_t need = ws_layout(d, T).total;
+  if (ws_bytes < need)
+    return fail(QMOE_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed for T=%d", ws_bytes, need, T);
+  return QMOE_OK;
+}
+
+int check_layer(const qmoe_layer *L) {
+  if (!L) return fail(QMOE_ERR_ARG, "layer is NULL");
+  int rc = check_dims(&L->d);
+  if (rc) return rc;
+  if (!L->r.codes || !L->r.scales || !L->r.biases || !L->r.per_expert_scale)
+    return fail(QMOE_ERR_ARG, "router codes/scales/biases/per_expert_scale must not be NULL");
+  if (!L->experts) return fail(QMOE_ERR_ARG, "expert store is NULL");
+  if (!aligned(L->experts, 256) || L->expert_stride % 256)
+    return fail(QMOE_ERR_ARG, "expert store base and stride must be 256-byte aligned");
+  if (L->expert_stride < block_stride_bytes(L->d.hidden, L->d.inter))
+    return fail(QMOE_ERR_ARG, "expert_stride %zu smaller than the packed block (%zu)",
+                L->expert_stride, block_stride_bytes(L->d.hidden, L->d.inter));
+  if (L->shared && L->d.shared_inter == 0)
+    return fail(QMOE_ERR_ARG, "shared block given but shared_inter is 0");
+  if (L->shared && !aligned(L->shared, 256))
+    return fail(QMOE_ERR_ARG, "shared block must be 256-byte aligned");
+  return QMOE_OK;
+}
+
+template <class K>
+int set_lds(K kernel, size_t bytes) {
+  if (bytes > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void *)kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e != hipSuccess) return fail(QMOE_ERR_HIP, "hipFuncSetAttribute(lds=%zu): %s", bytes,
+                                     hipGetErrorString(e));
+  }
+  return QMOE_OK;
+}
+
+size_t router_smem(const qmoe_dims *d) {
+  return std::max(router_lds_bytes(d->hidden), (size_t)(d->n_experts + 1 + 64) * 4);
+}
+
+RouterArgs make_router_args(const qmoe_dims *d, const qmoe_router *r, const uint16_t *x, int T,
+                            float *logits, int32_t *idx, float *w, void *ws) {
+  RouterArgs a;
+  memset(&a, 0, sizeof a);
+  a.x = x; a.rq = r->codes; a.rs = r->scales; a.rb = r->biases;
+  a.rscale = r->router_scale; a.pes = r->per_expert_scale; a.lbias = r->logit_bias;
+  a.T = T; a.H = d->hidden; a.E = d->n_experts; a.k = d->top_k;
+  a.inv_sqrt_h = (float)(1.0 / std::sqrt((double)d->hidden));
+  a.logits = logits; a.topk_idx = idx; a.topk_w = w;
+  const WsLayout wl = ws_layout(d, T);
+  a.cnt_all = at<unsigned>(ws, wl.cnt);
+  a.cnt_tb = at<unsigned>(ws, wl.cnt) + 64;
+  a.n_tb = (T + ROUTER_TB - 1) / ROUTER_TB;
+  a.n_eb = (d->n_experts + ROUTER_EPB - 1) / ROUTER_EPB;
+  return a;
+}
+
+int launch_router(const RouterArgs &a, size_t smem, hipStream_t s) {
+  int rc = set_lds(router_kernel, smem);
+  if (rc) return rc;
+  hipLaunchKernelGGL(router_kernel, dim3(a.n_tb * a.n_eb), dim3(ROUTER_THREADS), smem, s, a);
+  QMOE_LAUNCHED();
+  return QMOE_OK;
+}
+
+// layer path: router workgroups followed by shared gate/up workgroups in one launch
+__global__ void __launch_bounds__(ROUTER_THREADS) router_shared_kernel(RouterArgs ra, FfnArgs fa,
+                                                                       int n_router) {
+  extern __shared__ __align__(16) char smem[];
+  if ((int)blockIdx.x < n_router) {
+    const int tb = blockIdx.x / ra.n_eb, eb = blockIdx.x % ra.n_eb;
+    router_logits_block(ra, tb, eb, smem);
+    router_finish(ra, tb, smem);
+  } else {
+    SlotRows sr;
+    slot_rows(fa, 0, true, sr);
+    gu_tile<GU_W, GU_MB>(fa, sr, blockIdx.x - n_router, smem);
+  }
+}
+static_assert(GU_W * WAVE == ROUTER_THREADS, "fused router/shared kernel uses one block size");
+
+size_t gu_smem(int H) {
+  return (size_t)GU_MB * H * 2 + (size_t)GU_MB * (H / 32) * 4 + (size_t)GU_W * GU_MB * 32 * 4;
+}
+size_t d_smem(int K) {
+  return (size_t)D_MB * K * 4 + (size_t)D_MB * (K / 32) * 4 + (size_t)D_W * D_MB * 32 * 4;
+}
+
+}  // namespace
+
+// ====================================================================== exported entry points
+extern "C" {
+
+int qmoe_version(void) { return VERSION; }
+
+const char *qmoe_last_error(void) { return g_err.c_str(); }
+
+size_t qmoe_expert_stride(const qmoe_dims *d, int32_t inter) {
+  if (check_dims(d)) return 0;
+  if (!mult64(inter) || inter > 4096) {
+    fail(QMOE_ERR_SHAPE, "inter must be a positive multiple of 64 <= 4096 (got %d)", inter);
+    return 0;
+  }
+  return block_stride_bytes(d->hidden, inter);
+}
+
+size_t qmoe_workspace_bytes(const qmoe_dims *d, int32_t max_tokens) {
+  if (check_dims(d) || check_T(max_tokens)) return 0;
+  return ws_layout(d, std::max(max_tokens, 1)).total;
+}
+
+int qmoe_workspace_init(void *ws, size_t ws_bytes, qmoe_stream_t stream) {
+  if (!ws) return fail(QMOE_ERR_WORKSPACE, "workspace is NULL");
+  if (!aligned(ws, 256)) return fail(QMOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  int rc = check_arch();
+  if (rc) return rc;
+  const size_t n = std::min(ws_bytes, COUNTER_BYTES) / 4;
+  if (n == 0) return ok();
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     (hipStream_t)stream, (uint32_t *)ws, n);
+  QMOE_LAUNCHED();
+  return ok();
+}
+
+int qmoe_pack_expert(const qmoe_dims *d, int32_t inter, const uint8_t *gate_q,
+                     const uint16_t *gate_s, const uint16_t *gate_b, const uint8_t *up_q,
+                     const uint16_t *up_s, const uint16_t *up_b, const uint8_t *down_q,
+                     const uint16_t *down_s, const uint16_t *down_b, void *dst_block,
+                     qmoe_stream_t stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (!mult64(inter) || inter > 4096)
+    return fail(QMOE_ERR_SHAPE, "inter must be a positive multiple of 64 <= 4096 (got %d)", inter);
+  if (!gate_q || !gate_s || !gate_b || !up_q || !up_s || !up_b || !down_q || !down_s || !down_b ||
+      !dst_block)
+    return fail(QMOE_ERR_ARG, "pack_expert: NULL pointer");
+  if (!aligned(dst_block, 256)) return fail(QMOE_ERR_ARG, "dst_block must be 256-byte aligned");
+  if ((rc = check_arch())) return rc;
+  CanonExpert c{gate_q, up_q, down_q, gate_s, gate_b, up_s, up_b, down_s, down_b};
+  const BlockGeom g = block_geom(d->hidden, inter);
+  const long n = (long)(g.gu_tiles * g.gu_ks + g.d_tiles * g.d_ks) * 64;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     (hipStream_t)stream, c, d->hidden, inter, (uint8_t *)dst_block);
+  QMOE_LAUNCHED();
+  return ok();
+}
+
+int qmoe_unpack_expert(const qmoe_dims *d, int32_t inter, const void *src_block, uint8_t *gate_q,
+                       uint16_t *gate_s, uint16_t *gate_b, uint8_t *up_q, uint16_t *up_s,
+                       uint16_t *up_b, uint8_t *down_q, uint16_t *down_s, uint16_t *down_b,
+                       qmoe_stream_t stream) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (!mult64(inter) || inter > 4096)
+    return fail(QMOE_ERR_SHAPE, "inter must be a positive multiple of 64 <= 4096 (got %d)", inter);
+  if (!gate_q || !gate_s || !gate_b || !up_q || !up_s || !up_b || !down_q || !down_s || !down_b ||
+      !src_block)
+    return fail(QMOE_ERR_ARG, "unpack_expert: NULL pointer");
+  if (!aligned(src_block, 256)) return fail(QMOE_ERR_ARG, "src_block must be 256-byte aligned");
+  if ((rc = check_arch())) return rc;
+  CanonExpertOut c{gate_q, up_q, down_q, gate_s, gate_b, up_s, up_b, down_s, down_b};
+  const BlockGeom g = block_geom(d->hidden, inter);
+  const long n = (long)(g.gu_tiles * g.gu_ks + g.d_tiles * g.d_ks) * 64;
+  hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+                     (hipStream_t)stream, (const uint8_t *)src_block, d->hidden, inter, c);
+  QMOE_LAUNCHED();
+  return ok();
+}
+
+int qmoe_router_topk(const qmoe_dims *d, const qmoe_router *r, const uint16_t *x, int32_t T,
+                     int32_t *topk_idx, float *topk_w, float *logits_or_null, void *ws,
+                     size_t ws_bytes, qmoe_stream_t stream) {
+  int rc = check_dims(d);
+  if (rc || (rc = check_T(T))) return rc;
+  if (!r || !r->codes || !r->scales || !r->biases || !r->per_expert_scale)
+    return fail(QMOE_ERR_ARG, "router codes/scales/biases/per_expert_scale must not be NULL");
+  if (T == 0) return ok();
+  if (!x || !topk_idx || !topk_w) return fail(QMOE_ERR_ARG, "x/topk_idx/topk_w must not be NULL");
+  if ((rc = check_ws(d, T, ws, ws_bytes))) return rc;
+  if ((rc = check_arch())) return rc;
+  const WsLayout wl = ws_layout(d, T);
+  float *logits = logits_or_null ? logits_or_null : at<float>(ws, wl.logits);
+  RouterArgs a = make_router_args(d, r, x, T, logits, topk_idx, topk_w, ws);
+  if ((rc = launch_router(a, router_smem(d), (hipStream_t)stream))) return rc;
+  return ok();
+}
+
+int qmoe_bucket(const qmoe_dims *d, const int32_t *topk_idx, int32_t T, int32_t *counts,
+                int32_t *offsets, int32_t *sorted, int32_t *active, int32_t *n_active, void *ws,
+                size_t ws_bytes, qmoe_stream_t stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int rc = check_dims(d);
+  if (rc || (rc = check_T(T))) return rc;
+  if ((!topk_idx && T > 0) || !counts || !offsets || !sorted || !active || !n_active)
+    return fail(QMOE_ERR_ARG, "bucket: NULL pointer");
+  if ((rc = check_arch())) return rc;
+  hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, topk_idx,
+                     T * d->top_k, d->n_experts, counts, offsets, sorted, active, n_active);
+  QMOE_LAUNCHED();
+  return ok();
+}
+
+static FfnArgs make_ffn_args(const qmoe_layer *L, const uint16_t *x, int T, const int32_t *offsets,
+                             const int32_t *sorted, const int32_t *active, const int32_t *n_active,
+                             float *y, float *y_sh, void *ws, int Tws) {
+  FfnArgs a;
+  memset(&a, 0, sizeof a);
+  const WsLayout wl = ws_layout(&L->d, Tws);
+  a.experts = (const uint8_t *)L->experts;
+  a.stride = L->expert_stride;
+  a.shared = (const uint8_t *)L->shared;
+  a.H = L->d.hidden; a.I = L->d.inter; a.Is = L->d.shared_inter; a.k = L->d.top_k; a.T = T;
+  a.x = x;
+  a.offsets = offsets; a.sorted = sorted; a.active = active; a.n_active = n_active;
+  a.n_slots = std::min(L->d.n_experts, T * L->d.top_k);
+  a.hr_hi = at<uint16_t>(ws, wl.hr_hi); a.hr_lo = at<uint16_t>(ws, wl.hr_lo);
+  a.hs_hi = at<uint16_t>(ws, wl.hs_hi); a.hs_lo = at<uint16_t>(ws, wl.hs_lo);
+  a.y = y; a.y_sh = y_sh;
+  a.cnt_tile = at<unsigned>(ws, wl.cnt) + 64 + 16384;
+  return a;
+}
+
+static int launch_gu(FfnArgs a, int mode, hipStream_t s) {
+  // mode 0: routed + shared tiles, 1: routed only
+  const int tiles_r = a.I / 16;
+  const bool sh = (mode == 0) && a.shared && a.y_sh;
+  const int n = a.n_slots * tiles_r + (sh ? a.Is / 16 : 0);
+  a.gu_shared_only = 0;
+  if (!sh) a.shared = nullptr;
+  if (n == 0) return QMOE_OK;
+  const size_t smem = gu_smem(a.H);
+  int rc = set_lds(gu_kernel<GU_W, GU_MB>, smem);
+  if (rc) return rc;
+  hipLaunchKernelGGL((gu_kernel<GU_W, GU_MB>), dim3(n), dim3(GU_W * WAVE), smem, s, a);
+  QMOE_LAUNCHED();
+  return QMOE_OK;
+}
+
+static int launch_d(FfnArgs a, bool with_shared, hipStream_t s) {
+  const int slots = a.n_slots + (with_shared ? 1 : 0);
+  const size_t smem = d_smem(std::max(a.I, with_shared ? a.Is : 0));
+  int rc = set_lds(d_kernel<D_W, D_MB>, smem);
+  if (rc) return rc;
+  hipLaunchKernelGGL((d_kernel<D_W, D_MB>), dim3(a.H / TILE_ROWS, slots), dim3(D_W * WAVE), smem,
+                     s, a);
+  QMOE_LAUNCHED();
+  return QMOE_OK;
+}
+
+int qmoe_expert_ffn(const qmoe_layer *L, const uint16_t *x, int32_t T, const int32_t *offsets,
+                    const int32_t *sorted, const int32_t *active, const int32_t *n_active,
+                    float *y, float *y_shared_or_null, void *ws, size_t ws_bytes,
+                    qmoe_stream_t stream) {
+  int rc = check_layer(L);
+  if (rc || (rc = check_T(T))) return rc;
+  if (y_shared_or_null && !L->shared)
+    return fail(QMOE_ERR_ARG, "y_shared given but the layer has no shared block");
+  if (T == 0) return ok();
+  if (!x || !offsets || !sorted || !active || !n_active || !y)
+    return fail(QMOE_ERR_ARG, "expert_ffn: NULL pointer");
+  if ((rc = check_ws(&L->d, T, ws, ws_bytes))) return rc;
+  if ((rc = check_arch())) return rc;
+  FfnArgs a = make_ffn_args(L, x, T, offsets, sorted, active, n_active, y, y_shared_or_null, ws, T);
+  hipStream_t s = (hipStream_t)stream;
+  if ((rc = launch_gu(a, 0, s))) return rc;
+  const bool sh = L->shared && y_shared_or_null;
+  if (!sh) a.shared = nullptr;
+  if ((rc = launch_d(a, sh, s))) return rc;
+  return ok();
+}
+
+int qmoe_combine(const qmoe_dims *d, const uint16_t *x, const float *y, const float *topk_w,
+                 const float *y_shared_or_null, int32_t T, uint16_t *out, float *out_f32_or_null,
+                 qmoe_stream_t stream) {
+  int rc = check_dims(d);
+  if (rc || (rc = check_T(T))) return rc;
+  if (T == 0) return ok();
+  if (!x || !y || !topk_w || !out) return fail(QMOE_ERR_ARG, "combine: NULL pointer");
+  if ((rc = check_arch())) return rc;
+  const size_t n = (size_t)T * d->hidden;
+  const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 8192);
+  hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, x, y,
+                     topk_w, y_shared_or_null, T, d->hidden, d->top_k, out, out_f32_or_null);
+  QMOE_LAUNCHED();
+  return ok();
+}
+
+int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16_t *out,
+                       float *out_f32_or_null, int32_t *topk_idx_or_null, float *topk_w_or_null,
+                       void *ws, size_t ws_bytes, qmoe_stream_t stream) {
+  int rc = check_layer(L);
+  if (rc || (rc = check_T(T))) return rc;
+  if (T == 0) return ok();
+  if (!x || !out) return fail(QMOE_ERR_ARG, "layer_forward: x/out must not be NULL");
+  const int Tc_max = std::min<int>(T, CHUNK_TOKENS);
+  if ((rc = check_ws(&L->d, Tc_max, ws, ws_bytes))) return rc;
+  if ((rc = check_arch())) return rc;
+  const qmoe_dims *d = &L->d;
+  hipStream_t s = (hipStream_t)stream;
+  const WsLayout wl = ws_layout(d, Tc_max);
+  const int H = d->hidden, k = d->top_k;
+  const bool sh = L->shared != nullptr;
+  for (int c0 = 0; c0 < T; c0 += CHUNK_TOKENS) {
+    const int Tc = std::min(CHUNK_TOKENS, T - c0);
+    const uint16_t *xc = x + (size_t)c0 * H;
+    int32_t *idx = topk_idx_or_null ? topk_idx_or_null + (size_t)c0 * k : at<int32_t>(ws, wl.tidx);
+    float *w = topk_w_or_null ? topk_w_or_null + (size_t)c0 * k : at<float>(ws, wl.tw);
+    // kernel 1: router (+ top-k, bucketing) and shared gate/up
+    RouterArgs ra = make_router_args(d, &L->r, xc, Tc, at<float>(ws, wl.logits), idx, w, ws);
+    ra.counts = at<int32_t>(ws, wl.counts);
+    ra.offsets = at<int32_t>(ws, wl.offsets);
+    ra.sorted = at<int32_t>(ws, wl.sorted);
+    ra.active = at<int32_t>(ws, wl.active);
+    ra.n_active = at<int32_t>(ws, wl.nact);
+    FfnArgs fa = make_ffn_args(L, xc, Tc, ra.offsets, ra.sorted, ra.active, ra.n_active,
+                               at<float>(ws, wl.y), sh ? at<float>(ws, wl.ysh) : nullptr, ws,
+                               Tc_max);
+    fa.topk_w = w;
+    fa.out = out + (size_t)c0 * H;
+    fa.out_f32 = out_f32_or_null ? out_f32_or_null + (size_t)c0 * H : nullptr;
+    const int n_router = ra.n_tb * ra.n_eb;
+    const int n_sh = sh ? d->shared_inter / 16 : 0;
+    const size_t smem1 = std::max(router_smem(d), sh ? gu_smem(H) : (size_t)0);
+    if ((rc = set_lds(router_shared_kernel, smem1))) return rc;
+    hipLaunchKernelGGL(router_shared_kernel, dim3(n_router + n_sh), dim3(ROUTER_THREADS), smem1, s,
+                       ra, fa, n_router);
+    QMOE_LAUNCHED();
+    // kernel 2: routed gate/up + SwiGLU
+    if (g_prof_start) QMOE_HIP(hipEventRecord(g_prof_start, s));
+    if ((rc = launch_gu(fa, 1, s))) return rc;
+    if (g_prof_stop) QMOE_HIP(hipEventRecord(g_prof_stop, s));
+    // kernel 3: routed + shared down projection, combine in the last workgroup per tile
+    if (!sh) fa.shared = nullptr;
+    if ((rc = launch_d(fa, sh, s))) return rc;
+  }
+  return ok();
+}
+
+int qmoe_event_create(void **event_out) {
+  if (!event_out) return fail(QMOE_ERR_ARG, "event_out is NULL");
+  hipEvent_t e;
+  QMOE_HIP(hipEventCreate(&e));
+  *event_out = (void *)e;
+  return ok();
+}
+
+int qmoe_event_destroy(void *event) {
+  if (!event) return fail(QMOE_ERR_ARG, "event is NULL");
+  QMOE_HIP(hipEventDestroy((hipEvent_t)event));
+  return ok();
+}
+
+int qmoe_event_record(void *event, qmoe_stream_t stream) {
+  if (!event) return fail(QMOE_ERR_ARG, "event is NULL");
+  QMOE_HIP(hipEventRecord((hipEvent_t)event, (hipStream_t)stream));
+  return ok();
+}
+
+int qmoe_event_elapsed_ms(void *start, void *stop, float *ms_out) {
+  if (!start || !stop || !ms_out) return fail(QMOE_ERR_ARG, "event_elapsed_ms: NULL argument");
+  QMOE_HIP(hipEventSynchronize((hipEvent_t)stop));
+  QMOE_HIP(hipEventElapsedTime(ms_out, (hipEvent_t)start, (hipEvent_t)stop));
+  return ok();
+}
+
+int qmoe_set_profile_events(void *start, void *stop) {
+  if ((start == nullptr) != (stop == nullptr))
+    return fail(QMOE_ERR_ARG, "set_profile_events: pass both events or neither");
+  g_prof_start = (hipEvent_t)start;
+  g_prof_stop = (hipEvent_t)stop;
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,312 @@
+// Router and bucketing kernels.
+//
+// Router (TurboFieldfare post, section "TurboFieldfare의 전문가 스트리밍 구조", router
+// listing): scale-free RMS norm of the hidden state, times router_scale / sqrt(hidden), an
+// 8-bit affine projection to one logit per expert, the k largest logits, softmax over those
+// k logits only, times per_expert_scale of each kept expert.  The 8-bit format is the MLX
+// affine one of section "TurboFieldfare가 메모리를 아끼는 방식" (w = s*q + b, unsigned q,
+// bf16 s and b per 64 inputs).
+//
+// Bucketing groups token->expert assignments by expert so that one expert read serves every
+// row routed to it (the same post's 128-token prefill chunks).
+#pragma once
+#include "common.h"
+
+namespace qmoe {
+
+constexpr int ROUTER_TB = 4;     // tokens per router workgroup
+constexpr int ROUTER_EPW = 2;    // experts per wave
+constexpr int ROUTER_WAVES = 4;
+constexpr int ROUTER_EPB = ROUTER_EPW * ROUTER_WAVES;  // experts per router workgroup
+constexpr int ROUTER_THREADS = ROUTER_WAVES * WAVE;
+constexpr float RMS_EPS = 1e-6f;
+
+struct RouterArgs {
+  const uint16_t *x;          // [T, H] bf16
+  const uint8_t *rq;          // [E, H]
+  const uint16_t *rs;         // [E, H/64]
+  const uint16_t *rb;         // [E, H/64]
+  const float *rscale;        // [H] or null
+  const float *pes;           // [E]
+  const float *lbias;         // [E] or null
+  int T, H, E, k;
+  float inv_sqrt_h;           // fp32(1/sqrt(H))
+  float *logits;              // [T, E]
+  int32_t *topk_idx;          // [T, k]
+  float *topk_w;              // [T, k]
+  unsigned *cnt_tb;           // [n_tb] completion counters (zero on entry, zero on exit)
+  unsigned *cnt_all;          // [1]
+  int n_tb, n_eb;             // token blocks, expert blocks
+  // optional fused bucketing (layer path); null counts -> skip
+  int32_t *counts, *offsets, *sorted, *active, *n_active;
+};
+
+// LDS bytes of a router workgroup for hidden H
+inline size_t router_lds_bytes(int H) {
+  return (size_t)ROUTER_TB * H * 4 + (size_t)ROUTER_TB * (H / 16) * 4 + 64;
+}
+
+// ---------------------------------------------------------------- top-k of one token (one wave)
+// Exact order: larger logit first, equal logits -> lower expert index.
+QMOE_DEV void topk_one_token(const float *lrow, int E, int k, const float *pes,
+                             int32_t *idx_out, float *w_out) {
+  const int lane = threadIdx.x % WAVE;
+  float v[MAX_EXPERTS / WAVE];
+#pragma unroll
+  for (int j = 0; j < MAX_EXPERTS / WAVE; ++j) {
+    const int e = lane + WAVE * j;
+    v[j] = (e < E) ? lrow[e] : -INFINITY;
+  }
+  unsigned taken = 0;
+  float myv = 0.f;
+  int myi = 0;
+  for (int r = 0; r < k; ++r) {
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int j = 0; j < MAX_EXPERTS / WAVE; ++j) {
+      const int e = lane + WAVE * j;
+      if (e < E && !((taken >> j) & 1u)) {
+        if (v[j] > bv || (v[j] == bv && e < bi)) { bv = v[j]; bi = e; }
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, WAVE);
+      const int oi = __shfl_xor(bi, o, WAVE);
+      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    if ((bi % WAVE) == lane) taken |= 1u << (bi / WAVE);
+    if (lane == r) { myv = bv; myi = bi; }
+  }
+  const float vmax = __shfl(myv, 0, WAVE);
+  const float z = (lane < k) ? expf(myv - vmax) : 0.f;
+  const float zsum = wave_sum(z);
+  if (lane < k) {
+    idx_out[lane] = myi;
+    w_out[lane] = (z / zsum) * pes[myi];
+  }
+}
+
+// ---------------------------------------------------------------- bucketing (one workgroup)
+// Stable counting sort of N = T*k assignments by expert.  Counts via an LDS histogram; the
+// rank of an assignment among the earlier ones of its expert from wave ballots (one ballot
+// per distinct expert in a wave) plus a per-expert cursor advanced wave by wave in order.
+// lds: at least (E + 1) * 4 + 64 * 4 bytes.
+template <int NT>
+QMOE_DEV void bucket_block(const int32_t *idx, int N, int E, int32_t *counts, int32_t *offsets,
+                           int32_t *sorted, int32_t *active, int32_t *n_active, int *lds) {
+  constexpr int NW = NT / WAVE;
+  int *cnt = lds;                 // [E]
+  int *wsum = lds + E + 1;        // [NW] scratch for scans
+  const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
+  for (int e = tid; e < E; e += NT) cnt[e] = 0;
+  __syncthreads();
+  for (int f = tid; f < N; f += NT) atomicAdd(&cnt[idx[f]], 1);
+  __syncthreads();
+  // exclusive scan of counts and of (count > 0) flags, E <= MAX_EXPERTS
+  const int per = (E + NT - 1) / NT;
+  const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
+  int s_cnt = 0, s_act = 0;
+  for (int e = e0; e < e1; ++e) { s_cnt += cnt[e]; s_act += cnt[e] > 0; }
+  // inclusive wave scan of the pair (packed: counts < 2^20 per call segment, flags < 2^11)
+  long long pair = ((long long)s_cnt << 16) | s_act;
+  for (int o = 1; o < WAVE; o <<= 1) {
+    const long long up = __shfl_up(pair, o, WAVE);
+    if (lane >= o) pair += up;
+  }
+  __shared__ long long wtot[NW];
+  if (lane == WAVE - 1) wtot[wv] = pair;
+  __syncthreads();
+  long long before = 0;
+  for (int w = 0; w < wv; ++w) before += wtot[w];
+  long long excl = before + pair - (((long long)s_cnt << 16) | s_act);
+  int run_cnt = (int)(excl >> 16), run_act = (int)(excl & 0xFFFF);
+  for (int e = e0; e < e1; ++e) {
+    const int c = cnt[e];
+    counts[e] = c;
+    offsets[e] = run_cnt;
+    if (c > 0) active[run_act++] = e;
+    cnt[e] = run_cnt;  // becomes the cursor
+    run_cnt += c;
+  }
+  if (tid == NT - 1) {
+    long long tot = 0;
+    for (int w = 0; w < NW; ++w) tot += wtot[w];
+    offsets[E] = (int)(tot >> 16);
+    *n_active = (int)(tot & 0xFFFF);
+  }
+  (void)wsum;
+  __syncthreads();
+  // stable scatter, NT assignments per round
+  for (int base = 0; base < N; base += NT) {
+    const int f = base + tid;
+    const int e = (f < N) ? idx[f] : -1;
+    // rank among lower lanes of this wave with the same expert, and the wave's count of it
+    int rank = 0, tot = 0;
+    unsigned long long pending = __ballot(f < N);
+    while (pending) {
+      const int leader = __ffsll((long long)pending) - 1;
+      const int el = __shfl(e, leader, WAVE);
+      const unsigned long long same = __ballot(e == el && f < N);
+      if (e == el && f < N) {
+        rank = __popcll(same & ((1ull << lane) - 1ull));
+        tot = __popcll(same);
+      }
+      pending &= ~same;
+    }
+    for (int w = 0; w < NW; ++w) {
+      if (wv == w && f < N) {
+        const int cur = cnt[e];
+        sorted[cur + rank] = f;
+        __builtin_amdgcn_wave_barrier();
+        if (rank == 0) cnt[e] = cur + tot;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// ---------------------------------------------------------------- router logits
+// Workgroup (tb, eb): tokens [4 tb, 4 tb + 4) x experts [8 eb, 8 eb + 8).  Per token the
+// input is staged as z = x * router_scale (fp32) with per-16-element sums; the token's norm
+// factor f = (1/sqrt(H)) / sqrt(mean(x^2) + eps) multiplies the finished dot product:
+//   logit = f * sum_g [ s_g * sum_{h in g} q_h z_h + b_g * sum_{h in g} z_h ] + bias.
+QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *smem) {
+  const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
+  const int H = a.H;
+  const int t0 = tb * ROUTER_TB;
+  const int nt = min(ROUTER_TB, a.T - t0);
+  float *z = (float *)smem;                                  // [TB][H]
+  float *zs = z + ROUTER_TB * H;                             // [TB][H/16]
+  float *fac = zs + ROUTER_TB * (H / 16);                    // [TB]
+  // stage z and the 16-element sums; thread handles 8 consecutive elements
+  const int n8 = H / 8;
+  for (int i = 0; i < nt; ++i) {
+    const uint16_t *xr = a.x + (size_t)(t0 + i) * H;
+    float ss = 0.f;
+    for (int c = tid; c < n8; c += ROUTER_THREADS) {
+      const qmoe_u32x4 v = *(const qmoe_u32x4 *)(xr + 8 * c);
+      const uint32_t wv4[4] = {v.x, v.y, v.z, v.w};
+      float part = 0.f;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        float x0 = bf16lo(wv4[d]), x1 = bf16hi(wv4[d]);
+        ss = fmaf(x0, x0, ss);
+        ss = fmaf(x1, x1, ss);
+        if (a.rscale) { x0 *= a.rscale[8 * c + 2 * d]; x1 *= a.rscale[8 * c + 2 * d + 1]; }
+        z[i * H + 8 * c + 2 * d] = x0;
+        z[i * H + 8 * c + 2 * d + 1] = x1;
+        part += x0 + x1;
+      }
+      // two 8-element threads make one 16-element sum (c even/odd are adjacent lanes)
+      const float other = __shfl_xor(part, 1, WAVE);
+      if ((c & 1) == 0) zs[i * (H / 16) + c / 2] = part + other;
+    }
+    ss = wave_sum(ss);
+    __shared__ float red[ROUTER_WAVES];
+    if (lane == 0) red[wv] = ss;
+    __syncthreads();
+    if (tid == 0) {
+      float tot = 0.f;
+      for (int w = 0; w < ROUTER_WAVES; ++w) tot += red[w];
+      fac[i] = a.inv_sqrt_h / sqrtf(tot / (float)H + RMS_EPS);
+    }
+    __syncthreads();
+  }
+  // one wave per expert, lanes stride over 16-byte chunks of the expert's row
+  const int n16 = H / 16;
+  for (int ee = 0; ee < ROUTER_EPW; ++ee) {
+    const int e = eb * ROUTER_EPB + wv * ROUTER_EPW + ee;
+    if (e >= a.E) break;
+    float acc[ROUTER_TB];
+#pragma unroll
+    for (int i = 0; i < ROUTER_TB; ++i) acc[i] = 0.f;
+    const uint8_t *row = a.rq + (size_t)e * H;
+    for (int c = lane; c < n16; c += WAVE) {
+      const qmoe_u32x4 v = *(const qmoe_u32x4 *)(row + 16 * c);
+      const int g = c / 4;
+      const float s = bf16_to_f32(a.rs[(size_t)e * (H / GROUP) + g]);
+      const float b = bf16_to_f32(a.rb[(size_t)e * (H / GROUP) + g]);
+      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+      float q[16];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        q[4 * d + 0] = (float)(w4[d] & 0xFFu);
+        q[4 * d + 1] = (float)((w4[d] >> 8) & 0xFFu);
+        q[4 * d + 2] = (float)((w4[d] >> 16) & 0xFFu);
+        q[4 * d + 3] = (float)(w4[d] >> 24);
+      }
+#pragma unroll
+      for (int i = 0; i < ROUTER_TB; ++i) {
+        if (i < nt) {
+          const float *zr = z + i * H + 16 * c;
+          float dq = 0.f;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) dq = fmaf(q[j], zr[j], dq);
+          acc[i] = fmaf(s, dq, acc[i]);
+          acc[i] = fmaf(b, zs[i * (H / 16) + c], acc[i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < ROUTER_TB; ++i) {
+      if (i < nt) {
+        const float tot = wave_sum(acc[i]);
+        if (lane == 0) {
+          float l = fac[i] * tot;
+          if (a.lbias) l += a.lbias[e];
+          a.logits[(size_t)(t0 + i) * a.E + e] = l;
+        }
+      }
+    }
+  }
+}
+
+// After a router workgroup has written its logits: the last workgroup of a token block runs
+// top-k for that block; the last of those runs the bucketing (if requested).
+QMOE_DEV void router_finish(const RouterArgs &a, int tb, char *smem) {
+  __shared__ int last;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) last = (atomicAdd(&a.cnt_tb[tb], 1u) == (unsigned)(a.n_eb - 1));
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  const int wv = threadIdx.x / WAVE;
+  const int t0 = tb * ROUTER_TB;
+  const int nt = min(ROUTER_TB, a.T - t0);
+  for (int i = wv; i < nt; i += ROUTER_WAVES) {
+    const int t = t0 + i;
+    topk_one_token(a.logits + (size_t)t * a.E, a.E, a.k, a.pes, a.topk_idx + (size_t)t * a.k,
+                   a.topk_w + (size_t)t * a.k);
+  }
+  if (threadIdx.x == 0) a.cnt_tb[tb] = 0u;
+  if (a.counts == nullptr) return;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) last = (atomicAdd(a.cnt_all, 1u) == (unsigned)(a.n_tb - 1));
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  bucket_block<ROUTER_THREADS>(a.topk_idx, a.T * a.k, a.E, a.counts, a.offsets, a.sorted,
+                               a.active, a.n_active, (int *)smem);
+  if (threadIdx.x == 0) *a.cnt_all = 0u;
+}
+
+__global__ void __launch_bounds__(ROUTER_THREADS) router_kernel(RouterArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const int tb = blockIdx.x / a.n_eb, eb = blockIdx.x % a.n_eb;
+  router_logits_block(a, tb, eb, smem);
+  router_finish(a, tb, smem);
+}
+
+__global__ void __launch_bounds__(256) bucket_kernel(const int32_t *idx, int N, int E,
+                                                     int32_t *counts, int32_t *offsets,
+                                                     int32_t *sorted, int32_t *active,
+                                                     int32_t *n_active) {
+  __shared__ int lds[MAX_EXPERTS + 1 + 64];
+  bucket_block<256>(idx, N, E, counts, offsets, sorted, active, n_active, lds);
+}
+
+}  // namespace qmoe

@@ -1,0 +1,191 @@
+"""Torch-facing wrappers of the qmoe C ABI.
+
+Argument marshalling only: every step of the layer runs in the HIP library.  torch supplies
+device memory and the current HIP stream.  bf16 data may be passed as torch.bfloat16 or as
+any 2-byte integer tensor holding bf16 bit patterns.
+"""
+import ctypes
+
+import torch
+
+from ._lib import Dims, Layer, Router, check, lib, make_dims  # noqa: F401
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t, dtype_bytes=None, what="tensor", allow_none=False):
+    if t is None:
+        if allow_none:
+            return None
+        raise ValueError(f"{what} must not be None")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{what} must be a device tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if dtype_bytes is not None and t.element_size() != dtype_bytes:
+        raise ValueError(f"{what} must have {dtype_bytes}-byte elements (got {t.dtype})")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, dtype, what):
+    if t.dtype != dtype:
+        raise ValueError(f"{what} must be {dtype} (got {t.dtype})")
+
+
+def expert_stride(dims, inter):
+    return int(lib().qmoe_expert_stride(ctypes.byref(dims), int(inter)))
+
+
+def workspace_bytes(dims, max_tokens):
+    return int(lib().qmoe_workspace_bytes(ctypes.byref(dims), int(max_tokens)))
+
+
+def workspace(dims, max_tokens, device="cuda"):
+    """A zero-initialised workspace tensor for calls of up to max_tokens tokens."""
+    n = workspace_bytes(dims, max_tokens)
+    if n == 0:
+        check(-2)
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    check(lib().qmoe_workspace_init(_ptr(ws), n, _stream()))
+    return ws
+
+
+def pack_expert(dims, inter, gate_q, gate_s, gate_b, up_q, up_s, up_b, down_q, down_s, down_b, dst):
+    for t, n in ((gate_q, "gate_q"), (up_q, "up_q"), (down_q, "down_q")):
+        _need(t, torch.uint8, n)
+    check(lib().qmoe_pack_expert(
+        ctypes.byref(dims), int(inter), _ptr(gate_q, 1), _ptr(gate_s, 2), _ptr(gate_b, 2),
+        _ptr(up_q, 1), _ptr(up_s, 2), _ptr(up_b, 2), _ptr(down_q, 1), _ptr(down_s, 2),
+        _ptr(down_b, 2), _ptr(dst, 1, "dst"), _stream()))
+
+
+def unpack_expert(dims, inter, src, gate_q, gate_s, gate_b, up_q, up_s, up_b, down_q, down_s, down_b):
+    check(lib().qmoe_unpack_expert(
+        ctypes.byref(dims), int(inter), _ptr(src, 1, "src"), _ptr(gate_q, 1), _ptr(gate_s, 2),
+        _ptr(gate_b, 2), _ptr(up_q, 1), _ptr(up_s, 2), _ptr(up_b, 2), _ptr(down_q, 1),
+        _ptr(down_s, 2), _ptr(down_b, 2), _stream()))
+
+
+class RouterWeights:
+    """Device tensors of one layer's router (kept alive with the ctypes struct)."""
+
+    def __init__(self, codes, scales, biases, per_expert_scale, router_scale=None, logit_bias=None):
+        _need(codes, torch.uint8, "router codes")
+        _need(per_expert_scale, torch.float32, "per_expert_scale")
+        self.tensors = (codes, scales, biases, per_expert_scale, router_scale, logit_bias)
+        self.struct = Router(
+            _ptr(codes, 1).value, _ptr(scales, 2).value, _ptr(biases, 2).value,
+            _ptr(router_scale, 4, allow_none=True).value if router_scale is not None else None,
+            _ptr(per_expert_scale, 4).value,
+            _ptr(logit_bias, 4, allow_none=True).value if logit_bias is not None else None)
+
+
+class LayerWeights:
+    """A layer: router + packed expert store (+ shared block)."""
+
+    def __init__(self, dims, router, experts, stride, shared=None, experts_offset=0):
+        self.dims, self.router, self.experts, self.shared = dims, router, experts, shared
+        base = _ptr(experts, 1, "experts").value + int(experts_offset)
+        self.struct = Layer(dims, router.struct, base, int(stride),
+                            _ptr(shared, 1, "shared").value if shared is not None else None)
+
+
+def router_topk(dims, router, x, ws, topk_idx=None, topk_w=None, logits=None):
+    T = x.shape[0]
+    k = dims.top_k
+    if topk_idx is None:
+        topk_idx = torch.empty(T, k, dtype=torch.int32, device=x.device)
+    if topk_w is None:
+        topk_w = torch.empty(T, k, dtype=torch.float32, device=x.device)
+    _need(topk_idx, torch.int32, "topk_idx")
+    _need(topk_w, torch.float32, "topk_w")
+    check(lib().qmoe_router_topk(
+        ctypes.byref(dims), ctypes.byref(router.struct), _ptr(x, 2, "x"), T, _ptr(topk_idx, 4),
+        _ptr(topk_w, 4), _ptr(logits, 4, allow_none=True), _ptr(ws, 1, "ws"), ws.numel(), _stream()))
+    return topk_idx, topk_w
+
+
+def bucket(dims, topk_idx, ws=None):
+    T = topk_idx.shape[0]
+    E = dims.n_experts
+    dev = topk_idx.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    srt = torch.empty(max(T * dims.top_k, 1), dtype=torch.int32, device=dev)
+    active = torch.empty(E, dtype=torch.int32, device=dev)
+    n_active = torch.empty(1, dtype=torch.int32, device=dev)
+    _need(topk_idx, torch.int32, "topk_idx")
+    check(lib().qmoe_bucket(
+        ctypes.byref(dims), _ptr(topk_idx, 4), T, _ptr(counts), _ptr(offsets), _ptr(srt),
+        _ptr(active), _ptr(n_active), _ptr(ws, 1, allow_none=True),
+        0 if ws is None else ws.numel(), _stream()))
+    return counts, offsets, srt[:T * dims.top_k], active, n_active
+
+
+def expert_ffn(layer, x, offsets, srt, active, n_active, ws, y=None, y_shared=None, want_shared=True):
+    T = x.shape[0]
+    d = layer.dims
+    if y is None:
+        y = torch.empty(T * d.top_k, d.hidden, dtype=torch.float32, device=x.device)
+    if y_shared is None and want_shared and layer.shared is not None:
+        y_shared = torch.empty(T, d.hidden, dtype=torch.float32, device=x.device)
+    check(lib().qmoe_expert_ffn(
+        ctypes.byref(layer.struct), _ptr(x, 2, "x"), T, _ptr(offsets, 4), _ptr(srt, 4),
+        _ptr(active, 4), _ptr(n_active, 4), _ptr(y, 4, "y"), _ptr(y_shared, 4, allow_none=True),
+        _ptr(ws, 1, "ws"), ws.numel(), _stream()))
+    return y, y_shared
+
+
+def combine(dims, x, y, topk_w, y_shared=None, out=None, out_f32=None):
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty(T, dims.hidden, dtype=torch.bfloat16, device=x.device)
+    check(lib().qmoe_combine(
+        ctypes.byref(dims), _ptr(x, 2, "x"), _ptr(y, 4, "y"), _ptr(topk_w, 4, "topk_w"),
+        _ptr(y_shared, 4, allow_none=True), T, _ptr(out, 2, "out"),
+        _ptr(out_f32, 4, allow_none=True), _stream()))
+    return out
+
+
+def layer_forward(layer, x, ws, out=None, out_f32=None, topk_idx=None, topk_w=None):
+    T = x.shape[0]
+    d = layer.dims
+    if out is None:
+        out = torch.empty(T, d.hidden, dtype=torch.bfloat16, device=x.device)
+    check(lib().qmoe_layer_forward(
+        ctypes.byref(layer.struct), _ptr(x, 2, "x"), T, _ptr(out, 2, "out"),
+        _ptr(out_f32, 4, allow_none=True), _ptr(topk_idx, 4, allow_none=True),
+        _ptr(topk_w, 4, allow_none=True), _ptr(ws, 1, "ws"), ws.numel(), _stream()))
+    return out
+
+
+class Event:
+    """A HIP event created by the library (for timing kernels on the stream they run on)."""
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        check(lib().qmoe_event_create(ctypes.byref(h)))
+        self.h = h
+
+    def record(self):
+        check(lib().qmoe_event_record(self.h, _stream()))
+
+    def elapsed_ms(self, stop):
+        ms = ctypes.c_float()
+        check(lib().qmoe_event_elapsed_ms(self.h, stop.h, ctypes.byref(ms)))
+        return ms.value
+
+    def __del__(self):
+        try:
+            if self.h:
+                lib().qmoe_event_destroy(self.h)
+        except Exception:
+            pass
+
+
+def set_profile_events(start, stop):
+    check(lib().qmoe_set_profile_events(start.h if start else None, stop.h if stop else None))

@@ -1,0 +1,292 @@
+"""Parity of the HIP path (through the C ABI) against the fp64 oracle.  Needs an MI355X."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from parity import (assert_close_f32, check_out_bf16, compare_topk, rel_err_rows)
+from workloads import gen as G
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from quantized_moe_router_amd import _lib
+    _lib.lib()          # fails loudly if the HIP library is not built
+
+
+def _ops():
+    from quantized_moe_router_amd import ops
+    return ops
+
+
+def _stacks():
+    import stacks
+    return stacks
+
+
+_cache = {}
+
+
+def layer(name, idx=0):
+    key = (name, idx)
+    if key not in _cache:
+        cfg = G.config(name)
+        _cache[key] = _stacks().build_layer(cfg, idx, DEV)
+    return _cache[key]
+
+
+def np16(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+# ------------------------------------------------------------------ generator and store
+
+@pytest.mark.parametrize("name,experts", [("tiny", [0, 7, 15]), ("gemma4_26b_a4b_decode", [0, 77]),
+                                          ("qwen3_next_80b_a3b_decode_b1", [511])])
+def test_device_generator_matches_host(name, experts):
+    from workloads import device as D
+    cfg = G.config(name)
+    canon = D.CanonLayerExperts(cfg, 3, device=DEV)
+    for e in experts:
+        want = G.make_expert(cfg, 3, e).arrays()
+        for got, w in zip(canon.expert(e), want):
+            g = got.cpu().numpy()
+            g = g.view(np.uint16) if w.dtype == np.uint16 else g
+            assert np.array_equal(g, w), (name, e)
+
+
+@pytest.mark.parametrize("name", ["tiny", "gemma4_26b_a4b_decode"])
+def test_pack_unpack_round_trip(name):
+    ops = _ops()
+    cfg = G.config(name)
+    pl, li = layer(name)
+    for e, ew, inter, blk in [(5, li.expert(5), cfg.inter, pl.store[5 * pl.stride:6 * pl.stride]),
+                              ("sh", li.shared(), cfg.shared_inter, pl.shared)]:
+        outs = [torch.empty_like(torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a),
+                                 device=DEV) for a in ew.arrays()]
+        ops.unpack_expert(pl.dims, inter, blk, *outs)
+        for got, w in zip(outs, ew.arrays()):
+            g = got.cpu().numpy()
+            g = g.view(np.uint16) if w.dtype == np.uint16 else g
+            assert np.array_equal(g, w), (name, e)
+
+
+def test_pack_is_layout_only_byte_count():
+    ops = _ops()
+    cfg = G.config("gemma4_26b_a4b_decode")
+    pl, _ = layer("gemma4_26b_a4b_decode")
+    assert ops.expert_stride(pl.dims, cfg.inter) == 3346432          # 3,345,408 rounded to 4 KiB
+    assert G.expert_bytes(cfg) == 3345408
+
+
+# ------------------------------------------------------------------ router
+
+@pytest.mark.parametrize("name,T", [("tiny", 4), ("gemma4_26b_a4b_decode", 1),
+                                    ("gemma4_26b_a4b_prefill", 128),
+                                    ("qwen3_next_80b_a3b_decode_b16", 16),
+                                    ("qwen3_6_35b_a3b_long_prefill", 128), ("tiny", 131)])
+def test_router_parity(name, T):
+    ops = _ops()
+    cfg = G.config(name)
+    pl, li = layer(name) if name != "gemma4_26b_a4b_prefill" else layer("gemma4_26b_a4b_decode")
+    xb, x = _stacks().hidden(cfg, 0, T)
+    ws = ops.workspace(pl.dims, T)
+    logits = torch.empty(T, cfg.experts, dtype=torch.float32, device=DEV)
+    idx, w = ops.router_topk(pl.dims, pl.router, x, ws, logits=logits)
+    torch.cuda.synchronize()
+    top, wr, l64 = O.router(xb, li, cfg.top_k)
+    assert_close_f32(logits.cpu().numpy(), l64, "logits", rel=1e-4)
+    ties, differ = compare_topk(idx.cpu().numpy(), w.cpu().numpy(), l64, top, wr)
+    print(f"{name} T={T}: near-tie tokens {ties}, differing sets {len(differ)}")
+
+
+def test_router_duplicate_rows_tie_to_lower_index():
+    ops = _ops()
+    st = _stacks()
+    cfg = G.config("tiny")
+    li = G.make_router(cfg, 0)
+    xb, x = st.hidden(cfg, 0)
+    top0, _, _ = O.router(xb, li, 2)
+    e = int(top0[0, 0])
+    d = 15 if e != 15 else 0
+    for a in ("router_q", "router_s", "router_b"):
+        getattr(li, a)[d] = getattr(li, a)[e]
+    r = st.router_weights(li, DEV)
+    from quantized_moe_router_amd._lib import make_dims
+    dims = make_dims(cfg.hidden, cfg.experts, cfg.top_k, cfg.inter, cfg.shared_inter)
+    ws = ops.workspace(dims, 4)
+    idx, _ = ops.router_topk(dims, r, x[:1].contiguous(), ws)
+    assert idx.cpu().numpy()[0].tolist() == sorted([e, d])
+
+
+def test_router_zero_input():
+    ops = _ops()
+    cfg = G.config("tiny")
+    pl, li = layer("tiny")
+    x = torch.zeros(3, cfg.hidden, dtype=torch.int16, device=DEV)
+    ws = ops.workspace(pl.dims, 3)
+    idx, w = ops.router_topk(pl.dims, pl.router, x, ws)
+    assert idx.cpu().numpy().tolist() == [[0, 1]] * 3
+    assert np.allclose(w.cpu().numpy(), np.tile(li.pes[:2] / 2, (3, 1)), rtol=1e-6)
+
+
+# ------------------------------------------------------------------ bucket
+
+@pytest.mark.parametrize("T,k,E", [(1, 8, 128), (4, 2, 16), (16, 10, 512), (128, 8, 128),
+                                   (128, 8, 256), (37, 3, 7), (1000, 4, 64), (0, 2, 16)])
+def test_bucket_parity(T, k, E):
+    ops = _ops()
+    from quantized_moe_router_amd._lib import make_dims
+    rng = np.random.default_rng(T * 131 + k * 7 + E)
+    # Zipf-skewed picks so that some buckets are large and many empty
+    p = 1.0 / np.arange(1, E + 1) ** 1.1
+    p /= p.sum()
+    idx = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32) \
+        if T else np.zeros((0, k), np.int32)
+    dims = make_dims(64, E, k, 64, 0)
+    counts, offsets, srt, active, n_active = ops.bucket(dims, torch.from_numpy(idx).to(DEV))
+    c, o, s, a = O.bucket(idx, E)
+    assert np.array_equal(counts.cpu().numpy(), c)
+    assert np.array_equal(offsets.cpu().numpy(), o)
+    assert np.array_equal(srt.cpu().numpy(), s)
+    na = int(n_active.cpu().numpy()[0])
+    assert na == len(a) and np.array_equal(active.cpu().numpy()[:na], a)
+
+
+# ------------------------------------------------------------------ expert FFN + combine
+
+def _bucket_of(ops, dims, idx):
+    return ops.bucket(dims, idx)
+
+
+@pytest.mark.parametrize("name,T,sample", [("tiny", 4, None), ("tiny", 37, None),
+                                           ("gemma4_26b_a4b_decode", 1, None),
+                                           ("gemma4_26b_a4b_prefill", 128, [0, 77]),
+                                           ("qwen3_next_80b_a3b_decode_b16", 16, [3, 15])])
+def test_expert_ffn_and_combine_parity(name, T, sample):
+    ops = _ops()
+    cfg = G.config(name)
+    pl, li = layer(name) if "gemma" not in name else layer("gemma4_26b_a4b_decode")
+    xb, x = _stacks().hidden(cfg, 1, T)
+    ws = ops.workspace(pl.dims, T)
+    idx, w = ops.router_topk(pl.dims, pl.router, x, ws)
+    counts, offsets, srt, active, n_active = ops.bucket(pl.dims, idx)
+    y, y_sh = ops.expert_ffn(pl.weights, x, offsets, srt, active, n_active, ws)
+    out_f32 = torch.empty(T, cfg.hidden, dtype=torch.float32, device=DEV)
+    out = ops.combine(pl.dims, x, y, w, y_sh, out_f32=out_f32)
+    torch.cuda.synchronize()
+    idx_n, w_n = idx.cpu().numpy(), w.cpu().numpy()
+    y_n, ysh_n = y.cpu().numpy(), y_sh.cpu().numpy()
+    out_n, of_n = np16(out), out_f32.cpu().numpy()
+    toks = range(T) if sample is None else sample
+    xf = O.bf16_to_f64(xb)
+    sh = O.expert_ffn(xf[list(toks)], li.shared())
+    flips = 0
+    for n, t in enumerate(toks):
+        # y per assignment, with the GPU's routing (teacher forcing)
+        ys = np.stack([O.expert_ffn(xf[t:t + 1], li.expert(int(e)))[0] for e in idx_n[t]])
+        assert_close_f32(y_n[t * cfg.top_k:(t + 1) * cfg.top_k], ys, f"y token {t}")
+        assert_close_f32(ysh_n[t], sh[n], f"y_shared token {t}")
+        ref = xf[t] + sh[n] + (w_n[t].astype(np.float64)[:, None] * ys).sum(0)
+        assert_close_f32(of_n[t], ref, f"out_f32 token {t}")
+        flips += check_out_bf16(out_n[t], of_n[t], ref, f"out token {t}")
+    print(f"{name}: bf16 1-ulp flips {flips}")
+
+
+# ------------------------------------------------------------------ whole layer
+
+def _layer_check(cfg, li, xb, out, out_f32, idx, w, toks):
+    T = xb.shape[0]
+    idx_n = idx.cpu().numpy()
+    ref = O.layer_forward(xb[list(toks)], li, cfg.top_k)
+    ties, differ = compare_topk(idx_n[list(toks)], w.cpu().numpy()[list(toks)], ref["logits"],
+                                ref["top"], ref["w"])
+    out_n, of_n = np16(out), out_f32.cpu().numpy()
+    flips = 0
+    for n, t in enumerate(toks):
+        r = ref
+        if n in differ:      # near tie: re-evaluate the oracle with the GPU's valid selection
+            r = O.layer_forward(xb[t:t + 1], li, cfg.top_k, top_override=idx_n[t:t + 1])
+            rn = 0
+        else:
+            rn = n
+        assert_close_f32(of_n[t], r["out"][rn], f"layer out_f32 token {t}")
+        flips += check_out_bf16(out_n[t], of_n[t], r["out"][rn], f"layer out token {t}")
+    return ties, len(differ), flips
+
+
+@pytest.mark.parametrize("name,T,sample", [("tiny", 4, None), ("tiny", 1, None), ("tiny", 130, [0, 129]),
+                                           ("gemma4_26b_a4b_decode", 1, None),
+                                           ("gemma4_26b_a4b_prefill", 128, [5, 127]),
+                                           ("qwen3_next_80b_a3b_decode_b1", 1, None),
+                                           ("qwen3_next_80b_a3b_decode_b16", 16, [0, 9]),
+                                           ("qwen3_6_35b_a3b_long_prefill", 128, [64])])
+def test_layer_forward_parity(name, T, sample):
+    ops = _ops()
+    cfg = G.config(name)
+    src = {"gemma4_26b_a4b_prefill": "gemma4_26b_a4b_decode",
+           "qwen3_next_80b_a3b_decode_b16": "qwen3_next_80b_a3b_decode_b1"}.get(name, name)
+    pl, li = layer(src)
+    xb, x = _stacks().hidden(cfg, 2, T)
+    ws = ops.workspace(pl.dims, T)
+    out_f32 = torch.empty(T, cfg.hidden, dtype=torch.float32, device=DEV)
+    idx = torch.empty(T, cfg.top_k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, cfg.top_k, dtype=torch.float32, device=DEV)
+    out = ops.layer_forward(pl.weights, x, ws, out_f32=out_f32, topk_idx=idx, topk_w=w)
+    torch.cuda.synchronize()
+    toks = range(T) if sample is None else sample
+    ties, nd, flips = _layer_check(cfg, li, xb, out, out_f32, idx, w, toks)
+    print(f"{name} T={T}: near ties {ties}, re-evaluated {nd}, bf16 flips {flips}")
+
+
+def test_layer_forward_matches_stepwise_and_is_deterministic():
+    ops = _ops()
+    cfg = G.config("gemma4_26b_a4b_prefill")
+    pl, li = layer("gemma4_26b_a4b_decode")
+    xb, x = _stacks().hidden(cfg, 3, 128)
+    ws = ops.workspace(pl.dims, 128)
+    o32a = torch.empty(128, cfg.hidden, dtype=torch.float32, device=DEV)
+    o32b = torch.empty_like(o32a)
+    outa = ops.layer_forward(pl.weights, x, ws, out_f32=o32a)
+    outb = ops.layer_forward(pl.weights, x, ws, out_f32=o32b)
+    idx, w = ops.router_topk(pl.dims, pl.router, x, ws)
+    counts, offsets, srt, active, n_active = ops.bucket(pl.dims, idx)
+    y, y_sh = ops.expert_ffn(pl.weights, x, offsets, srt, active, n_active, ws)
+    o32c = torch.empty_like(o32a)
+    ops.combine(pl.dims, x, y, w, y_sh, out_f32=o32c)
+    torch.cuda.synchronize()
+    assert torch.equal(outa.view(torch.int16), outb.view(torch.int16))
+    assert torch.equal(o32a, o32b)
+    assert rel_err_rows(o32a.cpu().numpy(), o32c.cpu().numpy().astype(np.float64)) <= 1e-5
+
+
+def test_layer_forward_chunks_equal_single_calls():
+    ops = _ops()
+    cfg = G.config("tiny")
+    pl, li = layer("tiny")
+    xb, x = _stacks().hidden(cfg, 4, 300)
+    ws = ops.workspace(pl.dims, 300)
+    o_all = torch.empty(300, cfg.hidden, dtype=torch.float32, device=DEV)
+    ops.layer_forward(pl.weights, x, ws, out_f32=o_all)
+    parts = []
+    for a, b in [(0, 128), (128, 256), (256, 300)]:
+        o = torch.empty(b - a, cfg.hidden, dtype=torch.float32, device=DEV)
+        ops.layer_forward(pl.weights, x[a:b].contiguous(), ws, out_f32=o)
+        parts.append(o)
+    torch.cuda.synchronize()
+    assert torch.equal(o_all, torch.cat(parts))
+
+
+def test_zero_tokens_is_noop():
+    ops = _ops()
+    pl, _ = layer("tiny")
+    x = torch.empty(0, 256, dtype=torch.int16, device=DEV)
+    ws = ops.workspace(pl.dims, 1)
+    out = ops.layer_forward(pl.weights, x, ws)
+    assert out.shape == (0, 256)
