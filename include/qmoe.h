@@ -150,6 +150,7 @@ int qmoe_unpack_expert(const qmoe_dims *d, int32_t inter, const void *src_block,
 /* ---------------------------------------------------------------- the four steps */
 
 /* Step 1, router [TF-struct] router listing.  For each token t of x [T, H] (bf16):
+ * (a NaN logit ranks below every number, so topk_idx always holds valid expert ids)
  *   u = x / sqrt(mean(x^2) + 1e-6) * router_scale / sqrt(H)   (fp32)
  *   logit_e = sum_h (s*q+b)[e,h] * u_h + logit_bias_e          (fp32 accumulate)
  *   topk_idx[t, :] = the k largest logits, descending; equal logits -> lower expert index
@@ -167,8 +168,8 @@ int qmoe_router_topk(const qmoe_dims *d, const qmoe_router *r, const uint16_t *x
  *   sorted [T*k]    flat ids grouped by ascending expert, ascending flat id within an expert
  *   active [E]      the experts with a non-zero count, ascending (first *n_active entries valid)
  *   n_active [1]    number of active experts
- * Deterministic (bit-identical across runs).  Expert ids must lie in [0, E); behaviour is
- * undefined otherwise.  With T = 0 the outputs are still written (all counts zero) and
+ * Deterministic (bit-identical across runs).  Assignments whose expert id lies outside
+ * [0, E) are dropped: not counted and not listed (offsets[E] is then below T*k).  With T = 0 the outputs are still written (all counts zero) and
  * topk_idx may be NULL.  ws is not used and may be NULL. */
 int qmoe_bucket(const qmoe_dims *d, const int32_t *topk_idx, int32_t T,
                 int32_t *counts, int32_t *offsets, int32_t *sorted, int32_t *active,
@@ -180,7 +181,9 @@ int qmoe_bucket(const qmoe_dims *d, const int32_t *topk_idx, int32_t T,
  *   y[f, :] = down_e( silu(gate_e(x_t)) * up_e(x_t) )       fp32 [T*k, H]
  * and, if the layer has a shared block and y_shared_or_null != NULL, for every token
  *   y_shared[t, :] = shared FFN of x_t                        fp32 [T, H]
- * offsets/sorted/active/n_active come from qmoe_bucket (device pointers). */
+ * offsets/sorted/active/n_active come from qmoe_bucket (device pointers); slots whose bucket
+ * data would index outside the store or the assignment list are skipped, and their y rows are
+ * left unwritten. */
 int qmoe_expert_ffn(const qmoe_layer *L, const uint16_t *x, int32_t T,
                     const int32_t *offsets, const int32_t *sorted, const int32_t *active,
                     const int32_t *n_active, float *y, float *y_shared_or_null,

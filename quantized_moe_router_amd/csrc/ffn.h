@@ -19,7 +19,7 @@ struct FfnArgs {
   const uint8_t *experts;     // routed blocks
   size_t stride;
   const uint8_t *shared;      // shared block or null
-  int H, I, Is, k, T;
+  int H, I, Is, k, T, n_experts;
   const uint16_t *x;          // [T, H] bf16
   const int32_t *offsets, *sorted, *active, *n_active;
   int n_slots;                // routed slots in the grid (>= n_active)
@@ -50,18 +50,26 @@ struct SlotRows {
   bool shared;
 };
 
+// Bucket data that would index outside the store or the assignment list makes the slot
+// empty instead (the buffers are caller-provided in the standalone entry point).
 QMOE_DEV bool slot_rows(const FfnArgs &a, int slot, bool shared, SlotRows &r) {
   if (shared) {
     r.blk = a.shared; r.m = a.T; r.beg = 0; r.shared = true;
     return true;
   }
-  if (slot >= *a.n_active) return false;
+  if (slot >= min(*a.n_active, a.n_experts)) return false;
   const int e = a.active[slot];
+  if ((unsigned)e >= (unsigned)a.n_experts) return false;
   r.blk = a.experts + (size_t)e * a.stride;
   r.beg = a.offsets[e];
   r.m = a.offsets[e + 1] - r.beg;
   r.shared = false;
-  return r.m > 0;
+  return r.beg >= 0 && r.m > 0 && r.beg + r.m <= a.T * a.k;
+}
+
+// token of bucket position p (flat assignment id / k), kept inside [0, T)
+QMOE_DEV int token_of(const FfnArgs &a, int p) {
+  return min(max(a.sorted[p], 0), a.T * a.k - 1) / a.k;
 }
 
 // ---------------------------------------------------------------- gate/up tile
@@ -90,7 +98,7 @@ QMOE_DEV void gu_tile(const FfnArgs &a, const SlotRows &sr, int tile, char *smem
     for (int c = tid; c < MB * n8; c += W * WAVE) {
       const int i = c / n8, cc = c % n8;
       if (i < mb) {
-        const int t = sr.shared ? (r0 + i) : (a.sorted[sr.beg + r0 + i] / a.k);
+        const int t = sr.shared ? (r0 + i) : token_of(a, sr.beg + r0 + i);
         const qmoe_u32x4 v = *(const qmoe_u32x4 *)(a.x + (size_t)t * H + 8 * cc);
         *(qmoe_u32x4 *)(xl + (size_t)i * H + 8 * cc) = v;
         float p = bf16lo(v.x) + bf16hi(v.x) + bf16lo(v.y) + bf16hi(v.y) + bf16lo(v.z) +
@@ -257,7 +265,7 @@ QMOE_DEV void d_tile(const FfnArgs &a, const SlotRows &sr, int tile, char *smem)
       size_t yrow;
       float *dst;
       if (sr.shared) { yrow = (size_t)(r0 + i); dst = a.y_sh; }
-      else           { yrow = (size_t)a.sorted[sr.beg + r0 + i]; dst = a.y; }
+      else           { yrow = (size_t)min(max(a.sorted[sr.beg + r0 + i], 0), a.T * a.k - 1); dst = a.y; }
       dst[yrow * H + 32 * tile + r] = yv;
     }
     __syncthreads();

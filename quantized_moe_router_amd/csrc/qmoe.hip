@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <string>
 
@@ -167,14 +168,22 @@ int check_layer(const qmoe_layer *L) {
   return QMOE_OK;
 }
 
+// Raise a kernel's dynamic LDS limit once per (device, kernel) to the largest size used.
 template <class K>
 int set_lds(K kernel, size_t bytes) {
-  if (bytes > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void *)kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    if (e != hipSuccess) return fail(QMOE_ERR_HIP, "hipFuncSetAttribute(lds=%zu): %s", bytes,
-                                     hipGetErrorString(e));
-  }
+  if (bytes <= 64 * 1024) return QMOE_OK;
+  static std::mutex mu;
+  static std::map<std::pair<int, const void *>, size_t> done;
+  int dev = 0;
+  QMOE_HIP(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(mu);
+  size_t &have = done[{dev, (const void *)kernel}];
+  if (bytes <= have) return QMOE_OK;
+  hipError_t e = hipFuncSetAttribute((const void *)kernel,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  if (e != hipSuccess)
+    return fail(QMOE_ERR_HIP, "hipFuncSetAttribute(lds=%zu): %s", bytes, hipGetErrorString(e));
+  have = bytes;
   return QMOE_OK;
 }
 
@@ -222,6 +231,25 @@ __global__ void __launch_bounds__(ROUTER_THREADS) router_shared_kernel(RouterArg
   }
 }
 static_assert(GU_W * WAVE == ROUTER_THREADS, "fused router/shared kernel uses one block size");
+
+// Record an event; under stream capture it is added as an event-record node of the graph
+// after the captured work so far, and later captured work depends on it.
+int record_event(hipEvent_t e, hipStream_t s) {
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  QMOE_HIP(hipStreamIsCapturing(s, &st));
+  if (st != hipStreamCaptureStatusActive) {
+    QMOE_HIP(hipEventRecord(e, s));
+    return QMOE_OK;
+  }
+  hipGraph_t g = nullptr;
+  const hipGraphNode_t *deps = nullptr;
+  size_t ndeps = 0;
+  QMOE_HIP(hipStreamGetCaptureInfo_v2(s, &st, nullptr, &g, &deps, &ndeps));
+  hipGraphNode_t node;
+  QMOE_HIP(hipGraphAddEventRecordNode(&node, g, deps, ndeps, e));
+  QMOE_HIP(hipStreamUpdateCaptureDependencies(s, &node, 1, hipStreamSetCaptureDependencies));
+  return QMOE_OK;
+}
 
 size_t gu_smem(int H) {
   return (size_t)GU_MB * H * 2 + (size_t)GU_MB * (H / 32) * 4 + (size_t)GU_W * GU_MB * 32 * 4;
@@ -355,6 +383,7 @@ static FfnArgs make_ffn_args(const qmoe_layer *L, const uint16_t *x, int T, cons
   a.stride = L->expert_stride;
   a.shared = (const uint8_t *)L->shared;
   a.H = L->d.hidden; a.I = L->d.inter; a.Is = L->d.shared_inter; a.k = L->d.top_k; a.T = T;
+  a.n_experts = L->d.n_experts;
   a.x = x;
   a.offsets = offsets; a.sorted = sorted; a.active = active; a.n_active = n_active;
   a.n_slots = std::min(L->d.n_experts, T * L->d.top_k);
@@ -471,9 +500,9 @@ int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16
                        ra, fa, n_router);
     QMOE_LAUNCHED();
     // kernel 2: routed gate/up + SwiGLU
-    if (g_prof_start) QMOE_HIP(hipEventRecord(g_prof_start, s));
+    if (g_prof_start && (rc = record_event(g_prof_start, s))) return rc;
     if ((rc = launch_gu(fa, 1, s))) return rc;
-    if (g_prof_stop) QMOE_HIP(hipEventRecord(g_prof_stop, s));
+    if (g_prof_stop && (rc = record_event(g_prof_stop, s))) return rc;
     // kernel 3: routed + shared down projection, combine in the last workgroup per tile
     if (!sh) fa.shared = nullptr;
     if ((rc = launch_d(fa, sh, s))) return rc;
@@ -497,8 +526,8 @@ int qmoe_event_destroy(void *event) {
 
 int qmoe_event_record(void *event, qmoe_stream_t stream) {
   if (!event) return fail(QMOE_ERR_ARG, "event is NULL");
-  QMOE_HIP(hipEventRecord((hipEvent_t)event, (hipStream_t)stream));
-  return ok();
+  int rc = record_event((hipEvent_t)event, (hipStream_t)stream);
+  return rc ? rc : ok();
 }
 
 int qmoe_event_elapsed_ms(void *start, void *stop, float *ms_out) {

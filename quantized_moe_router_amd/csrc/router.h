@@ -47,7 +47,9 @@ inline size_t router_lds_bytes(int H) {
 }
 
 // ---------------------------------------------------------------- top-k of one token (one wave)
-// Exact order: larger logit first, equal logits -> lower expert index.
+// Exact order: larger logit first, equal logits -> lower expert index.  A NaN logit ranks
+// as -inf, so every selected index is a valid expert id whatever the logits hold (the
+// sentinel index of an empty candidate always loses to a real expert).
 QMOE_DEV void topk_one_token(const float *lrow, int E, int k, const float *pes,
                              int32_t *idx_out, float *w_out) {
   const int lane = threadIdx.x % WAVE;
@@ -55,7 +57,8 @@ QMOE_DEV void topk_one_token(const float *lrow, int E, int k, const float *pes,
 #pragma unroll
   for (int j = 0; j < MAX_EXPERTS / WAVE; ++j) {
     const int e = lane + WAVE * j;
-    v[j] = (e < E) ? lrow[e] : -INFINITY;
+    const float l = (e < E) ? lrow[e] : -INFINITY;
+    v[j] = (l == l) ? l : -INFINITY;
   }
   unsigned taken = 0;
   float myv = 0.f;
@@ -89,7 +92,8 @@ QMOE_DEV void topk_one_token(const float *lrow, int E, int k, const float *pes,
 }
 
 // ---------------------------------------------------------------- bucketing (one workgroup)
-// Stable counting sort of N = T*k assignments by expert.  Counts via an LDS histogram; the
+// Stable counting sort of N = T*k assignments by expert (ids outside [0, E) are dropped).
+// Counts via an LDS histogram; the
 // rank of an assignment among the earlier ones of its expert from wave ballots (one ballot
 // per distinct expert in a wave) plus a per-expert cursor advanced wave by wave in order.
 // lds: at least (E + 1) * 4 + 64 * 4 bytes.
@@ -102,7 +106,10 @@ QMOE_DEV void bucket_block(const int32_t *idx, int N, int E, int32_t *counts, in
   const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
   for (int e = tid; e < E; e += NT) cnt[e] = 0;
   __syncthreads();
-  for (int f = tid; f < N; f += NT) atomicAdd(&cnt[idx[f]], 1);
+  for (int f = tid; f < N; f += NT) {
+    const int e = idx[f];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
+  }
   __syncthreads();
   // exclusive scan of counts and of (count > 0) flags, E <= MAX_EXPERTS
   const int per = (E + NT - 1) / NT;
@@ -142,21 +149,22 @@ QMOE_DEV void bucket_block(const int32_t *idx, int N, int E, int32_t *counts, in
   for (int base = 0; base < N; base += NT) {
     const int f = base + tid;
     const int e = (f < N) ? idx[f] : -1;
+    const bool valid = (f < N) && ((unsigned)e < (unsigned)E);
     // rank among lower lanes of this wave with the same expert, and the wave's count of it
     int rank = 0, tot = 0;
-    unsigned long long pending = __ballot(f < N);
+    unsigned long long pending = __ballot(valid);
     while (pending) {
       const int leader = __ffsll((long long)pending) - 1;
       const int el = __shfl(e, leader, WAVE);
-      const unsigned long long same = __ballot(e == el && f < N);
-      if (e == el && f < N) {
+      const unsigned long long same = __ballot(valid && e == el);
+      if (valid && e == el) {
         rank = __popcll(same & ((1ull << lane) - 1ull));
         tot = __popcll(same);
       }
       pending &= ~same;
     }
     for (int w = 0; w < NW; ++w) {
-      if (wv == w && f < N) {
+      if (wv == w && valid) {
         const int cur = cnt[e];
         sorted[cur + rank] = f;
         __builtin_amdgcn_wave_barrier();

@@ -136,6 +136,40 @@ def test_router_zero_input():
     assert np.allclose(w.cpu().numpy(), np.tile(li.pes[:2] / 2, (3, 1)), rtol=1e-6)
 
 
+def test_nonfinite_input_routes_to_valid_experts():
+    """Regression: NaN logits once left an out-of-range expert id in the top-k."""
+    ops = _ops()
+    cfg = G.config("gemma4_26b_a4b_decode")
+    pl, _ = layer("gemma4_26b_a4b_decode")
+    x = torch.zeros(3, cfg.hidden, dtype=torch.int16, device=DEV)
+    x[0] = 0x7FC0                               # NaN everywhere
+    x[1, :7] = 0x7F80                           # a few +inf
+    xb, xr = _stacks().hidden(cfg, 5, 1)
+    x[2] = xr[0]
+    ws = ops.workspace(pl.dims, 3)
+    idx, w = ops.router_topk(pl.dims, pl.router, x, ws)
+    out = ops.layer_forward(pl.weights, x, ws)
+    torch.cuda.synchronize()
+    i = idx.cpu().numpy()
+    assert np.all((i >= 0) & (i < cfg.experts))
+    assert i[0].tolist() == list(range(cfg.top_k))        # all NaN: ties -> lowest ids
+    assert all(len(set(r)) == cfg.top_k for r in i.tolist())
+    assert out.shape == (3, cfg.hidden)
+
+
+def test_bucket_drops_out_of_range_ids():
+    ops = _ops()
+    from quantized_moe_router_amd._lib import make_dims
+    idx = np.array([[3, 7], [-1, 3], [16, 2], [7, 2]], np.int32)
+    dims = make_dims(64, 16, 2, 64, 0)
+    counts, offsets, srt, active, n_active = ops.bucket(dims, torch.from_numpy(idx).to(DEV))
+    c = counts.cpu().numpy()
+    assert c[[2, 3, 7]].tolist() == [2, 2, 2] and c.sum() == 6
+    assert offsets.cpu().numpy()[-1] == 6
+    assert srt.cpu().numpy()[:6].tolist() == [5, 7, 0, 3, 1, 6]
+    assert int(n_active.cpu()[0]) == 3
+
+
 # ------------------------------------------------------------------ bucket
 
 @pytest.mark.parametrize("T,k,E", [(1, 8, 128), (4, 2, 16), (16, 10, 512), (128, 8, 128),
