@@ -31,15 +31,7 @@ struct FfnArgs {
   const float *topk_w;        // [T, k]
   uint16_t *out;              // [T, H] bf16
   float *out_f32;             // [T, H] or null
-  unsigned *cnt_tile;         // [H/32] completion counters
   int gu_shared_only;         // gate/up launch covers only the shared expert's tiles
-};
-
-template <int MB>
-struct TokList {
-  int tok[MB];   // token index of each row of the block
-  int hpos[MB];  // row of h (and, for the down kernel, the source row of h)
-  int ypos[MB];  // row of y to write (down kernel)
 };
 
 // Resolve the rows handled by a workgroup of slot `slot` (routed) or the shared slot.
@@ -72,14 +64,88 @@ QMOE_DEV int token_of(const FfnArgs &a, int p) {
   return min(max(a.sorted[p], 0), a.T * a.k - 1) / a.k;
 }
 
+// ---------------------------------------------------------------- staging helpers
+// Stage mb activation rows (bf16, row r read from src + rowsel(r) * K) into LDS, with the
+// sum of every 32 consecutive elements (fp32) next to them.
+template <int NT, class RowSel>
+QMOE_DEV void stage_rows_bf16(const uint16_t *src, int K, int mb, RowSel rowsel, uint16_t *dst,
+                              float *sums) {
+  const int n8 = K / 8;
+  for (int c = threadIdx.x; c < mb * n8; c += NT) {
+    const int i = c / n8, cc = c % n8;
+    const qmoe_u32x4 v = *(const qmoe_u32x4 *)(src + (size_t)rowsel(i) * K + 8 * cc);
+    *(qmoe_u32x4 *)(dst + (size_t)i * K + 8 * cc) = v;
+    float p = bf16lo(v.x) + bf16hi(v.x) + bf16lo(v.y) + bf16hi(v.y) + bf16lo(v.z) +
+              bf16hi(v.z) + bf16lo(v.w) + bf16hi(v.w);
+    p += __shfl_xor(p, 1, WAVE);
+    p += __shfl_xor(p, 2, WAVE);
+    if ((cc & 3) == 0) sums[i * (K / 32) + cc / 4] = p;
+  }
+}
+
+// Same for h carried as hi/lo bf16 planes; the sums are of hi + lo.
+template <int NT, class RowSel>
+QMOE_DEV void stage_rows_hilo(const uint16_t *src_hi, const uint16_t *src_lo, int K, int mb,
+                              RowSel rowsel, uint16_t *dst_hi, uint16_t *dst_lo, float *sums) {
+  const int n8 = K / 8;
+  for (int c = threadIdx.x; c < mb * n8; c += NT) {
+    const int i = c / n8, cc = c % n8;
+    const size_t row = (size_t)rowsel(i);
+    const qmoe_u32x4 vh = *(const qmoe_u32x4 *)(src_hi + row * K + 8 * cc);
+    const qmoe_u32x4 vl = *(const qmoe_u32x4 *)(src_lo + row * K + 8 * cc);
+    *(qmoe_u32x4 *)(dst_hi + (size_t)i * K + 8 * cc) = vh;
+    *(qmoe_u32x4 *)(dst_lo + (size_t)i * K + 8 * cc) = vl;
+    float p = (bf16lo(vh.x) + bf16lo(vl.x)) + (bf16hi(vh.x) + bf16hi(vl.x)) +
+              (bf16lo(vh.y) + bf16lo(vl.y)) + (bf16hi(vh.y) + bf16hi(vl.y)) +
+              (bf16lo(vh.z) + bf16lo(vl.z)) + (bf16hi(vh.z) + bf16hi(vl.z)) +
+              (bf16lo(vh.w) + bf16lo(vl.w)) + (bf16hi(vh.w) + bf16hi(vl.w));
+    p += __shfl_xor(p, 1, WAVE);
+    p += __shfl_xor(p, 2, WAVE);
+    if ((cc & 3) == 0) sums[i * (K / 32) + cc / 4] = p;
+  }
+}
+
+QMOE_DEV void lds_row16(const uint16_t *p, uint32_t v[16]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const qmoe_u32x4 t4 = *(const qmoe_u32x4 *)(p + 8 * q);
+    v[4 * q] = t4.x; v[4 * q + 1] = t4.y; v[4 * q + 2] = t4.z; v[4 * q + 3] = t4.w;
+  }
+}
+
+// Contribution of one k-step (32 codes of this lane, scale|bias word sb) to a row:
+//   s * sum (128+q) x + (b - 128 s) * sum x
+QMOE_DEV float kstep_bf16(const qmoe_u32x4 cv, uint32_t sb, const uint16_t *xrow, float xsum) {
+  const uint32_t w4[4] = {cv.x, cv.y, cv.z, cv.w};
+  uint32_t xv[16];
+  lds_row16(xrow, xv);
+  const float s = bf16lo(sb), b = bf16hi(sb);
+  const float d = dot32_q4_bf16(w4, xv);
+  return fmaf(s, d, fmaf(-128.f, s, b) * xsum);
+}
+
+QMOE_DEV float kstep_hilo(const qmoe_u32x4 cv, uint32_t sb, const uint16_t *hrow,
+                          const uint16_t *lrow, float hsum) {
+  const uint32_t w4[4] = {cv.x, cv.y, cv.z, cv.w};
+  uint32_t xh[16], xl[16];
+  lds_row16(hrow, xh);
+  lds_row16(lrow, xl);
+  const float s = bf16lo(sb), b = bf16hi(sb);
+  const float d = dot32_q4_bf16(w4, xh) + dot32_q4_bf16(w4, xl);
+  return fmaf(s, d, fmaf(-128.f, s, b) * hsum);
+}
+
 // ---------------------------------------------------------------- gate/up tile
 // LDS: x [MB][H] bf16, xs [MB][H/32] fp32, red [W][MB][32] fp32
 template <int W, int MB>
-QMOE_DEV size_t gu_lds_bytes(int H) {
+inline __host__ __device__ size_t gu_lds_bytes(int H) {
   return (size_t)MB * H * 2 + (size_t)MB * (H / 32) * 4 + (size_t)W * MB * 32 * 4;
 }
 
-template <int W, int MB>
+// One tile (16 gate rows + the 16 matching up rows) for the rows of slot `sr`, split-K over
+// W waves; each wave loads its k-steps in batches of KB (all loads of a batch in flight
+// together, out-of-range entries re-read the last valid k-step and are not used).
+template <int W, int MB, int KB>
 QMOE_DEV void gu_tile(const FfnArgs &a, const SlotRows &sr, int tile, char *smem) {
   const int H = a.H;
   const int I = sr.shared ? a.Is : a.I;
@@ -90,48 +156,32 @@ QMOE_DEV void gu_tile(const FfnArgs &a, const SlotRows &sr, int tile, char *smem
   float *xs = (float *)(smem + (size_t)MB * H * 2);              // [MB][H/32]
   float *red = xs + MB * (H / 32);                               // [W][MB][32]
   const uint8_t *tbase = sr.blk + (size_t)tile * KS * KSTEP_BYTES;
-  const int ks0 = (KS * wv) / W, ks1 = (KS * (wv + 1)) / W;
+  const int ks0 = (KS * wv) / W, nk = (KS * (wv + 1)) / W - ks0;
   for (int r0 = 0; r0 < sr.m; r0 += MB) {
     const int mb = min(MB, sr.m - r0);
-    // stage activations and their 32-element sums
-    const int n8 = H / 8;
-    for (int c = tid; c < MB * n8; c += W * WAVE) {
-      const int i = c / n8, cc = c % n8;
-      if (i < mb) {
-        const int t = sr.shared ? (r0 + i) : token_of(a, sr.beg + r0 + i);
-        const qmoe_u32x4 v = *(const qmoe_u32x4 *)(a.x + (size_t)t * H + 8 * cc);
-        *(qmoe_u32x4 *)(xl + (size_t)i * H + 8 * cc) = v;
-        float p = bf16lo(v.x) + bf16hi(v.x) + bf16lo(v.y) + bf16hi(v.y) + bf16lo(v.z) +
-                  bf16hi(v.z) + bf16lo(v.w) + bf16hi(v.w);
-        p += __shfl_xor(p, 1, WAVE);
-        p += __shfl_xor(p, 2, WAVE);
-        if ((cc & 3) == 0) xs[i * (H / 32) + cc / 4] = p;
-      }
-    }
+    stage_rows_bf16<W * WAVE>(a.x, H, mb, [&](int i) {
+      return sr.shared ? (r0 + i) : token_of(a, sr.beg + r0 + i); }, xl, xs);
     __syncthreads();
     float acc[MB];
 #pragma unroll
     for (int i = 0; i < MB; ++i) acc[i] = 0.f;
-    for (int ks = ks0; ks < ks1; ++ks) {
-      const uint8_t *kb = tbase + (size_t)ks * KSTEP_BYTES;
-      const qmoe_u32x4 cv = *(const qmoe_u32x4 *)(kb + lane * 16);
-      const uint32_t sb = *(const uint32_t *)(kb + 1024 + rr * 4);
-      const uint32_t w4[4] = {cv.x, cv.y, cv.z, cv.w};
-      const float s = bf16lo(sb), b = bf16hi(sb);
-      const float bb = fmaf(-128.f, s, b);
+    for (int kc = 0; kc < nk; kc += KB) {
+      qmoe_u32x4 cv[KB];
+      uint32_t sb[KB];
 #pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        if (i < mb) {
-          const uint32_t *xp = (const uint32_t *)(xl + (size_t)i * H + ks * GROUP + half * 32);
-          uint32_t xv[16];
+      for (int u = 0; u < KB; ++u) {
+        const uint8_t *kb = tbase + (size_t)(ks0 + min(kc + u, nk - 1)) * KSTEP_BYTES;
+        cv[u] = *(const qmoe_u32x4 *)(kb + lane * 16);
+        sb[u] = *(const uint32_t *)(kb + 1024 + rr * 4);
+      }
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const qmoe_u32x4 t4 = *(const qmoe_u32x4 *)(xp + 4 * q);
-            xv[4 * q] = t4.x; xv[4 * q + 1] = t4.y; xv[4 * q + 2] = t4.z; xv[4 * q + 3] = t4.w;
-          }
-          const float d = dot32_q4_bf16(w4, xv);
-          acc[i] = fmaf(s, d, acc[i]);
-          acc[i] = fmaf(bb, xs[i * (H / 32) + ks * 2 + half], acc[i]);
+      for (int u = 0; u < KB; ++u) {
+        if (kc + u < nk) {
+          const int col = (ks0 + kc + u) * GROUP + half * 32;
+#pragma unroll
+          for (int i = 0; i < MB; ++i)
+            if (i < mb)
+              acc[i] += kstep_bf16(cv[u], sb[u], xl + (size_t)i * H + col, xs[i * (H / 32) + col / 32]);
         }
       }
     }
@@ -162,7 +212,7 @@ QMOE_DEV void gu_tile(const FfnArgs &a, const SlotRows &sr, int tile, char *smem
 }
 
 // grid.x = n_slots * (I/16) routed tiles, then Is/16 shared tiles (if a.shared)
-template <int W, int MB>
+template <int W, int MB, int KB>
 __global__ void __launch_bounds__(W * WAVE) gu_kernel(FfnArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int tiles_r = a.I / 16;
@@ -177,17 +227,17 @@ __global__ void __launch_bounds__(W * WAVE) gu_kernel(FfnArgs a) {
     slot_rows(a, 0, true, sr);
     tile = bid - n_routed;
   }
-  gu_tile<W, MB>(a, sr, tile, smem);
+  gu_tile<W, MB, KB>(a, sr, tile, smem);
 }
 
-// ---------------------------------------------------------------- down tile
+// ---------------------------------------------------------------- down tile (per slot)
 // LDS: h hi [MB][K] bf16, h lo [MB][K] bf16, hsum [MB][K/32] fp32, red [W][MB][32] fp32
 template <int W, int MB>
-QMOE_DEV size_t d_lds_bytes(int K) {
+inline __host__ __device__ size_t d_lds_bytes(int K) {
   return (size_t)MB * K * 4 + (size_t)MB * (K / 32) * 4 + (size_t)W * MB * 32 * 4;
 }
 
-template <int W, int MB>
+template <int W, int MB, int KB>
 QMOE_DEV void d_tile(const FfnArgs &a, const SlotRows &sr, int tile, char *smem) {
   const int H = a.H;
   const int K = sr.shared ? a.Is : a.I;
@@ -200,55 +250,35 @@ QMOE_DEV void d_tile(const FfnArgs &a, const SlotRows &sr, int tile, char *smem)
   float *red = hs + MB * (K / 32);                              // [W][MB][32]
   const BlockGeom geo = block_geom(H, K);
   const uint8_t *tbase = sr.blk + geo.gu_bytes + (size_t)tile * KS * KSTEP_BYTES;
-  const int ks0 = (KS * wv) / W, ks1 = (KS * (wv + 1)) / W;
+  const int ks0 = (KS * wv) / W, nk = (KS * (wv + 1)) / W - ks0;
   const uint16_t *src_hi = sr.shared ? a.hs_hi : a.hr_hi;
   const uint16_t *src_lo = sr.shared ? a.hs_lo : a.hr_lo;
   for (int r0 = 0; r0 < sr.m; r0 += MB) {
     const int mb = min(MB, sr.m - r0);
-    const int n8 = K / 8;
-    for (int c = tid; c < MB * n8; c += W * WAVE) {
-      const int i = c / n8, cc = c % n8;
-      if (i < mb) {
-        const size_t row = (size_t)(sr.beg + r0 + i);
-        const qmoe_u32x4 vh = *(const qmoe_u32x4 *)(src_hi + row * K + 8 * cc);
-        const qmoe_u32x4 vl = *(const qmoe_u32x4 *)(src_lo + row * K + 8 * cc);
-        *(qmoe_u32x4 *)(hh + (size_t)i * K + 8 * cc) = vh;
-        *(qmoe_u32x4 *)(hl + (size_t)i * K + 8 * cc) = vl;
-        float p = (bf16lo(vh.x) + bf16lo(vl.x)) + (bf16hi(vh.x) + bf16hi(vl.x)) +
-                  (bf16lo(vh.y) + bf16lo(vl.y)) + (bf16hi(vh.y) + bf16hi(vl.y)) +
-                  (bf16lo(vh.z) + bf16lo(vl.z)) + (bf16hi(vh.z) + bf16hi(vl.z)) +
-                  (bf16lo(vh.w) + bf16lo(vl.w)) + (bf16hi(vh.w) + bf16hi(vl.w));
-        p += __shfl_xor(p, 1, WAVE);
-        p += __shfl_xor(p, 2, WAVE);
-        if ((cc & 3) == 0) hs[i * (K / 32) + cc / 4] = p;
-      }
-    }
+    stage_rows_hilo<W * WAVE>(src_hi, src_lo, K, mb, [&](int i) { return sr.beg + r0 + i; },
+                              hh, hl, hs);
     __syncthreads();
     float acc[MB];
 #pragma unroll
     for (int i = 0; i < MB; ++i) acc[i] = 0.f;
-    for (int ks = ks0; ks < ks1; ++ks) {
-      const uint8_t *kb = tbase + (size_t)ks * KSTEP_BYTES;
-      const qmoe_u32x4 cv = *(const qmoe_u32x4 *)(kb + lane * 16);
-      const uint32_t sb = *(const uint32_t *)(kb + 1024 + rr * 4);
-      const uint32_t w4[4] = {cv.x, cv.y, cv.z, cv.w};
-      const float s = bf16lo(sb), b = bf16hi(sb);
-      const float bb = fmaf(-128.f, s, b);
+    for (int kc = 0; kc < nk; kc += KB) {
+      qmoe_u32x4 cv[KB];
+      uint32_t sb[KB];
 #pragma unroll
-      for (int i = 0; i < MB; ++i) {
-        if (i < mb) {
-          const size_t off = (size_t)i * K + ks * GROUP + half * 32;
-          uint32_t xh[16], xlo[16];
+      for (int u = 0; u < KB; ++u) {
+        const uint8_t *kb = tbase + (size_t)(ks0 + min(kc + u, nk - 1)) * KSTEP_BYTES;
+        cv[u] = *(const qmoe_u32x4 *)(kb + lane * 16);
+        sb[u] = *(const uint32_t *)(kb + 1024 + rr * 4);
+      }
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const qmoe_u32x4 th = *(const qmoe_u32x4 *)((const uint32_t *)(hh + off) + 4 * q);
-            const qmoe_u32x4 tl = *(const qmoe_u32x4 *)((const uint32_t *)(hl + off) + 4 * q);
-            xh[4 * q] = th.x; xh[4 * q + 1] = th.y; xh[4 * q + 2] = th.z; xh[4 * q + 3] = th.w;
-            xlo[4 * q] = tl.x; xlo[4 * q + 1] = tl.y; xlo[4 * q + 2] = tl.z; xlo[4 * q + 3] = tl.w;
-          }
-          const float d = dot32_q4_bf16(w4, xh) + dot32_q4_bf16(w4, xlo);
-          acc[i] = fmaf(s, d, acc[i]);
-          acc[i] = fmaf(bb, hs[i * (K / 32) + ks * 2 + half], acc[i]);
+      for (int u = 0; u < KB; ++u) {
+        if (kc + u < nk) {
+          const int col = (ks0 + kc + u) * GROUP + half * 32;
+#pragma unroll
+          for (int i = 0; i < MB; ++i)
+            if (i < mb)
+              acc[i] += kstep_hilo(cv[u], sb[u], hh + (size_t)i * K + col, hl + (size_t)i * K + col,
+                                   hs[i * (K / 32) + col / 32]);
         }
       }
     }
@@ -272,41 +302,101 @@ QMOE_DEV void d_tile(const FfnArgs &a, const SlotRows &sr, int tile, char *smem)
   }
 }
 
-// combine of one 32-row tile for every token (fused into the down kernel of the layer path)
-QMOE_DEV void combine_tile(const FfnArgs &a, int tile) {
-  const int H = a.H;
-  for (int o = threadIdx.x; o < a.T * 32; o += blockDim.x) {
-    const int t = o / 32, col = 32 * tile + o % 32;
-    float acc = 0.f;
-    for (int j = 0; j < a.k; ++j)
-      acc = fmaf(a.topk_w[(size_t)t * a.k + j], a.y[((size_t)t * a.k + j) * H + col], acc);
-    if (a.y_sh) acc += a.y_sh[(size_t)t * H + col];
-    acc += bf16_to_f32(a.x[(size_t)t * H + col]);
-    a.out[(size_t)t * H + col] = (uint16_t)f32_to_bf16_bits(acc);
-    if (a.out_f32) a.out_f32[(size_t)t * H + col] = acc;
-  }
-}
-
 // grid = (H/32 tiles, n_slots routed slots + 1 shared slot if a.shared && a.y_sh)
-template <int W, int MB>
+template <int W, int MB, int KB>
 __global__ void __launch_bounds__(W * WAVE) d_kernel(FfnArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int tile = blockIdx.x;
   const int slot = blockIdx.y;
   SlotRows sr;
   const bool shared = slot >= a.n_slots;
-  if (slot_rows(a, slot, shared, sr)) d_tile<W, MB>(a, sr, tile, smem);
-  if (a.out == nullptr) return;
-  // the last workgroup of this row tile adds routed rows, shared row and residual
-  __shared__ int last;
-  __threadfence();
+  if (slot_rows(a, slot, shared, sr)) d_tile<W, MB, KB>(a, sr, tile, smem);
+}
+
+// ---------------------------------------------------------------- one-token down + combine
+// Decode with one token: a workgroup owns one 32-row output tile and runs the down
+// projection of every routed slot and of the shared block for those rows, weighting each
+// routed k-step by its router weight, then adds the residual:
+//   out[r] = bf16( x[r] + sum_slots w_slot * (W_down,slot h_slot)[r] + (W_down,sh h_sh)[r] )
+// The (slot, k-step) items are split evenly over the W waves.  No cross-workgroup traffic.
+// LDS: h hi/lo of every slot [n_slots*I + Is] x 2 bf16, sums, red [W][32].
+inline __host__ __device__ size_t d1_lds_bytes(int n_slots, int I, int Is, int W) {
+  const size_t cols = (size_t)n_slots * I + Is;
+  return cols * 4 + cols / 32 * 4 + (size_t)W * 32 * 4;
+}
+
+template <int W, int KB>
+__global__ void __launch_bounds__(W * WAVE) d1_kernel(FfnArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const int H = a.H, I = a.I, Is = a.shared ? a.Is : 0;
+  const int tile = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
+  const int rr = lane % 32, half = lane / 32;
+  const int ns = min(min(*a.n_active, a.n_slots), a.n_experts);   // routed slots (1 row each)
+  const int cols = ns * I + Is;
+  uint16_t *hh = (uint16_t *)smem;
+  uint16_t *hl = hh + (size_t)a.n_slots * I + Is;
+  float *hs = (float *)(hl + (size_t)a.n_slots * I + Is);
+  float *red = hs + ((size_t)a.n_slots * I + Is) / 32;
+  // routed rows 0..ns-1 of the bucket (one token: one row per active expert), then shared row
+  stage_rows_hilo<W * WAVE>(a.hr_hi, a.hr_lo, I, ns, [&](int i) { return i; }, hh, hl, hs);
+  if (Is) stage_rows_hilo<W * WAVE>(a.hs_hi, a.hs_lo, Is, 1, [&](int) { return 0; },
+                                    hh + (size_t)ns * I, hl + (size_t)ns * I, hs + ns * I / 32);
   __syncthreads();
-  if (threadIdx.x == 0) last = (atomicAdd(&a.cnt_tile[tile], 1u) == gridDim.y - 1);
+  const BlockGeom gr = block_geom(H, I);
+  const int KSr = I / GROUP, KSs = Is / GROUP;
+  const int n_items = ns * KSr + KSs;
+  const int it0 = (n_items * wv) / W, nk = (n_items * (wv + 1)) / W - it0;
+  float acc = 0.f;
+  for (int kc = 0; kc < nk; kc += KB) {
+    qmoe_u32x4 cv[KB];
+    uint32_t sb[KB];
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      const int it = it0 + min(kc + u, nk - 1);
+      const uint8_t *kb;
+      if (it < ns * KSr) {
+        const int slot = it / KSr, ks = it % KSr;
+        const int e = min(max(a.active[slot], 0), a.n_experts - 1);
+        kb = a.experts + (size_t)e * a.stride + gr.gu_bytes +
+             ((size_t)tile * KSr + ks) * KSTEP_BYTES;
+      } else {
+        const BlockGeom gs = block_geom(H, Is);
+        kb = a.shared + gs.gu_bytes + ((size_t)tile * KSs + (it - ns * KSr)) * KSTEP_BYTES;
+      }
+      cv[u] = *(const qmoe_u32x4 *)(kb + lane * 16);
+      sb[u] = *(const uint32_t *)(kb + 1024 + rr * 4);
+    }
+#pragma unroll
+    for (int u = 0; u < KB; ++u) {
+      if (kc + u < nk) {
+        const int it = it0 + kc + u;
+        int col;
+        float wt;
+        if (it < ns * KSr) {
+          const int slot = it / KSr;
+          col = slot * I + (it % KSr) * GROUP + half * 32;
+          wt = a.topk_w[min(max(a.sorted[slot], 0), a.k - 1)];
+        } else {
+          col = ns * I + (it - ns * KSr) * GROUP + half * 32;
+          wt = 1.f;
+        }
+        acc = fmaf(wt, kstep_hilo(cv[u], sb[u], hh + col, hl + col, hs[col / 32]), acc);
+      }
+    }
+  }
+  (void)cols;
+  acc += __shfl_xor(acc, 32, WAVE);
+  if (half == 0) red[wv * 32 + rr] = acc;
   __syncthreads();
-  if (!last) return;
-  __threadfence();
-  combine_tile(a, tile);
-  if (threadIdx.x == 0) a.cnt_tile[tile] = 0u;
+  if (tid < 32) {
+    float y = 0.f;
+    for (int w = 0; w < W; ++w) y += red[w * 32 + tid];
+    const int col = 32 * tile + tid;
+    const float o = bf16_to_f32(a.x[col]) + y;
+    a.out[col] = (uint16_t)f32_to_bf16_bits(o);
+    if (a.out_f32) a.out_f32[col] = o;
+  }
 }
 
 // ---------------------------------------------------------------- standalone combine

@@ -23,8 +23,12 @@ namespace {
 
 constexpr int VERSION = 100;               // 0.1.0
 constexpr size_t COUNTER_BYTES = 128 * 1024;
-constexpr int GU_W = 4, GU_MB = 8;
-constexpr int D_W = 4, D_MB = 8;
+constexpr int GU_W = 4;     // waves per gate/up workgroup (split-K)
+constexpr int D_W = 4;      // waves per per-slot down workgroup (split-K)
+constexpr int D1_W = 16;    // waves per one-token down workgroup
+constexpr int KB = 12;      // k-steps loaded per batch by a wave
+constexpr int MB_MAX = 8;   // rows (tokens) per activation block
+constexpr size_t D1_LDS_MAX = 144 * 1024;
 constexpr int MAX_T = 65536;
 
 thread_local std::string g_err;
@@ -217,6 +221,7 @@ int launch_router(const RouterArgs &a, size_t smem, hipStream_t s) {
 }
 
 // layer path: router workgroups followed by shared gate/up workgroups in one launch
+template <int MB>
 __global__ void __launch_bounds__(ROUTER_THREADS) router_shared_kernel(RouterArgs ra, FfnArgs fa,
                                                                        int n_router) {
   extern __shared__ __align__(16) char smem[];
@@ -227,7 +232,7 @@ __global__ void __launch_bounds__(ROUTER_THREADS) router_shared_kernel(RouterArg
   } else {
     SlotRows sr;
     slot_rows(fa, 0, true, sr);
-    gu_tile<GU_W, GU_MB>(fa, sr, blockIdx.x - n_router, smem);
+    gu_tile<GU_W, MB, KB>(fa, sr, blockIdx.x - n_router, smem);
   }
 }
 static_assert(GU_W * WAVE == ROUTER_THREADS, "fused router/shared kernel uses one block size");
@@ -251,11 +256,72 @@ int record_event(hipEvent_t e, hipStream_t s) {
   return QMOE_OK;
 }
 
-size_t gu_smem(int H) {
-  return (size_t)GU_MB * H * 2 + (size_t)GU_MB * (H / 32) * 4 + (size_t)GU_W * GU_MB * 32 * 4;
+// rows per activation block: one-token calls stage a single row
+inline int mb_for(int T) { return T == 1 ? 1 : MB_MAX; }
+
+size_t gu_smem(int H, int mb) {
+  return mb == 1 ? gu_lds_bytes<GU_W, 1>(H) : gu_lds_bytes<GU_W, MB_MAX>(H);
 }
-size_t d_smem(int K) {
-  return (size_t)D_MB * K * 4 + (size_t)D_MB * (K / 32) * 4 + (size_t)D_W * D_MB * 32 * 4;
+size_t d_smem(int K, int mb) {
+  return mb == 1 ? d_lds_bytes<D_W, 1>(K) : d_lds_bytes<D_W, MB_MAX>(K);
+}
+
+static FfnArgs make_ffn_args(const qmoe_layer *L, const uint16_t *x, int T, const int32_t *offsets,
+                             const int32_t *sorted, const int32_t *active, const int32_t *n_active,
+                             float *y, float *y_sh, void *ws, int Tws) {
+  FfnArgs a;
+  memset(&a, 0, sizeof a);
+  const WsLayout wl = ws_layout(&L->d, Tws);
+  a.experts = (const uint8_t *)L->experts;
+  a.stride = L->expert_stride;
+  a.shared = (const uint8_t *)L->shared;
+  a.H = L->d.hidden; a.I = L->d.inter; a.Is = L->d.shared_inter; a.k = L->d.top_k; a.T = T;
+  a.n_experts = L->d.n_experts;
+  a.x = x;
+  a.offsets = offsets; a.sorted = sorted; a.active = active; a.n_active = n_active;
+  a.n_slots = std::min(L->d.n_experts, T * L->d.top_k);
+  a.hr_hi = at<uint16_t>(ws, wl.hr_hi); a.hr_lo = at<uint16_t>(ws, wl.hr_lo);
+  a.hs_hi = at<uint16_t>(ws, wl.hs_hi); a.hs_lo = at<uint16_t>(ws, wl.hs_lo);
+  a.y = y; a.y_sh = y_sh;
+  return a;
+}
+
+template <int MB>
+static int launch_gu_t(const FfnArgs &a, int n, hipStream_t s) {
+  const size_t smem = gu_lds_bytes<GU_W, MB>(a.H);
+  int rc = set_lds(gu_kernel<GU_W, MB, KB>, smem);
+  if (rc) return rc;
+  hipLaunchKernelGGL((gu_kernel<GU_W, MB, KB>), dim3(n), dim3(GU_W * WAVE), smem, s, a);
+  QMOE_LAUNCHED();
+  return QMOE_OK;
+}
+
+static int launch_gu(FfnArgs a, int mode, hipStream_t s) {
+  // mode 0: routed + shared tiles, 1: routed only
+  const int tiles_r = a.I / 16;
+  const bool sh = (mode == 0) && a.shared && a.y_sh;
+  const int n = a.n_slots * tiles_r + (sh ? a.Is / 16 : 0);
+  a.gu_shared_only = 0;
+  if (!sh) a.shared = nullptr;
+  if (n == 0) return QMOE_OK;
+  return mb_for(a.T) == 1 ? launch_gu_t<1>(a, n, s) : launch_gu_t<MB_MAX>(a, n, s);
+}
+
+template <int MB>
+static int launch_d_t(const FfnArgs &a, int slots, int K, hipStream_t s) {
+  const size_t smem = d_lds_bytes<D_W, MB>(K);
+  int rc = set_lds(d_kernel<D_W, MB, KB>, smem);
+  if (rc) return rc;
+  hipLaunchKernelGGL((d_kernel<D_W, MB, KB>), dim3(a.H / TILE_ROWS, slots), dim3(D_W * WAVE),
+                     smem, s, a);
+  QMOE_LAUNCHED();
+  return QMOE_OK;
+}
+
+static int launch_d(FfnArgs a, bool with_shared, hipStream_t s) {
+  const int slots = a.n_slots + (with_shared ? 1 : 0);
+  const int K = std::max(a.I, with_shared ? a.Is : 0);
+  return mb_for(a.T) == 1 ? launch_d_t<1>(a, slots, K, s) : launch_d_t<MB_MAX>(a, slots, K, s);
 }
 
 }  // namespace
@@ -373,54 +439,6 @@ int qmoe_bucket(const qmoe_dims *d, const int32_t *topk_idx, int32_t T, int32_t 
   return ok();
 }
 
-static FfnArgs make_ffn_args(const qmoe_layer *L, const uint16_t *x, int T, const int32_t *offsets,
-                             const int32_t *sorted, const int32_t *active, const int32_t *n_active,
-                             float *y, float *y_sh, void *ws, int Tws) {
-  FfnArgs a;
-  memset(&a, 0, sizeof a);
-  const WsLayout wl = ws_layout(&L->d, Tws);
-  a.experts = (const uint8_t *)L->experts;
-  a.stride = L->expert_stride;
-  a.shared = (const uint8_t *)L->shared;
-  a.H = L->d.hidden; a.I = L->d.inter; a.Is = L->d.shared_inter; a.k = L->d.top_k; a.T = T;
-  a.n_experts = L->d.n_experts;
-  a.x = x;
-  a.offsets = offsets; a.sorted = sorted; a.active = active; a.n_active = n_active;
-  a.n_slots = std::min(L->d.n_experts, T * L->d.top_k);
-  a.hr_hi = at<uint16_t>(ws, wl.hr_hi); a.hr_lo = at<uint16_t>(ws, wl.hr_lo);
-  a.hs_hi = at<uint16_t>(ws, wl.hs_hi); a.hs_lo = at<uint16_t>(ws, wl.hs_lo);
-  a.y = y; a.y_sh = y_sh;
-  a.cnt_tile = at<unsigned>(ws, wl.cnt) + 64 + 16384;
-  return a;
-}
-
-static int launch_gu(FfnArgs a, int mode, hipStream_t s) {
-  // mode 0: routed + shared tiles, 1: routed only
-  const int tiles_r = a.I / 16;
-  const bool sh = (mode == 0) && a.shared && a.y_sh;
-  const int n = a.n_slots * tiles_r + (sh ? a.Is / 16 : 0);
-  a.gu_shared_only = 0;
-  if (!sh) a.shared = nullptr;
-  if (n == 0) return QMOE_OK;
-  const size_t smem = gu_smem(a.H);
-  int rc = set_lds(gu_kernel<GU_W, GU_MB>, smem);
-  if (rc) return rc;
-  hipLaunchKernelGGL((gu_kernel<GU_W, GU_MB>), dim3(n), dim3(GU_W * WAVE), smem, s, a);
-  QMOE_LAUNCHED();
-  return QMOE_OK;
-}
-
-static int launch_d(FfnArgs a, bool with_shared, hipStream_t s) {
-  const int slots = a.n_slots + (with_shared ? 1 : 0);
-  const size_t smem = d_smem(std::max(a.I, with_shared ? a.Is : 0));
-  int rc = set_lds(d_kernel<D_W, D_MB>, smem);
-  if (rc) return rc;
-  hipLaunchKernelGGL((d_kernel<D_W, D_MB>), dim3(a.H / TILE_ROWS, slots), dim3(D_W * WAVE), smem,
-                     s, a);
-  QMOE_LAUNCHED();
-  return QMOE_OK;
-}
-
 int qmoe_expert_ffn(const qmoe_layer *L, const uint16_t *x, int32_t T, const int32_t *offsets,
                     const int32_t *sorted, const int32_t *active, const int32_t *n_active,
                     float *y, float *y_shared_or_null, void *ws, size_t ws_bytes,
@@ -494,18 +512,39 @@ int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16
     fa.out_f32 = out_f32_or_null ? out_f32_or_null + (size_t)c0 * H : nullptr;
     const int n_router = ra.n_tb * ra.n_eb;
     const int n_sh = sh ? d->shared_inter / 16 : 0;
-    const size_t smem1 = std::max(router_smem(d), sh ? gu_smem(H) : (size_t)0);
-    if ((rc = set_lds(router_shared_kernel, smem1))) return rc;
-    hipLaunchKernelGGL(router_shared_kernel, dim3(n_router + n_sh), dim3(ROUTER_THREADS), smem1, s,
-                       ra, fa, n_router);
+    const int mb = mb_for(Tc);
+    const size_t smem1 = std::max(router_smem(d), sh ? gu_smem(H, mb) : (size_t)0);
+    if (mb == 1) {
+      if ((rc = set_lds(router_shared_kernel<1>, smem1))) return rc;
+      hipLaunchKernelGGL(router_shared_kernel<1>, dim3(n_router + n_sh), dim3(ROUTER_THREADS),
+                         smem1, s, ra, fa, n_router);
+    } else {
+      if ((rc = set_lds(router_shared_kernel<MB_MAX>, smem1))) return rc;
+      hipLaunchKernelGGL(router_shared_kernel<MB_MAX>, dim3(n_router + n_sh),
+                         dim3(ROUTER_THREADS), smem1, s, ra, fa, n_router);
+    }
     QMOE_LAUNCHED();
     // kernel 2: routed gate/up + SwiGLU
     if (g_prof_start && (rc = record_event(g_prof_start, s))) return rc;
     if ((rc = launch_gu(fa, 1, s))) return rc;
     if (g_prof_stop && (rc = record_event(g_prof_stop, s))) return rc;
-    // kernel 3: routed + shared down projection, combine in the last workgroup per tile
     if (!sh) fa.shared = nullptr;
-    if ((rc = launch_d(fa, sh, s))) return rc;
+    const size_t d1_smem = d1_lds_bytes(fa.n_slots, d->inter, sh ? d->shared_inter : 0, D1_W);
+    if (Tc == 1 && d1_smem <= D1_LDS_MAX) {
+      // kernel 3 (one token): down projection of all slots per output tile + combine
+      if ((rc = set_lds(d1_kernel<D1_W, 8>, d1_smem))) return rc;
+      hipLaunchKernelGGL((d1_kernel<D1_W, 8>), dim3(H / TILE_ROWS), dim3(D1_W * WAVE), d1_smem, s,
+                         fa);
+      QMOE_LAUNCHED();
+    } else {
+      // kernel 3: routed + shared down projection per slot; kernel 4: combine
+      if ((rc = launch_d(fa, sh, s))) return rc;
+      const size_t n = (size_t)Tc * H;
+      const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 8192);
+      hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, s, xc, fa.y, w, fa.y_sh, Tc,
+                         H, k, fa.out, fa.out_f32);
+      QMOE_LAUNCHED();
+    }
   }
   return ok();
 }

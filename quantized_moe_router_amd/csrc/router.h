@@ -15,7 +15,7 @@
 namespace qmoe {
 
 constexpr int ROUTER_TB = 4;     // tokens per router workgroup
-constexpr int ROUTER_EPW = 2;    // experts per wave
+constexpr int ROUTER_EPW = 1;    // experts per wave
 constexpr int ROUTER_WAVES = 4;
 constexpr int ROUTER_EPB = ROUTER_EPW * ROUTER_WAVES;  // experts per router workgroup
 constexpr int ROUTER_THREADS = ROUTER_WAVES * WAVE;
@@ -176,7 +176,7 @@ QMOE_DEV void bucket_block(const int32_t *idx, int N, int E, int32_t *counts, in
 }
 
 // ---------------------------------------------------------------- router logits
-// Workgroup (tb, eb): tokens [4 tb, 4 tb + 4) x experts [8 eb, 8 eb + 8).  Per token the
+// Workgroup (tb, eb): tokens [4 tb, 4 tb + 4) x experts [4 eb, 4 eb + 4).  Per token the
 // input is staged as z = x * router_scale (fp32) with per-16-element sums; the token's norm
 // factor f = (1/sqrt(H)) / sqrt(mean(x^2) + eps) multiplies the finished dot product:
 //   logit = f * sum_g [ s_g * sum_{h in g} q_h z_h + b_g * sum_{h in g} z_h ] + bias.
@@ -222,38 +222,50 @@ QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *sme
     }
     __syncthreads();
   }
-  // one wave per expert, lanes stride over 16-byte chunks of the expert's row
+  // one wave per expert; lane l holds chunks l, l+64, ... (16 codes each) of the expert's
+  // row, all loaded up front (H <= 8192 -> at most 8 chunks per lane)
+  constexpr int NCH = 8;
   const int n16 = H / 16;
   for (int ee = 0; ee < ROUTER_EPW; ++ee) {
     const int e = eb * ROUTER_EPB + wv * ROUTER_EPW + ee;
     if (e >= a.E) break;
+    const uint8_t *row = a.rq + (size_t)e * H;
+    qmoe_u32x4 v[NCH];
+    uint16_t sv[NCH], bv[NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) {
+      const int c = min(lane + WAVE * j, n16 - 1);
+      v[j] = *(const qmoe_u32x4 *)(row + 16 * c);
+      sv[j] = a.rs[(size_t)e * (H / GROUP) + c / 4];
+      bv[j] = a.rb[(size_t)e * (H / GROUP) + c / 4];
+    }
     float acc[ROUTER_TB];
 #pragma unroll
     for (int i = 0; i < ROUTER_TB; ++i) acc[i] = 0.f;
-    const uint8_t *row = a.rq + (size_t)e * H;
-    for (int c = lane; c < n16; c += WAVE) {
-      const qmoe_u32x4 v = *(const qmoe_u32x4 *)(row + 16 * c);
-      const int g = c / 4;
-      const float s = bf16_to_f32(a.rs[(size_t)e * (H / GROUP) + g]);
-      const float b = bf16_to_f32(a.rb[(size_t)e * (H / GROUP) + g]);
-      const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
-      float q[16];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        q[4 * d + 0] = (float)(w4[d] & 0xFFu);
-        q[4 * d + 1] = (float)((w4[d] >> 8) & 0xFFu);
-        q[4 * d + 2] = (float)((w4[d] >> 16) & 0xFFu);
-        q[4 * d + 3] = (float)(w4[d] >> 24);
-      }
+    for (int j = 0; j < NCH; ++j) {
+      const int c = lane + WAVE * j;
+      if (c < n16) {
+        const float s = bf16_to_f32(sv[j]), b = bf16_to_f32(bv[j]);
+        const uint32_t w4[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        float q[16];
 #pragma unroll
-      for (int i = 0; i < ROUTER_TB; ++i) {
-        if (i < nt) {
-          const float *zr = z + i * H + 16 * c;
-          float dq = 0.f;
+        for (int d = 0; d < 4; ++d) {
+          q[4 * d + 0] = (float)(w4[d] & 0xFFu);
+          q[4 * d + 1] = (float)((w4[d] >> 8) & 0xFFu);
+          q[4 * d + 2] = (float)((w4[d] >> 16) & 0xFFu);
+          q[4 * d + 3] = (float)(w4[d] >> 24);
+        }
 #pragma unroll
-          for (int j = 0; j < 16; ++j) dq = fmaf(q[j], zr[j], dq);
-          acc[i] = fmaf(s, dq, acc[i]);
-          acc[i] = fmaf(b, zs[i * (H / 16) + c], acc[i]);
+        for (int i = 0; i < ROUTER_TB; ++i) {
+          if (i < nt) {
+            const float *zr = z + i * H + 16 * c;
+            float dq = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) dq = fmaf(q[jj], zr[jj], dq);
+            acc[i] = fmaf(s, dq, acc[i]);
+            acc[i] = fmaf(b, zs[i * (H / 16) + c], acc[i]);
+          }
         }
       }
     }
