@@ -26,7 +26,11 @@ struct FfnArgs {
   uint16_t *hr_hi, *hr_lo;    // routed h [T*k, I] in bucket order
   uint16_t *hs_hi, *hs_lo;    // shared h [T, Is]
   float *y;                   // routed y [T*k, H] by flat id
-  float *y_sh;                // shared y [T, H] or null
+  float *y_sh;                // shared y [T, H] or null (one shared chunk)
+  float *y_sh_part;           // shared partials [n_sh_chunks][T, H] (several chunks)
+  const int32_t *slot_tab;    // [n_slots][4] {expert, first position, rows, first flat id} or null
+  int n_sh_chunks;            // down-projection workgroups per tile for the shared block
+  unsigned *cnt_tile;         // [H/32] completion counters of the fused combine
   // fused combine (down kernel of the layer path); out == null -> no combine
   const float *topk_w;        // [T, k]
   uint16_t *out;              // [T, H] bf16
@@ -39,29 +43,42 @@ struct SlotRows {
   const uint8_t *blk;
   int m;       // number of rows
   int beg;     // first bucket position (routed) / 0 (shared)
+  int first;   // flat assignment id of the first row (routed, from the slot table) or -1
   bool shared;
 };
 
 // Bucket data that would index outside the store or the assignment list makes the slot
-// empty instead (the buffers are caller-provided in the standalone entry point).
+// empty instead (the buffers are caller-provided in the standalone entry point).  With a
+// slot table (layer path) one 16-byte load resolves the slot.
 QMOE_DEV bool slot_rows(const FfnArgs &a, int slot, bool shared, SlotRows &r) {
+  r.first = -1;
   if (shared) {
     r.blk = a.shared; r.m = a.T; r.beg = 0; r.shared = true;
     return true;
   }
-  if (slot >= min(*a.n_active, a.n_experts)) return false;
-  const int e = a.active[slot];
+  int e;
+  if (a.slot_tab) {
+    const qmoe_u32x4 ent = *(const qmoe_u32x4 *)(a.slot_tab + 4 * slot);
+    e = (int)ent.x; r.beg = (int)ent.y; r.m = (int)ent.z; r.first = (int)ent.w;
+    if (r.m <= 0) return false;
+  } else {
+    if (slot >= min(*a.n_active, a.n_experts)) return false;
+    e = a.active[slot];
+    if ((unsigned)e >= (unsigned)a.n_experts) return false;
+    r.beg = a.offsets[e];
+    r.m = a.offsets[e + 1] - r.beg;
+  }
   if ((unsigned)e >= (unsigned)a.n_experts) return false;
   r.blk = a.experts + (size_t)e * a.stride;
-  r.beg = a.offsets[e];
-  r.m = a.offsets[e + 1] - r.beg;
   r.shared = false;
+  if (r.first < 0 || r.first >= a.T * a.k) r.first = -1;
   return r.beg >= 0 && r.m > 0 && r.beg + r.m <= a.T * a.k;
 }
 
-// token of bucket position p (flat assignment id / k), kept inside [0, T)
-QMOE_DEV int token_of(const FfnArgs &a, int p) {
-  return min(max(a.sorted[p], 0), a.T * a.k - 1) / a.k;
+// flat assignment id of row i of slot sr (bucket position sr.beg + i), kept inside [0, T*k)
+QMOE_DEV int flat_of(const FfnArgs &a, const SlotRows &sr, int i) {
+  if (i == 0 && sr.first >= 0) return sr.first;
+  return min(max(a.sorted[sr.beg + i], 0), a.T * a.k - 1);
 }
 
 // ---------------------------------------------------------------- staging helpers
@@ -135,6 +152,20 @@ QMOE_DEV float kstep_hilo(const qmoe_u32x4 cv, uint32_t sb, const uint16_t *hrow
   return fmaf(s, d, fmaf(-128.f, s, b) * hsum);
 }
 
+// Load k-steps ks0 + kc .. ks0 + kc + KB - 1 of a tile (clamped to the wave's last k-step,
+// whose duplicates are loaded but not used): this lane's 16 code bytes and its row's
+// scale|bias word, all loads issued before any is used.
+template <int KB>
+QMOE_DEV void load_batch(const uint8_t *tbase, int ks0, int kc, int nk, int lane, int rr,
+                         qmoe_u32x4 cv[KB], uint32_t sb[KB]) {
+#pragma unroll
+  for (int u = 0; u < KB; ++u) {
+    const uint8_t *kb = tbase + (size_t)(ks0 + min(kc + u, nk - 1)) * KSTEP_BYTES;
+    cv[u] = *(const qmoe_u32x4 *)(kb + lane * 16);
+    sb[u] = *(const uint32_t *)(kb + 1024 + rr * 4);
+  }
+}
+
 // ---------------------------------------------------------------- gate/up tile
 // LDS: x [MB][H] bf16, xs [MB][H/32] fp32, red [W][MB][32] fp32
 template <int W, int MB>
@@ -157,23 +188,20 @@ QMOE_DEV void gu_tile(const FfnArgs &a, const SlotRows &sr, int tile, char *smem
   float *red = xs + MB * (H / 32);                               // [W][MB][32]
   const uint8_t *tbase = sr.blk + (size_t)tile * KS * KSTEP_BYTES;
   const int ks0 = (KS * wv) / W, nk = (KS * (wv + 1)) / W - ks0;
+  qmoe_u32x4 cv[KB];
+  uint32_t sb[KB];
+  // the first batch of weights is in flight while the activations are staged
+  if (nk > 0) load_batch<KB>(tbase, ks0, 0, nk, lane, rr, cv, sb);
   for (int r0 = 0; r0 < sr.m; r0 += MB) {
     const int mb = min(MB, sr.m - r0);
     stage_rows_bf16<W * WAVE>(a.x, H, mb, [&](int i) {
-      return sr.shared ? (r0 + i) : token_of(a, sr.beg + r0 + i); }, xl, xs);
+      return sr.shared ? (r0 + i) : flat_of(a, sr, r0 + i) / a.k; }, xl, xs);
     __syncthreads();
     float acc[MB];
 #pragma unroll
     for (int i = 0; i < MB; ++i) acc[i] = 0.f;
     for (int kc = 0; kc < nk; kc += KB) {
-      qmoe_u32x4 cv[KB];
-      uint32_t sb[KB];
-#pragma unroll
-      for (int u = 0; u < KB; ++u) {
-        const uint8_t *kb = tbase + (size_t)(ks0 + min(kc + u, nk - 1)) * KSTEP_BYTES;
-        cv[u] = *(const qmoe_u32x4 *)(kb + lane * 16);
-        sb[u] = *(const uint32_t *)(kb + 1024 + rr * 4);
-      }
+      if (kc > 0 || r0 > 0) load_batch<KB>(tbase, ks0, kc, nk, lane, rr, cv, sb);
 #pragma unroll
       for (int u = 0; u < KB; ++u) {
         if (kc + u < nk) {
@@ -231,45 +259,62 @@ __global__ void __launch_bounds__(W * WAVE) gu_kernel(FfnArgs a) {
 }
 
 // ---------------------------------------------------------------- down tile (per slot)
-// LDS: h hi [MB][K] bf16, h lo [MB][K] bf16, hsum [MB][K/32] fp32, red [W][MB][32] fp32
+// LDS: h hi [MB][Kc] bf16, h lo [MB][Kc] bf16, hsum [MB][Kc/32] fp32, red [W][MB][32] fp32
+// where Kc = 64 * (k-steps of the workgroup)
 template <int W, int MB>
-inline __host__ __device__ size_t d_lds_bytes(int K) {
-  return (size_t)MB * K * 4 + (size_t)MB * (K / 32) * 4 + (size_t)W * MB * 32 * 4;
+inline __host__ __device__ size_t d_lds_bytes(int Kc) {
+  return (size_t)MB * Kc * 4 + (size_t)MB * (Kc / 32) * 4 + (size_t)W * MB * 32 * 4;
 }
 
-template <int W, int MB, int KB>
-QMOE_DEV void d_tile(const FfnArgs &a, const SlotRows &sr, int tile, char *smem) {
+// k-steps [kb0, kb0 + nks) of one 32-row output tile of the down projection of slot `sr`
+// (K = the block's width).  Output rows go to dst (row of token r0+i = ysel(r0+i)), written
+// with system-scope stores when `handoff` (another workgroup of this launch reads them).
+template <int W, int MB, int KB, class YSel>
+QMOE_DEV void d_tile(const FfnArgs &a, const SlotRows &sr, int tile, int kb0, int nks,
+                     float *dst, YSel ysel, bool handoff, char *smem) {
   const int H = a.H;
   const int K = sr.shared ? a.Is : a.I;
   const int KS = K / GROUP;
+  const int Kc = nks * GROUP;
   const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
   const int rr = lane % 32, half = lane / 32;
-  uint16_t *hh = (uint16_t *)smem;                              // [MB][K]
-  uint16_t *hl = hh + (size_t)MB * K;                           // [MB][K]
-  float *hs = (float *)(hl + (size_t)MB * K);                   // [MB][K/32]
-  float *red = hs + MB * (K / 32);                              // [W][MB][32]
+  uint16_t *hh = (uint16_t *)smem;                              // [MB][Kc]
+  uint16_t *hl = hh + (size_t)MB * Kc;                          // [MB][Kc]
+  float *hs = (float *)(hl + (size_t)MB * Kc);                  // [MB][Kc/32]
+  float *red = hs + MB * (Kc / 32);                             // [W][MB][32]
   const BlockGeom geo = block_geom(H, K);
-  const uint8_t *tbase = sr.blk + geo.gu_bytes + (size_t)tile * KS * KSTEP_BYTES;
-  const int ks0 = (KS * wv) / W, nk = (KS * (wv + 1)) / W - ks0;
-  const uint16_t *src_hi = sr.shared ? a.hs_hi : a.hr_hi;
-  const uint16_t *src_lo = sr.shared ? a.hs_lo : a.hr_lo;
+  const uint8_t *tbase = sr.blk + geo.gu_bytes + ((size_t)tile * KS + kb0) * KSTEP_BYTES;
+  const int ks0 = (nks * wv) / W, nk = (nks * (wv + 1)) / W - ks0;
+  const uint16_t *src_hi = (sr.shared ? a.hs_hi : a.hr_hi) + (size_t)kb0 * GROUP;
+  const uint16_t *src_lo = (sr.shared ? a.hs_lo : a.hr_lo) + (size_t)kb0 * GROUP;
+  qmoe_u32x4 cv[KB];
+  uint32_t sb[KB];
+  if (nk > 0) load_batch<KB>(tbase, ks0, 0, nk, lane, rr, cv, sb);
   for (int r0 = 0; r0 < sr.m; r0 += MB) {
     const int mb = min(MB, sr.m - r0);
-    stage_rows_hilo<W * WAVE>(src_hi, src_lo, K, mb, [&](int i) { return sr.beg + r0 + i; },
-                              hh, hl, hs);
+    // h columns [kb0*64, kb0*64 + Kc) of the rows; source rows have stride K
+    const int n8 = Kc / 8;
+    for (int c = tid; c < mb * n8; c += W * WAVE) {
+      const int i = c / n8, cc = c % n8;
+      const size_t row = (size_t)(sr.beg + r0 + i);
+      const qmoe_u32x4 vh = *(const qmoe_u32x4 *)(src_hi + row * K + 8 * cc);
+      const qmoe_u32x4 vl = *(const qmoe_u32x4 *)(src_lo + row * K + 8 * cc);
+      *(qmoe_u32x4 *)(hh + (size_t)i * Kc + 8 * cc) = vh;
+      *(qmoe_u32x4 *)(hl + (size_t)i * Kc + 8 * cc) = vl;
+      float p = (bf16lo(vh.x) + bf16lo(vl.x)) + (bf16hi(vh.x) + bf16hi(vl.x)) +
+                (bf16lo(vh.y) + bf16lo(vl.y)) + (bf16hi(vh.y) + bf16hi(vl.y)) +
+                (bf16lo(vh.z) + bf16lo(vl.z)) + (bf16hi(vh.z) + bf16hi(vl.z)) +
+                (bf16lo(vh.w) + bf16lo(vl.w)) + (bf16hi(vh.w) + bf16hi(vl.w));
+      p += __shfl_xor(p, 1, WAVE);
+      p += __shfl_xor(p, 2, WAVE);
+      if ((cc & 3) == 0) hs[i * (Kc / 32) + cc / 4] = p;
+    }
     __syncthreads();
     float acc[MB];
 #pragma unroll
     for (int i = 0; i < MB; ++i) acc[i] = 0.f;
     for (int kc = 0; kc < nk; kc += KB) {
-      qmoe_u32x4 cv[KB];
-      uint32_t sb[KB];
-#pragma unroll
-      for (int u = 0; u < KB; ++u) {
-        const uint8_t *kb = tbase + (size_t)(ks0 + min(kc + u, nk - 1)) * KSTEP_BYTES;
-        cv[u] = *(const qmoe_u32x4 *)(kb + lane * 16);
-        sb[u] = *(const uint32_t *)(kb + 1024 + rr * 4);
-      }
+      if (kc > 0 || r0 > 0) load_batch<KB>(tbase, ks0, kc, nk, lane, rr, cv, sb);
 #pragma unroll
       for (int u = 0; u < KB; ++u) {
         if (kc + u < nk) {
@@ -277,8 +322,8 @@ QMOE_DEV void d_tile(const FfnArgs &a, const SlotRows &sr, int tile, char *smem)
 #pragma unroll
           for (int i = 0; i < MB; ++i)
             if (i < mb)
-              acc[i] += kstep_hilo(cv[u], sb[u], hh + (size_t)i * K + col, hl + (size_t)i * K + col,
-                                   hs[i * (K / 32) + col / 32]);
+              acc[i] += kstep_hilo(cv[u], sb[u], hh + (size_t)i * Kc + col,
+                                   hl + (size_t)i * Kc + col, hs[i * (Kc / 32) + col / 32]);
         }
       }
     }
@@ -292,111 +337,59 @@ QMOE_DEV void d_tile(const FfnArgs &a, const SlotRows &sr, int tile, char *smem)
       const int i = o / 32, r = o % 32;
       float yv = 0.f;
       for (int w = 0; w < W; ++w) yv += red[(w * MB + i) * 32 + r];
-      size_t yrow;
-      float *dst;
-      if (sr.shared) { yrow = (size_t)(r0 + i); dst = a.y_sh; }
-      else           { yrow = (size_t)min(max(a.sorted[sr.beg + r0 + i], 0), a.T * a.k - 1); dst = a.y; }
-      dst[yrow * H + 32 * tile + r] = yv;
+      float *p = dst + (size_t)ysel(r0 + i) * H + 32 * tile + r;
+      if (handoff) st_sys(p, yv); else *p = yv;
     }
     __syncthreads();
   }
 }
 
-// grid = (H/32 tiles, n_slots routed slots + 1 shared slot if a.shared && a.y_sh)
+// Combine of one 32-row tile for every token, by the workgroup that completes the tile:
+//   out = bf16( x + sum_j w_j y_j + sum_c y_shared_c )  (fp32, fixed order)
+QMOE_DEV void combine_tile(const FfnArgs &a, int tile) {
+  const int H = a.H;
+  for (int o = threadIdx.x; o < a.T * 32; o += blockDim.x) {
+    const int t = o / 32, col = 32 * tile + o % 32;
+    float acc = 0.f;
+    for (int j = 0; j < a.k; ++j)
+      acc = fmaf(ld_sys(a.topk_w + (size_t)t * a.k + j),
+                 ld_sys(a.y + ((size_t)t * a.k + j) * H + col), acc);
+    if (a.shared)
+      for (int c = 0; c < a.n_sh_chunks; ++c)
+        acc += ld_sys(a.y_sh_part + ((size_t)c * a.T + t) * H + col);
+    acc += bf16_to_f32(a.x[(size_t)t * H + col]);
+    a.out[(size_t)t * H + col] = (uint16_t)f32_to_bf16_bits(acc);
+    if (a.out_f32) a.out_f32[(size_t)t * H + col] = acc;
+  }
+}
+
+// grid = (H/32 tiles, n_slots routed slots + n_sh_chunks shared chunks if a.shared).
+// Without a.out: routed rows go to a.y, the (single-chunk) shared rows to a.y_sh.  With
+// a.out: every workgroup hands its rows over (system-scope stores) and the workgroup that
+// completes a tile combines it.
 template <int W, int MB, int KB>
 __global__ void __launch_bounds__(W * WAVE) d_kernel(FfnArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int tile = blockIdx.x;
   const int slot = blockIdx.y;
+  const bool fused = a.out != nullptr;
   SlotRows sr;
   const bool shared = slot >= a.n_slots;
-  if (slot_rows(a, slot, shared, sr)) d_tile<W, MB, KB>(a, sr, tile, smem);
-}
-
-// ---------------------------------------------------------------- one-token down + combine
-// Decode with one token: a workgroup owns one 32-row output tile and runs the down
-// projection of every routed slot and of the shared block for those rows, weighting each
-// routed k-step by its router weight, then adds the residual:
-//   out[r] = bf16( x[r] + sum_slots w_slot * (W_down,slot h_slot)[r] + (W_down,sh h_sh)[r] )
-// The (slot, k-step) items are split evenly over the W waves.  No cross-workgroup traffic.
-// LDS: h hi/lo of every slot [n_slots*I + Is] x 2 bf16, sums, red [W][32].
-inline __host__ __device__ size_t d1_lds_bytes(int n_slots, int I, int Is, int W) {
-  const size_t cols = (size_t)n_slots * I + Is;
-  return cols * 4 + cols / 32 * 4 + (size_t)W * 32 * 4;
-}
-
-template <int W, int KB>
-__global__ void __launch_bounds__(W * WAVE) d1_kernel(FfnArgs a) {
-  extern __shared__ __align__(16) char smem[];
-  const int H = a.H, I = a.I, Is = a.shared ? a.Is : 0;
-  const int tile = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
-  const int rr = lane % 32, half = lane / 32;
-  const int ns = min(min(*a.n_active, a.n_slots), a.n_experts);   // routed slots (1 row each)
-  const int cols = ns * I + Is;
-  uint16_t *hh = (uint16_t *)smem;
-  uint16_t *hl = hh + (size_t)a.n_slots * I + Is;
-  float *hs = (float *)(hl + (size_t)a.n_slots * I + Is);
-  float *red = hs + ((size_t)a.n_slots * I + Is) / 32;
-  // routed rows 0..ns-1 of the bucket (one token: one row per active expert), then shared row
-  stage_rows_hilo<W * WAVE>(a.hr_hi, a.hr_lo, I, ns, [&](int i) { return i; }, hh, hl, hs);
-  if (Is) stage_rows_hilo<W * WAVE>(a.hs_hi, a.hs_lo, Is, 1, [&](int) { return 0; },
-                                    hh + (size_t)ns * I, hl + (size_t)ns * I, hs + ns * I / 32);
-  __syncthreads();
-  const BlockGeom gr = block_geom(H, I);
-  const int KSr = I / GROUP, KSs = Is / GROUP;
-  const int n_items = ns * KSr + KSs;
-  const int it0 = (n_items * wv) / W, nk = (n_items * (wv + 1)) / W - it0;
-  float acc = 0.f;
-  for (int kc = 0; kc < nk; kc += KB) {
-    qmoe_u32x4 cv[KB];
-    uint32_t sb[KB];
-#pragma unroll
-    for (int u = 0; u < KB; ++u) {
-      const int it = it0 + min(kc + u, nk - 1);
-      const uint8_t *kb;
-      if (it < ns * KSr) {
-        const int slot = it / KSr, ks = it % KSr;
-        const int e = min(max(a.active[slot], 0), a.n_experts - 1);
-        kb = a.experts + (size_t)e * a.stride + gr.gu_bytes +
-             ((size_t)tile * KSr + ks) * KSTEP_BYTES;
-      } else {
-        const BlockGeom gs = block_geom(H, Is);
-        kb = a.shared + gs.gu_bytes + ((size_t)tile * KSs + (it - ns * KSr)) * KSTEP_BYTES;
-      }
-      cv[u] = *(const qmoe_u32x4 *)(kb + lane * 16);
-      sb[u] = *(const uint32_t *)(kb + 1024 + rr * 4);
-    }
-#pragma unroll
-    for (int u = 0; u < KB; ++u) {
-      if (kc + u < nk) {
-        const int it = it0 + kc + u;
-        int col;
-        float wt;
-        if (it < ns * KSr) {
-          const int slot = it / KSr;
-          col = slot * I + (it % KSr) * GROUP + half * 32;
-          wt = a.topk_w[min(max(a.sorted[slot], 0), a.k - 1)];
-        } else {
-          col = ns * I + (it - ns * KSr) * GROUP + half * 32;
-          wt = 1.f;
-        }
-        acc = fmaf(wt, kstep_hilo(cv[u], sb[u], hh + col, hl + col, hs[col / 32]), acc);
-      }
+  if (slot_rows(a, slot, shared, sr)) {
+    if (!shared) {
+      d_tile<W, MB, KB>(a, sr, tile, 0, a.I / GROUP, a.y,
+                        [&](int r) { return flat_of(a, sr, r); },
+                        fused, smem);
+    } else {
+      const int KSs = a.Is / GROUP, c = slot - a.n_slots, nc = a.n_sh_chunks;
+      const int kb0 = (KSs * c) / nc, kb1 = (KSs * (c + 1)) / nc;
+      float *dst = fused ? a.y_sh_part + (size_t)c * a.T * a.H : a.y_sh;
+      d_tile<W, MB, KB>(a, sr, tile, kb0, kb1 - kb0, dst, [](int r) { return r; }, fused, smem);
     }
   }
-  (void)cols;
-  acc += __shfl_xor(acc, 32, WAVE);
-  if (half == 0) red[wv * 32 + rr] = acc;
-  __syncthreads();
-  if (tid < 32) {
-    float y = 0.f;
-    for (int w = 0; w < W; ++w) y += red[w * 32 + tid];
-    const int col = 32 * tile + tid;
-    const float o = bf16_to_f32(a.x[col]) + y;
-    a.out[col] = (uint16_t)f32_to_bf16_bits(o);
-    if (a.out_f32) a.out_f32[col] = o;
-  }
+  if (!fused) return;
+  if (!arrive_last(&a.cnt_tile[tile], gridDim.y)) return;
+  combine_tile(a, tile);
 }
 
 // ---------------------------------------------------------------- standalone combine

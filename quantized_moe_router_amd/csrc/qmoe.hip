@@ -25,10 +25,9 @@ constexpr int VERSION = 100;               // 0.1.0
 constexpr size_t COUNTER_BYTES = 128 * 1024;
 constexpr int GU_W = 4;     // waves per gate/up workgroup (split-K)
 constexpr int D_W = 4;      // waves per per-slot down workgroup (split-K)
-constexpr int D1_W = 16;    // waves per one-token down workgroup
 constexpr int KB = 12;      // k-steps loaded per batch by a wave
 constexpr int MB_MAX = 8;   // rows (tokens) per activation block
-constexpr size_t D1_LDS_MAX = 144 * 1024;
+constexpr int CNT_TILE_WORD = 64 + 16384;  // first word of the per-tile combine counters
 constexpr int MAX_T = 65536;
 
 thread_local std::string g_err;
@@ -112,9 +111,19 @@ int check_arch() {
 
 inline size_t al(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Down-projection workgroups per output tile for the shared block in the layer path: the
+// shared width is cut into chunks about as wide as a routed expert, so that every workgroup
+// of the launch has a similar amount of work.
+inline int shared_chunks(const qmoe_dims *d) {
+  if (d->shared_inter == 0) return 0;
+  const int ks = d->shared_inter / GROUP;
+  const int c = (d->shared_inter + d->inter / 2) / d->inter;
+  return std::max(1, std::min(c, ks));
+}
+
 struct WsLayout {
-  size_t cnt, logits, tidx, tw, counts, offsets, sorted, active, nact;
-  size_t hr_hi, hr_lo, hs_hi, hs_lo, y, ysh, total;
+  size_t cnt, logits, tidx, tw, counts, offsets, sorted, active, nact, slot_tab;
+  size_t hr_hi, hr_lo, hs_hi, hs_lo, y, ysh, ysh_part, total;
 };
 
 WsLayout ws_layout(const qmoe_dims *d, int Tmax) {
@@ -131,12 +140,14 @@ WsLayout ws_layout(const qmoe_dims *d, int Tmax) {
   w.sorted = o; o += al(T * k * 4);
   w.active = o; o += al(E * 4);
   w.nact = o; o += al(4);
+  w.slot_tab = o; o += al(E * 16);
   w.hr_hi = o; o += al(T * k * d->inter * 2);
   w.hr_lo = o; o += al(T * k * d->inter * 2);
   w.hs_hi = o; o += al(T * (size_t)d->shared_inter * 2);
   w.hs_lo = o; o += al(T * (size_t)d->shared_inter * 2);
   w.y = o; o += al(Tc * k * H * 4);
   w.ysh = o; o += al(Tc * H * 4);
+  w.ysh_part = o; o += al((size_t)shared_chunks(d) * Tc * H * 4);
   w.total = o;
   return w;
 }
@@ -192,7 +203,7 @@ int set_lds(K kernel, size_t bytes) {
 }
 
 size_t router_smem(const qmoe_dims *d) {
-  return std::max(router_lds_bytes(d->hidden), (size_t)(d->n_experts + 1 + 64) * 4);
+  return std::max(router_lds_bytes(d->hidden), (size_t)(2 * d->n_experts) * 4);
 }
 
 RouterArgs make_router_args(const qmoe_dims *d, const qmoe_router *r, const uint16_t *x, int T,
@@ -283,6 +294,9 @@ static FfnArgs make_ffn_args(const qmoe_layer *L, const uint16_t *x, int T, cons
   a.hr_hi = at<uint16_t>(ws, wl.hr_hi); a.hr_lo = at<uint16_t>(ws, wl.hr_lo);
   a.hs_hi = at<uint16_t>(ws, wl.hs_hi); a.hs_lo = at<uint16_t>(ws, wl.hs_lo);
   a.y = y; a.y_sh = y_sh;
+  a.y_sh_part = at<float>(ws, wl.ysh_part);
+  a.n_sh_chunks = 1;
+  a.cnt_tile = at<unsigned>(ws, wl.cnt) + CNT_TILE_WORD;
   return a;
 }
 
@@ -308,8 +322,8 @@ static int launch_gu(FfnArgs a, int mode, hipStream_t s) {
 }
 
 template <int MB>
-static int launch_d_t(const FfnArgs &a, int slots, int K, hipStream_t s) {
-  const size_t smem = d_lds_bytes<D_W, MB>(K);
+static int launch_d_t(const FfnArgs &a, int slots, int Kc, hipStream_t s) {
+  const size_t smem = d_lds_bytes<D_W, MB>(Kc);
   int rc = set_lds(d_kernel<D_W, MB, KB>, smem);
   if (rc) return rc;
   hipLaunchKernelGGL((d_kernel<D_W, MB, KB>), dim3(a.H / TILE_ROWS, slots), dim3(D_W * WAVE),
@@ -318,10 +332,17 @@ static int launch_d_t(const FfnArgs &a, int slots, int K, hipStream_t s) {
   return QMOE_OK;
 }
 
+// Down projection: routed slots plus a.n_sh_chunks shared chunks when with_shared.  The LDS
+// holds the h columns of the widest workgroup.
 static int launch_d(FfnArgs a, bool with_shared, hipStream_t s) {
-  const int slots = a.n_slots + (with_shared ? 1 : 0);
-  const int K = std::max(a.I, with_shared ? a.Is : 0);
-  return mb_for(a.T) == 1 ? launch_d_t<1>(a, slots, K, s) : launch_d_t<MB_MAX>(a, slots, K, s);
+  if (!with_shared) a.shared = nullptr;
+  const int slots = a.n_slots + (with_shared ? a.n_sh_chunks : 0);
+  int Kc = a.I;
+  if (with_shared) {
+    const int KSs = a.Is / GROUP;
+    Kc = std::max(Kc, GROUP * ((KSs + a.n_sh_chunks - 1) / a.n_sh_chunks));
+  }
+  return mb_for(a.T) == 1 ? launch_d_t<1>(a, slots, Kc, s) : launch_d_t<MB_MAX>(a, slots, Kc, s);
 }
 
 }  // namespace
@@ -504,10 +525,13 @@ int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16
     ra.sorted = at<int32_t>(ws, wl.sorted);
     ra.active = at<int32_t>(ws, wl.active);
     ra.n_active = at<int32_t>(ws, wl.nact);
+    ra.slot_tab = at<int32_t>(ws, wl.slot_tab);
     FfnArgs fa = make_ffn_args(L, xc, Tc, ra.offsets, ra.sorted, ra.active, ra.n_active,
                                at<float>(ws, wl.y), sh ? at<float>(ws, wl.ysh) : nullptr, ws,
                                Tc_max);
     fa.topk_w = w;
+    fa.slot_tab = ra.slot_tab;
+    ra.n_slots = fa.n_slots;
     fa.out = out + (size_t)c0 * H;
     fa.out_f32 = out_f32_or_null ? out_f32_or_null + (size_t)c0 * H : nullptr;
     const int n_router = ra.n_tb * ra.n_eb;
@@ -528,23 +552,9 @@ int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16
     if (g_prof_start && (rc = record_event(g_prof_start, s))) return rc;
     if ((rc = launch_gu(fa, 1, s))) return rc;
     if (g_prof_stop && (rc = record_event(g_prof_stop, s))) return rc;
-    if (!sh) fa.shared = nullptr;
-    const size_t d1_smem = d1_lds_bytes(fa.n_slots, d->inter, sh ? d->shared_inter : 0, D1_W);
-    if (Tc == 1 && d1_smem <= D1_LDS_MAX) {
-      // kernel 3 (one token): down projection of all slots per output tile + combine
-      if ((rc = set_lds(d1_kernel<D1_W, 8>, d1_smem))) return rc;
-      hipLaunchKernelGGL((d1_kernel<D1_W, 8>), dim3(H / TILE_ROWS), dim3(D1_W * WAVE), d1_smem, s,
-                         fa);
-      QMOE_LAUNCHED();
-    } else {
-      // kernel 3: routed + shared down projection per slot; kernel 4: combine
-      if ((rc = launch_d(fa, sh, s))) return rc;
-      const size_t n = (size_t)Tc * H;
-      const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 8192);
-      hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, s, xc, fa.y, w, fa.y_sh, Tc,
-                         H, k, fa.out, fa.out_f32);
-      QMOE_LAUNCHED();
-    }
+    // kernel 3: routed + shared down projection, combined by the last workgroup of each tile
+    fa.n_sh_chunks = sh ? shared_chunks(d) : 0;
+    if ((rc = launch_d(fa, sh, s))) return rc;
   }
   return ok();
 }

@@ -39,6 +39,8 @@ struct RouterArgs {
   int n_tb, n_eb;             // token blocks, expert blocks
   // optional fused bucketing (layer path); null counts -> skip
   int32_t *counts, *offsets, *sorted, *active, *n_active;
+  int32_t *slot_tab;          // [n_slots][4] {expert, first bucket position, rows, first flat id}
+  int n_slots;
 };
 
 // LDS bytes of a router workgroup for hidden H
@@ -57,7 +59,7 @@ QMOE_DEV void topk_one_token(const float *lrow, int E, int k, const float *pes,
 #pragma unroll
   for (int j = 0; j < MAX_EXPERTS / WAVE; ++j) {
     const int e = lane + WAVE * j;
-    const float l = (e < E) ? lrow[e] : -INFINITY;
+    const float l = (e < E) ? ld_sys(lrow + e) : -INFINITY;
     v[j] = (l == l) ? l : -INFINITY;
   }
   unsigned taken = 0;
@@ -86,29 +88,35 @@ QMOE_DEV void topk_one_token(const float *lrow, int E, int k, const float *pes,
   const float z = (lane < k) ? expf(myv - vmax) : 0.f;
   const float zsum = wave_sum(z);
   if (lane < k) {
-    idx_out[lane] = myi;
-    w_out[lane] = (z / zsum) * pes[myi];
+    st_sys(idx_out + lane, myi);
+    st_sys(w_out + lane, (z / zsum) * pes[myi]);
   }
 }
 
 // ---------------------------------------------------------------- bucketing (one workgroup)
 // Stable counting sort of N = T*k assignments by expert (ids outside [0, E) are dropped).
-// Counts via an LDS histogram; the
-// rank of an assignment among the earlier ones of its expert from wave ballots (one ballot
-// per distinct expert in a wave) plus a per-expert cursor advanced wave by wave in order.
-// lds: at least (E + 1) * 4 + 64 * 4 bytes.
-template <int NT>
-QMOE_DEV void bucket_block(const int32_t *idx, int N, int E, int32_t *counts, int32_t *offsets,
-                           int32_t *sorted, int32_t *active, int32_t *n_active, int *lds) {
+// Counts via an LDS histogram; the rank of an assignment among the earlier ones of its
+// expert from wave ballots (one ballot per distinct expert in a wave) plus a per-expert cursor
+// advanced wave by wave in order.  Optionally also writes the slot table used by the expert
+// kernels: entry s = {expert, first bucket position, rows, first flat id} of the s-th active
+// expert, zero rows for s in [n_active, n_slots).
+// lds: at least 2 * E * 4 bytes.  get(f) returns the expert id of assignment f.
+template <int NT, class Get>
+QMOE_DEV void bucket_block(Get get, int N, int E, int32_t *counts, int32_t *offsets,
+                           int32_t *sorted, int32_t *active, int32_t *n_active, int32_t *slot_tab,
+                           int n_slots, int *lds) {
   constexpr int NW = NT / WAVE;
   int *cnt = lds;                 // [E]
-  int *wsum = lds + E + 1;        // [NW] scratch for scans
+  int *first = lds + E;           // [E] smallest flat id of each expert
   const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
-  for (int e = tid; e < E; e += NT) cnt[e] = 0;
+  for (int e = tid; e < E; e += NT) { cnt[e] = 0; first[e] = 0x7FFFFFFF; }
   __syncthreads();
   for (int f = tid; f < N; f += NT) {
-    const int e = idx[f];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[e], 1);
+    const int e = get(f);
+    if ((unsigned)e < (unsigned)E) {
+      atomicAdd(&cnt[e], 1);
+      atomicMin(&first[e], f);
+    }
   }
   __syncthreads();
   // exclusive scan of counts and of (count > 0) flags, E <= MAX_EXPERTS
@@ -116,42 +124,54 @@ QMOE_DEV void bucket_block(const int32_t *idx, int N, int E, int32_t *counts, in
   const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
   int s_cnt = 0, s_act = 0;
   for (int e = e0; e < e1; ++e) { s_cnt += cnt[e]; s_act += cnt[e] > 0; }
-  // inclusive wave scan of the pair (packed: counts < 2^20 per call segment, flags < 2^11)
+  // inclusive wave scan of the pair (count total in the high bits, active flags in the low 16)
   long long pair = ((long long)s_cnt << 16) | s_act;
   for (int o = 1; o < WAVE; o <<= 1) {
     const long long up = __shfl_up(pair, o, WAVE);
     if (lane >= o) pair += up;
   }
   __shared__ long long wtot[NW];
+  __shared__ int n_act_sh;
   if (lane == WAVE - 1) wtot[wv] = pair;
   __syncthreads();
-  long long before = 0;
-  for (int w = 0; w < wv; ++w) before += wtot[w];
+  long long before = 0, tot = 0;
+  for (int w = 0; w < NW; ++w) {
+    if (w < wv) before += wtot[w];
+    tot += wtot[w];
+  }
   long long excl = before + pair - (((long long)s_cnt << 16) | s_act);
   int run_cnt = (int)(excl >> 16), run_act = (int)(excl & 0xFFFF);
   for (int e = e0; e < e1; ++e) {
     const int c = cnt[e];
     counts[e] = c;
     offsets[e] = run_cnt;
-    if (c > 0) active[run_act++] = e;
+    if (c > 0) {
+      active[run_act] = e;
+      if (slot_tab && run_act < n_slots)
+        *(qmoe_u32x4 *)(slot_tab + 4 * run_act) =
+            qmoe_u32x4{(uint32_t)e, (uint32_t)run_cnt, (uint32_t)c, (uint32_t)first[e]};
+      ++run_act;
+    }
     cnt[e] = run_cnt;  // becomes the cursor
     run_cnt += c;
   }
+  const int na = (int)(tot & 0xFFFF);
   if (tid == NT - 1) {
-    long long tot = 0;
-    for (int w = 0; w < NW; ++w) tot += wtot[w];
     offsets[E] = (int)(tot >> 16);
-    *n_active = (int)(tot & 0xFFFF);
+    *n_active = na;
   }
-  (void)wsum;
+  if (slot_tab)
+    for (int sl = na + tid; sl < n_slots; sl += NT)
+      *(qmoe_u32x4 *)(slot_tab + 4 * sl) = qmoe_u32x4{0u, 0u, 0u, 0u};
+  (void)n_act_sh;
   __syncthreads();
   // stable scatter, NT assignments per round
   for (int base = 0; base < N; base += NT) {
     const int f = base + tid;
-    const int e = (f < N) ? idx[f] : -1;
+    const int e = (f < N) ? get(f) : -1;
     const bool valid = (f < N) && ((unsigned)e < (unsigned)E);
     // rank among lower lanes of this wave with the same expert, and the wave's count of it
-    int rank = 0, tot = 0;
+    int rank = 0, wtotal = 0;
     unsigned long long pending = __ballot(valid);
     while (pending) {
       const int leader = __ffsll((long long)pending) - 1;
@@ -159,7 +179,7 @@ QMOE_DEV void bucket_block(const int32_t *idx, int N, int E, int32_t *counts, in
       const unsigned long long same = __ballot(valid && e == el);
       if (valid && e == el) {
         rank = __popcll(same & ((1ull << lane) - 1ull));
-        tot = __popcll(same);
+        wtotal = __popcll(same);
       }
       pending &= ~same;
     }
@@ -168,7 +188,7 @@ QMOE_DEV void bucket_block(const int32_t *idx, int N, int E, int32_t *counts, in
         const int cur = cnt[e];
         sorted[cur + rank] = f;
         __builtin_amdgcn_wave_barrier();
-        if (rank == 0) cnt[e] = cur + tot;
+        if (rank == 0) cnt[e] = cur + wtotal;
       }
       __syncthreads();
     }
@@ -185,6 +205,22 @@ QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *sme
   const int H = a.H;
   const int t0 = tb * ROUTER_TB;
   const int nt = min(ROUTER_TB, a.T - t0);
+  // this wave's expert row: lane l holds chunks l, l+64, ... (16 codes each), loaded before
+  // the activations are staged (H <= 8192 -> at most 8 chunks per lane)
+  constexpr int NCH = 8;
+  const int n16 = H / 16;
+  const int e = eb * ROUTER_EPB + wv;
+  const int ec = min(e, a.E - 1);
+  const uint8_t *row = a.rq + (size_t)ec * H;
+  qmoe_u32x4 v[NCH];
+  uint16_t sv[NCH], bv[NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = min(lane + WAVE * j, n16 - 1);
+    v[j] = *(const qmoe_u32x4 *)(row + 16 * c);
+    sv[j] = a.rs[(size_t)ec * (H / GROUP) + c / 4];
+    bv[j] = a.rb[(size_t)ec * (H / GROUP) + c / 4];
+  }
   float *z = (float *)smem;                                  // [TB][H]
   float *zs = z + ROUTER_TB * H;                             // [TB][H/16]
   float *fac = zs + ROUTER_TB * (H / 16);                    // [TB]
@@ -222,77 +258,55 @@ QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *sme
     }
     __syncthreads();
   }
-  // one wave per expert; lane l holds chunks l, l+64, ... (16 codes each) of the expert's
-  // row, all loaded up front (H <= 8192 -> at most 8 chunks per lane)
-  constexpr int NCH = 8;
-  const int n16 = H / 16;
-  for (int ee = 0; ee < ROUTER_EPW; ++ee) {
-    const int e = eb * ROUTER_EPB + wv * ROUTER_EPW + ee;
-    if (e >= a.E) break;
-    const uint8_t *row = a.rq + (size_t)e * H;
-    qmoe_u32x4 v[NCH];
-    uint16_t sv[NCH], bv[NCH];
+  if (e >= a.E) return;
+  float acc[ROUTER_TB];
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int c = min(lane + WAVE * j, n16 - 1);
-      v[j] = *(const qmoe_u32x4 *)(row + 16 * c);
-      sv[j] = a.rs[(size_t)e * (H / GROUP) + c / 4];
-      bv[j] = a.rb[(size_t)e * (H / GROUP) + c / 4];
-    }
-    float acc[ROUTER_TB];
+  for (int i = 0; i < ROUTER_TB; ++i) acc[i] = 0.f;
 #pragma unroll
-    for (int i = 0; i < ROUTER_TB; ++i) acc[i] = 0.f;
+  for (int j = 0; j < NCH; ++j) {
+    const int c = lane + WAVE * j;
+    if (c < n16) {
+      const float s = bf16_to_f32(sv[j]), b = bf16_to_f32(bv[j]);
+      const uint32_t w4[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+      float q[16];
 #pragma unroll
-    for (int j = 0; j < NCH; ++j) {
-      const int c = lane + WAVE * j;
-      if (c < n16) {
-        const float s = bf16_to_f32(sv[j]), b = bf16_to_f32(bv[j]);
-        const uint32_t w4[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-        float q[16];
+      for (int d = 0; d < 4; ++d) {
+        q[4 * d + 0] = (float)(w4[d] & 0xFFu);
+        q[4 * d + 1] = (float)((w4[d] >> 8) & 0xFFu);
+        q[4 * d + 2] = (float)((w4[d] >> 16) & 0xFFu);
+        q[4 * d + 3] = (float)(w4[d] >> 24);
+      }
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          q[4 * d + 0] = (float)(w4[d] & 0xFFu);
-          q[4 * d + 1] = (float)((w4[d] >> 8) & 0xFFu);
-          q[4 * d + 2] = (float)((w4[d] >> 16) & 0xFFu);
-          q[4 * d + 3] = (float)(w4[d] >> 24);
-        }
+      for (int i = 0; i < ROUTER_TB; ++i) {
+        if (i < nt) {
+          const float *zr = z + i * H + 16 * c;
+          float dq = 0.f;
 #pragma unroll
-        for (int i = 0; i < ROUTER_TB; ++i) {
-          if (i < nt) {
-            const float *zr = z + i * H + 16 * c;
-            float dq = 0.f;
-#pragma unroll
-            for (int jj = 0; jj < 16; ++jj) dq = fmaf(q[jj], zr[jj], dq);
-            acc[i] = fmaf(s, dq, acc[i]);
-            acc[i] = fmaf(b, zs[i * (H / 16) + c], acc[i]);
-          }
+          for (int jj = 0; jj < 16; ++jj) dq = fmaf(q[jj], zr[jj], dq);
+          acc[i] = fmaf(s, dq, acc[i]);
+          acc[i] = fmaf(b, zs[i * (H / 16) + c], acc[i]);
         }
       }
     }
+  }
 #pragma unroll
-    for (int i = 0; i < ROUTER_TB; ++i) {
-      if (i < nt) {
-        const float tot = wave_sum(acc[i]);
-        if (lane == 0) {
-          float l = fac[i] * tot;
-          if (a.lbias) l += a.lbias[e];
-          a.logits[(size_t)(t0 + i) * a.E + e] = l;
-        }
+  for (int i = 0; i < ROUTER_TB; ++i) {
+    if (i < nt) {
+      const float tot = wave_sum(acc[i]);
+      if (lane == 0) {
+        float l = fac[i] * tot;
+        if (a.lbias) l += a.lbias[e];
+        st_sys(a.logits + (size_t)(t0 + i) * a.E + e, l);
       }
     }
   }
 }
 
 // After a router workgroup has written its logits: the last workgroup of a token block runs
-// top-k for that block; the last of those runs the bucketing (if requested).
+// top-k for that block; with bucketing requested, the last of those (or that workgroup
+// itself when there is a single token block) runs the bucketing.
 QMOE_DEV void router_finish(const RouterArgs &a, int tb, char *smem) {
-  __shared__ int last;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) last = (atomicAdd(&a.cnt_tb[tb], 1u) == (unsigned)(a.n_eb - 1));
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
+  if (!arrive_last(&a.cnt_tb[tb], (unsigned)a.n_eb)) return;
   const int wv = threadIdx.x / WAVE;
   const int t0 = tb * ROUTER_TB;
   const int nt = min(ROUTER_TB, a.T - t0);
@@ -301,17 +315,16 @@ QMOE_DEV void router_finish(const RouterArgs &a, int tb, char *smem) {
     topk_one_token(a.logits + (size_t)t * a.E, a.E, a.k, a.pes, a.topk_idx + (size_t)t * a.k,
                    a.topk_w + (size_t)t * a.k);
   }
-  if (threadIdx.x == 0) a.cnt_tb[tb] = 0u;
   if (a.counts == nullptr) return;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) last = (atomicAdd(a.cnt_all, 1u) == (unsigned)(a.n_tb - 1));
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  bucket_block<ROUTER_THREADS>(a.topk_idx, a.T * a.k, a.E, a.counts, a.offsets, a.sorted,
-                               a.active, a.n_active, (int *)smem);
-  if (threadIdx.x == 0) *a.cnt_all = 0u;
+  if (a.n_tb == 1) {
+    drain_memory();    // this workgroup wrote every assignment
+    __syncthreads();
+  } else if (!arrive_last(a.cnt_all, (unsigned)a.n_tb)) {
+    return;
+  }
+  bucket_block<ROUTER_THREADS>([&](int f) { return ld_sys(a.topk_idx + f); }, a.T * a.k, a.E,
+                               a.counts, a.offsets, a.sorted, a.active, a.n_active, a.slot_tab,
+                               a.n_slots, (int *)smem);
 }
 
 __global__ void __launch_bounds__(ROUTER_THREADS) router_kernel(RouterArgs a) {
@@ -325,8 +338,9 @@ __global__ void __launch_bounds__(256) bucket_kernel(const int32_t *idx, int N, 
                                                      int32_t *counts, int32_t *offsets,
                                                      int32_t *sorted, int32_t *active,
                                                      int32_t *n_active) {
-  __shared__ int lds[MAX_EXPERTS + 1 + 64];
-  bucket_block<256>(idx, N, E, counts, offsets, sorted, active, n_active, lds);
+  __shared__ int lds[2 * MAX_EXPERTS];
+  bucket_block<256>([&](int f) { return idx[f]; }, N, E, counts, offsets, sorted, active, n_active,
+                    nullptr, 0, lds);
 }
 
 }  // namespace qmoe
