@@ -116,14 +116,14 @@ size_t qmoe_expert_stride(const qmoe_dims *d, int32_t inter);
 
 /* Workspace bytes needed by qmoe_router_topk / qmoe_bucket / qmoe_expert_ffn /
  * qmoe_layer_forward for calls with up to max_tokens tokens (0 on invalid dims).  The
- * workspace is device memory owned by the caller.  Its first 128 KiB hold completion counters
+ * workspace is device memory owned by the caller.  Its first 512 KiB hold completion counters
  * that must be zero when a call starts: initialise a new workspace once with
  * qmoe_workspace_init (or a zero fill); every call returns the counters it used to zero
  * before it completes, so later calls need no re-initialisation.  Calls that share one
  * workspace must be ordered (same stream, or synchronised). */
 size_t qmoe_workspace_bytes(const qmoe_dims *d, int32_t max_tokens);
 
-/* Zero the counter area (the first 128 KiB, or all of a smaller workspace) with a kernel
+/* Zero the counter area (the first 512 KiB, or all of a smaller workspace) with a kernel
  * on `stream` (graph-capturable). */
 int qmoe_workspace_init(void *ws, size_t ws_bytes, qmoe_stream_t stream);
 
@@ -197,7 +197,10 @@ int qmoe_combine(const qmoe_dims *d, const uint16_t *x, const float *y, const fl
                  const float *y_shared_or_null, int32_t T, uint16_t *out,
                  float *out_f32_or_null, qmoe_stream_t stream);
 
-/* The whole layer (steps 1-4) as three kernels with no host round trip:
+/* The whole layer (steps 1-4) with no host round trip.  A one-token call runs as a single
+ * launch whose workgroups take the roles router, shared gate/up, routed gate/up, shared down
+ * and routed down, handing data to each other through the workspace (each role starts loading
+ * its weights as soon as it knows them).  Larger calls run as three launches:
  *   kernel 1: router logits, then (last workgroup) top-k, softmax and bucketing, while other
  *             workgroups of the same launch run the shared expert's gate/up projection;
  *   kernel 2: routed gate/up projection + SwiGLU over the buckets;
@@ -211,6 +214,12 @@ int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16
                        float *out_f32_or_null, int32_t *topk_idx_or_null,
                        float *topk_w_or_null, void *ws, size_t ws_bytes,
                        qmoe_stream_t stream);
+
+/* Diagnostic: copy the workspace's status word to *status_out (0 = no fault; 1 = a one-token
+ * layer call gave up waiting for another workgroup, so its results are not valid).
+ * Synchronises `stream`; not for use under graph capture. */
+int qmoe_workspace_status(const void *ws, size_t ws_bytes, int32_t *status_out,
+                          qmoe_stream_t stream);
 
 /* ---------------------------------------------------------------- timing helpers */
 

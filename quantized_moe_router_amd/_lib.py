@@ -17,7 +17,7 @@ EXPORTS = [
     "qmoe_workspace_init", "qmoe_pack_expert", "qmoe_unpack_expert", "qmoe_router_topk",
     "qmoe_bucket", "qmoe_expert_ffn", "qmoe_combine", "qmoe_layer_forward",
     "qmoe_event_create", "qmoe_event_destroy", "qmoe_event_record", "qmoe_event_elapsed_ms",
-    "qmoe_set_profile_events",
+    "qmoe_set_profile_events", "qmoe_workspace_status",
 ]
 
 
@@ -78,6 +78,7 @@ def lib():
         "qmoe_event_record": (ctypes.c_int, [P, P]),
         "qmoe_event_elapsed_ms": (ctypes.c_int, [P, P, ctypes.POINTER(ctypes.c_float)]),
         "qmoe_set_profile_events": (ctypes.c_int, [P, P]),
+        "qmoe_workspace_status": (ctypes.c_int, [P, SZ, ctypes.POINTER(ctypes.c_int32), P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)

@@ -82,6 +82,15 @@ QMOE_DEV void st_sys(float *p, float v) { __hip_atomic_store(p, v, __ATOMIC_RELA
 QMOE_DEV void st_sys(int32_t *p, int32_t v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM); }
 QMOE_DEV float ld_sys(const float *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM); }
 QMOE_DEV int32_t ld_sys(const int32_t *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM); }
+// Tagged words: a 32-bit value with a 32-bit tag (the launch epoch) in one 64-bit word, stored
+// and loaded as single atomic accesses, so a reader that sees the tag it expects also sees
+// the value written with it, without any counter or flag.
+QMOE_DEV void st_tag(uint64_t *p, unsigned tag, float v) {
+  __hip_atomic_store(p, ((uint64_t)tag << 32) | __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+QMOE_DEV uint64_t ld_tag(const uint64_t *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM); }
+QMOE_DEV bool tag_is(uint64_t v, unsigned tag) { return (uint32_t)(v >> 32) == tag; }
+QMOE_DEV float tag_val(uint64_t v) { return __uint_as_float((uint32_t)v); }
 QMOE_DEV void drain_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
 // Every thread of the workgroup has issued its hand-off stores: drain them, count this

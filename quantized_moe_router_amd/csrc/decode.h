@@ -1,0 +1,444 @@
+// One-token decode of a whole routed MoE layer in a single launch.
+//
+// The layer's steps (TurboFieldfare post, section "TurboFieldfare의 전문가 스트리밍 구조":
+// router -> expert reads/compute -> cb2 combine with the shared branch and the residual) are
+// run by workgroups with different roles, ordered by block index:
+//   R   router: 4 experts' logits each
+//   SG  shared gate/up: 16 rows of h_shared each
+//   RG  routed gate/up: (slot, 16-row tile); it ranks the logits itself to find the slot's
+//       expert (the first RG workgroup also writes the top-k outputs)
+//   SD  shared down: (32-row output tile, K chunk)
+//   RD  routed down: (slot, group of output tiles); it ranks the logits itself, loads its
+//       weights, then waits for the slot's h; its rows are scaled by the slot's router weight.
+//       The RD workgroups of the last slot also combine: routed rows of every slot + shared
+//       rows + residual -> output rows.
+//
+// Hand-off without counters or fences: every value that one workgroup passes to another is
+// published as a tagged word (common.h) whose tag is this launch's epoch, and a consumer
+// waits until every word it needs carries the epoch.  The epoch is read from the workspace at
+// the start and advanced by the last combining workgroup (the only counter of the launch), so
+// stale words of an earlier call never match.
+//
+// A workgroup only ever waits for words written by workgroups with smaller block indices, and
+// the hardware dispatches workgroups of a launch in index order, so every wait ends; each wait
+// is also bounded and reports a timeout in the status word instead of spinning on.
+#pragma once
+#include "common.h"
+#include "store.h"
+#include "router.h"
+#include "ffn.h"
+
+namespace qmoe {
+
+// Sync area of the workspace (zero-initialised, one 256-byte line each)
+constexpr int SY_LINE = 64;                    // words per line
+enum : int { SY_EPOCH = 0, SY_STATUS = 1, SY_DONE = 2, SY_LINES = 3 };
+constexpr unsigned WAIT_LIMIT = 1u << 20;      // polls: well over a second
+constexpr int DEC_W = 4;                       // waves per workgroup (every role)
+constexpr int KB_DEC = 12;                     // k-steps a wave holds in registers
+constexpr int DEC_THREADS = DEC_W * WAVE;
+// Values that many workgroups wait for are published in several copies, each on its own
+// memory pages, and a reader polls one of them, so that polling does not pile onto a few
+// memory lines: the logits in LOGIT_COPIES copies, h (routed and shared) in H_COPIES.
+constexpr int LOGIT_COPIES = 32, H_COPIES = 4;
+inline __host__ __device__ size_t dec_copy_stride(size_t words) {
+  return ((words * 8 + 4095) / 4096) * 4096;   // bytes
+}
+
+struct DecodeArgs {
+  const uint16_t *x;            // [H] bf16
+  const uint8_t *rq;
+  const uint16_t *rs, *rb;
+  const float *rscale, *pes, *lbias;
+  const uint8_t *experts;
+  size_t stride;
+  const uint8_t *shared;        // null: no shared expert
+  int H, E, k, I, Is;
+  int nc;                       // shared down K chunks per output tile
+  int wpt;                      // waves per routed down tile (1, 2 or 4)
+  float inv_sqrt_h;
+  unsigned *sync;               // [SY_LINES * SY_LINE]
+  uint64_t *logits;             // [LOGIT_COPIES][E] tagged, copies logit_copy words apart
+  uint64_t *h_r;                // [H_COPIES][k][I] tagged, copies hr_copy words apart
+  uint64_t *h_sh;               // [H_COPIES][Is] tagged, copies hsh_copy words apart
+  size_t logit_copy, hr_copy, hsh_copy;
+  uint64_t *y_r;                // [k-1][H] tagged routed rows of slots 0..k-2, router-weighted
+  uint64_t *y_sh;               // [nc][H] tagged shared rows
+  int32_t *topk_idx;            // [k]
+  float *topk_w;                // [k]
+  uint16_t *out;                // [H]
+  float *out_f32;               // [H] or null
+  int nR, nSG, nRG, nSD, nRD;
+};
+
+// LDS map (bytes) shared by every role: [top-k ranking][per-expert scales][reduction]
+// [union: staged x | staged h + combine rows]
+struct DecLds {
+  size_t tk, pes, red, x, xs, hf, hh, hl, hs, comb, total;
+};
+inline __host__ __device__ size_t al16(size_t v) { return (v + 15) & ~(size_t)15; }
+inline __host__ __device__ int dec_tiles_per_wg(int wpt) { return DEC_W / wpt; }
+inline __host__ __device__ DecLds dec_lds(int H, int E, int k, int I, int Kc_sh, int nc, int wpt) {
+  DecLds L;
+  size_t o = 0;
+  L.tk = o; o = al16(o + topk_lds_bytes(E, k));
+  L.pes = o; o = al16(o + (size_t)E * 4 + 16);
+  L.red = o; o = al16(o + (size_t)DEC_W * 32 * 4);
+  const size_t u = o;
+  L.x = u;
+  L.xs = al16(L.x + (size_t)H * 2);
+  const size_t xend = al16(L.xs + (size_t)(H / 32) * 4);
+  const int K = I > Kc_sh ? I : Kc_sh;
+  L.hf = u;
+  L.hh = al16(L.hf + (size_t)K * 4);
+  L.hl = al16(L.hh + (size_t)K * 2);
+  L.hs = al16(L.hl + (size_t)K * 2);
+  L.comb = al16(L.hs + (size_t)(K / 32) * 4);
+  const size_t hend = al16(L.comb + (size_t)(k - 1 + nc) * TILE_ROWS * dec_tiles_per_wg(wpt) * 4);
+  L.total = xend > hend ? xend : hend;
+  return L;
+}
+
+QMOE_DEV void st_sys_u(unsigned *p, unsigned v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM); }
+QMOE_DEV unsigned ld_sys_u(const unsigned *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM); }
+QMOE_DEV unsigned *sy(const DecodeArgs &a, int line) { return a.sync + (size_t)line * SY_LINE; }
+QMOE_DEV void give_up(const DecodeArgs &a) { st_sys_u(sy(a, SY_STATUS), 1u); }
+
+// Bounded wait of the whole workgroup until the n tagged words p[i * stride] carry tag ep
+// (used on one word per producer, as a cheap first test before a full fetch).
+QMOE_DEV void wait_tags(const DecodeArgs &a, const uint64_t *p, int n, int stride, unsigned ep) {
+  for (unsigned it = 0;; ++it) {
+    bool ok = true;
+    for (int i = threadIdx.x; i < n; i += DEC_THREADS) ok &= tag_is(ld_tag(p + (size_t)i * stride), ep);
+    if (__syncthreads_and(ok)) return;
+    if (it == WAIT_LIMIT) {
+      if (threadIdx.x == 0) give_up(a);
+      return;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// Bounded fetch, by the whole workgroup, of n tagged words (word i at addr(i)): f(i, value)
+// is called for every word that carries tag ep (possibly more than once), and the fetch is
+// repeated until all of them do.  PT words per thread are loaded together per pass.
+template <int PT, class Addr, class F>
+QMOE_DEV void fetch_tags(const DecodeArgs &a, int n, unsigned ep, Addr addr, F f) {
+  for (int base = 0; base < n; base += DEC_THREADS * PT) {
+    for (unsigned it = 0;; ++it) {
+      uint64_t v[PT];
+#pragma unroll
+      for (int j = 0; j < PT; ++j) {
+        const int i = base + (int)threadIdx.x + j * DEC_THREADS;
+        v[j] = (i < n) ? ld_tag(addr(i)) : 0;
+      }
+      bool ok = true;
+#pragma unroll
+      for (int j = 0; j < PT; ++j) {
+        const int i = base + (int)threadIdx.x + j * DEC_THREADS;
+        if (i < n) {
+          if (tag_is(v[j], ep)) f(i, tag_val(v[j]));
+          else ok = false;
+        }
+      }
+      if (__syncthreads_and(ok)) break;
+      if (it == WAIT_LIMIT) {
+        if (threadIdx.x == 0) give_up(a);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- R: router
+QMOE_DEV void dec_router(const DecodeArgs &a, int rb, unsigned ep, char *smem) {
+  RouterArgs ra;
+  ra.x = a.x; ra.rq = a.rq; ra.rs = a.rs; ra.rb = a.rb; ra.rscale = a.rscale; ra.pes = a.pes;
+  ra.lbias = a.lbias; ra.T = 1; ra.H = a.H; ra.E = a.E; ra.k = a.k; ra.inv_sqrt_h = a.inv_sqrt_h;
+  ra.logits = nullptr; ra.logits_tag = a.logits; ra.tag = ep;
+  ra.tag_copies = LOGIT_COPIES; ra.tag_copy_stride = a.logit_copy;
+  ra.topk_idx = nullptr; ra.topk_w = nullptr; ra.cnt_tb = nullptr;
+  ra.cnt_all = nullptr; ra.n_tb = 1; ra.n_eb = a.nR; ra.counts = nullptr; ra.offsets = nullptr;
+  ra.sorted = nullptr; ra.active = nullptr; ra.n_active = nullptr; ra.slot_tab = nullptr;
+  ra.n_slots = 0;
+  router_logits_block<1>(ra, 0, rb, smem);
+}
+
+// ---------------------------------------------------------------- top-k (whole workgroup)
+// Expert and weight of `slot` (returned to every thread); with `publish`, the top-k outputs
+// are written too.  The E logits are fetched (tagged) into keys; chunks are ranked by the
+// four waves in parallel, the survivors by wave 0.
+QMOE_DEV void dec_topk(const DecodeArgs &a, unsigned ep, int slot, bool publish, int &e_out,
+                       float &w_out, char *smem, const DecLds &L) {
+  const int tid = threadIdx.x, wv = tid / WAVE, lane = tid % WAVE;
+  const int E = a.E, k = a.k, nch = topk_chunks(E);
+  uint64_t *keys = (uint64_t *)(smem + L.tk);
+  uint64_t *surv = keys + nch * WAVE, *sel = surv + nch * k;
+  float *pes = (float *)(smem + L.pes);
+  int *se = (int *)(pes + E);
+  float *sw = (float *)(se + 1);
+  // per-expert scales into LDS (loads in flight while the logits are fetched)
+  constexpr int PJ = MAX_EXPERTS / DEC_THREADS;
+  float pv[PJ];
+#pragma unroll
+  for (int j = 0; j < PJ; ++j) {
+    const int i = tid + j * DEC_THREADS;
+    pv[j] = (i < E) ? a.pes[i] : 0.f;
+  }
+  for (int i = E + tid; i < nch * WAVE; i += DEC_THREADS) keys[i] = topk_pad_key(i);
+  const uint64_t *lg = a.logits + (size_t)(blockIdx.x % LOGIT_COPIES) * a.logit_copy;
+  fetch_tags<PJ>(a, E, ep, [&](int i) { return lg + i; },
+                 [&](int i, float v) { keys[i] = topk_key(v, i); });
+#pragma unroll
+  for (int j = 0; j < PJ; ++j) {
+    const int i = tid + j * DEC_THREADS;
+    if (i < E) pes[i] = pv[j];
+  }
+  for (int c = wv; c < nch; c += DEC_W) topk_rank_chunk(keys + c * WAVE, k, surv + c * k);
+  __syncthreads();
+  if (wv == 0) {
+    topk_rank_survivors(surv, nch * k, k, sel);
+    __builtin_amdgcn_wave_barrier();
+    int myi;
+    float myw;
+    topk_weights(sel, k, pes, myi, myw);
+    if (publish && lane < k) {
+      a.topk_idx[lane] = myi;
+      a.topk_w[lane] = myw;
+    }
+    if (lane == slot) { *se = myi; *sw = myw; }
+  }
+  __syncthreads();
+  e_out = min(max(*se, 0), E - 1);
+  w_out = *sw;
+}
+
+// ---------------------------------------------------------------- gate/up of one tile, one token
+QMOE_DEV void dec_stage_x(const DecodeArgs &a, char *smem, const DecLds &L) {
+  stage_rows_bf16<DEC_THREADS>(a.x, a.H, 1, [](int) { return 0; }, (uint16_t *)(smem + L.x),
+                               (float *)(smem + L.xs));
+}
+
+// 16 gate + 16 up rows of store tile `tile` of block `blk` against the staged x (split-K over
+// the four waves); the 16 values silu(g)*u are published (tagged) at h_out[16*tile + r] of
+// each of the H_COPIES copies.
+QMOE_DEV void dec_gate_up(const DecodeArgs &a, const uint8_t *blk, int tile, uint64_t *h_out,
+                          size_t copy_stride, unsigned ep, char *smem, const DecLds &L) {
+  const int H = a.H, KS = H / GROUP;
+  const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
+  const int rr = lane % 32, half = lane / 32;
+  const uint16_t *xl = (const uint16_t *)(smem + L.x);
+  const float *xs = (const float *)(smem + L.xs);
+  float *red = (float *)(smem + L.red);
+  const uint8_t *tbase = blk + (size_t)tile * KS * KSTEP_BYTES;
+  const int ks0 = (KS * wv) / DEC_W, nk = (KS * (wv + 1)) / DEC_W - ks0;
+  float acc = 0.f;
+  for (int kc = 0; kc < nk; kc += KB_DEC) {
+    qmoe_u32x4 cv[KB_DEC];
+    uint32_t sb[KB_DEC];
+    load_batch<KB_DEC>(tbase, ks0, kc, nk, lane, rr, cv, sb);
+#pragma unroll
+    for (int u = 0; u < KB_DEC; ++u)
+      if (kc + u < nk) {
+        const int col = (ks0 + kc + u) * GROUP + half * 32;
+        acc += kstep_bf16(cv[u], sb[u], xl + col, xs[col / 32]);
+      }
+  }
+  acc += __shfl_xor(acc, 32, WAVE);
+  if (half == 0) red[wv * 32 + rr] = acc;
+  __syncthreads();
+  if (tid < 16 * H_COPIES) {
+    const int r = tid % 16, c = tid / 16;
+    float g = 0.f, u = 0.f;
+    for (int w = 0; w < DEC_W; ++w) { g += red[w * 32 + r]; u += red[w * 32 + 16 + r]; }
+    st_tag(h_out + (size_t)c * copy_stride + 16 * tile + r, ep, silu(g) * u);
+  }
+}
+
+// ---------------------------------------------------------------- down projection pieces
+struct DownRegs {
+  qmoe_u32x4 cv[KB_DEC];
+  uint32_t sb[KB_DEC];
+  int nk;
+};
+
+// This wave's k-steps [kb0, kb0 + nk) (nk <= KB_DEC) of output tile `tile` of the down
+// section of block `blk` (input width K).
+QMOE_DEV void dec_down_load(const DecodeArgs &a, const uint8_t *blk, int K, int tile, int kb0,
+                            int nk, DownRegs &d) {
+  const int lane = threadIdx.x % WAVE;
+  const BlockGeom geo = block_geom(a.H, K);
+  const uint8_t *tbase = blk + geo.gu_bytes + (size_t)tile * (K / GROUP) * KSTEP_BYTES;
+  d.nk = nk;
+  if (nk > 0) load_batch<KB_DEC>(tbase, kb0, 0, nk, lane, lane % 32, d.cv, d.sb);
+}
+
+// Fetch the n tagged h values src[0..n) (n a multiple of 64) and stage them as hi/lo bf16
+// planes with 32-column sums of hi + lo.  Called after the caller's weight loads were issued:
+// those are awaited first, so that polling starts about when h is due.
+QMOE_DEV void dec_stage_h(const DecodeArgs &a, const uint64_t *src, int n, unsigned ep, char *smem,
+                          const DecLds &L) {
+  float *hf = (float *)(smem + L.hf);
+  uint16_t *hh = (uint16_t *)(smem + L.hh), *hl = (uint16_t *)(smem + L.hl);
+  float *hs = (float *)(smem + L.hs);
+  drain_memory();
+  fetch_tags<4>(a, n, ep, [&](int i) { return src + i; }, [&](int i, float v) { hf[i] = v; });
+  for (int c = threadIdx.x; c < n / 8; c += DEC_THREADS) {
+    uint32_t hi2[4], lo2[4];
+    float p = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float v0 = hf[8 * c + 2 * q], v1 = hf[8 * c + 2 * q + 1];
+      const uint32_t h0 = f32_to_bf16_bits(v0), h1 = f32_to_bf16_bits(v1);
+      const uint32_t l0 = f32_to_bf16_bits(v0 - __uint_as_float(h0 << 16));
+      const uint32_t l1 = f32_to_bf16_bits(v1 - __uint_as_float(h1 << 16));
+      hi2[q] = h0 | (h1 << 16);
+      lo2[q] = l0 | (l1 << 16);
+      p += (__uint_as_float(h0 << 16) + __uint_as_float(l0 << 16)) +
+           (__uint_as_float(h1 << 16) + __uint_as_float(l1 << 16));
+    }
+    *(qmoe_u32x4 *)(hh + 8 * c) = qmoe_u32x4{hi2[0], hi2[1], hi2[2], hi2[3]};
+    *(qmoe_u32x4 *)(hl + 8 * c) = qmoe_u32x4{lo2[0], lo2[1], lo2[2], lo2[3]};
+    p += __shfl_xor(p, 1, WAVE);
+    p += __shfl_xor(p, 2, WAVE);
+    if ((c & 3) == 0) hs[c / 4] = p;
+  }
+  __syncthreads();
+}
+
+// This wave's partial dot products for its 32 rows over its loaded k-steps; local k-step u
+// of the wave is column block kb0 + u of the staged h.  The 32 sums go to red[wave][row].
+QMOE_DEV void dec_down_dot(const DownRegs &d, int kb0, char *smem, const DecLds &L) {
+  const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
+  const int rr = lane % 32, half = lane / 32;
+  const uint16_t *hh = (const uint16_t *)(smem + L.hh), *hl = (const uint16_t *)(smem + L.hl);
+  const float *hs = (const float *)(smem + L.hs);
+  float *red = (float *)(smem + L.red);
+  float acc = 0.f;
+#pragma unroll
+  for (int u = 0; u < KB_DEC; ++u)
+    if (u < d.nk) {
+      const int col = (kb0 + u) * GROUP + half * 32;
+      acc += kstep_hilo(d.cv[u], d.sb[u], hh + col, hl + col, hs[col / 32]);
+    }
+  acc += __shfl_xor(acc, 32, WAVE);
+  if (half == 0) red[wv * 32 + rr] = acc;
+}
+
+// ---------------------------------------------------------------- roles
+QMOE_DEV void dec_shared_down(const DecodeArgs &a, int b, unsigned ep, char *smem, const DecLds &L) {
+  const int tiles_d = a.H / TILE_ROWS;
+  const int tile = b % tiles_d, c = b / tiles_d;
+  const int KS = a.Is / GROUP;
+  const int kb0 = (KS * c) / a.nc, kb1 = (KS * (c + 1)) / a.nc;
+  const int wv = threadIdx.x / WAVE;
+  const int n = kb1 - kb0;
+  const int w0 = (n * wv) / DEC_W, w1 = (n * (wv + 1)) / DEC_W;
+  // once the last router workgroup has published (so that the router's loads go first),
+  // load the weights, then wait for h_shared
+  wait_tags(a, a.logits + (size_t)(blockIdx.x % LOGIT_COPIES) * a.logit_copy + (a.E - 1), 1, 1, ep);
+  DownRegs d;
+  dec_down_load(a, a.shared, a.Is, tile, kb0 + w0, w1 - w0, d);
+  dec_stage_h(a, a.h_sh + (size_t)(tile % H_COPIES) * a.hsh_copy + (size_t)kb0 * GROUP, n * GROUP,
+              ep, smem, L);
+  dec_down_dot(d, w0, smem, L);
+  __syncthreads();
+  if (threadIdx.x < 32) {
+    const float *red = (const float *)(smem + L.red);
+    float yv = 0.f;
+    for (int w = 0; w < DEC_W; ++w) yv += red[w * 32 + threadIdx.x];
+    st_tag(a.y_sh + (size_t)c * a.H + TILE_ROWS * tile + threadIdx.x, ep, yv);
+  }
+}
+
+QMOE_DEV void dec_routed_down(const DecodeArgs &a, int b, unsigned ep, char *smem, const DecLds &L) {
+  const int tiles_d = a.H / TILE_ROWS, tpw = dec_tiles_per_wg(a.wpt);
+  const int groups = (tiles_d + tpw - 1) / tpw;
+  const int slot = b / groups, g = b % groups;
+  const int tid = threadIdx.x, wv = tid / WAVE;
+  int e;
+  float w;
+  dec_topk(a, ep, slot, false, e, w, smem, L);
+  const int KS = a.I / GROUP;
+  const int tile = g * tpw + wv / a.wpt, part = wv % a.wpt;
+  const int kb0 = (KS * part) / a.wpt, kb1 = (KS * (part + 1)) / a.wpt;
+  DownRegs d;
+  dec_down_load(a, a.experts + (size_t)e * a.stride, a.I, min(tile, tiles_d - 1), kb0,
+                tile < tiles_d ? kb1 - kb0 : 0, d);
+  dec_stage_h(a, a.h_r + (size_t)(g % H_COPIES) * a.hr_copy + (size_t)slot * a.I, a.I, ep, smem, L);
+  dec_down_dot(d, kb0, smem, L);
+  __syncthreads();
+  // row r of this group (tile r / 32 of the group): the wpt waves of its tile add up
+  const float *red = (const float *)(smem + L.red);
+  const int row0 = g * TILE_ROWS * tpw;
+  const int nr = min(TILE_ROWS * tpw, a.H - row0);
+  const int r = tid;
+  const bool mine = r < nr;
+  float yv = 0.f;
+  if (mine) {
+    const int t = r / TILE_ROWS, rw = r % TILE_ROWS;
+    for (int p = 0; p < a.wpt; ++p) yv += red[(t * a.wpt + p) * 32 + rw];
+    yv *= w;
+  }
+  if (slot < a.k - 1) {
+    if (mine) st_tag(a.y_r + (size_t)slot * a.H + row0 + r, ep, yv);
+    return;
+  }
+  // last slot: combine the rows of this group
+  const int nsrc = a.k - 1 + (a.shared ? a.nc : 0);
+  float *comb = (float *)(smem + L.comb);
+  fetch_tags<4>(a, nsrc * nr, ep,
+                [&](int i) {
+                  const int s = i / nr, rw = i % nr;
+                  return (s < a.k - 1) ? a.y_r + (size_t)s * a.H + row0 + rw
+                                       : a.y_sh + (size_t)(s - (a.k - 1)) * a.H + row0 + rw;
+                },
+                [&](int i, float v) { comb[i] = v; });
+  if (mine) {
+    float acc = yv;
+    for (int s = 0; s < a.k - 1; ++s) acc += comb[s * nr + r];
+    float sh = 0.f;
+    for (int s = a.k - 1; s < nsrc; ++s) sh += comb[s * nr + r];
+    acc += sh;
+    acc += bf16_to_f32(a.x[row0 + r]);
+    a.out[row0 + r] = (uint16_t)f32_to_bf16_bits(acc);
+    if (a.out_f32) a.out_f32[row0 + r] = acc;
+  }
+  // the last combining workgroup advances the epoch
+  if (arrive_last(sy(a, SY_DONE), (unsigned)groups) && tid == 0) st_sys_u(sy(a, SY_EPOCH), ep);
+}
+
+__global__ void __launch_bounds__(DEC_THREADS) decode_layer_kernel(DecodeArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const unsigned ep = ld_sys_u(sy(a, SY_EPOCH)) + 1u;
+  const int Kc_sh = a.shared ? GROUP * ((a.Is / GROUP + a.nc - 1) / a.nc) : 0;
+  const DecLds L = dec_lds(a.H, a.E, a.k, a.I, Kc_sh, a.nc, a.wpt);
+  int b = blockIdx.x;
+  if (b < a.nR) { dec_router(a, b, ep, smem); return; }
+  b -= a.nR;
+  if (b < a.nSG) {
+    dec_stage_x(a, smem, L);
+    wait_tags(a, a.logits + (size_t)(blockIdx.x % LOGIT_COPIES) * a.logit_copy + (a.E - 1), 1, 1, ep);
+    dec_gate_up(a, a.shared, b, a.h_sh, a.hsh_copy, ep, smem, L);
+    return;
+  }
+  b -= a.nSG;
+  if (b < a.nRG) {
+    const int tiles_r = a.I / 16;
+    const int slot = b / tiles_r, tile = b % tiles_r;
+    dec_stage_x(a, smem, L);
+    int e;
+    float w;
+    dec_topk(a, ep, slot, b == 0, e, w, smem, L);
+    dec_gate_up(a, a.experts + (size_t)e * a.stride, tile, a.h_r + (size_t)slot * a.I, a.hr_copy, ep,
+                smem, L);
+    return;
+  }
+  b -= a.nRG;
+  if (b < a.nSD) { dec_shared_down(a, b, ep, smem, L); return; }
+  b -= a.nSD;
+  if (b < a.nRD) dec_routed_down(a, b, ep, smem, L);
+}
+
+}  // namespace qmoe

@@ -16,18 +16,21 @@
 #include "store.h"
 #include "router.h"
 #include "ffn.h"
+#include "decode.h"
 
 using namespace qmoe;
 
 namespace {
 
 constexpr int VERSION = 100;               // 0.1.0
-constexpr size_t COUNTER_BYTES = 128 * 1024;
-constexpr int GU_W = 4;     // waves per gate/up workgroup (split-K)
-constexpr int D_W = 4;      // waves per per-slot down workgroup (split-K)
+constexpr size_t COUNTER_BYTES = 512 * 1024;
+constexpr int GU_W = 8;     // waves per routed gate/up workgroup (split-K)
+constexpr int SH_W = 4;     // waves per shared gate/up workgroup (inside the router launch)
+constexpr int D_W = 8;      // waves per down workgroup (split-K)
 constexpr int KB = 12;      // k-steps loaded per batch by a wave
 constexpr int MB_MAX = 8;   // rows (tokens) per activation block
 constexpr int CNT_TILE_WORD = 64 + 16384;  // first word of the per-tile combine counters
+constexpr int DEC_SYNC_WORD = 32768;       // first word of the one-token decode sync area
 constexpr int MAX_T = 65536;
 
 thread_local std::string g_err;
@@ -121,9 +124,18 @@ inline int shared_chunks(const qmoe_dims *d) {
   return std::max(1, std::min(c, ks));
 }
 
+// The same for the one-token decode launch, whose shared down workgroups split one output
+// tile's k-steps over their four waves (at most DEC_W * KB_DEC k-steps per chunk).
+inline int dec_shared_chunks(const qmoe_dims *d) {
+  if (d->shared_inter == 0) return 0;
+  const int ks = d->shared_inter / GROUP;
+  return (ks + DEC_W * KB_DEC - 1) / (DEC_W * KB_DEC);
+}
+
 struct WsLayout {
   size_t cnt, logits, tidx, tw, counts, offsets, sorted, active, nact, slot_tab;
-  size_t hr_hi, hr_lo, hs_hi, hs_lo, y, ysh, ysh_part, total;
+  size_t hr_hi, hr_lo, hs_hi, hs_lo, y, ysh, ysh_part;
+  size_t dec_logits, dec_hr, dec_hsh, dec_yr, dec_ysh, total;
 };
 
 WsLayout ws_layout(const qmoe_dims *d, int Tmax) {
@@ -148,6 +160,11 @@ WsLayout ws_layout(const qmoe_dims *d, int Tmax) {
   w.y = o; o += al(Tc * k * H * 4);
   w.ysh = o; o += al(Tc * H * 4);
   w.ysh_part = o; o += al((size_t)shared_chunks(d) * Tc * H * 4);
+  w.dec_logits = o; o += (size_t)LOGIT_COPIES * dec_copy_stride(E);
+  w.dec_hr = o; o += (size_t)H_COPIES * dec_copy_stride(k * d->inter);
+  w.dec_hsh = o; o += (size_t)H_COPIES * dec_copy_stride((size_t)d->shared_inter);
+  w.dec_yr = o; o += al((k - 1) * H * 8);
+  w.dec_ysh = o; o += al((size_t)dec_shared_chunks(d) * H * 8);
   w.total = o;
   return w;
 }
@@ -164,12 +181,18 @@ int check_ws(const qmoe_dims *d, int T, void *ws, size_t ws_bytes) {
   return QMOE_OK;
 }
 
+int check_router(const qmoe_router *r) {
+  if (!r || !r->codes || !r->scales || !r->biases || !r->per_expert_scale)
+    return fail(QMOE_ERR_ARG, "router codes/scales/biases/per_expert_scale must not be NULL");
+  if (r->router_scale && !aligned(r->router_scale, 16))
+    return fail(QMOE_ERR_ARG, "router_scale must be 16-byte aligned");
+  return QMOE_OK;
+}
+
 int check_layer(const qmoe_layer *L) {
   if (!L) return fail(QMOE_ERR_ARG, "layer is NULL");
   int rc = check_dims(&L->d);
-  if (rc) return rc;
-  if (!L->r.codes || !L->r.scales || !L->r.biases || !L->r.per_expert_scale)
-    return fail(QMOE_ERR_ARG, "router codes/scales/biases/per_expert_scale must not be NULL");
+  if (rc || (rc = check_router(&L->r))) return rc;
   if (!L->experts) return fail(QMOE_ERR_ARG, "expert store is NULL");
   if (!aligned(L->experts, 256) || L->expert_stride % 256)
     return fail(QMOE_ERR_ARG, "expert store base and stride must be 256-byte aligned");
@@ -203,7 +226,8 @@ int set_lds(K kernel, size_t bytes) {
 }
 
 size_t router_smem(const qmoe_dims *d) {
-  return std::max(router_lds_bytes(d->hidden), (size_t)(2 * d->n_experts) * 4);
+  return std::max({router_lds_bytes(d->hidden), (size_t)(2 * d->n_experts) * 4,
+                   ROUTER_WAVES * topk_lds_bytes(d->n_experts, d->top_k)});
 }
 
 RouterArgs make_router_args(const qmoe_dims *d, const qmoe_router *r, const uint16_t *x, int T,
@@ -238,15 +262,17 @@ __global__ void __launch_bounds__(ROUTER_THREADS) router_shared_kernel(RouterArg
   extern __shared__ __align__(16) char smem[];
   if ((int)blockIdx.x < n_router) {
     const int tb = blockIdx.x / ra.n_eb, eb = blockIdx.x % ra.n_eb;
-    router_logits_block(ra, tb, eb, smem);
+    router_logits_block<ROUTER_TB>(ra, tb, eb, smem);
     router_finish(ra, tb, smem);
   } else {
     SlotRows sr;
     slot_rows(fa, 0, true, sr);
-    gu_tile<GU_W, MB, KB>(fa, sr, blockIdx.x - n_router, smem);
+    gu_tile<SH_W, MB, KB>(fa, sr, blockIdx.x - n_router, smem);
   }
 }
-static_assert(GU_W * WAVE == ROUTER_THREADS, "fused router/shared kernel uses one block size");
+static_assert(SH_W * WAVE == ROUTER_THREADS, "fused router/shared kernel uses one block size");
+static_assert((size_t)(DEC_SYNC_WORD + SY_LINES * SY_LINE) * 4 <= COUNTER_BYTES,
+              "decode sync area inside the counter area");
 
 // Record an event; under stream capture it is added as an event-record node of the graph
 // after the captured work so far, and later captured work depends on it.
@@ -271,7 +297,7 @@ int record_event(hipEvent_t e, hipStream_t s) {
 inline int mb_for(int T) { return T == 1 ? 1 : MB_MAX; }
 
 size_t gu_smem(int H, int mb) {
-  return mb == 1 ? gu_lds_bytes<GU_W, 1>(H) : gu_lds_bytes<GU_W, MB_MAX>(H);
+  return mb == 1 ? gu_lds_bytes<SH_W, 1>(H) : gu_lds_bytes<SH_W, MB_MAX>(H);
 }
 size_t d_smem(int K, int mb) {
   return mb == 1 ? d_lds_bytes<D_W, 1>(K) : d_lds_bytes<D_W, MB_MAX>(K);
@@ -345,6 +371,67 @@ static int launch_d(FfnArgs a, bool with_shared, hipStream_t s) {
   return mb_for(a.T) == 1 ? launch_d_t<1>(a, slots, Kc, s) : launch_d_t<MB_MAX>(a, slots, Kc, s);
 }
 
+// One-token decode in a single launch (decode.h) when every down-projection wave's k-steps
+// fit in its register batch.  Routed down tiles take 1, 2 or 4 waves (wpt) so that a wave
+// holds at most KB_DEC k-steps; the shared down width is cut into chunks of at most
+// DEC_W * KB_DEC k-steps.
+static int dec_wpt(const qmoe_dims *d) {
+  const int ks = d->inter / GROUP;
+  for (int w = 1; w <= DEC_W; w *= 2)
+    if ((ks + w - 1) / w <= KB_DEC) return w;
+  return 0;
+}
+
+static bool decode_fits(const qmoe_dims *d) {
+  return dec_wpt(d) > 0 && d->top_k <= MAX_TOPK && d->n_experts <= MAX_EXPERTS;
+}
+
+static DecLds dec_lds_of(const qmoe_dims *d, bool sh) {
+  const int nc = sh ? dec_shared_chunks(d) : 0;
+  const int kc = sh ? GROUP * ((d->shared_inter / GROUP + nc - 1) / nc) : 0;
+  return dec_lds(d->hidden, d->n_experts, d->top_k, d->inter, kc, nc, dec_wpt(d));
+}
+
+static int launch_decode(const qmoe_layer *L, const uint16_t *x, uint16_t *out, float *out_f32,
+                         int32_t *idx, float *w, void *ws, const WsLayout &wl, hipStream_t s) {
+  const qmoe_dims *d = &L->d;
+  const bool sh = L->shared != nullptr;
+  DecodeArgs a;
+  memset(&a, 0, sizeof a);
+  a.x = x; a.rq = L->r.codes; a.rs = L->r.scales; a.rb = L->r.biases;
+  a.rscale = L->r.router_scale; a.pes = L->r.per_expert_scale; a.lbias = L->r.logit_bias;
+  a.experts = (const uint8_t *)L->experts; a.stride = L->expert_stride;
+  a.shared = sh ? (const uint8_t *)L->shared : nullptr;
+  a.H = d->hidden; a.E = d->n_experts; a.k = d->top_k; a.I = d->inter;
+  a.Is = sh ? d->shared_inter : 0;
+  a.nc = sh ? dec_shared_chunks(d) : 0;
+  a.wpt = dec_wpt(d);
+  a.inv_sqrt_h = (float)(1.0 / std::sqrt((double)d->hidden));
+  a.sync = at<unsigned>(ws, wl.cnt) + DEC_SYNC_WORD;
+  a.logits = at<uint64_t>(ws, wl.dec_logits);
+  a.logit_copy = dec_copy_stride(a.E) / 8;
+  a.h_r = at<uint64_t>(ws, wl.dec_hr);
+  a.hr_copy = dec_copy_stride((size_t)a.k * a.I) / 8;
+  a.h_sh = at<uint64_t>(ws, wl.dec_hsh);
+  a.hsh_copy = dec_copy_stride((size_t)a.Is) / 8;
+  a.y_r = at<uint64_t>(ws, wl.dec_yr);
+  a.y_sh = at<uint64_t>(ws, wl.dec_ysh);
+  a.topk_idx = idx; a.topk_w = w; a.out = out; a.out_f32 = out_f32;
+  const int tiles_d = a.H / TILE_ROWS, tpw = dec_tiles_per_wg(a.wpt);
+  a.nR = (a.E + ROUTER_EPB - 1) / ROUTER_EPB;
+  a.nSG = sh ? a.Is / 16 : 0;
+  a.nRG = a.k * (a.I / 16);
+  a.nSD = sh ? tiles_d * a.nc : 0;
+  a.nRD = a.k * ((tiles_d + tpw - 1) / tpw);
+  const size_t lds = std::max(router_lds_bytes(a.H, 1), dec_lds_of(d, sh).total);
+  int rc = set_lds(decode_layer_kernel, lds);
+  if (rc) return rc;
+  const int n = a.nR + a.nSG + a.nRG + a.nSD + a.nRD;
+  hipLaunchKernelGGL(decode_layer_kernel, dim3(n), dim3(DEC_THREADS), lds, s, a);
+  QMOE_LAUNCHED();
+  return QMOE_OK;
+}
+
 }  // namespace
 
 // ====================================================================== exported entry points
@@ -373,7 +460,7 @@ int qmoe_workspace_init(void *ws, size_t ws_bytes, qmoe_stream_t stream) {
   if (!aligned(ws, 256)) return fail(QMOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   int rc = check_arch();
   if (rc) return rc;
-  const size_t n = std::min(ws_bytes, COUNTER_BYTES) / 4;
+  const size_t n = ws_bytes / 4;
   if (n == 0) return ok();
   hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
                      (hipStream_t)stream, (uint32_t *)ws, n);
@@ -430,9 +517,7 @@ int qmoe_router_topk(const qmoe_dims *d, const qmoe_router *r, const uint16_t *x
                      int32_t *topk_idx, float *topk_w, float *logits_or_null, void *ws,
                      size_t ws_bytes, qmoe_stream_t stream) {
   int rc = check_dims(d);
-  if (rc || (rc = check_T(T))) return rc;
-  if (!r || !r->codes || !r->scales || !r->biases || !r->per_expert_scale)
-    return fail(QMOE_ERR_ARG, "router codes/scales/biases/per_expert_scale must not be NULL");
+  if (rc || (rc = check_T(T)) || (rc = check_router(r))) return rc;
   if (T == 0) return ok();
   if (!x || !topk_idx || !topk_w) return fail(QMOE_ERR_ARG, "x/topk_idx/topk_w must not be NULL");
   if ((rc = check_ws(d, T, ws, ws_bytes))) return rc;
@@ -513,6 +598,14 @@ int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16
   const WsLayout wl = ws_layout(d, Tc_max);
   const int H = d->hidden, k = d->top_k;
   const bool sh = L->shared != nullptr;
+  if (T == 1 && decode_fits(d)) {
+    int32_t *idx = topk_idx_or_null ? topk_idx_or_null : at<int32_t>(ws, wl.tidx);
+    float *w = topk_w_or_null ? topk_w_or_null : at<float>(ws, wl.tw);
+    if (g_prof_start && (rc = record_event(g_prof_start, s))) return rc;
+    if ((rc = launch_decode(L, x, out, out_f32_or_null, idx, w, ws, wl, s))) return rc;
+    if (g_prof_stop && (rc = record_event(g_prof_stop, s))) return rc;
+    return ok();
+  }
   for (int c0 = 0; c0 < T; c0 += CHUNK_TOKENS) {
     const int Tc = std::min(CHUNK_TOKENS, T - c0);
     const uint16_t *xc = x + (size_t)c0 * H;
@@ -583,6 +676,20 @@ int qmoe_event_elapsed_ms(void *start, void *stop, float *ms_out) {
   if (!start || !stop || !ms_out) return fail(QMOE_ERR_ARG, "event_elapsed_ms: NULL argument");
   QMOE_HIP(hipEventSynchronize((hipEvent_t)stop));
   QMOE_HIP(hipEventElapsedTime(ms_out, (hipEvent_t)start, (hipEvent_t)stop));
+  return ok();
+}
+
+int qmoe_workspace_status(const void *ws, size_t ws_bytes, int32_t *status_out,
+                          qmoe_stream_t stream) {
+  if (!ws || !status_out) return fail(QMOE_ERR_ARG, "workspace_status: NULL argument");
+  if (ws_bytes < COUNTER_BYTES) return fail(QMOE_ERR_WORKSPACE, "workspace smaller than its counter area");
+  int rc = check_arch();
+  if (rc) return rc;
+  unsigned v = 0;
+  const unsigned *p = (const unsigned *)ws + DEC_SYNC_WORD + SY_STATUS * SY_LINE;
+  QMOE_HIP(hipMemcpyAsync(&v, p, sizeof v, hipMemcpyDeviceToHost, (hipStream_t)stream));
+  QMOE_HIP(hipStreamSynchronize((hipStream_t)stream));
+  *status_out = (int32_t)v;
   return ok();
 }
 

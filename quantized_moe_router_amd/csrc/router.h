@@ -31,7 +31,11 @@ struct RouterArgs {
   const float *lbias;         // [E] or null
   int T, H, E, k;
   float inv_sqrt_h;           // fp32(1/sqrt(H))
-  float *logits;              // [T, E]
+  float *logits;              // [T, E] (unless logits_tag is set)
+  uint64_t *logits_tag;       // or null: logits published as tagged words (tag << 32 | bits),
+  unsigned tag;               //   tag_copies copies of [T, E], tag_copy_stride words apart
+  int tag_copies;
+  size_t tag_copy_stride;
   int32_t *topk_idx;          // [T, k]
   float *topk_w;              // [T, k]
   unsigned *cnt_tb;           // [n_tb] completion counters (zero on entry, zero on exit)
@@ -43,54 +47,99 @@ struct RouterArgs {
   int n_slots;
 };
 
-// LDS bytes of a router workgroup for hidden H
-inline size_t router_lds_bytes(int H) {
-  return (size_t)ROUTER_TB * H * 4 + (size_t)ROUTER_TB * (H / 16) * 4 + 64;
+// LDS bytes of the logits part of a router workgroup for hidden H and up to nt tokens
+inline __host__ __device__ size_t router_lds_bytes(int H, int nt = ROUTER_TB) {
+  return (size_t)nt * H * 4 + (size_t)nt * (H / 16) * 4 + 64;
 }
 
-// ---------------------------------------------------------------- top-k of one token (one wave)
-// Exact order: larger logit first, equal logits -> lower expert index.  A NaN logit ranks
-// as -inf, so every selected index is a valid expert id whatever the logits hold (the
-// sentinel index of an empty candidate always loses to a real expert).
-QMOE_DEV void topk_one_token(const float *lrow, int E, int k, const float *pes,
-                             int32_t *idx_out, float *w_out) {
+// ---------------------------------------------------------------- top-k by exact ranking
+// Order: larger logit first, equal logits -> lower expert index.  A NaN logit ranks as -inf
+// (so every selected index is a valid expert id whatever the logits hold) and -0 as +0.
+// Each (logit, expert) pair becomes one 64-bit key whose unsigned order is exactly that
+// order; all keys are distinct, so the selection is a rank computation with no branches:
+//   1. the keys are cut into chunks of 64; a lane ranks its key inside its chunk with 64
+//      broadcast LDS reads, and the keys of rank < k ("survivors") go to slot rank of their
+//      chunk's k survivor slots (every global top-k key survives its chunk);
+//   2. each survivor is ranked among all survivors; rank r < k is the r-th selected expert.
+// Padding keys (chunk positions >= E) sort below every real key.
+QMOE_DEV uint64_t topk_key(float l, int e) {
+  if (!(l == l)) l = -INFINITY;
+  if (l == 0.f) l = 0.f;
+  uint32_t u = __float_as_uint(l);
+  u ^= (u & 0x80000000u) ? 0xFFFFFFFFu : 0x80000000u;
+  return ((uint64_t)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+QMOE_DEV uint64_t topk_pad_key(int e) { return (uint64_t)(0xFFFFFFFFu - (uint32_t)e); }
+QMOE_DEV int key_expert(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
+QMOE_DEV float key_logit(uint64_t key) {
+  uint32_t u = (uint32_t)(key >> 32);
+  u ^= (u & 0x80000000u) ? 0x80000000u : 0xFFFFFFFFu;
+  return __uint_as_float(u);
+}
+
+inline __host__ __device__ int topk_chunks(int E) { return (E + WAVE - 1) / WAVE; }
+// LDS of one ranking: keys [chunks*64], survivors [chunks*k], result [k] (64-bit each)
+inline __host__ __device__ size_t topk_lds_bytes(int E, int k) {
+  return (size_t)8 * (topk_chunks(E) * WAVE + topk_chunks(E) * k + k);
+}
+
+// Step 1 for one chunk, by one wave: ck = the chunk's 64 keys.
+QMOE_DEV void topk_rank_chunk(const uint64_t *ck, int k, uint64_t *surv) {
   const int lane = threadIdx.x % WAVE;
+  const uint64_t K = ck[lane];
+  int r = 0;
+#pragma unroll 16
+  for (int j = 0; j < WAVE; ++j) r += (ck[j] > K) ? 1 : 0;
+  if (r < k) surv[r] = K;
+}
+
+// Step 2, by one wave: sel[r] = the key of rank r < k among the n survivors.
+QMOE_DEV void topk_rank_survivors(const uint64_t *surv, int n, int k, uint64_t *sel) {
+  for (int i = threadIdx.x % WAVE; i < n; i += WAVE) {
+    const uint64_t K = surv[i];
+    int r = 0;
+    for (int j = 0; j < n; ++j) r += (surv[j] > K) ? 1 : 0;
+    if (r < k) sel[r] = K;
+  }
+}
+
+// Lane j < k of the wave gets the j-th selected expert and its weight: softmax over the kept
+// logits, times per_expert_scale (pes, global or LDS) of that expert.  Other lanes get 0, 0.
+QMOE_DEV void topk_weights(const uint64_t *sel, int k, const float *pes, int &myi, float &myw) {
+  const int lane = threadIdx.x % WAVE;
+  const uint64_t K = sel[min(lane, k - 1)];
+  const float lv = key_logit(K);
+  const float vmax = __shfl(lv, 0, WAVE);
+  const float z = (lane < k) ? expf(lv - vmax) : 0.f;
+  const float zsum = wave_sum(z);
+  myi = (lane < k) ? key_expert(K) : 0;
+  myw = (lane < k) ? (z / zsum) * pes[myi] : 0.f;
+}
+
+// The whole selection by one wave for one token.  lrow: E logits written by other
+// workgroups of the launch (system-scope loads).  lds: topk_lds_bytes(E, k) bytes owned by
+// this wave.
+QMOE_DEV void topk_wave(const float *lrow, int E, int k, const float *pes, uint64_t *lds,
+                        int &myi, float &myw) {
+  const int lane = threadIdx.x % WAVE, nch = topk_chunks(E);
+  uint64_t *keys = lds, *surv = lds + nch * WAVE, *sel = surv + nch * k;
   float v[MAX_EXPERTS / WAVE];
 #pragma unroll
-  for (int j = 0; j < MAX_EXPERTS / WAVE; ++j) {
-    const int e = lane + WAVE * j;
-    const float l = (e < E) ? ld_sys(lrow + e) : -INFINITY;
-    v[j] = (l == l) ? l : -INFINITY;
+  for (int c = 0; c < MAX_EXPERTS / WAVE; ++c) {
+    const int e = c * WAVE + lane;
+    v[c] = (c < nch && e < E) ? ld_sys(lrow + e) : 0.f;
   }
-  unsigned taken = 0;
-  float myv = 0.f;
-  int myi = 0;
-  for (int r = 0; r < k; ++r) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
 #pragma unroll
-    for (int j = 0; j < MAX_EXPERTS / WAVE; ++j) {
-      const int e = lane + WAVE * j;
-      if (e < E && !((taken >> j) & 1u)) {
-        if (v[j] > bv || (v[j] == bv && e < bi)) { bv = v[j]; bi = e; }
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, WAVE);
-      const int oi = __shfl_xor(bi, o, WAVE);
-      if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-    }
-    if ((bi % WAVE) == lane) taken |= 1u << (bi / WAVE);
-    if (lane == r) { myv = bv; myi = bi; }
+  for (int c = 0; c < MAX_EXPERTS / WAVE; ++c) {
+    const int e = c * WAVE + lane;
+    if (c < nch) keys[e] = (e < E) ? topk_key(v[c], e) : topk_pad_key(e);
   }
-  const float vmax = __shfl(myv, 0, WAVE);
-  const float z = (lane < k) ? expf(myv - vmax) : 0.f;
-  const float zsum = wave_sum(z);
-  if (lane < k) {
-    st_sys(idx_out + lane, myi);
-    st_sys(w_out + lane, (z / zsum) * pes[myi]);
-  }
+  __builtin_amdgcn_wave_barrier();
+  for (int c = 0; c < nch; ++c) topk_rank_chunk(keys + c * WAVE, k, surv + c * k);
+  __builtin_amdgcn_wave_barrier();
+  topk_rank_survivors(surv, nch * k, k, sel);
+  __builtin_amdgcn_wave_barrier();
+  topk_weights(sel, k, pes, myi, myw);
 }
 
 // ---------------------------------------------------------------- bucketing (one workgroup)
@@ -196,17 +245,20 @@ QMOE_DEV void bucket_block(Get get, int N, int E, int32_t *counts, int32_t *offs
 }
 
 // ---------------------------------------------------------------- router logits
-// Workgroup (tb, eb): tokens [4 tb, 4 tb + 4) x experts [4 eb, 4 eb + 4).  Per token the
+// Workgroup (tb, eb): tokens [TB tb, TB tb + TB) x experts [4 eb, 4 eb + 4).  Per token the
 // input is staged as z = x * router_scale (fp32) with per-16-element sums; the token's norm
 // factor f = (1/sqrt(H)) / sqrt(mean(x^2) + eps) multiplies the finished dot product:
 //   logit = f * sum_g [ s_g * sum_{h in g} q_h z_h + b_g * sum_{h in g} z_h ] + bias.
+// Every global load (codes, scales, activations, router_scale) is issued before the first
+// one is used, so the workgroup waits for memory once.
+template <int TB>
 QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *smem) {
   const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
   const int H = a.H;
-  const int t0 = tb * ROUTER_TB;
-  const int nt = min(ROUTER_TB, a.T - t0);
-  // this wave's expert row: lane l holds chunks l, l+64, ... (16 codes each), loaded before
-  // the activations are staged (H <= 8192 -> at most 8 chunks per lane)
+  const int t0 = tb * TB;
+  const int nt = min(TB, a.T - t0);
+  // this wave's expert row: lane l holds chunks l, l+64, ... (16 codes each; H <= 8192 -> at
+  // most 8 chunks per lane)
   constexpr int NCH = 8;
   const int n16 = H / 16;
   const int e = eb * ROUTER_EPB + wv;
@@ -221,34 +273,54 @@ QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *sme
     sv[j] = a.rs[(size_t)ec * (H / GROUP) + c / 4];
     bv[j] = a.rb[(size_t)ec * (H / GROUP) + c / 4];
   }
-  float *z = (float *)smem;                                  // [TB][H]
-  float *zs = z + ROUTER_TB * H;                             // [TB][H/16]
-  float *fac = zs + ROUTER_TB * (H / 16);                    // [TB]
-  // stage z and the 16-element sums; thread handles 8 consecutive elements
+  // activations: thread tid holds the 8-element chunks tid + 256 j (j < XC) of each token,
+  // with the matching router_scale entries
+  constexpr int XC = 4;
   const int n8 = H / 8;
-  for (int i = 0; i < nt; ++i) {
-    const uint16_t *xr = a.x + (size_t)(t0 + i) * H;
-    float ss = 0.f;
-    for (int c = tid; c < n8; c += ROUTER_THREADS) {
-      const qmoe_u32x4 v = *(const qmoe_u32x4 *)(xr + 8 * c);
-      const uint32_t wv4[4] = {v.x, v.y, v.z, v.w};
-      float part = 0.f;
+  qmoe_u32x4 xv[TB][XC];
+  float4 rsv[XC][2];
 #pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        float x0 = bf16lo(wv4[d]), x1 = bf16hi(wv4[d]);
-        ss = fmaf(x0, x0, ss);
-        ss = fmaf(x1, x1, ss);
-        if (a.rscale) { x0 *= a.rscale[8 * c + 2 * d]; x1 *= a.rscale[8 * c + 2 * d + 1]; }
-        z[i * H + 8 * c + 2 * d] = x0;
-        z[i * H + 8 * c + 2 * d + 1] = x1;
-        part += x0 + x1;
+  for (int j = 0; j < XC; ++j) {
+    const int c = min(tid + ROUTER_THREADS * j, n8 - 1);
+    if (a.rscale) {
+      rsv[j][0] = *(const float4 *)(a.rscale + 8 * c);
+      rsv[j][1] = *(const float4 *)(a.rscale + 8 * c + 4);
+    }
+#pragma unroll
+    for (int i = 0; i < TB; ++i)
+      xv[i][j] = *(const qmoe_u32x4 *)(a.x + (size_t)(t0 + min(i, nt - 1)) * H + 8 * c);
+  }
+  float *z = (float *)smem;                                  // [nt][H]
+  float *zs = z + nt * H;                                    // [nt][H/16]
+  float *fac = zs + nt * (H / 16);                           // [nt]
+  __shared__ float red[ROUTER_WAVES];
+  for (int i = 0; i < TB; ++i) {
+    if (i >= nt) break;
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < XC; ++j) {
+      const int c = tid + ROUTER_THREADS * j;
+      if (c < n8) {
+        const uint32_t wv4[4] = {xv[i][j].x, xv[i][j].y, xv[i][j].z, xv[i][j].w};
+        const float rs8[8] = {rsv[j][0].x, rsv[j][0].y, rsv[j][0].z, rsv[j][0].w,
+                              rsv[j][1].x, rsv[j][1].y, rsv[j][1].z, rsv[j][1].w};
+        float part = 0.f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          float x0 = bf16lo(wv4[d]), x1 = bf16hi(wv4[d]);
+          ss = fmaf(x0, x0, ss);
+          ss = fmaf(x1, x1, ss);
+          if (a.rscale) { x0 *= rs8[2 * d]; x1 *= rs8[2 * d + 1]; }
+          z[i * H + 8 * c + 2 * d] = x0;
+          z[i * H + 8 * c + 2 * d + 1] = x1;
+          part += x0 + x1;
+        }
+        // two 8-element threads make one 16-element sum (c even/odd are adjacent lanes)
+        const float other = __shfl_xor(part, 1, WAVE);
+        if ((c & 1) == 0) zs[i * (H / 16) + c / 2] = part + other;
       }
-      // two 8-element threads make one 16-element sum (c even/odd are adjacent lanes)
-      const float other = __shfl_xor(part, 1, WAVE);
-      if ((c & 1) == 0) zs[i * (H / 16) + c / 2] = part + other;
     }
     ss = wave_sum(ss);
-    __shared__ float red[ROUTER_WAVES];
     if (lane == 0) red[wv] = ss;
     __syncthreads();
     if (tid == 0) {
@@ -259,9 +331,9 @@ QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *sme
     __syncthreads();
   }
   if (e >= a.E) return;
-  float acc[ROUTER_TB];
+  float acc[TB];
 #pragma unroll
-  for (int i = 0; i < ROUTER_TB; ++i) acc[i] = 0.f;
+  for (int i = 0; i < TB; ++i) acc[i] = 0.f;
 #pragma unroll
   for (int j = 0; j < NCH; ++j) {
     const int c = lane + WAVE * j;
@@ -277,7 +349,7 @@ QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *sme
         q[4 * d + 3] = (float)(w4[d] >> 24);
       }
 #pragma unroll
-      for (int i = 0; i < ROUTER_TB; ++i) {
+      for (int i = 0; i < TB; ++i) {
         if (i < nt) {
           const float *zr = z + i * H + 16 * c;
           float dq = 0.f;
@@ -290,13 +362,16 @@ QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *sme
     }
   }
 #pragma unroll
-  for (int i = 0; i < ROUTER_TB; ++i) {
+  for (int i = 0; i < TB; ++i) {
     if (i < nt) {
       const float tot = wave_sum(acc[i]);
-      if (lane == 0) {
-        float l = fac[i] * tot;
-        if (a.lbias) l += a.lbias[e];
-        st_sys(a.logits + (size_t)(t0 + i) * a.E + e, l);
+      float l = fac[i] * tot;
+      if (a.lbias) l += a.lbias[e];
+      const size_t o = (size_t)(t0 + i) * a.E + e;
+      if (a.logits_tag) {
+        if (lane < a.tag_copies) st_tag(a.logits_tag + (size_t)lane * a.tag_copy_stride + o, a.tag, l);
+      } else if (lane == 0) {
+        st_sys(a.logits + o, l);
       }
     }
   }
@@ -307,14 +382,21 @@ QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *sme
 // itself when there is a single token block) runs the bucketing.
 QMOE_DEV void router_finish(const RouterArgs &a, int tb, char *smem) {
   if (!arrive_last(&a.cnt_tb[tb], (unsigned)a.n_eb)) return;
-  const int wv = threadIdx.x / WAVE;
+  const int wv = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   const int t0 = tb * ROUTER_TB;
   const int nt = min(ROUTER_TB, a.T - t0);
+  uint64_t *lds = (uint64_t *)(smem + (size_t)wv * topk_lds_bytes(a.E, a.k));
   for (int i = wv; i < nt; i += ROUTER_WAVES) {
     const int t = t0 + i;
-    topk_one_token(a.logits + (size_t)t * a.E, a.E, a.k, a.pes, a.topk_idx + (size_t)t * a.k,
-                   a.topk_w + (size_t)t * a.k);
+    int myi;
+    float myw;
+    topk_wave(a.logits + (size_t)t * a.E, a.E, a.k, a.pes, lds, myi, myw);
+    if (lane < a.k) {
+      st_sys(a.topk_idx + (size_t)t * a.k + lane, myi);
+      st_sys(a.topk_w + (size_t)t * a.k + lane, myw);
+    }
   }
+  __syncthreads();
   if (a.counts == nullptr) return;
   if (a.n_tb == 1) {
     drain_memory();    // this workgroup wrote every assignment
@@ -330,7 +412,7 @@ QMOE_DEV void router_finish(const RouterArgs &a, int tb, char *smem) {
 __global__ void __launch_bounds__(ROUTER_THREADS) router_kernel(RouterArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int tb = blockIdx.x / a.n_eb, eb = blockIdx.x % a.n_eb;
-  router_logits_block(a, tb, eb, smem);
+  router_logits_block<ROUTER_TB>(a, tb, eb, smem);
   router_finish(a, tb, smem);
 }
 

@@ -189,3 +189,10 @@ class Event:
 
 def set_profile_events(start, stop):
     check(lib().qmoe_set_profile_events(start.h if start else None, stop.h if stop else None))
+
+
+def workspace_status(ws):
+    """0 when no one-token layer call on this workspace gave up waiting (synchronises)."""
+    v = ctypes.c_int32()
+    check(lib().qmoe_workspace_status(_ptr(ws, 1, "ws"), ws.numel(), ctypes.byref(v), _stream()))
+    return v.value

@@ -324,3 +324,56 @@ def test_zero_tokens_is_noop():
     ws = ops.workspace(pl.dims, 1)
     out = ops.layer_forward(pl.weights, x, ws)
     assert out.shape == (0, 256)
+
+
+# ------------------------------------------------------------------ one-token launches and graphs
+
+@pytest.mark.parametrize("name", ["tiny", "gemma4_26b_a4b_decode", "qwen3_next_80b_a3b_decode_b1"])
+def test_one_token_calls_repeat_and_report_no_timeout(name):
+    """Back-to-back one-token calls on one workspace (each advances its epoch) give the same
+    bits as a fresh workspace, and the workspace status reports no timed-out wait."""
+    ops = _ops()
+    cfg = G.config(name)
+    pl, li = layer(name)
+    xb, x = _stacks().hidden(cfg, 7, 1)
+    ws = ops.workspace(pl.dims, 1)
+    outs = [ops.layer_forward(pl.weights, x, ws) for _ in range(5)]
+    ws2 = ops.workspace(pl.dims, 1)
+    o32 = torch.empty(1, cfg.hidden, dtype=torch.float32, device=DEV)
+    fresh = ops.layer_forward(pl.weights, x, ws2, out_f32=o32)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o.view(torch.int16), fresh.view(torch.int16))
+    assert ops.workspace_status(ws) == 0 and ops.workspace_status(ws2) == 0
+    ref = O.layer_forward(xb, li, cfg.top_k)
+    assert_close_f32(o32.cpu().numpy()[0], ref["out"][0], "one-token out_f32")
+    check_out_bf16(np16(fresh)[0], o32.cpu().numpy()[0], ref["out"][0], "one-token out")
+
+
+@pytest.mark.parametrize("T", [1, 128])
+def test_graph_replays_match_eager(T):
+    """A captured layer call replayed several times, with eager work in between, reproduces the
+    eager result on every replay."""
+    ops = _ops()
+    cfg = G.config("gemma4_26b_a4b_decode")
+    pl, _ = layer("gemma4_26b_a4b_decode")
+    ws = ops.workspace(pl.dims, T)
+    xs = [_stacks().hidden(cfg, 20 + i, T)[1] for i in range(3)]
+    x_static = xs[0].clone()
+    out_static = torch.empty(T, cfg.hidden, dtype=torch.bfloat16, device=DEV)
+    ref = [ops.layer_forward(pl.weights, xi, ws).clone() for xi in xs]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ops.layer_forward(pl.weights, x_static, ws, out=out_static)
+    for rep in range(6):
+        i = rep % 3
+        x_static.copy_(xs[i])
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_static.view(torch.int16), ref[i].view(torch.int16)), rep
+        # eager work on the same workspace between replays
+        e = ops.layer_forward(pl.weights, xs[(i + 1) % 3], ws)
+        torch.cuda.synchronize()
+        assert torch.equal(e.view(torch.int16), ref[(i + 1) % 3].view(torch.int16))
+    assert ops.workspace_status(ws) == 0
