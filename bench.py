@@ -5,7 +5,7 @@ combine) through every layer of a synthetic stack resident in HBM, for one batch
 tokens.  Default workload: Gemma-4-26B-A4B-shaped decode -- hidden 2816, 128 experts, top-8,
 expert width 704, shared width 2112, int4 groups of 64 with bf16 scale and bias, int8
 router, 30 stacked layers with distinct seeds, 1 token per step.  Each step is one HIP graph
-replay (3 kernels per layer).
+replay (one kernel per layer for a single token).
 
 Every layer of the stack receives its own N(0,1) bf16 hidden states (the layer-input
 distribution of the workload).  The synthetic weights come without the model's
@@ -13,9 +13,10 @@ normalisation layers, so feeding one layer's raw output into the next grows the 
 stream quadratically (inf after about ten layers); the layers still run back to back, each
 writing its own output.
 
-Prints one JSON line with the throughput, the roofline of the dominant kernel (the routed
-gate/up kernel, timed with HIP events on the stream it runs on, inside the timed region) and
-the CPU oracle timed on a bounded sample on the host.
+Prints one JSON line with the throughput, the roofline of the dominant kernel (for one token
+the single layer kernel; for more tokens the routed gate/up kernel), timed with HIP events on
+the stream it runs on inside the timed region, and the CPU oracle timed on a bounded sample
+on the host.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -47,7 +48,50 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--cpu-sample", type=int, default=8, help="token-layers timed on the oracle")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB (reads MIB, writes MIB) a few "
+                        "times and exit: the reference kernel for scaling rocprof byte counters")
     return p.parse_args()
+
+
+def sources_digest():
+    """sha256 over the HIP sources of the library (kernels and their launch code)."""
+    import hashlib
+    csrc = os.path.join(ROOT, "quantized_moe_router_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".h", ".hip")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()
+
+
+def stored_traffic(name):
+    """HBM bytes per launch of a kernel from the counter summary profiles/<name>.md, if that
+    summary was taken on the current sources (else None: the kernel may have changed)."""
+    path = os.path.join(ROOT, "profiles", name + ".md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and line.strip().startswith(("traffic_bytes_per_launch", "sources_sha256")):
+            k, v = line.strip().strip("`").split("=", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("sources_sha256") != sources_digest() or "traffic_bytes_per_launch" not in vals:
+        return None
+    return int(float(vals["traffic_bytes_per_launch"]))
+
+
+def copy_calibration(mib):
+    """A plain copy kernel of known size (torch copy_), run 5 times."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copied {mib} MiB 5 times")
 
 
 def build_stack(cfg, n_layers):
@@ -61,16 +105,24 @@ def build_stack(cfg, n_layers):
     return layers
 
 
-def capture_step(ops, layers, xin, outs, ws, events=None):
-    """One HIP graph: every layer of the stack, xin[l] -> outs[l]."""
+def capture_step(ops, layers, xin, outs, ws, events=None, timed_layer=-1):
+    """One HIP graph: every layer of the stack, xin[l] -> outs[l].  With `events` (start,
+    stop): for one token, graph event nodes right before the first layer's kernel and right
+    after the last one's (the step is nothing but those kernels); for more tokens, around the
+    routed gate/up kernel of layer `timed_layer`."""
     import torch
     g = torch.cuda.CUDAGraph()
+    L = len(layers)
     with torch.cuda.graph(g):
         for l, (pl, _) in enumerate(layers):
             if events is not None:
-                ops.set_profile_events(*events[l])
+                if xin.shape[1] == 1:
+                    ops.set_profile_events(events[0] if l == 0 else None,
+                                           events[1] if l == L - 1 else None)
+                elif l == timed_layer:
+                    ops.set_profile_events(*events)
             ops.layer_forward(pl.weights, xin[l], ws, out=outs[l])
-        ops.set_profile_events(None, None)
+            ops.set_profile_events(None, None)
     return g
 
 
@@ -96,12 +148,13 @@ def eager_kernel_times(ops, layers, xs, outs, ws, steps):
         for l, (pl, _) in enumerate(layers):
             ops.set_profile_events(*evs[s][l])
             ops.layer_forward(pl.weights, xs[s + 1][l], ws, out=outs[l])
-        ops.set_profile_events(None, None)
+            ops.set_profile_events(None, None)
     torch.cuda.synchronize()
     return [evs[s][l][0].elapsed_ms(evs[s][l][1]) for s in range(steps) for l in range(L)]
 
 
 def run_decode(args, cfg, layers):
+    import numpy as np
     import torch
     from quantized_moe_router_amd import ops
     from workloads import gen as G
@@ -113,14 +166,18 @@ def run_decode(args, cfg, layers):
     outs = [torch.empty(T, H, dtype=torch.bfloat16, device="cuda") for _ in range(L)]
     xs = [layer_inputs(cfg, s, L, T) for s in range(args.steps + 1)]
 
-    # eager warm-up, then graphs: one per timed step (own inputs and own events)
+    # eager warm-up, then graphs: one per timed step (own inputs; an event pair around the
+    # dominant kernel of one layer, a different layer each step)
+    idx = [torch.empty(T, cfg.top_k, dtype=torch.int32, device="cuda") for _ in range(L)]
     for l, (pl, _) in enumerate(layers):
-        ops.layer_forward(pl.weights, xs[0][l], ws, out=outs[l])
+        ops.layer_forward(pl.weights, xs[0][l], ws, out=outs[l], topk_idx=idx[l])
     torch.cuda.synchronize()
+    distinct = [len(np.unique(i.cpu().numpy())) for i in idx]
     g_plain = capture_step(ops, layers, xs[0], outs, ws)
-    evs = [[(ops.Event(), ops.Event()) for _ in range(L)] for _ in range(args.steps)]
+    evs = [(ops.Event(), ops.Event()) for _ in range(args.steps)]
     try:
-        graphs = [capture_step(ops, layers, xs[s + 1], outs, ws, evs[s]) for s in range(args.steps)]
+        graphs = [capture_step(ops, layers, xs[s + 1], outs, ws, evs[s], s % L)
+                  for s in range(args.steps)]
         graph_events = True
     except Exception as e:
         log(f"event nodes could not be captured ({e}); graphs without events")
@@ -140,20 +197,26 @@ def run_decode(args, cfg, layers):
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
 
-    # dominant kernel (routed gate/up): event pairs recorded around it in every layer call
+    # dominant kernel: the event pairs recorded around it inside the timed replays
     durs = None
     if graph_events:
         try:
-            durs = [evs[s][l][0].elapsed_ms(evs[s][l][1]) for s in range(args.steps) for l in range(L)]
-            timing_src = "HIP event nodes around the kernel in the timed graph replays"
+            if T == 1:      # one pair around the step's L back-to-back layer kernels
+                durs = [evs[s][0].elapsed_ms(evs[s][1]) / L for s in range(args.steps)]
+                timing_src = ("HIP event nodes before the first and after the last of the "
+                              f"{L} layer kernels of each timed graph replay, divided by {L}")
+            else:
+                durs = [evs[s][0].elapsed_ms(evs[s][1]) for s in range(args.steps)]
+                timing_src = ("HIP event nodes around the kernel (one layer per step) in the "
+                              "timed graph replays")
         except Exception as e:      # event nodes not timed by this runtime: eager instrumented pass
             log(f"graph event timing unavailable ({e})")
     if durs is None:
         durs = eager_kernel_times(ops, layers, xs, outs, ws, args.steps)
         timing_src = "HIP events around the kernel in eager calls (same inputs, after the timed region)"
-    gu_ms = sum(durs) / len(durs)
+    kern_ms = sum(durs) / len(durs)
 
-    # the same stack without the timing events, for reference
+    # the same stack without any timing events, for reference
     torch.cuda.synchronize()
     t2 = time.perf_counter()
     for s in range(args.steps):
@@ -161,20 +224,27 @@ def run_decode(args, cfg, layers):
     torch.cuda.synchronize()
     ms_plain = (time.perf_counter() - t2) * 1e3 / args.steps
 
-    k = cfg.top_k
-    distinct = k if T == 1 else None
-    gu_bytes = distinct * 2 * G.matrix_bytes(cfg.inter, H)          # routed gate+up per launch
-    credited = G.credited_expert_bytes(cfg, distinct)                 # routed bytes per layer
+    n_dist = float(np.mean(distinct))
+    credited = G.credited_expert_bytes(cfg, n_dist)                   # routed bytes per layer
     all_bytes = credited + G.expert_bytes(cfg, cfg.shared_inter) + G.router_bytes(cfg)
+    if T == 1:
+        kernel = "decode_layer_kernel (the whole one-token layer in one launch)"
+        kern_bytes = all_bytes
+        traffic = stored_traffic(f"decode_layer_kernel_{cfg.name}")
+    else:
+        kernel = "gu_kernel (routed gate/up + SwiGLU)"
+        kern_bytes = n_dist * 2 * G.matrix_bytes(cfg.inter, H)
+        traffic = None
     tok_s_layer = T * L / (ms_step / 1e3)
     layer_s = ms_step / 1e3 / L
-    gu_gbps = gu_bytes / (gu_ms / 1e3) / 1e9
+    kern_gbps = kern_bytes / (kern_ms / 1e3) / 1e9
     return dict(
         ms_step=ms_step, ms_plain=ms_plain, tok_s_layer=tok_s_layer, L=L, T=T,
-        gu_ms=gu_ms, gu_bytes=gu_bytes, gu_gbps=gu_gbps,
+        kern_ms=kern_ms, kern_bytes=kern_bytes, kern_gbps=kern_gbps, kernel=kernel,
         layer_credited_gbps=credited / layer_s / 1e9,
         layer_all_gbps=all_bytes / layer_s / 1e9,
-        credited=credited, all_bytes=all_bytes, distinct=distinct, timing_src=timing_src,
+        credited=credited, all_bytes=all_bytes, distinct=n_dist, timing_src=timing_src,
+        traffic=traffic,
     )
 
 
@@ -245,6 +315,10 @@ def main():
               f"single MI355X and a multi-GPU figure is not produced.", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.copy_calibration:
+        torch.cuda.set_device(0)
+        copy_calibration(args.copy_calibration)
+        return
     import __graft_entry__ as GE
     GE._ensure_built()
     from workloads import gen as G
@@ -257,7 +331,7 @@ def main():
     log("decode timing")
     d = run_decode(args, cfg, layers)
     log(f"decode: {d['ms_step']:.3f} ms/step ({d['ms_plain']:.3f} without events), "
-        f"routed gate/up {d['gu_ms'] * 1e3:.2f} us = {d['gu_gbps']:.0f} GB/s")
+        f"{d['kernel'].split()[0]} {d['kern_ms'] * 1e3:.2f} us = {d['kern_gbps']:.0f} GB/s")
     pf = None
     if not args.no_prefill and cfg.name == "gemma4_26b_a4b_decode":
         log("prefill timing")
@@ -287,14 +361,14 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "gu_kernel (routed gate/up + SwiGLU)",
-            "achieved": round(d["gu_gbps"], 1),
+            "kernel": d["kernel"],
+            "achieved": round(d["kern_gbps"], 1),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
-            "frac": round(d["gu_gbps"] / HBM_PEAK_GBPS, 4),
-            "traffic": None,
-            "bytes_per_launch": d["gu_bytes"],
-            "avg_launch_us": round(d["gu_ms"] * 1e3, 3),
+            "frac": round(d["kern_gbps"] / HBM_PEAK_GBPS, 4),
+            "traffic": d["traffic"],
+            "bytes_per_launch": int(d["kern_bytes"]),
+            "avg_launch_us": round(d["kern_ms"] * 1e3, 3),
             "timing": d["timing_src"],
         },
         "layer": {
@@ -303,6 +377,7 @@ def main():
             "all_bytes_GBps": round(d["layer_all_gbps"], 1),
             "us_per_layer": round(d["ms_step"] * 1e3 / d["L"], 3),
             "us_per_layer_without_events": round(d["ms_plain"] * 1e3 / d["L"], 3),
+            "distinct_experts_per_layer": round(d["distinct"], 2),
         },
     }
     if pf:

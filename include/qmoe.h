@@ -88,7 +88,8 @@ typedef struct {
     const uint8_t *codes;            /* [E, H] uint8 codes */
     const uint16_t *scales;          /* [E, H/64] bf16 */
     const uint16_t *biases;          /* [E, H/64] bf16 */
-    const float *router_scale;       /* [H] fp32 multiplier after the norm, or NULL for all ones */
+    const float *router_scale;       /* [H] fp32 multiplier after the norm (16-byte aligned), or
+                                        NULL for all ones */
     const float *per_expert_scale;   /* [E] fp32, multiplies the softmax weights */
     const float *logit_bias;         /* [E] fp32 added to the logits before top-k, or NULL */
 } qmoe_router;
@@ -116,15 +117,16 @@ size_t qmoe_expert_stride(const qmoe_dims *d, int32_t inter);
 
 /* Workspace bytes needed by qmoe_router_topk / qmoe_bucket / qmoe_expert_ffn /
  * qmoe_layer_forward for calls with up to max_tokens tokens (0 on invalid dims).  The
- * workspace is device memory owned by the caller.  Its first 512 KiB hold completion counters
- * that must be zero when a call starts: initialise a new workspace once with
- * qmoe_workspace_init (or a zero fill); every call returns the counters it used to zero
- * before it completes, so later calls need no re-initialisation.  Calls that share one
- * workspace must be ordered (same stream, or synchronised). */
+ * workspace is device memory owned by the caller and must be zero before its first use:
+ * initialise a new workspace once with qmoe_workspace_init (or a zero fill).  Every call leaves
+ * it ready for the next one (counters return to zero; the one-token path advances an epoch
+ * word that tags its hand-off data), so later calls need no re-initialisation.  Calls that
+ * share one workspace must be ordered (same stream, or synchronised). */
 size_t qmoe_workspace_bytes(const qmoe_dims *d, int32_t max_tokens);
 
-/* Zero the counter area (the first 512 KiB, or all of a smaller workspace) with a kernel
- * on `stream` (graph-capturable). */
+/* Zero the whole workspace with a kernel on `stream` (graph-capturable).  Needed once per new
+ * workspace: the counters and the epoch-tagged hand-off words of the one-token path must start
+ * at zero. */
 int qmoe_workspace_init(void *ws, size_t ws_bytes, qmoe_stream_t stream);
 
 /* ---------------------------------------------------------------- expert store */
@@ -225,10 +227,11 @@ int qmoe_workspace_status(const void *ws, size_t ws_bytes, int32_t *status_out,
 
 /* Thin wrappers over HIP events so that callers can time individual kernels of
  * qmoe_layer_forward on the stream they run on.  qmoe_set_profile_events(start, stop)
- * makes subsequent qmoe_layer_forward calls on this thread record `start` right before and
- * `stop` right after their routed gate/up kernel (pass NULL, NULL to stop).  Events are
- * created with qmoe_event_create and read with qmoe_event_elapsed_ms (which synchronises on
- * `stop`). */
+ * makes subsequent qmoe_layer_forward calls on this thread record `start` (if not NULL) right
+ * before and `stop` (if not NULL) right after their dominant kernel: the single kernel of a
+ * one-token call, else the routed gate/up kernel (pass NULL, NULL to stop).  Under stream
+ * capture the records become graph event nodes.  Events are created with qmoe_event_create
+ * and read with qmoe_event_elapsed_ms (which synchronises on `stop`). */
 int qmoe_event_create(void **event_out);
 int qmoe_event_destroy(void *event);
 int qmoe_event_record(void *event, qmoe_stream_t stream);

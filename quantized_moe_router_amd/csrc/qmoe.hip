@@ -372,13 +372,15 @@ static int launch_d(FfnArgs a, bool with_shared, hipStream_t s) {
 }
 
 // One-token decode in a single launch (decode.h) when every down-projection wave's k-steps
-// fit in its register batch.  Routed down tiles take 1, 2 or 4 waves (wpt) so that a wave
-// holds at most KB_DEC k-steps; the shared down width is cut into chunks of at most
-// DEC_W * KB_DEC k-steps.
+// fit in its register batch.  Routed down tiles take 1, 2 or 4 waves (wpt): the fewest that
+// give each wave at most KB_DEC / 2 k-steps (the dot products of a wave are a serial chain on
+// the critical path), else the fewest that fit KB_DEC; the shared down width is cut into
+// chunks of at most DEC_W * KB_DEC k-steps.
 static int dec_wpt(const qmoe_dims *d) {
   const int ks = d->inter / GROUP;
-  for (int w = 1; w <= DEC_W; w *= 2)
-    if ((ks + w - 1) / w <= KB_DEC) return w;
+  for (int lim : {KB_DEC / 2, KB_DEC})
+    for (int w = 1; w <= DEC_W; w *= 2)
+      if ((ks + w - 1) / w <= lim) return w;
   return 0;
 }
 
@@ -694,8 +696,6 @@ int qmoe_workspace_status(const void *ws, size_t ws_bytes, int32_t *status_out,
 }
 
 int qmoe_set_profile_events(void *start, void *stop) {
-  if ((start == nullptr) != (stop == nullptr))
-    return fail(QMOE_ERR_ARG, "set_profile_events: pass both events or neither");
   g_prof_start = (hipEvent_t)start;
   g_prof_stop = (hipEvent_t)stop;
   return ok();

@@ -273,6 +273,7 @@ QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *sme
     sv[j] = a.rs[(size_t)ec * (H / GROUP) + c / 4];
     bv[j] = a.rb[(size_t)ec * (H / GROUP) + c / 4];
   }
+  const float lb = a.lbias ? a.lbias[ec] : 0.f;
   // activations: thread tid holds the 8-element chunks tid + 256 j (j < XC) of each token,
   // with the matching router_scale entries
   constexpr int XC = 4;
@@ -366,7 +367,7 @@ QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *sme
     if (i < nt) {
       const float tot = wave_sum(acc[i]);
       float l = fac[i] * tot;
-      if (a.lbias) l += a.lbias[e];
+      if (a.lbias) l += lb;
       const size_t o = (size_t)(t0 + i) * a.E + e;
       if (a.logits_tag) {
         if (lane < a.tag_copies) st_tag(a.logits_tag + (size_t)lane * a.tag_copy_stride + o, a.tag, l);
