@@ -376,16 +376,16 @@ __global__ void __launch_bounds__(W * WAVE) d_kernel(FfnArgs a) {
   SlotRows sr;
   const bool shared = slot >= a.n_slots;
   if (slot_rows(a, slot, shared, sr)) {
-    if (!shared) {
-      d_tile<W, MB, KB>(a, sr, tile, 0, a.I / GROUP, a.y,
-                        [&](int r) { return flat_of(a, sr, r); },
-                        fused, smem);
-    } else {
+    int kb0 = 0, nks = a.I / GROUP;
+    float *dst = a.y;
+    if (shared) {
       const int KSs = a.Is / GROUP, c = slot - a.n_slots, nc = a.n_sh_chunks;
-      const int kb0 = (KSs * c) / nc, kb1 = (KSs * (c + 1)) / nc;
-      float *dst = fused ? a.y_sh_part + (size_t)c * a.T * a.H : a.y_sh;
-      d_tile<W, MB, KB>(a, sr, tile, kb0, kb1 - kb0, dst, [](int r) { return r; }, fused, smem);
+      kb0 = (KSs * c) / nc;
+      nks = (KSs * (c + 1)) / nc - kb0;
+      dst = fused ? a.y_sh_part + (size_t)c * a.T * a.H : a.y_sh;
     }
+    auto ysel = [&](int r) { return shared ? r : flat_of(a, sr, r); };
+    d_tile<W, MB, KB>(a, sr, tile, kb0, nks, dst, ysel, fused, smem);
   }
   if (!fused) return;
   if (!arrive_last(&a.cnt_tile[tile], gridDim.y)) return;
@@ -418,3 +418,5 @@ __global__ void zero_kernel(uint32_t *p, size_t n) {
 }
 
 }  // namespace qmoe
+
+#include "mfma.h"

@@ -25,7 +25,6 @@ namespace {
 constexpr int VERSION = 100;               // 0.1.0
 constexpr size_t COUNTER_BYTES = 512 * 1024;
 constexpr int GU_W = 8;     // waves per routed gate/up workgroup (split-K)
-constexpr int SH_W = 4;     // waves per shared gate/up workgroup (inside the router launch)
 constexpr int D_W = 8;      // waves per down workgroup (split-K)
 constexpr int KB = 12;      // k-steps loaded per batch by a wave
 constexpr int MB_MAX = 8;   // rows (tokens) per activation block
@@ -124,6 +123,14 @@ inline int shared_chunks(const qmoe_dims *d) {
   return std::max(1, std::min(c, ks));
 }
 
+// The same for the matrix-core down kernel, whose workgroups stage at most PF_KMAX k-steps
+// of h.
+inline int pf_sh_chunks(const qmoe_dims *d) {
+  if (d->shared_inter == 0) return 0;
+  const int ks = d->shared_inter / GROUP;
+  return std::max(shared_chunks(d), (ks + PF_KMAX - 1) / PF_KMAX);
+}
+
 // The same for the one-token decode launch, whose shared down workgroups split one output
 // tile's k-steps over their four waves (at most DEC_W * KB_DEC k-steps per chunk).
 inline int dec_shared_chunks(const qmoe_dims *d) {
@@ -159,7 +166,7 @@ WsLayout ws_layout(const qmoe_dims *d, int Tmax) {
   w.hs_lo = o; o += al(T * (size_t)d->shared_inter * 2);
   w.y = o; o += al(Tc * k * H * 4);
   w.ysh = o; o += al(Tc * H * 4);
-  w.ysh_part = o; o += al((size_t)shared_chunks(d) * Tc * H * 4);
+  w.ysh_part = o; o += al((size_t)pf_sh_chunks(d) * Tc * H * 4);
   w.dec_logits = o; o += (size_t)LOGIT_COPIES * dec_copy_stride(E);
   w.dec_hr = o; o += (size_t)H_COPIES * dec_copy_stride(k * d->inter);
   w.dec_hsh = o; o += (size_t)H_COPIES * dec_copy_stride((size_t)d->shared_inter);
@@ -255,22 +262,6 @@ int launch_router(const RouterArgs &a, size_t smem, hipStream_t s) {
   return QMOE_OK;
 }
 
-// layer path: router workgroups followed by shared gate/up workgroups in one launch
-template <int MB>
-__global__ void __launch_bounds__(ROUTER_THREADS) router_shared_kernel(RouterArgs ra, FfnArgs fa,
-                                                                       int n_router) {
-  extern __shared__ __align__(16) char smem[];
-  if ((int)blockIdx.x < n_router) {
-    const int tb = blockIdx.x / ra.n_eb, eb = blockIdx.x % ra.n_eb;
-    router_logits_block<ROUTER_TB>(ra, tb, eb, smem);
-    router_finish(ra, tb, smem);
-  } else {
-    SlotRows sr;
-    slot_rows(fa, 0, true, sr);
-    gu_tile<SH_W, MB, KB>(fa, sr, blockIdx.x - n_router, smem);
-  }
-}
-static_assert(SH_W * WAVE == ROUTER_THREADS, "fused router/shared kernel uses one block size");
 static_assert((size_t)(DEC_SYNC_WORD + SY_LINES * SY_LINE) * 4 <= COUNTER_BYTES,
               "decode sync area inside the counter area");
 
@@ -295,13 +286,6 @@ int record_event(hipEvent_t e, hipStream_t s) {
 
 // rows per activation block: one-token calls stage a single row
 inline int mb_for(int T) { return T == 1 ? 1 : MB_MAX; }
-
-size_t gu_smem(int H, int mb) {
-  return mb == 1 ? gu_lds_bytes<SH_W, 1>(H) : gu_lds_bytes<SH_W, MB_MAX>(H);
-}
-size_t d_smem(int K, int mb) {
-  return mb == 1 ? d_lds_bytes<D_W, 1>(K) : d_lds_bytes<D_W, MB_MAX>(K);
-}
 
 static FfnArgs make_ffn_args(const qmoe_layer *L, const uint16_t *x, int T, const int32_t *offsets,
                              const int32_t *sorted, const int32_t *active, const int32_t *n_active,
@@ -369,6 +353,56 @@ static int launch_d(FfnArgs a, bool with_shared, hipStream_t s) {
     Kc = std::max(Kc, GROUP * ((KSs + a.n_sh_chunks - 1) / a.n_sh_chunks));
   }
   return mb_for(a.T) == 1 ? launch_d_t<1>(a, slots, Kc, s) : launch_d_t<MB_MAX>(a, slots, Kc, s);
+}
+
+// Matrix-core grouped GEMM (mfma.h) for calls with more than one token: usable when the
+// staged activation rows fit in LDS.
+static bool pf_fits(const qmoe_dims *d) {
+  return gu_pf_lds(d->hidden) <= 160 * 1024 && d->inter / GROUP <= PF_KMAX;
+}
+
+// gate/up then down; routed rows go to a.y, shared rows (if a.shared) to the a.n_sh_chunks
+// partials in a.y_sh_part.  Profile events (if set) bracket the gate/up kernel.
+static int launch_pf(const FfnArgs &a, hipStream_t s) {
+  int rc;
+  const int tiles_s = a.shared ? a.Is / 16 : 0;
+  const int n_sh = tiles_s * ((a.T + GU_SH_PASSES * GU_MT - 1) / (GU_SH_PASSES * GU_MT));
+  const int n_gu = n_sh + a.n_slots * (a.I / 16);
+  const size_t lds_gu = gu_pf_lds(a.H);
+  if ((rc = set_lds(gu_pf_kernel, lds_gu))) return rc;
+  if (g_prof_start && (rc = record_event(g_prof_start, s))) return rc;
+  if (n_gu > 0) {
+    hipLaunchKernelGGL(gu_pf_kernel, dim3(n_gu), dim3(PF_THREADS), lds_gu, s, a);
+    QMOE_LAUNCHED();
+  }
+  if (g_prof_stop && (rc = record_event(g_prof_stop, s))) return rc;
+  const int groups = (a.H / TILE_ROWS + D_TPW - 1) / D_TPW;
+  const int mblk = (a.T + D_SH_PASSES * D_MT - 1) / (D_SH_PASSES * D_MT);
+  const int n_dsh = a.shared ? a.n_sh_chunks * groups * mblk : 0;
+  const int n_d = n_dsh + a.n_slots * groups;
+  int kc = a.I;
+  if (a.shared) {
+    const int ks = a.Is / GROUP;
+    kc = std::max(kc, GROUP * ((ks + a.n_sh_chunks - 1) / a.n_sh_chunks));
+  }
+  const size_t lds_d = d_pf_lds(kc);
+  if ((rc = set_lds(d_pf_kernel, lds_d))) return rc;
+  if (n_d > 0) {
+    hipLaunchKernelGGL(d_pf_kernel, dim3(n_d), dim3(PF_THREADS), lds_d, s, a);
+    QMOE_LAUNCHED();
+  }
+  return QMOE_OK;
+}
+
+static int launch_combine_pf(const uint16_t *x, const float *y, const float *w,
+                             const float *y_sh_part, int nsh, int T, int H, int k, uint16_t *out,
+                             float *out_f32, float *y_sh, hipStream_t s) {
+  const size_t n4 = (size_t)T * H / 4;
+  const unsigned blocks = (unsigned)std::min<size_t>((n4 + 255) / 256, 8192);
+  hipLaunchKernelGGL(combine_pf_kernel, dim3(blocks), dim3(256), 0, s, x, y, w, y_sh_part, nsh, T,
+                     H, k, out, out_f32, y_sh);
+  QMOE_LAUNCHED();
+  return QMOE_OK;
 }
 
 // One-token decode in a single launch (decode.h) when every down-projection wave's k-steps
@@ -562,6 +596,17 @@ int qmoe_expert_ffn(const qmoe_layer *L, const uint16_t *x, int32_t T, const int
   if ((rc = check_arch())) return rc;
   FfnArgs a = make_ffn_args(L, x, T, offsets, sorted, active, n_active, y, y_shared_or_null, ws, T);
   hipStream_t s = (hipStream_t)stream;
+  if (T <= CHUNK_TOKENS && pf_fits(&L->d)) {
+    const bool shp = L->shared && y_shared_or_null;
+    if (!shp) a.shared = nullptr;
+    a.n_sh_chunks = shp ? pf_sh_chunks(&L->d) : 0;
+    if ((rc = launch_pf(a, s))) return rc;
+    if (shp && (rc = launch_combine_pf(x, y, nullptr, a.y_sh_part, a.n_sh_chunks, T,
+                                       L->d.hidden, L->d.top_k, nullptr, nullptr,
+                                       y_shared_or_null, s)))
+      return rc;
+    return ok();
+  }
   if ((rc = launch_gu(a, 0, s))) return rc;
   const bool sh = L->shared && y_shared_or_null;
   if (!sh) a.shared = nullptr;
@@ -613,7 +658,7 @@ int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16
     const uint16_t *xc = x + (size_t)c0 * H;
     int32_t *idx = topk_idx_or_null ? topk_idx_or_null + (size_t)c0 * k : at<int32_t>(ws, wl.tidx);
     float *w = topk_w_or_null ? topk_w_or_null + (size_t)c0 * k : at<float>(ws, wl.tw);
-    // kernel 1: router (+ top-k, bucketing) and shared gate/up
+    // kernel 1: router, top-k and bucketing (with the slot table)
     RouterArgs ra = make_router_args(d, &L->r, xc, Tc, at<float>(ws, wl.logits), idx, w, ws);
     ra.counts = at<int32_t>(ws, wl.counts);
     ra.offsets = at<int32_t>(ws, wl.offsets);
@@ -622,34 +667,34 @@ int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16
     ra.n_active = at<int32_t>(ws, wl.nact);
     ra.slot_tab = at<int32_t>(ws, wl.slot_tab);
     FfnArgs fa = make_ffn_args(L, xc, Tc, ra.offsets, ra.sorted, ra.active, ra.n_active,
-                               at<float>(ws, wl.y), sh ? at<float>(ws, wl.ysh) : nullptr, ws,
-                               Tc_max);
-    fa.topk_w = w;
+                               at<float>(ws, wl.y), nullptr, ws, Tc_max);
     fa.slot_tab = ra.slot_tab;
     ra.n_slots = fa.n_slots;
-    fa.out = out + (size_t)c0 * H;
-    fa.out_f32 = out_f32_or_null ? out_f32_or_null + (size_t)c0 * H : nullptr;
-    const int n_router = ra.n_tb * ra.n_eb;
-    const int n_sh = sh ? d->shared_inter / 16 : 0;
-    const int mb = mb_for(Tc);
-    const size_t smem1 = std::max(router_smem(d), sh ? gu_smem(H, mb) : (size_t)0);
-    if (mb == 1) {
-      if ((rc = set_lds(router_shared_kernel<1>, smem1))) return rc;
-      hipLaunchKernelGGL(router_shared_kernel<1>, dim3(n_router + n_sh), dim3(ROUTER_THREADS),
-                         smem1, s, ra, fa, n_router);
+    if ((rc = launch_router(ra, router_smem(d), s))) return rc;
+    uint16_t *oc = out + (size_t)c0 * H;
+    float *oc32 = out_f32_or_null ? out_f32_or_null + (size_t)c0 * H : nullptr;
+    if (pf_fits(d)) {
+      // kernels 2-4: gate/up, down (matrix cores), combine with the shared rows and residual
+      if (!sh) fa.shared = nullptr;
+      fa.n_sh_chunks = sh ? pf_sh_chunks(d) : 0;
+      if ((rc = launch_pf(fa, s))) return rc;
+      if ((rc = launch_combine_pf(xc, fa.y, w, fa.y_sh_part, fa.n_sh_chunks, Tc, H, k, oc, oc32,
+                                  nullptr, s)))
+        return rc;
     } else {
-      if ((rc = set_lds(router_shared_kernel<MB_MAX>, smem1))) return rc;
-      hipLaunchKernelGGL(router_shared_kernel<MB_MAX>, dim3(n_router + n_sh),
-                         dim3(ROUTER_THREADS), smem1, s, ra, fa, n_router);
+      // VALU kernels: gate/up (routed + shared), down (routed + shared, one chunk), combine
+      fa.y_sh = sh ? at<float>(ws, wl.ysh) : nullptr;
+      if (!sh) fa.shared = nullptr;
+      if (g_prof_start && (rc = record_event(g_prof_start, s))) return rc;
+      if ((rc = launch_gu(fa, 0, s))) return rc;
+      if (g_prof_stop && (rc = record_event(g_prof_stop, s))) return rc;
+      if ((rc = launch_d(fa, sh, s))) return rc;
+      const size_t n = (size_t)Tc * H;
+      const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
+      hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, s, xc, fa.y, w, fa.y_sh, Tc,
+                         H, k, oc, oc32);
+      QMOE_LAUNCHED();
     }
-    QMOE_LAUNCHED();
-    // kernel 2: routed gate/up + SwiGLU
-    if (g_prof_start && (rc = record_event(g_prof_start, s))) return rc;
-    if ((rc = launch_gu(fa, 1, s))) return rc;
-    if (g_prof_stop && (rc = record_event(g_prof_stop, s))) return rc;
-    // kernel 3: routed + shared down projection, combined by the last workgroup of each tile
-    fa.n_sh_chunks = sh ? shared_chunks(d) : 0;
-    if ((rc = launch_d(fa, sh, s))) return rc;
   }
   return ok();
 }

@@ -295,8 +295,9 @@ QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *sme
   float *zs = z + nt * H;                                    // [nt][H/16]
   float *fac = zs + nt * (H / 16);                           // [nt]
   __shared__ float red[ROUTER_WAVES];
+#pragma unroll
   for (int i = 0; i < TB; ++i) {
-    if (i >= nt) break;
+    if (i >= nt) continue;       // nt is the same for the whole workgroup
     float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < XC; ++j) {

@@ -255,7 +255,8 @@ def _layer_check(cfg, li, xb, out, out_f32, idx, w, toks):
     return ties, len(differ), flips
 
 
-@pytest.mark.parametrize("name,T,sample", [("tiny", 4, None), ("tiny", 1, None), ("tiny", 130, [0, 129]),
+@pytest.mark.parametrize("name,T,sample", [("tiny", 4, None), ("tiny", 1, None), ("tiny", 64, None),
+                                           ("tiny", 130, [0, 129]),
                                            ("gemma4_26b_a4b_decode", 1, None),
                                            ("gemma4_26b_a4b_prefill", 128, [5, 127]),
                                            ("qwen3_next_80b_a3b_decode_b1", 1, None),
