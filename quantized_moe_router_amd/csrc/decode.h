@@ -162,7 +162,7 @@ QMOE_DEV void dec_router(const DecodeArgs &a, int rb, unsigned ep, char *smem) {
   ra.cnt_all = nullptr; ra.n_tb = 1; ra.n_eb = a.nR; ra.counts = nullptr; ra.offsets = nullptr;
   ra.sorted = nullptr; ra.active = nullptr; ra.n_active = nullptr; ra.slot_tab = nullptr;
   ra.n_slots = 0;
-  router_logits_block<1>(ra, 0, rb, smem);
+  router_logits_block<1, 1>(ra, 0, rb, smem);
 }
 
 // ---------------------------------------------------------------- top-k (whole workgroup)

@@ -232,8 +232,8 @@ int set_lds(K kernel, size_t bytes) {
   return QMOE_OK;
 }
 
-size_t router_smem(const qmoe_dims *d) {
-  return std::max({router_lds_bytes(d->hidden), (size_t)(2 * d->n_experts) * 4,
+size_t router_smem(const qmoe_dims *d, int T) {
+  return std::max({router_lds_bytes(d->hidden), bucket_lds_bytes(T * d->top_k, d->n_experts),
                    ROUTER_WAVES * topk_lds_bytes(d->n_experts, d->top_k)});
 }
 
@@ -454,7 +454,7 @@ static int launch_decode(const qmoe_layer *L, const uint16_t *x, uint16_t *out, 
   a.y_sh = at<uint64_t>(ws, wl.dec_ysh);
   a.topk_idx = idx; a.topk_w = w; a.out = out; a.out_f32 = out_f32;
   const int tiles_d = a.H / TILE_ROWS, tpw = dec_tiles_per_wg(a.wpt);
-  a.nR = (a.E + ROUTER_EPB - 1) / ROUTER_EPB;
+  a.nR = (a.E + ROUTER_WAVES - 1) / ROUTER_WAVES;   // one expert per wave
   a.nSG = sh ? a.Is / 16 : 0;
   a.nRG = a.k * (a.I / 16);
   a.nSD = sh ? tiles_d * a.nc : 0;
@@ -561,7 +561,7 @@ int qmoe_router_topk(const qmoe_dims *d, const qmoe_router *r, const uint16_t *x
   const WsLayout wl = ws_layout(d, T);
   float *logits = logits_or_null ? logits_or_null : at<float>(ws, wl.logits);
   RouterArgs a = make_router_args(d, r, x, T, logits, topk_idx, topk_w, ws);
-  if ((rc = launch_router(a, router_smem(d), (hipStream_t)stream))) return rc;
+  if ((rc = launch_router(a, router_smem(d, T), (hipStream_t)stream))) return rc;
   return ok();
 }
 
@@ -575,7 +575,9 @@ int qmoe_bucket(const qmoe_dims *d, const int32_t *topk_idx, int32_t T, int32_t 
   if ((!topk_idx && T > 0) || !counts || !offsets || !sorted || !active || !n_active)
     return fail(QMOE_ERR_ARG, "bucket: NULL pointer");
   if ((rc = check_arch())) return rc;
-  hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(256), 0, (hipStream_t)stream, topk_idx,
+  const size_t lds = bucket_lds_bytes(T * d->top_k, d->n_experts);
+  if ((rc = set_lds(bucket_kernel, lds))) return rc;
+  hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(256), lds, (hipStream_t)stream, topk_idx,
                      T * d->top_k, d->n_experts, counts, offsets, sorted, active, n_active);
   QMOE_LAUNCHED();
   return ok();
@@ -670,7 +672,7 @@ int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16
                                at<float>(ws, wl.y), nullptr, ws, Tc_max);
     fa.slot_tab = ra.slot_tab;
     ra.n_slots = fa.n_slots;
-    if ((rc = launch_router(ra, router_smem(d), s))) return rc;
+    if ((rc = launch_router(ra, router_smem(d, Tc), s))) return rc;
     uint16_t *oc = out + (size_t)c0 * H;
     float *oc32 = out_f32_or_null ? out_f32_or_null + (size_t)c0 * H : nullptr;
     if (pf_fits(d)) {

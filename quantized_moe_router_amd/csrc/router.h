@@ -14,8 +14,8 @@
 
 namespace qmoe {
 
-constexpr int ROUTER_TB = 4;     // tokens per router workgroup
-constexpr int ROUTER_EPW = 1;    // experts per wave
+constexpr int ROUTER_TB = 4;     // tokens per router workgroup (multi-token router)
+constexpr int ROUTER_EPW = 4;    // experts per wave (multi-token router)
 constexpr int ROUTER_WAVES = 4;
 constexpr int ROUTER_EPB = ROUTER_EPW * ROUTER_WAVES;  // experts per router workgroup
 constexpr int ROUTER_THREADS = ROUTER_WAVES * WAVE;
@@ -47,10 +47,6 @@ struct RouterArgs {
   int n_slots;
 };
 
-// LDS bytes of the logits part of a router workgroup for hidden H and up to nt tokens
-inline __host__ __device__ size_t router_lds_bytes(int H, int nt = ROUTER_TB) {
-  return (size_t)nt * H * 4 + (size_t)nt * (H / 16) * 4 + 64;
-}
 
 // ---------------------------------------------------------------- top-k by exact ranking
 // Order: larger logit first, equal logits -> lower expert index.  A NaN logit ranks as -inf
@@ -143,31 +139,19 @@ QMOE_DEV void topk_wave(const float *lrow, int E, int k, const float *pes, uint6
 }
 
 // ---------------------------------------------------------------- bucketing (one workgroup)
-// Stable counting sort of N = T*k assignments by expert (ids outside [0, E) are dropped).
-// Counts via an LDS histogram; the rank of an assignment among the earlier ones of its
-// expert from wave ballots (one ballot per distinct expert in a wave) plus a per-expert cursor
-// advanced wave by wave in order.  Optionally also writes the slot table used by the expert
-// kernels: entry s = {expert, first bucket position, rows, first flat id} of the s-th active
-// expert, zero rows for s in [n_active, n_slots).
-// lds: at least 2 * E * 4 bytes.  get(f) returns the expert id of assignment f.
-template <int NT, class Get>
-QMOE_DEV void bucket_block(Get get, int N, int E, int32_t *counts, int32_t *offsets,
-                           int32_t *sorted, int32_t *active, int32_t *n_active, int32_t *slot_tab,
-                           int n_slots, int *lds) {
+// Stable counting sort of N = T*k assignments by expert (ids outside [0, E) are dropped):
+// position of assignment f = (first position of its expert) + (number of assignments f' < f
+// with the same expert).  Optionally also writes the slot table used by the expert kernels:
+// entry s = {expert, first bucket position, rows, first flat id} of the s-th active expert,
+// zero rows for s in [n_active, n_slots).  get(f) returns the expert id of assignment f.
+
+// Per-expert totals -> counts, offsets, active list, slot table; cnt[e] becomes the expert's
+// first position.  first[e]: smallest flat id of the expert.
+template <int NT>
+QMOE_DEV void bucket_offsets(int *cnt, const int *first, int E, int32_t *counts, int32_t *offsets,
+                             int32_t *active, int32_t *n_active, int32_t *slot_tab, int n_slots) {
   constexpr int NW = NT / WAVE;
-  int *cnt = lds;                 // [E]
-  int *first = lds + E;           // [E] smallest flat id of each expert
   const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
-  for (int e = tid; e < E; e += NT) { cnt[e] = 0; first[e] = 0x7FFFFFFF; }
-  __syncthreads();
-  for (int f = tid; f < N; f += NT) {
-    const int e = get(f);
-    if ((unsigned)e < (unsigned)E) {
-      atomicAdd(&cnt[e], 1);
-      atomicMin(&first[e], f);
-    }
-  }
-  __syncthreads();
   // exclusive scan of counts and of (count > 0) flags, E <= MAX_EXPERTS
   const int per = (E + NT - 1) / NT;
   const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
@@ -180,7 +164,6 @@ QMOE_DEV void bucket_block(Get get, int N, int E, int32_t *counts, int32_t *offs
     if (lane >= o) pair += up;
   }
   __shared__ long long wtot[NW];
-  __shared__ int n_act_sh;
   if (lane == WAVE - 1) wtot[wv] = pair;
   __syncthreads();
   long long before = 0, tot = 0;
@@ -201,7 +184,7 @@ QMOE_DEV void bucket_block(Get get, int N, int E, int32_t *counts, int32_t *offs
             qmoe_u32x4{(uint32_t)e, (uint32_t)run_cnt, (uint32_t)c, (uint32_t)first[e]};
       ++run_act;
     }
-    cnt[e] = run_cnt;  // becomes the cursor
+    cnt[e] = run_cnt;
     run_cnt += c;
   }
   const int na = (int)(tot & 0xFFFF);
@@ -212,8 +195,112 @@ QMOE_DEV void bucket_block(Get get, int N, int E, int32_t *counts, int32_t *offs
   if (slot_tab)
     for (int sl = na + tid; sl < n_slots; sl += NT)
       *(qmoe_u32x4 *)(slot_tab + 4 * sl) = qmoe_u32x4{0u, 0u, 0u, 0u};
-  (void)n_act_sh;
   __syncthreads();
+}
+
+// Segmented form, for up to BUCKET_SEG_N assignments with segments x experts <=
+// BUCKET_SEG_CELLS: the assignments are cut into 64-long segments (one wave each); an
+// assignment's rank among the same expert's earlier ones is its rank inside its segment (64
+// broadcast compares) plus the expert's counts in the earlier segments (a prefix per expert).
+// Every step is parallel.  lds: bucket_lds_bytes(N, E).
+constexpr int BUCKET_SEG_N = 4096, BUCKET_SEG_CELLS = 16384;
+inline __host__ __device__ bool bucket_seg_ok(int N, int E) {
+  return N <= BUCKET_SEG_N && ((N + WAVE - 1) / WAVE) * E <= BUCKET_SEG_CELLS;
+}
+inline __host__ __device__ size_t bucket_lds_bytes(int N, int E) {
+  return bucket_seg_ok(N, E) ? ((size_t)((N + WAVE - 1) / WAVE) * E + 2 * (size_t)E + N) * 4
+                             : (size_t)2 * E * 4;
+}
+
+template <int NT, class Get>
+QMOE_DEV void bucket_block_seg(Get get, int N, int E, int32_t *counts, int32_t *offsets,
+                               int32_t *sorted, int32_t *active, int32_t *n_active,
+                               int32_t *slot_tab, int n_slots, int *lds) {
+  constexpr int NW = NT / WAVE;
+  const int S = (N + WAVE - 1) / WAVE;
+  int *cnt = lds;                   // [S][E] counts per segment, then prefix over segments
+  int *tot = cnt + S * E;           // [E] totals, then first positions
+  int *first = tot + E;             // [E] smallest flat id
+  int *er = first + E;              // [N] expert << 8 | rank inside the segment (-1: dropped)
+  const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
+  for (int i = tid; i < S * E; i += NT) cnt[i] = 0;
+  for (int e = tid; e < E; e += NT) first[e] = 0x7FFFFFFF;
+  // every id into er[], eight loads per thread in flight
+  for (int base = 0; base < N; base += 8 * NT) {
+    int v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int f = base + tid + j * NT;
+      v[j] = (f < N) ? get(f) : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int f = base + tid + j * NT;
+      if (f < N) er[f] = v[j];
+    }
+  }
+  __syncthreads();
+  for (int sg = wv; sg < S; sg += NW) {
+    const int f = sg * WAVE + lane;
+    const int e = (f < N) ? er[f] : -1;
+    const bool valid = (f < N) && ((unsigned)e < (unsigned)E);
+    int rank = 0;
+    const int *seg = er + sg * WAVE;
+    const int n = min(WAVE, N - sg * WAVE);
+    for (int j = 0; j < n; ++j) rank += (j < lane && seg[j] == e) ? 1 : 0;
+    __builtin_amdgcn_wave_barrier();
+    if (f < N) er[f] = valid ? ((e << 8) | rank) : -1;
+    if (valid) {
+      atomicAdd(&cnt[sg * E + e], 1);
+      atomicMin(&first[e], f);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += NT) {
+    int run = 0;
+    for (int sg = 0; sg < S; ++sg) {
+      const int c = cnt[sg * E + e];
+      cnt[sg * E + e] = run;
+      run += c;
+    }
+    tot[e] = run;
+  }
+  __syncthreads();
+  bucket_offsets<NT>(tot, first, E, counts, offsets, active, n_active, slot_tab, n_slots);
+  for (int f = tid; f < N; f += NT) {
+    const int v = er[f];
+    if (v < 0) continue;
+    const int e = v >> 8, rank = v & 0xFF;
+    sorted[tot[e] + cnt[(f / WAVE) * E + e] + rank] = f;
+  }
+}
+
+// General form (any N): LDS histogram, then a stable scatter with one ballot per distinct
+// expert of a wave and a per-expert cursor advanced wave by wave.  lds: 2 * E * 4 bytes.
+template <int NT, class Get>
+QMOE_DEV void bucket_block(Get get, int N, int E, int32_t *counts, int32_t *offsets,
+                           int32_t *sorted, int32_t *active, int32_t *n_active, int32_t *slot_tab,
+                           int n_slots, int *lds) {
+  if (bucket_seg_ok(N, E)) {
+    bucket_block_seg<NT>(get, N, E, counts, offsets, sorted, active, n_active, slot_tab, n_slots,
+                         lds);
+    return;
+  }
+  constexpr int NW = NT / WAVE;
+  int *cnt = lds;                 // [E]
+  int *first = lds + E;           // [E] smallest flat id of each expert
+  const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
+  for (int e = tid; e < E; e += NT) { cnt[e] = 0; first[e] = 0x7FFFFFFF; }
+  __syncthreads();
+  for (int f = tid; f < N; f += NT) {
+    const int e = get(f);
+    if ((unsigned)e < (unsigned)E) {
+      atomicAdd(&cnt[e], 1);
+      atomicMin(&first[e], f);
+    }
+  }
+  __syncthreads();
+  bucket_offsets<NT>(cnt, first, E, counts, offsets, active, n_active, slot_tab, n_slots);
   // stable scatter, NT assignments per round
   for (int base = 0; base < N; base += NT) {
     const int f = base + tid;
@@ -245,135 +332,158 @@ QMOE_DEV void bucket_block(Get get, int N, int E, int32_t *counts, int32_t *offs
 }
 
 // ---------------------------------------------------------------- router logits
-// Workgroup (tb, eb): tokens [TB tb, TB tb + TB) x experts [4 eb, 4 eb + 4).  Per token the
-// input is staged as z = x * router_scale (fp32) with per-16-element sums; the token's norm
-// factor f = (1/sqrt(H)) / sqrt(mean(x^2) + eps) multiplies the finished dot product:
-//   logit = f * sum_g [ s_g * sum_{h in g} q_h z_h + b_g * sum_{h in g} z_h ] + bias.
-// Every global load (codes, scales, activations, router_scale) is issued before the first
-// one is used, so the workgroup waits for memory once.
-template <int TB>
+// Workgroup (tb, eb): tokens [TB tb, TB tb + TB) x experts [EPB eb, EPB eb + EPB), EPW
+// experts per wave.  Per token the input is staged in LDS as z = x * router_scale (fp32);
+// the token's norm factor f = (1/sqrt(H)) / sqrt(mean(x^2) + eps) multiplies the finished
+// dot product:
+//   logit = f * sum_h (s q + b)_h z_h + bias.
+// Lane l of a wave works on elements 256 j + 4 l .. + 3 of the rows, so both the code loads
+// (4 bytes per lane) and the LDS reads of z (16 bytes per lane) are contiguous across lanes;
+// each z read serves the wave's EPW experts.
+constexpr int ROUTER_MAX_H = 8192;
+constexpr int ROUTER_RB = 11;          // 256-element blocks of codes a wave loads per batch
+
+inline __host__ __device__ size_t router_lds_bytes(int H, int nt = ROUTER_TB) {
+  return (size_t)nt * H * 4 + 64;
+}
+
+template <int TB, int EPW>
 QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *smem) {
+  constexpr int EPB = EPW * ROUTER_WAVES;
   const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
   const int H = a.H;
   const int t0 = tb * TB;
   const int nt = min(TB, a.T - t0);
-  // this wave's expert row: lane l holds chunks l, l+64, ... (16 codes each; H <= 8192 -> at
-  // most 8 chunks per lane)
-  constexpr int NCH = 8;
-  const int n16 = H / 16;
-  const int e = eb * ROUTER_EPB + wv;
-  const int ec = min(e, a.E - 1);
-  const uint8_t *row = a.rq + (size_t)ec * H;
-  qmoe_u32x4 v[NCH];
-  uint16_t sv[NCH], bv[NCH];
+  const int e_first = eb * EPB + wv * EPW;
+  const int nb = (H + 255) / 256;                  // blocks of 256 elements (last may be partial)
+  // first batch of this wave's codes and group scales/biases, issued before the activations
+  uint32_t cq[EPW][ROUTER_RB];
+  uint32_t sbw[EPW][ROUTER_RB];
+  auto load_codes = [&](int b0) {
 #pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const int c = min(lane + WAVE * j, n16 - 1);
-    v[j] = *(const qmoe_u32x4 *)(row + 16 * c);
-    sv[j] = a.rs[(size_t)ec * (H / GROUP) + c / 4];
-    bv[j] = a.rb[(size_t)ec * (H / GROUP) + c / 4];
-  }
-  const float lb = a.lbias ? a.lbias[ec] : 0.f;
-  // activations: thread tid holds the 8-element chunks tid + 256 j (j < XC) of each token,
-  // with the matching router_scale entries
-  constexpr int XC = 4;
-  const int n8 = H / 8;
-  qmoe_u32x4 xv[TB][XC];
-  float4 rsv[XC][2];
+    for (int x = 0; x < EPW; ++x) {
+      const int ec = min(e_first + x, a.E - 1);
+      const uint8_t *row = a.rq + (size_t)ec * H;
+      const uint16_t *rs = a.rs + (size_t)ec * (H / GROUP), *rb = a.rb + (size_t)ec * (H / GROUP);
 #pragma unroll
-  for (int j = 0; j < XC; ++j) {
-    const int c = min(tid + ROUTER_THREADS * j, n8 - 1);
-    if (a.rscale) {
-      rsv[j][0] = *(const float4 *)(a.rscale + 8 * c);
-      rsv[j][1] = *(const float4 *)(a.rscale + 8 * c + 4);
+      for (int j = 0; j < ROUTER_RB; ++j) {
+        const int el = min(256 * (b0 + j) + 4 * lane, H - 4);
+        cq[x][j] = *(const uint32_t *)(row + el);
+        sbw[x][j] = (uint32_t)rs[el / GROUP] | ((uint32_t)rb[el / GROUP] << 16);
+      }
     }
+  };
+  load_codes(0);
+  float lb[EPW];
 #pragma unroll
-    for (int i = 0; i < TB; ++i)
-      xv[i][j] = *(const qmoe_u32x4 *)(a.x + (size_t)(t0 + min(i, nt - 1)) * H + 8 * c);
-  }
+  for (int x = 0; x < EPW; ++x) lb[x] = a.lbias ? a.lbias[min(e_first + x, a.E - 1)] : 0.f;
+  // activations: thread tid stages elements 4 (tid + 256 j) .. + 3 of each token, XB chunks
+  // per batch (one batch for H <= 3072)
+  constexpr int XB = 3;
+  const int n4 = H / 4;
   float *z = (float *)smem;                                  // [nt][H]
-  float *zs = z + nt * H;                                    // [nt][H/16]
-  float *fac = zs + nt * (H / 16);                           // [nt]
-  __shared__ float red[ROUTER_WAVES];
+  float *fac = z + nt * H;                                   // [TB]
+  __shared__ float red[ROUTER_WAVES][TB];
+  float ss[TB];
 #pragma unroll
-  for (int i = 0; i < TB; ++i) {
-    if (i >= nt) continue;       // nt is the same for the whole workgroup
-    float ss = 0.f;
+  for (int i = 0; i < TB; ++i) ss[i] = 0.f;
+  for (int j0 = 0; j0 * ROUTER_THREADS < n4; j0 += XB) {
+    uint2 xv[TB][XB];
+    float4 rsv[XB];
 #pragma unroll
-    for (int j = 0; j < XC; ++j) {
-      const int c = tid + ROUTER_THREADS * j;
-      if (c < n8) {
-        const uint32_t wv4[4] = {xv[i][j].x, xv[i][j].y, xv[i][j].z, xv[i][j].w};
-        const float rs8[8] = {rsv[j][0].x, rsv[j][0].y, rsv[j][0].z, rsv[j][0].w,
-                              rsv[j][1].x, rsv[j][1].y, rsv[j][1].z, rsv[j][1].w};
-        float part = 0.f;
+    for (int j = 0; j < XB; ++j) {
+      const int c = min(tid + ROUTER_THREADS * (j0 + j), n4 - 1);
+      rsv[j] = a.rscale ? *(const float4 *)(a.rscale + 4 * c) : float4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          float x0 = bf16lo(wv4[d]), x1 = bf16hi(wv4[d]);
-          ss = fmaf(x0, x0, ss);
-          ss = fmaf(x1, x1, ss);
-          if (a.rscale) { x0 *= rs8[2 * d]; x1 *= rs8[2 * d + 1]; }
-          z[i * H + 8 * c + 2 * d] = x0;
-          z[i * H + 8 * c + 2 * d + 1] = x1;
-          part += x0 + x1;
-        }
-        // two 8-element threads make one 16-element sum (c even/odd are adjacent lanes)
-        const float other = __shfl_xor(part, 1, WAVE);
-        if ((c & 1) == 0) zs[i * (H / 16) + c / 2] = part + other;
-      }
+      for (int i = 0; i < TB; ++i)
+        xv[i][j] = *(const uint2 *)(a.x + (size_t)(t0 + min(i, nt - 1)) * H + 4 * c);
     }
-    ss = wave_sum(ss);
-    if (lane == 0) red[wv] = ss;
-    __syncthreads();
-    if (tid == 0) {
-      float tot = 0.f;
-      for (int w = 0; w < ROUTER_WAVES; ++w) tot += red[w];
-      fac[i] = a.inv_sqrt_h / sqrtf(tot / (float)H + RMS_EPS);
-    }
-    __syncthreads();
-  }
-  if (e >= a.E) return;
-  float acc[TB];
 #pragma unroll
-  for (int i = 0; i < TB; ++i) acc[i] = 0.f;
+    for (int i = 0; i < TB; ++i) {
+      if (i >= nt) continue;
 #pragma unroll
-  for (int j = 0; j < NCH; ++j) {
-    const int c = lane + WAVE * j;
-    if (c < n16) {
-      const float s = bf16_to_f32(sv[j]), b = bf16_to_f32(bv[j]);
-      const uint32_t w4[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
-      float q[16];
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        q[4 * d + 0] = (float)(w4[d] & 0xFFu);
-        q[4 * d + 1] = (float)((w4[d] >> 8) & 0xFFu);
-        q[4 * d + 2] = (float)((w4[d] >> 16) & 0xFFu);
-        q[4 * d + 3] = (float)(w4[d] >> 24);
-      }
-#pragma unroll
-      for (int i = 0; i < TB; ++i) {
-        if (i < nt) {
-          const float *zr = z + i * H + 16 * c;
-          float dq = 0.f;
-#pragma unroll
-          for (int jj = 0; jj < 16; ++jj) dq = fmaf(q[jj], zr[jj], dq);
-          acc[i] = fmaf(s, dq, acc[i]);
-          acc[i] = fmaf(b, zs[i * (H / 16) + c], acc[i]);
+      for (int j = 0; j < XB; ++j) {
+        const int c = tid + ROUTER_THREADS * (j0 + j);
+        if (c < n4) {
+          const float x0 = bf16lo(xv[i][j].x), x1 = bf16hi(xv[i][j].x);
+          const float x2 = bf16lo(xv[i][j].y), x3 = bf16hi(xv[i][j].y);
+          ss[i] = fmaf(x0, x0, ss[i]);
+          ss[i] = fmaf(x1, x1, ss[i]);
+          ss[i] = fmaf(x2, x2, ss[i]);
+          ss[i] = fmaf(x3, x3, ss[i]);
+          *(float4 *)(z + i * H + 4 * c) =
+              float4{x0 * rsv[j].x, x1 * rsv[j].y, x2 * rsv[j].z, x3 * rsv[j].w};
         }
       }
     }
   }
 #pragma unroll
   for (int i = 0; i < TB; ++i) {
-    if (i < nt) {
-      const float tot = wave_sum(acc[i]);
-      float l = fac[i] * tot;
-      if (a.lbias) l += lb;
-      const size_t o = (size_t)(t0 + i) * a.E + e;
-      if (a.logits_tag) {
-        if (lane < a.tag_copies) st_tag(a.logits_tag + (size_t)lane * a.tag_copy_stride + o, a.tag, l);
-      } else if (lane == 0) {
-        st_sys(a.logits + o, l);
+    if (i >= nt) continue;
+    ss[i] = wave_sum(ss[i]);
+    if (lane == 0) red[wv][i] = ss[i];
+  }
+  __syncthreads();
+  if (tid < nt) {
+    float tot = 0.f;
+    for (int w = 0; w < ROUTER_WAVES; ++w) tot += red[w][tid];
+    fac[tid] = a.inv_sqrt_h / sqrtf(tot / (float)H + RMS_EPS);
+  }
+  __syncthreads();
+  if (e_first >= a.E) return;
+  float acc[EPW][TB];
+#pragma unroll
+  for (int x = 0; x < EPW; ++x)
+#pragma unroll
+    for (int i = 0; i < TB; ++i) acc[x][i] = 0.f;
+  for (int b0 = 0; b0 < nb; b0 += ROUTER_RB) {
+    if (b0 > 0) load_codes(b0);
+#pragma unroll
+    for (int j = 0; j < ROUTER_RB; ++j) {
+      const int el = 256 * (b0 + j) + 4 * lane;
+      if (b0 + j < nb && el < H) {
+        float4 zz[TB];
+#pragma unroll
+        for (int i = 0; i < TB; ++i)
+          if (i < nt) zz[i] = *(const float4 *)(z + i * H + el);
+#pragma unroll
+        for (int x = 0; x < EPW; ++x) {
+          const float s = bf16_to_f32((uint16_t)(sbw[x][j] & 0xFFFFu));
+          const float bb = bf16_to_f32((uint16_t)(sbw[x][j] >> 16));
+          const float w0 = fmaf(s, (float)(cq[x][j] & 0xFFu), bb);
+          const float w1 = fmaf(s, (float)((cq[x][j] >> 8) & 0xFFu), bb);
+          const float w2 = fmaf(s, (float)((cq[x][j] >> 16) & 0xFFu), bb);
+          const float w3 = fmaf(s, (float)(cq[x][j] >> 24), bb);
+#pragma unroll
+          for (int i = 0; i < TB; ++i) {
+            if (i < nt) {
+              acc[x][i] = fmaf(w0, zz[i].x, acc[x][i]);
+              acc[x][i] = fmaf(w1, zz[i].y, acc[x][i]);
+              acc[x][i] = fmaf(w2, zz[i].z, acc[x][i]);
+              acc[x][i] = fmaf(w3, zz[i].w, acc[x][i]);
+            }
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < EPW; ++x) {
+    const int e = e_first + x;
+#pragma unroll
+    for (int i = 0; i < TB; ++i) {
+      if (i < nt) {
+        const float tot = wave_sum(acc[x][i]);
+        float l = fac[i] * tot;
+        if (a.lbias) l += lb[x];
+        const size_t o = (size_t)(t0 + i) * a.E + e;
+        if (e < a.E) {
+          if (a.logits_tag) {
+            if (lane < a.tag_copies) st_tag(a.logits_tag + (size_t)lane * a.tag_copy_stride + o, a.tag, l);
+          } else if (lane == 0) {
+            st_sys(a.logits + o, l);
+          }
+        }
       }
     }
   }
@@ -414,7 +524,7 @@ QMOE_DEV void router_finish(const RouterArgs &a, int tb, char *smem) {
 __global__ void __launch_bounds__(ROUTER_THREADS) router_kernel(RouterArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int tb = blockIdx.x / a.n_eb, eb = blockIdx.x % a.n_eb;
-  router_logits_block<ROUTER_TB>(a, tb, eb, smem);
+  router_logits_block<ROUTER_TB, ROUTER_EPW>(a, tb, eb, smem);
   router_finish(a, tb, smem);
 }
 
@@ -422,9 +532,9 @@ __global__ void __launch_bounds__(256) bucket_kernel(const int32_t *idx, int N, 
                                                      int32_t *counts, int32_t *offsets,
                                                      int32_t *sorted, int32_t *active,
                                                      int32_t *n_active) {
-  __shared__ int lds[2 * MAX_EXPERTS];
+  extern __shared__ __align__(16) char smem[];
   bucket_block<256>([&](int f) { return idx[f]; }, N, E, counts, offsets, sorted, active, n_active,
-                    nullptr, 0, lds);
+                    nullptr, 0, (int *)smem);
 }
 
 }  // namespace qmoe

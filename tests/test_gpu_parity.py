@@ -172,16 +172,23 @@ def test_bucket_drops_out_of_range_ids():
 
 # ------------------------------------------------------------------ bucket
 
-@pytest.mark.parametrize("T,k,E", [(1, 8, 128), (4, 2, 16), (16, 10, 512), (128, 8, 128),
-                                   (128, 8, 256), (37, 3, 7), (1000, 4, 64), (0, 2, 16)])
-def test_bucket_parity(T, k, E):
+# the first eight cases take the segmented bucketing (at most 4096 assignments and 16384
+# segment x expert cells), the last two the general one; `repeat` lets a token name the same
+# expert several times (the standalone entry point accepts any ids)
+@pytest.mark.parametrize("T,k,E,repeat", [(1, 8, 128, False), (4, 2, 16, False),
+                                          (16, 10, 512, False), (128, 8, 128, False),
+                                          (128, 8, 256, False), (37, 3, 7, False),
+                                          (1000, 4, 64, False), (0, 2, 16, False),
+                                          (100, 8, 16, True), (2048, 4, 64, False),
+                                          (64, 32, 1024, False), (1500, 4, 8, True)])
+def test_bucket_parity(T, k, E, repeat):
     ops = _ops()
     from quantized_moe_router_amd._lib import make_dims
     rng = np.random.default_rng(T * 131 + k * 7 + E)
     # Zipf-skewed picks so that some buckets are large and many empty
     p = 1.0 / np.arange(1, E + 1) ** 1.1
     p /= p.sum()
-    idx = np.stack([rng.choice(E, size=k, replace=False, p=p) for _ in range(T)]).astype(np.int32) \
+    idx = np.stack([rng.choice(E, size=k, replace=repeat, p=p) for _ in range(T)]).astype(np.int32) \
         if T else np.zeros((0, k), np.int32)
     dims = make_dims(64, E, k, 64, 0)
     counts, offsets, srt, active, n_active = ops.bucket(dims, torch.from_numpy(idx).to(DEV))
