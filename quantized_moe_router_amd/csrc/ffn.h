@@ -30,12 +30,6 @@ struct FfnArgs {
   float *y_sh_part;           // shared partials [n_sh_chunks][T, H] (several chunks)
   const int32_t *slot_tab;    // [n_slots][4] {expert, first position, rows, first flat id} or null
   int n_sh_chunks;            // down-projection workgroups per tile for the shared block
-  unsigned *cnt_tile;         // [H/32] completion counters of the fused combine
-  // fused combine (down kernel of the layer path); out == null -> no combine
-  const float *topk_w;        // [T, k]
-  uint16_t *out;              // [T, H] bf16
-  float *out_f32;             // [T, H] or null
-  int gu_shared_only;         // gate/up launch covers only the shared expert's tiles
 };
 
 // Resolve the rows handled by a workgroup of slot `slot` (routed) or the shared slot.
@@ -244,7 +238,7 @@ template <int W, int MB, int KB>
 __global__ void __launch_bounds__(W * WAVE) gu_kernel(FfnArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int tiles_r = a.I / 16;
-  const int n_routed = a.gu_shared_only ? 0 : a.n_slots * tiles_r;
+  const int n_routed = a.n_slots * tiles_r;
   int bid = blockIdx.x;
   SlotRows sr;
   int tile;
@@ -267,11 +261,10 @@ inline __host__ __device__ size_t d_lds_bytes(int Kc) {
 }
 
 // k-steps [kb0, kb0 + nks) of one 32-row output tile of the down projection of slot `sr`
-// (K = the block's width).  Output rows go to dst (row of token r0+i = ysel(r0+i)), written
-// with system-scope stores when `handoff` (another workgroup of this launch reads them).
+// (K = the block's width).  Output rows go to dst (row of token r0+i = ysel(r0+i)).
 template <int W, int MB, int KB, class YSel>
 QMOE_DEV void d_tile(const FfnArgs &a, const SlotRows &sr, int tile, int kb0, int nks,
-                     float *dst, YSel ysel, bool handoff, char *smem) {
+                     float *dst, YSel ysel, char *smem) {
   const int H = a.H;
   const int K = sr.shared ? a.Is : a.I;
   const int KS = K / GROUP;
@@ -337,59 +330,32 @@ QMOE_DEV void d_tile(const FfnArgs &a, const SlotRows &sr, int tile, int kb0, in
       const int i = o / 32, r = o % 32;
       float yv = 0.f;
       for (int w = 0; w < W; ++w) yv += red[(w * MB + i) * 32 + r];
-      float *p = dst + (size_t)ysel(r0 + i) * H + 32 * tile + r;
-      if (handoff) st_sys(p, yv); else *p = yv;
+      dst[(size_t)ysel(r0 + i) * H + 32 * tile + r] = yv;
     }
     __syncthreads();
   }
 }
 
-// Combine of one 32-row tile for every token, by the workgroup that completes the tile:
-//   out = bf16( x + sum_j w_j y_j + sum_c y_shared_c )  (fp32, fixed order)
-QMOE_DEV void combine_tile(const FfnArgs &a, int tile) {
-  const int H = a.H;
-  for (int o = threadIdx.x; o < a.T * 32; o += blockDim.x) {
-    const int t = o / 32, col = 32 * tile + o % 32;
-    float acc = 0.f;
-    for (int j = 0; j < a.k; ++j)
-      acc = fmaf(ld_sys(a.topk_w + (size_t)t * a.k + j),
-                 ld_sys(a.y + ((size_t)t * a.k + j) * H + col), acc);
-    if (a.shared)
-      for (int c = 0; c < a.n_sh_chunks; ++c)
-        acc += ld_sys(a.y_sh_part + ((size_t)c * a.T + t) * H + col);
-    acc += bf16_to_f32(a.x[(size_t)t * H + col]);
-    a.out[(size_t)t * H + col] = (uint16_t)f32_to_bf16_bits(acc);
-    if (a.out_f32) a.out_f32[(size_t)t * H + col] = acc;
-  }
-}
-
-// grid = (H/32 tiles, n_slots routed slots + n_sh_chunks shared chunks if a.shared).
-// Without a.out: routed rows go to a.y, the (single-chunk) shared rows to a.y_sh.  With
-// a.out: every workgroup hands its rows over (system-scope stores) and the workgroup that
-// completes a tile combines it.
+// grid = (H/32 tiles, n_slots routed slots + n_sh_chunks shared chunks if a.shared): routed
+// rows go to a.y, the shared rows (one chunk) to a.y_sh.
 template <int W, int MB, int KB>
 __global__ void __launch_bounds__(W * WAVE) d_kernel(FfnArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int tile = blockIdx.x;
   const int slot = blockIdx.y;
-  const bool fused = a.out != nullptr;
   SlotRows sr;
   const bool shared = slot >= a.n_slots;
-  if (slot_rows(a, slot, shared, sr)) {
-    int kb0 = 0, nks = a.I / GROUP;
-    float *dst = a.y;
-    if (shared) {
-      const int KSs = a.Is / GROUP, c = slot - a.n_slots, nc = a.n_sh_chunks;
-      kb0 = (KSs * c) / nc;
-      nks = (KSs * (c + 1)) / nc - kb0;
-      dst = fused ? a.y_sh_part + (size_t)c * a.T * a.H : a.y_sh;
-    }
-    auto ysel = [&](int r) { return shared ? r : flat_of(a, sr, r); };
-    d_tile<W, MB, KB>(a, sr, tile, kb0, nks, dst, ysel, fused, smem);
+  if (!slot_rows(a, slot, shared, sr)) return;
+  int kb0 = 0, nks = a.I / GROUP;
+  float *dst = a.y;
+  if (shared) {
+    const int KSs = a.Is / GROUP, c = slot - a.n_slots, nc = a.n_sh_chunks;
+    kb0 = (KSs * c) / nc;
+    nks = (KSs * (c + 1)) / nc - kb0;
+    dst = a.y_sh;
   }
-  if (!fused) return;
-  if (!arrive_last(&a.cnt_tile[tile], gridDim.y)) return;
-  combine_tile(a, tile);
+  auto ysel = [&](int r) { return shared ? r : flat_of(a, sr, r); };
+  d_tile<W, MB, KB>(a, sr, tile, kb0, nks, dst, ysel, smem);
 }
 
 // ---------------------------------------------------------------- standalone combine

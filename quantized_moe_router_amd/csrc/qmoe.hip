@@ -28,7 +28,6 @@ constexpr int GU_W = 8;     // waves per routed gate/up workgroup (split-K)
 constexpr int D_W = 8;      // waves per down workgroup (split-K)
 constexpr int KB = 12;      // k-steps loaded per batch by a wave
 constexpr int MB_MAX = 8;   // rows (tokens) per activation block
-constexpr int CNT_TILE_WORD = 64 + 16384;  // first word of the per-tile combine counters
 constexpr int DEC_SYNC_WORD = 32768;       // first word of the one-token decode sync area
 constexpr int MAX_T = 65536;
 
@@ -306,7 +305,6 @@ static FfnArgs make_ffn_args(const qmoe_layer *L, const uint16_t *x, int T, cons
   a.y = y; a.y_sh = y_sh;
   a.y_sh_part = at<float>(ws, wl.ysh_part);
   a.n_sh_chunks = 1;
-  a.cnt_tile = at<unsigned>(ws, wl.cnt) + CNT_TILE_WORD;
   return a;
 }
 
@@ -320,12 +318,11 @@ static int launch_gu_t(const FfnArgs &a, int n, hipStream_t s) {
   return QMOE_OK;
 }
 
-static int launch_gu(FfnArgs a, int mode, hipStream_t s) {
-  // mode 0: routed + shared tiles, 1: routed only
+// routed tiles, plus the shared block's tiles when a.shared and a.y_sh are set
+static int launch_gu(FfnArgs a, hipStream_t s) {
   const int tiles_r = a.I / 16;
-  const bool sh = (mode == 0) && a.shared && a.y_sh;
+  const bool sh = a.shared && a.y_sh;
   const int n = a.n_slots * tiles_r + (sh ? a.Is / 16 : 0);
-  a.gu_shared_only = 0;
   if (!sh) a.shared = nullptr;
   if (n == 0) return QMOE_OK;
   return mb_for(a.T) == 1 ? launch_gu_t<1>(a, n, s) : launch_gu_t<MB_MAX>(a, n, s);
@@ -609,7 +606,7 @@ int qmoe_expert_ffn(const qmoe_layer *L, const uint16_t *x, int32_t T, const int
       return rc;
     return ok();
   }
-  if ((rc = launch_gu(a, 0, s))) return rc;
+  if ((rc = launch_gu(a, s))) return rc;
   const bool sh = L->shared && y_shared_or_null;
   if (!sh) a.shared = nullptr;
   if ((rc = launch_d(a, sh, s))) return rc;
@@ -688,7 +685,7 @@ int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16
       fa.y_sh = sh ? at<float>(ws, wl.ysh) : nullptr;
       if (!sh) fa.shared = nullptr;
       if (g_prof_start && (rc = record_event(g_prof_start, s))) return rc;
-      if ((rc = launch_gu(fa, 0, s))) return rc;
+      if ((rc = launch_gu(fa, s))) return rc;
       if (g_prof_stop && (rc = record_event(g_prof_stop, s))) return rc;
       if ((rc = launch_d(fa, sh, s))) return rc;
       const size_t n = (size_t)Tc * H;

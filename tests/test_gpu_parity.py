@@ -206,7 +206,8 @@ def _bucket_of(ops, dims, idx):
     return ops.bucket(dims, idx)
 
 
-@pytest.mark.parametrize("name,T,sample", [("tiny", 4, None), ("tiny", 37, None),
+# T <= 128 takes the matrix-core kernels, T = 200 the VALU ones
+@pytest.mark.parametrize("name,T,sample", [("tiny", 4, None), ("tiny", 37, None), ("tiny", 200, None),
                                            ("gemma4_26b_a4b_decode", 1, None),
                                            ("gemma4_26b_a4b_prefill", 128, [0, 77]),
                                            ("qwen3_next_80b_a3b_decode_b16", 16, [3, 15])])
