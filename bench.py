@@ -74,9 +74,10 @@ def stored_traffic(name):
         return None
     vals = {}
     for line in open(path):
-        if "=" in line and line.strip().startswith(("traffic_bytes_per_launch", "sources_sha256")):
-            k, v = line.strip().strip("`").split("=", 1)
-            vals[k.strip()] = v.strip().strip("`")
+        item = line.strip().lstrip("-").strip().strip("`")
+        if "=" in item and item.startswith(("traffic_bytes_per_launch", "sources_sha256")):
+            k, v = item.split("=", 1)
+            vals[k.strip()] = v.strip()
     if vals.get("sources_sha256") != sources_digest() or "traffic_bytes_per_launch" not in vals:
         return None
     return int(float(vals["traffic_bytes_per_launch"]))
