@@ -13,7 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libqmoe.so")
 SOURCES = ["qmoe.hip"]
-HEADERS = ["common.h", "store.h", "router.h", "ffn.h"]
+HEADERS = ["common.h", "store.h", "router.h", "ffn.h", "mfma.h", "decode.h"]
 
 
 def hipcc():
@@ -28,6 +28,9 @@ def flags():
         "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
         # packed fp32 instructions are disabled for all device code
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # matrix-core accumulators stay in VGPRs: the prefill kernels scale them with VALU FMAs
+        # between products, which would otherwise copy them out of and back into AGPRs
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-I", INCLUDE, "-I", CSRC,
         "-Wno-unused-result",
     ]

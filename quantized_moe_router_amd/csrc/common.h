@@ -41,8 +41,18 @@ QMOE_DEV float dot2bf(uint32_t a, uint32_t b, float c) {
 // turns two codes into a bf16 pair (128+q_2i, 128+q_2i+1) aligned with the activation pair
 // (x_2i, x_2i+1).  The dot products therefore sum (128 + q) * x; callers subtract
 // 128 * sum(x) through the group bias term.
+// The mask and the exponent pattern are handed over in VGPRs: a VOP3 instruction takes no
+// literal operand on gfx950, and with both constants in registers the AND-OR is one
+// v_and_or_b32 instead of a v_and_b32 and a v_or_b32 with literals.
 constexpr uint32_t MAGIC2 = 0x43004300u;
-QMOE_DEV uint32_t nib_pair(uint32_t w, int i) { return ((w >> (4 * i)) & 0x000F000Fu) | MAGIC2; }
+QMOE_DEV uint32_t vreg_const(uint32_t v) {
+  uint32_t r;
+  asm("v_mov_b32 %0, %1" : "=v"(r) : "i"(v));
+  return r;
+}
+QMOE_DEV uint32_t nib_pair(uint32_t w, int i) {
+  return ((w >> (4 * i)) & vreg_const(0x000F000Fu)) | vreg_const(MAGIC2);
+}
 
 // sum over 32 elements of (128 + q_j) * x_j; w: 4 packed words, x: 16 bf16 pairs
 QMOE_DEV float dot32_q4_bf16(const uint32_t w[4], const uint32_t x[16]) {

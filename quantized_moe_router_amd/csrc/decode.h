@@ -161,8 +161,8 @@ QMOE_DEV void dec_router(const DecodeArgs &a, int rb, unsigned ep, char *smem) {
   ra.topk_idx = nullptr; ra.topk_w = nullptr; ra.cnt_tb = nullptr;
   ra.cnt_all = nullptr; ra.n_tb = 1; ra.n_eb = a.nR; ra.counts = nullptr; ra.offsets = nullptr;
   ra.sorted = nullptr; ra.active = nullptr; ra.n_active = nullptr; ra.slot_tab = nullptr;
-  ra.n_slots = 0;
-  router_logits_block<1, 1>(ra, 0, rb, smem);
+  ra.n_slots = 0; ra.gsum = nullptr;
+  router_logits_block<1, 1, false>(ra, 0, rb, smem);
 }
 
 // ---------------------------------------------------------------- top-k (whole workgroup)

@@ -26,10 +26,11 @@ struct FfnArgs {
   uint16_t *hr_hi, *hr_lo;    // routed h [T*k, I] in bucket order
   uint16_t *hs_hi, *hs_lo;    // shared h [T, Is]
   float *y;                   // routed y [T*k, H] by flat id
-  float *y_sh;                // shared y [T, H] or null (one shared chunk)
-  float *y_sh_part;           // shared partials [n_sh_chunks][T, H] (several chunks)
+  float *y_sh;                // shared y [T, H] or null
+  const float *gx;            // sums of every 64-column group of x [T, H/64] (matrix-core path)
+  float *gh_r, *gh_s;         // the same for h hi + lo: routed [T*k, I/64], shared [T, Is/64]
   const int32_t *slot_tab;    // [n_slots][4] {expert, first position, rows, first flat id} or null
-  int n_sh_chunks;            // down-projection workgroups per tile for the shared block
+  int n_sh_chunks;            // VALU down kernel: workgroups per tile for the shared block
 };
 
 // Resolve the rows handled by a workgroup of slot `slot` (routed) or the shared slot.

@@ -122,14 +122,6 @@ inline int shared_chunks(const qmoe_dims *d) {
   return std::max(1, std::min(c, ks));
 }
 
-// The same for the matrix-core down kernel, whose workgroups stage at most PF_KMAX k-steps
-// of h.
-inline int pf_sh_chunks(const qmoe_dims *d) {
-  if (d->shared_inter == 0) return 0;
-  const int ks = d->shared_inter / GROUP;
-  return std::max(shared_chunks(d), (ks + PF_KMAX - 1) / PF_KMAX);
-}
-
 // The same for the one-token decode launch, whose shared down workgroups split one output
 // tile's k-steps over their four waves (at most DEC_W * KB_DEC k-steps per chunk).
 inline int dec_shared_chunks(const qmoe_dims *d) {
@@ -140,7 +132,7 @@ inline int dec_shared_chunks(const qmoe_dims *d) {
 
 struct WsLayout {
   size_t cnt, logits, tidx, tw, counts, offsets, sorted, active, nact, slot_tab;
-  size_t hr_hi, hr_lo, hs_hi, hs_lo, y, ysh, ysh_part;
+  size_t hr_hi, hr_lo, hs_hi, hs_lo, y, ysh, gx, ghr, ghs;
   size_t dec_logits, dec_hr, dec_hsh, dec_yr, dec_ysh, total;
 };
 
@@ -165,7 +157,9 @@ WsLayout ws_layout(const qmoe_dims *d, int Tmax) {
   w.hs_lo = o; o += al(T * (size_t)d->shared_inter * 2);
   w.y = o; o += al(Tc * k * H * 4);
   w.ysh = o; o += al(Tc * H * 4);
-  w.ysh_part = o; o += al((size_t)pf_sh_chunks(d) * Tc * H * 4);
+  w.gx = o; o += al(T * (H / GROUP) * 4);
+  w.ghr = o; o += al(T * k * (size_t)(d->inter / GROUP) * 4);
+  w.ghs = o; o += al(T * (size_t)(d->shared_inter / GROUP) * 4);
   w.dec_logits = o; o += (size_t)LOGIT_COPIES * dec_copy_stride(E);
   w.dec_hr = o; o += (size_t)H_COPIES * dec_copy_stride(k * d->inter);
   w.dec_hsh = o; o += (size_t)H_COPIES * dec_copy_stride((size_t)d->shared_inter);
@@ -303,7 +297,9 @@ static FfnArgs make_ffn_args(const qmoe_layer *L, const uint16_t *x, int T, cons
   a.hr_hi = at<uint16_t>(ws, wl.hr_hi); a.hr_lo = at<uint16_t>(ws, wl.hr_lo);
   a.hs_hi = at<uint16_t>(ws, wl.hs_hi); a.hs_lo = at<uint16_t>(ws, wl.hs_lo);
   a.y = y; a.y_sh = y_sh;
-  a.y_sh_part = at<float>(ws, wl.ysh_part);
+  a.gx = at<float>(ws, wl.gx);
+  a.gh_r = at<float>(ws, wl.ghr);
+  a.gh_s = at<float>(ws, wl.ghs);
   a.n_sh_chunks = 1;
   return a;
 }
@@ -352,52 +348,46 @@ static int launch_d(FfnArgs a, bool with_shared, hipStream_t s) {
   return mb_for(a.T) == 1 ? launch_d_t<1>(a, slots, Kc, s) : launch_d_t<MB_MAX>(a, slots, Kc, s);
 }
 
-// Matrix-core grouped GEMM (mfma.h) for calls with more than one token: usable when the
-// staged activation rows fit in LDS.
-static bool pf_fits(const qmoe_dims *d) {
-  return gu_pf_lds(d->hidden) <= 160 * 1024 && d->inter / GROUP <= PF_KMAX;
-}
-
-// gate/up then down; routed rows go to a.y, shared rows (if a.shared) to the a.n_sh_chunks
-// partials in a.y_sh_part.  Profile events (if set) bracket the gate/up kernel.
+// Matrix-core grouped GEMM (mfma.h): gate/up then down.  Routed rows go to a.y, shared rows
+// (if a.shared) to a.y_sh; a.gx must hold the group sums of x.  Profile events (if set)
+// bracket the gate/up kernel.
 static int launch_pf(const FfnArgs &a, hipStream_t s) {
   int rc;
-  const int tiles_s = a.shared ? a.Is / 16 : 0;
-  const int n_sh = tiles_s * ((a.T + GU_SH_PASSES * GU_MT - 1) / (GU_SH_PASSES * GU_MT));
-  const int n_gu = n_sh + a.n_slots * (a.I / 16);
-  const size_t lds_gu = gu_pf_lds(a.H);
-  if ((rc = set_lds(gu_pf_kernel, lds_gu))) return rc;
+  const int n_gu = (a.shared ? (a.Is / GROUP) * ((a.T + GU_MT - 1) / GU_MT) : 0) +
+                   a.n_slots * (a.I / GROUP);
   if (g_prof_start && (rc = record_event(g_prof_start, s))) return rc;
   if (n_gu > 0) {
-    hipLaunchKernelGGL(gu_pf_kernel, dim3(n_gu), dim3(PF_THREADS), lds_gu, s, a);
+    hipLaunchKernelGGL(gu_pf_kernel, dim3(n_gu), dim3(PF_THREADS), 0, s, a);
     QMOE_LAUNCHED();
   }
   if (g_prof_stop && (rc = record_event(g_prof_stop, s))) return rc;
-  const int groups = (a.H / TILE_ROWS + D_TPW - 1) / D_TPW;
-  const int mblk = (a.T + D_SH_PASSES * D_MT - 1) / (D_SH_PASSES * D_MT);
-  const int n_dsh = a.shared ? a.n_sh_chunks * groups * mblk : 0;
-  const int n_d = n_dsh + a.n_slots * groups;
-  int kc = a.I;
-  if (a.shared) {
-    const int ks = a.Is / GROUP;
-    kc = std::max(kc, GROUP * ((ks + a.n_sh_chunks - 1) / a.n_sh_chunks));
-  }
-  const size_t lds_d = d_pf_lds(kc);
-  if ((rc = set_lds(d_pf_kernel, lds_d))) return rc;
+  const int tgroups = (a.H / TILE_ROWS + PF_W - 1) / PF_W;
+  const int n_d = (a.shared ? tgroups * ((a.T + D_MT - 1) / D_MT) : 0) + a.n_slots * tgroups;
   if (n_d > 0) {
-    hipLaunchKernelGGL(d_pf_kernel, dim3(n_d), dim3(PF_THREADS), lds_d, s, a);
+    hipLaunchKernelGGL(d_pf_kernel, dim3(n_d), dim3(PF_THREADS), 0, s, a);
     QMOE_LAUNCHED();
   }
   return QMOE_OK;
 }
 
-static int launch_combine_pf(const uint16_t *x, const float *y, const float *w,
-                             const float *y_sh_part, int nsh, int T, int H, int k, uint16_t *out,
-                             float *out_f32, float *y_sh, hipStream_t s) {
+// Chunks with fewer tokens than this take the VALU kernels (ffn.h): the matrix-core blocks
+// would be mostly padding rows.
+constexpr int PF_MIN_TOKENS = 2;
+static bool valu_ffn(int T) { return T < PF_MIN_TOKENS; }
+
+static int launch_gsum(const uint16_t *x, int T, int H, float *g, hipStream_t s) {
+  const int n = T * (H / GROUP);
+  hipLaunchKernelGGL(gsum_kernel, dim3((n + 255) / 256), dim3(256), 0, s, x, n, g);
+  QMOE_LAUNCHED();
+  return QMOE_OK;
+}
+
+static int launch_combine_pf(const uint16_t *x, const float *y, const float *w, const float *y_sh,
+                             int T, int H, int k, uint16_t *out, float *out_f32, hipStream_t s) {
   const size_t n4 = (size_t)T * H / 4;
   const unsigned blocks = (unsigned)std::min<size_t>((n4 + 255) / 256, 8192);
-  hipLaunchKernelGGL(combine_pf_kernel, dim3(blocks), dim3(256), 0, s, x, y, w, y_sh_part, nsh, T,
-                     H, k, out, out_f32, y_sh);
+  hipLaunchKernelGGL(combine_pf_kernel, dim3(blocks), dim3(256), 0, s, x, y, w, y_sh, T, H, k,
+                     out, out_f32);
   QMOE_LAUNCHED();
   return QMOE_OK;
 }
@@ -595,21 +585,16 @@ int qmoe_expert_ffn(const qmoe_layer *L, const uint16_t *x, int32_t T, const int
   if ((rc = check_arch())) return rc;
   FfnArgs a = make_ffn_args(L, x, T, offsets, sorted, active, n_active, y, y_shared_or_null, ws, T);
   hipStream_t s = (hipStream_t)stream;
-  if (T <= CHUNK_TOKENS && pf_fits(&L->d)) {
-    const bool shp = L->shared && y_shared_or_null;
-    if (!shp) a.shared = nullptr;
-    a.n_sh_chunks = shp ? pf_sh_chunks(&L->d) : 0;
-    if ((rc = launch_pf(a, s))) return rc;
-    if (shp && (rc = launch_combine_pf(x, y, nullptr, a.y_sh_part, a.n_sh_chunks, T,
-                                       L->d.hidden, L->d.top_k, nullptr, nullptr,
-                                       y_shared_or_null, s)))
-      return rc;
+  if (valu_ffn(T)) {
+    if ((rc = launch_gu(a, s))) return rc;
+    const bool sh = L->shared && y_shared_or_null;
+    if (!sh) a.shared = nullptr;
+    if ((rc = launch_d(a, sh, s))) return rc;
     return ok();
   }
-  if ((rc = launch_gu(a, s))) return rc;
-  const bool sh = L->shared && y_shared_or_null;
-  if (!sh) a.shared = nullptr;
-  if ((rc = launch_d(a, sh, s))) return rc;
+  if (!y_shared_or_null) a.shared = nullptr;
+  if ((rc = launch_gsum(x, T, L->d.hidden, at<float>(ws, ws_layout(&L->d, T).gx), s))) return rc;
+  if ((rc = launch_pf(a, s))) return rc;
   return ok();
 }
 
@@ -669,17 +654,17 @@ int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16
                                at<float>(ws, wl.y), nullptr, ws, Tc_max);
     fa.slot_tab = ra.slot_tab;
     ra.n_slots = fa.n_slots;
+    const bool mfma = !valu_ffn(Tc);
+    if (mfma) ra.gsum = at<float>(ws, wl.gx);
     if ((rc = launch_router(ra, router_smem(d, Tc), s))) return rc;
     uint16_t *oc = out + (size_t)c0 * H;
     float *oc32 = out_f32_or_null ? out_f32_or_null + (size_t)c0 * H : nullptr;
-    if (pf_fits(d)) {
+    if (mfma) {
       // kernels 2-4: gate/up, down (matrix cores), combine with the shared rows and residual
+      fa.y_sh = sh ? at<float>(ws, wl.ysh) : nullptr;
       if (!sh) fa.shared = nullptr;
-      fa.n_sh_chunks = sh ? pf_sh_chunks(d) : 0;
       if ((rc = launch_pf(fa, s))) return rc;
-      if ((rc = launch_combine_pf(xc, fa.y, w, fa.y_sh_part, fa.n_sh_chunks, Tc, H, k, oc, oc32,
-                                  nullptr, s)))
-        return rc;
+      if ((rc = launch_combine_pf(xc, fa.y, w, fa.y_sh, Tc, H, k, oc, oc32, s))) return rc;
     } else {
       // VALU kernels: gate/up (routed + shared), down (routed + shared, one chunk), combine
       fa.y_sh = sh ? at<float>(ws, wl.ysh) : nullptr;

@@ -44,6 +44,7 @@ struct RouterArgs {
   // optional fused bucketing (layer path); null counts -> skip
   int32_t *counts, *offsets, *sorted, *active, *n_active;
   int32_t *slot_tab;          // [n_slots][4] {expert, first bucket position, rows, first flat id}
+  float *gsum;                // [T, H/64] sums of every 64-column group of x, or null
   int n_slots;
 };
 
@@ -347,7 +348,7 @@ inline __host__ __device__ size_t router_lds_bytes(int H, int nt = ROUTER_TB) {
   return (size_t)nt * H * 4 + 64;
 }
 
-template <int TB, int EPW>
+template <int TB, int EPW, bool GSUM>
 QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *smem) {
   constexpr int EPB = EPW * ROUTER_WAVES;
   const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
@@ -413,6 +414,17 @@ QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *sme
           ss[i] = fmaf(x3, x3, ss[i]);
           *(float4 *)(z + i * H + 4 * c) =
               float4{x0 * rsv[j].x, x1 * rsv[j].y, x2 * rsv[j].z, x3 * rsv[j].w};
+        }
+        if (GSUM && a.gsum && eb == 0) {
+          // group sums of the raw x: 16 consecutive threads hold one 64-column group
+          float g = 0.f;
+          if (c < n4)
+            g = (bf16lo(xv[i][j].x) + bf16hi(xv[i][j].x)) + (bf16lo(xv[i][j].y) + bf16hi(xv[i][j].y));
+          g += __shfl_xor(g, 1, WAVE);
+          g += __shfl_xor(g, 2, WAVE);
+          g += __shfl_xor(g, 4, WAVE);
+          g += __shfl_xor(g, 8, WAVE);
+          if (c < n4 && (c & 15) == 0) a.gsum[(size_t)(t0 + i) * (H / GROUP) + c / 16] = g;
         }
       }
     }
@@ -524,7 +536,7 @@ QMOE_DEV void router_finish(const RouterArgs &a, int tb, char *smem) {
 __global__ void __launch_bounds__(ROUTER_THREADS) router_kernel(RouterArgs a) {
   extern __shared__ __align__(16) char smem[];
   const int tb = blockIdx.x / a.n_eb, eb = blockIdx.x % a.n_eb;
-  router_logits_block<ROUTER_TB, ROUTER_EPW>(a, tb, eb, smem);
+  router_logits_block<ROUTER_TB, ROUTER_EPW, true>(a, tb, eb, smem);
   router_finish(a, tb, smem);
 }
 
