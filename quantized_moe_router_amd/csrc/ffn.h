@@ -22,14 +22,16 @@ struct FfnArgs {
   int H, I, Is, k, T, n_experts;
   const uint16_t *x;          // [T, H] bf16
   const int32_t *offsets, *sorted, *active, *n_active;
-  int n_slots;                // routed slots in the grid (>= n_active)
+  int n_slots;                // routed slots in the grid: active experts (no slot table) or
+                              //   bucket blocks (slot table)
   uint16_t *hr_hi, *hr_lo;    // routed h [T*k, I] in bucket order
   uint16_t *hs_hi, *hs_lo;    // shared h [T, Is]
   float *y;                   // routed y [T*k, H] by flat id
   float *y_sh;                // shared y [T, H] or null
   const float *gx;            // sums of every 64-column group of x [T, H/64] (matrix-core path)
   float *gh_r, *gh_s;         // the same for h hi + lo: routed [T*k, I/64], shared [T, Is/64]
-  const int32_t *slot_tab;    // [n_slots][4] {expert, first position, rows, first flat id} or null
+  const int32_t *slot_tab;    // [n_slots][4] block table {expert, first position, rows, first
+                              //   flat id or -1} or null
   int n_sh_chunks;            // VALU down kernel: workgroups per tile for the shared block
 };
 

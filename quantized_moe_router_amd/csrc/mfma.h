@@ -4,27 +4,31 @@
 //
 // Operands are exact: the int4 codes become the bf16 values 128 + q (one AND-OR per two
 // codes), activations are bf16 (x) or hi/lo bf16 planes (h).  Per k-step (one 64-input group
-// with scale s and bias b of each weight row) and 32x32 output block:
-//   t   = sum over the group of a * (128 + q)        four v_mfma_f32_32x32x16_bf16
+// with scale s and bias b of each weight row) and 16x16 output block:
+//   t   = sum over the group of a * (128 + q)        v_mfma_f32_16x16x32_bf16, two per
+//                                                     activation plane
 //   acc += s * t                                      one FMA per accumulator (VALU)
-//   acc += (b - 128 s) * sum over the group of a      one v_mfma_f32_32x32x2_f32 (the
-//                                                     group sum in one K entry, 0 in the
-//                                                     other)
-// so the result equals sum (s q + b) a with fp32 accumulation, as in the VALU path.
+//   acc += (b - 128 s) * sum over the group of a      one v_mfma_f32_16x16x4_f32 (the group
+//                                                     sum in K entry 0, zeros in the others)
+// so the result equals sum (s q + b) a with fp32 accumulation, as in the VALU path.  For h the
+// two planes hi and lo go through the same accumulation (the product is linear in a), and
+// the group sum is that of hi + lo.
 //
-// Lane layout (v_mfma_f32_32x32x16_bf16): lane l supplies row (l % 32) of both operands for
-// the 8-element sub-block (l / 32) of each 16-deep K block.  The store's k-step gives lane l
-// the codes of weight row l % 32 for columns 32 (l / 32) + [0, 32), so word j of the lane's
-// 16 bytes is K block j.  Activation rows (tokens) are M and weight rows are N, so every
-// accumulator of a lane belongs to the lane's own weight row and uses its own scale.
-// Accumulator r of lane l holds row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32.
+// Lane layout (v_mfma_f32_16x16x32_bf16): lane l supplies row l % 16 of A and column l % 16
+// of B for K entries 8 (l / 16) + [0, 8); accumulator i of lane l is row 4 (l / 16) + i,
+// column l % 16.  Activation rows (tokens) are M and weight rows are N.  The store's k-step
+// gives lane l the 32 codes of tile row l % 32 for the columns 32 (l / 32) + [0, 32), word j
+// holding columns 8 j + [0, 8) of them.  Four lane swaps (two v_permlane32_swap, two
+// v_permlane16_swap) transpose the 16-lane groups against the four words, after which word
+// G of lane l holds, for tile row 16 (G % 2) + l % 16, the columns 32 (G / 2) + 8 (l / 16) +
+// [0, 8): exactly the B operand of weight block G % 2 for column half G / 2.
 //
-// A wave owns one weight tile and runs over all of its k-steps.  Its activation row is read
-// straight from memory (every wave of a bucket reads the same rows at the same k-steps, so
-// they hit in L1/L2); nothing is staged in LDS.  The bias term needs the sum of each
-// 64-column group of every activation row: for x they are computed once per chunk (by the
-// router pass or gsum_kernel), for h by the gate/up kernel that writes h (the four waves of a
-// gate/up workgroup own exactly one 64-column group of h).
+// A wave owns one weight tile (32 rows) and runs over all of its k-steps; its activation rows
+// are read straight from memory (every wave of a bucket reads the same rows at the same
+// k-steps, so they hit in L1/L2), nothing is staged in LDS.  The bias term needs the sum of
+// each 64-column group of every activation row: for x they are computed once per chunk (by
+// the router pass or gsum_kernel), for h by the gate/up kernel that writes h (the four waves
+// of a gate/up workgroup own exactly one 64-column group of h).
 #pragma once
 #include "common.h"
 #include "store.h"
@@ -32,15 +36,13 @@
 namespace qmoe {
 
 typedef __bf16 qmoe_bf16x8 __attribute__((ext_vector_type(8)));
-typedef float qmoe_f32x16 __attribute__((ext_vector_type(16)));
+typedef float qmoe_f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int PF_W = 4;                 // waves per workgroup
 constexpr int PF_THREADS = PF_W * WAVE;
-constexpr int PF_KB = 3;                // k-steps per load batch of a wave
-constexpr int GU_MT = 32;               // rows per gate/up pass (MFMA rows)
-constexpr int D_MT = 16;                // tokens per down pass (hi + lo planes: 32 MFMA rows)
-
-QMOE_DEV int mfma_row(int lane, int r) { return 8 * (r / 4) + 4 * (lane / 32) + (r % 4); }
+constexpr int PF_MT = 16;               // activation rows per pass (MFMA rows)
+constexpr int GU_KB = 4;                // k-steps per load batch: gate/up (one plane)
+constexpr int D_KB = 3;                 //                          down (hi and lo planes)
 
 // B operand: the 8 codes of word w as bf16 (128 + q), element order
 QMOE_DEV qmoe_bf16x8 q4_operand(uint32_t w) {
@@ -48,82 +50,103 @@ QMOE_DEV qmoe_bf16x8 q4_operand(uint32_t w) {
   return __builtin_bit_cast(qmoe_bf16x8, v);
 }
 
-// One k-step: t = A (128 + q) on the matrix cores, acc += s t, then acc += (b - 128 s) G with
-// G the group sum of the lane's activation row (given by half-0 lanes, 0 by the others, so
-// the K = 2 product adds it once).
-QMOE_DEV void pf_kstep(qmoe_f32x16 &acc, const qmoe_u32x4 (&xa)[4], qmoe_u32x4 cv, float g,
-                       uint32_t sb) {
-  qmoe_f32x16 t = {};
-  t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(qmoe_bf16x8, xa[0]),
-                                              q4_operand(cv.x), t, 0, 0, 0);
-  t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(qmoe_bf16x8, xa[1]),
-                                              q4_operand(cv.y), t, 0, 0, 0);
-  t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(qmoe_bf16x8, xa[2]),
-                                              q4_operand(cv.z), t, 0, 0, 0);
-  t = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(qmoe_bf16x8, xa[3]),
-                                              q4_operand(cv.w), t, 0, 0, 0);
-  const float s = bf16lo(sb), c = fmaf(-128.f, s, bf16hi(sb));
-#pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = fmaf(s, t[r], acc[r]);
-  acc = __builtin_amdgcn_mfma_f32_32x32x2f32(g, c, acc, 0, 0, 0);
+QMOE_DEV qmoe_f32x4 mfma16(qmoe_u32x4 a, uint32_t w, qmoe_f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(qmoe_bf16x8, a),
+                                                 q4_operand(w), c, 0, 0, 0);
 }
 
-// PF_KB consecutive k-steps from ks0 (or, with TAIL, the ones below nks; the loads past
-// the end re-read the last k-step and are not used), all loads issued before any product.
-template <bool TAIL>
-QMOE_DEV void pf_batch(qmoe_f32x16 &acc, const uint8_t *tbase, int ks0, int nks,
-                       const uint16_t *arow, const float *grow, bool gmask) {
-  const int lane = threadIdx.x % WAVE, rr = lane % 32;
-  qmoe_u32x4 cv[PF_KB], xa[PF_KB][4];
-  uint32_t sb[PF_KB];
-  float g[PF_KB];
+// One k-step of a 32-row tile: acc0 (tile rows 0..15) and acc1 (rows 16..31) for the 16
+// activation rows.  xa[p][h]: plane p, column half h of the lane's row; s0/s1: scale|bias of
+// the lane's column in each block; g: group sum of the lane's row (used where gmask).
+template <int NP>
+QMOE_DEV void pf_kstep(qmoe_f32x4 &acc0, qmoe_f32x4 &acc1, qmoe_u32x4 cv,
+                       const qmoe_u32x4 (&xa)[NP][2], uint32_t s0, uint32_t s1, float g,
+                       bool gmask) {
+  const auto x02 = __builtin_amdgcn_permlane32_swap(cv.x, cv.z, false, false);
+  const auto x13 = __builtin_amdgcn_permlane32_swap(cv.y, cv.w, false, false);
+  const auto y01 = __builtin_amdgcn_permlane16_swap(x02[0], x13[0], false, false);
+  const auto y23 = __builtin_amdgcn_permlane16_swap(x02[1], x13[1], false, false);
+  qmoe_f32x4 t0 = {}, t1 = {};
 #pragma unroll
-  for (int u = 0; u < PF_KB; ++u) {
+  for (int p = 0; p < NP; ++p) {
+    t0 = mfma16(xa[p][0], y01[0], t0);
+    t1 = mfma16(xa[p][0], y01[1], t1);
+    t0 = mfma16(xa[p][1], y23[0], t0);
+    t1 = mfma16(xa[p][1], y23[1], t1);
+  }
+  const float sc0 = bf16lo(s0), c0 = fmaf(-128.f, sc0, bf16hi(s0));
+  const float sc1 = bf16lo(s1), c1 = fmaf(-128.f, sc1, bf16hi(s1));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc0[i] = fmaf(sc0, t0[i], acc0[i]);
+    acc1[i] = fmaf(sc1, t1[i], acc1[i]);
+  }
+  const float gv = gmask ? g : 0.f;
+  acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(gv, c0, acc0, 0, 0, 0);
+  acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(gv, c1, acc1, 0, 0, 0);
+}
+
+// KB consecutive k-steps from ks0 (with TAIL only those below nks; the loads past the end
+// re-read the last k-step and are not used), all loads issued before any product.  ap[p]:
+// the lane's row of plane p, offset to its 8-column piece (k-step ks, half h at
+// ap[p] + 64 ks + 32 h); grow: the row's group sums.
+template <int NP, int KB, bool TAIL>
+QMOE_DEV void pf_batch(qmoe_f32x4 &acc0, qmoe_f32x4 &acc1, const uint8_t *tbase, int ks0,
+                       int nks, const uint16_t *const (&ap)[NP], const float *grow, bool gmask) {
+  const int lane = threadIdx.x % WAVE, n = lane % 16;
+  qmoe_u32x4 cv[KB], xa[KB][NP][2];
+  uint32_t s0[KB], s1[KB];
+  float g[KB];
+#pragma unroll
+  for (int u = 0; u < KB; ++u) {
     const int ks = TAIL ? min(ks0 + u, nks - 1) : ks0 + u;
     const uint8_t *st = tbase + (size_t)ks * KSTEP_BYTES;
     cv[u] = *(const qmoe_u32x4 *)(st + 16 * lane);
-    sb[u] = *(const uint32_t *)(st + 1024 + 4 * rr);
+    s0[u] = *(const uint32_t *)(st + 1024 + 4 * n);
+    s1[u] = *(const uint32_t *)(st + 1024 + 64 + 4 * n);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xa[u][j] = *(const qmoe_u32x4 *)(arow + GROUP * ks + 8 * j);
+    for (int p = 0; p < NP; ++p) {
+      xa[u][p][0] = *(const qmoe_u32x4 *)(ap[p] + GROUP * ks);
+      xa[u][p][1] = *(const qmoe_u32x4 *)(ap[p] + GROUP * ks + 32);
+    }
     g[u] = grow[ks];
   }
 #pragma unroll
-  for (int u = 0; u < PF_KB; ++u)
-    if (!TAIL || ks0 + u < nks) pf_kstep(acc, xa[u], cv[u], gmask ? g[u] : 0.f, sb[u]);
+  for (int u = 0; u < KB; ++u)
+    if (!TAIL || ks0 + u < nks) pf_kstep<NP>(acc0, acc1, cv[u], xa[u], s0[u], s1[u], g[u], gmask);
 }
 
-// All nks k-steps of the tile at tbase.  arow: the lane's activation row, offset to its half
-// (k-step ks covers columns 64 ks + 32 half + [0, 32)); grow: the row's group sums, used
-// where gmask is set (a padding lane reads a valid row; its MFMA rows are not used).
-QMOE_DEV qmoe_f32x16 pf_tile(const uint8_t *tbase, int nks, const uint16_t *arow,
-                             const float *grow, bool gmask) {
-  qmoe_f32x16 acc = {};
+template <int NP, int KB>
+QMOE_DEV void pf_tile(qmoe_f32x4 &acc0, qmoe_f32x4 &acc1, const uint8_t *tbase, int nks,
+                      const uint16_t *const (&ap)[NP], const float *grow, bool gmask) {
+  acc0 = qmoe_f32x4{0.f, 0.f, 0.f, 0.f};
+  acc1 = qmoe_f32x4{0.f, 0.f, 0.f, 0.f};
   int k0 = 0;
-  for (; k0 + PF_KB <= nks; k0 += PF_KB) pf_batch<false>(acc, tbase, k0, nks, arow, grow, gmask);
-  if (k0 < nks) pf_batch<true>(acc, tbase, k0, nks, arow, grow, gmask);
-  return acc;
+  for (; k0 + KB <= nks; k0 += KB) pf_batch<NP, KB, false>(acc0, acc1, tbase, k0, nks, ap, grow, gmask);
+  if (k0 < nks) pf_batch<NP, KB, true>(acc0, acc1, tbase, k0, nks, ap, grow, gmask);
 }
 
 // ---------------------------------------------------------------- gate/up + SwiGLU
-// grid: shared workgroups first (h group, block of GU_MT tokens), then routed (slot, h group).
-// Wave w computes tile 4 group + w (h columns 16 tile .. + 15); a routed workgroup loops over
-// its bucket GU_MT rows at a time.  Lanes with n = lane % 32 < 16 hold gate row 16 tile + n,
-// the others the matching up row.  h = silu(gate) up goes to the hi/lo planes (routed rows in
-// bucket order), and the group sums of hi + lo to gh_r / gh_s.
+// grid: shared workgroups first (h group, block of PF_MT tokens), then routed (slot, h
+// group).  Wave w computes tile 4 group + w: gate rows 16 tile + [0, 16) in acc0 and the
+// matching up rows in acc1, so lane l holds gate and up of the same (row, h column
+// 16 tile + l % 16).  A routed workgroup loops over its bucket PF_MT rows at a time.
+// h = silu(gate) up goes to the hi/lo planes (routed rows in bucket order), and the group
+// sums of hi + lo to gh_r / gh_s.
 __global__ void __launch_bounds__(PF_THREADS) gu_pf_kernel(FfnArgs a) {
-  __shared__ float gpart[PF_W][GU_MT];
+  __shared__ float gpart[PF_W][PF_MT];
   const int H = a.H, KS = H / GROUP;
-  const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE, n = lane % 32, half = lane / 32;
+  const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE, n = lane % 16, lg = lane / 16;
   const int grp_s = a.shared ? a.Is / GROUP : 0;
-  const int n_sh = grp_s * ((a.T + GU_MT - 1) / GU_MT);
+  const int n_sh = grp_s * ((a.T + PF_MT - 1) / PF_MT);
   int bid = blockIdx.x;
   SlotRows sr;
   int grp, m0, m1;
   if (bid < n_sh) {
     slot_rows(a, 0, true, sr);
     grp = bid % grp_s;
-    m0 = (bid / grp_s) * GU_MT;
-    m1 = min(a.T, m0 + GU_MT);
+    m0 = (bid / grp_s) * PF_MT;
+    m1 = min(a.T, m0 + PF_MT);
   } else {
     bid -= n_sh;
     const int grp_r = a.I / GROUP;
@@ -139,39 +162,39 @@ __global__ void __launch_bounds__(PF_THREADS) gu_pf_kernel(FfnArgs a) {
   uint16_t *hlo = sr.shared ? a.hs_lo : a.hr_lo;
   float *gh = sr.shared ? a.gh_s : a.gh_r;
   const int pos0 = sr.shared ? 0 : sr.beg;
-  for (int p0 = m0; p0 < m1; p0 += GU_MT) {
-    const int mt = min(GU_MT, m1 - p0);
-    const int i = min(n, mt - 1);  // padding lanes repeat the last row
-    const int tok = sr.shared ? p0 + i : flat_of(a, sr, p0 + i) / a.k;
-    const qmoe_f32x16 acc = pf_tile(tbase, KS, a.x + (size_t)tok * H + 32 * half,
-                                    a.gx + (size_t)tok * KS, half == 0);
-    float hs[16];
+  for (int p0 = m0; p0 < m1; p0 += PF_MT) {
+    const int mt = min(PF_MT, m1 - p0);
+    const int r = min(n, mt - 1);  // padding lanes repeat the last row
+    const int tok = sr.shared ? p0 + r : flat_of(a, sr, p0 + r) / a.k;
+    const uint16_t *const ap[1] = {a.x + (size_t)tok * H + 8 * lg};
+    qmoe_f32x4 gate, up;
+    pf_tile<1, GU_KB>(gate, up, tbase, KS, ap, a.gx + (size_t)tok * KS, lg == 0);
+    float hs[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float up = __shfl_xor(acc[r], 16, WAVE);
-      const int m = mfma_row(lane, r);
-      hs[r] = 0.f;
-      if (n < 16 && m < mt) {
-        const float h = silu(acc[r]) * up;
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * lg + i;
+      hs[i] = 0.f;
+      if (m < mt) {
+        const float h = silu(gate[i]) * up[i];
         const uint32_t hi = f32_to_bf16_bits(h);
         const uint32_t lo = f32_to_bf16_bits(h - __uint_as_float(hi << 16));
         const size_t row = (size_t)(pos0 + p0 + m);
         hhi[row * I + 16 * tile + n] = (uint16_t)hi;
         hlo[row * I + 16 * tile + n] = (uint16_t)lo;
-        hs[r] = __uint_as_float(hi << 16) + __uint_as_float(lo << 16);
+        hs[i] = __uint_as_float(hi << 16) + __uint_as_float(lo << 16);
       }
     }
-    // group sums: over the 16 gate lanes of each half, then over the four waves
+    // group sums: over the 16 lanes of each lane group, then over the four waves
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      hs[r] += __shfl_xor(hs[r], 1, WAVE);
-      hs[r] += __shfl_xor(hs[r], 2, WAVE);
-      hs[r] += __shfl_xor(hs[r], 4, WAVE);
-      hs[r] += __shfl_xor(hs[r], 8, WAVE);
+    for (int i = 0; i < 4; ++i) {
+      hs[i] += __shfl_xor(hs[i], 1, WAVE);
+      hs[i] += __shfl_xor(hs[i], 2, WAVE);
+      hs[i] += __shfl_xor(hs[i], 4, WAVE);
+      hs[i] += __shfl_xor(hs[i], 8, WAVE);
     }
     if (n == 0) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) gpart[wv][mfma_row(lane, r)] = hs[r];
+      for (int i = 0; i < 4; ++i) gpart[wv][4 * lg + i] = hs[i];
     }
     __syncthreads();
     if ((int)threadIdx.x < mt) {
@@ -184,23 +207,22 @@ __global__ void __launch_bounds__(PF_THREADS) gu_pf_kernel(FfnArgs a) {
 }
 
 // ---------------------------------------------------------------- down projection
-// grid: shared workgroups first (tile group, block of D_MT tokens), then routed (slot, tile
-// group).  Wave w computes output tile 4 group + w (32 rows of H) over all of K.  MFMA rows
-// 0..15 are D_MT tokens' h hi planes, rows 16..31 their lo planes; a token's output is the
-// sum of its two rows, accumulators r and r + 8 of the same lane.  Routed rows go to y by
-// flat assignment id, shared rows to y_sh.
+// grid: shared workgroups first (tile group, block of PF_MT tokens), then routed (slot, tile
+// group).  Wave w computes output tile 4 group + w (32 rows of H: acc0 rows 0..15, acc1 rows
+// 16..31) over all of K, with the h hi and lo planes of PF_MT tokens as the activation rows.
+// Routed rows go to y by flat assignment id, shared rows to y_sh.
 __global__ void __launch_bounds__(PF_THREADS) d_pf_kernel(FfnArgs a) {
   const int H = a.H, tiles = H / TILE_ROWS, tgroups = (tiles + PF_W - 1) / PF_W;
-  const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE, rr = lane % 32, half = lane / 32;
-  const int n_sh = a.shared ? tgroups * ((a.T + D_MT - 1) / D_MT) : 0;
+  const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE, n = lane % 16, lg = lane / 16;
+  const int n_sh = a.shared ? tgroups * ((a.T + PF_MT - 1) / PF_MT) : 0;
   int bid = blockIdx.x;
   SlotRows sr;
   int tg, m0, m1;
   if (bid < n_sh) {
     slot_rows(a, 0, true, sr);
     tg = bid % tgroups;
-    m0 = (bid / tgroups) * D_MT;
-    m1 = min(a.T, m0 + D_MT);
+    m0 = (bid / tgroups) * PF_MT;
+    m1 = min(a.T, m0 + PF_MT);
   } else {
     bid -= n_sh;
     if (!slot_rows(a, bid / tgroups, false, sr)) return;
@@ -212,46 +234,53 @@ __global__ void __launch_bounds__(PF_THREADS) d_pf_kernel(FfnArgs a) {
   if (tile >= tiles) return;  // no barrier in this kernel
   const int K = sr.shared ? a.Is : a.I, KSd = K / GROUP;
   const uint8_t *tbase = sr.blk + block_geom(H, K).gu_bytes + (size_t)tile * KSd * KSTEP_BYTES;
-  const uint16_t *src = rr < 16 ? (sr.shared ? a.hs_hi : a.hr_hi) : (sr.shared ? a.hs_lo : a.hr_lo);
+  const uint16_t *phi = sr.shared ? a.hs_hi : a.hr_hi;
+  const uint16_t *plo = sr.shared ? a.hs_lo : a.hr_lo;
   const float *gh = sr.shared ? a.gh_s : a.gh_r;
   const int pos0 = sr.shared ? 0 : sr.beg;
-  for (int p0 = m0; p0 < m1; p0 += D_MT) {
-    const int mt = min(D_MT, m1 - p0);
-    const int tok = min(rr % 16, mt - 1);  // padding lanes repeat the last row
-    const size_t pos = (size_t)(pos0 + p0 + tok);
-    const qmoe_f32x16 acc = pf_tile(tbase, KSd, src + pos * K + 32 * half, gh + pos * KSd,
-                                    rr < 16 && half == 0);
+  for (int p0 = m0; p0 < m1; p0 += PF_MT) {
+    const int mt = min(PF_MT, m1 - p0);
+    const size_t pos = (size_t)(pos0 + p0 + min(n, mt - 1));  // padding lanes repeat the last row
+    const uint16_t *const ap[2] = {phi + pos * K + 8 * lg, plo + pos * K + 8 * lg};
+    qmoe_f32x4 y0, y1;
+    pf_tile<2, D_KB>(y0, y1, tbase, KSd, ap, gh + pos * KSd, lg == 0);
     int flat = 0;
     if (!sr.shared && lane < mt) flat = flat_of(a, sr, p0 + lane);
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int m = mfma_row(lane, r);
+    for (int i = 0; i < 4; ++i) {
+      const int m = 4 * lg + i;
       const int fm = __shfl(flat, m, WAVE);
       if (m < mt) {
-        const float yv = acc[r] + acc[r + 8];
-        if (sr.shared)
-          a.y_sh[(size_t)(p0 + m) * H + TILE_ROWS * tile + rr] = yv;
-        else
-          a.y[(size_t)fm * H + TILE_ROWS * tile + rr] = yv;
+        float *dst = sr.shared ? a.y_sh + (size_t)(p0 + m) * H : a.y + (size_t)fm * H;
+        dst[TILE_ROWS * tile + n] = y0[i];
+        dst[TILE_ROWS * tile + 16 + n] = y1[i];
       }
     }
   }
 }
 
 // Sums of every 64-element group of x [T, H] (n_groups = T H / 64), the gate/up bias term's
-// operand, where no router pass has produced them.
+// operand, where no router pass has produced them.  The sum is the balanced pairwise tree
+// over the 64 elements, the order the router pass uses, so both give the same bits.
 __global__ void __launch_bounds__(256) gsum_kernel(const uint16_t *x, int n_groups, float *g) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n_groups) return;
   const qmoe_u32x4 *p = (const qmoe_u32x4 *)(x + (size_t)i * GROUP);
-  float s = 0.f;
+  float v[32];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const qmoe_u32x4 v = p[j];
-    s += (bf16lo(v.x) + bf16hi(v.x)) + (bf16lo(v.y) + bf16hi(v.y)) +
-         (bf16lo(v.z) + bf16hi(v.z)) + (bf16lo(v.w) + bf16hi(v.w));
+    const qmoe_u32x4 w = p[j];
+    v[4 * j + 0] = bf16lo(w.x) + bf16hi(w.x);
+    v[4 * j + 1] = bf16lo(w.y) + bf16hi(w.y);
+    v[4 * j + 2] = bf16lo(w.z) + bf16hi(w.z);
+    v[4 * j + 3] = bf16lo(w.w) + bf16hi(w.w);
   }
-  g[i] = s;
+#pragma unroll
+  for (int w = 16; w >= 1; w /= 2) {
+#pragma unroll
+    for (int j = 0; j < w; ++j) v[j] = v[2 * j] + v[2 * j + 1];
+  }
+  g[i] = v[0];
 }
 
 // out[t, :] = bf16( x[t, :] + sum_j w[t,j] y[t*k+j, :] + y_sh[t, :] ) in fp32, j ascending,

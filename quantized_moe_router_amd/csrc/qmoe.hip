@@ -150,7 +150,7 @@ WsLayout ws_layout(const qmoe_dims *d, int Tmax) {
   w.sorted = o; o += al(T * k * 4);
   w.active = o; o += al(E * 4);
   w.nact = o; o += al(4);
-  w.slot_tab = o; o += al(E * 16);
+  w.slot_tab = o; o += al((size_t)bucket_max_blocks((int)(Tc * k), (int)E) * 16);
   w.hr_hi = o; o += al(T * k * d->inter * 2);
   w.hr_lo = o; o += al(T * k * d->inter * 2);
   w.hs_hi = o; o += al(T * (size_t)d->shared_inter * 2);
@@ -255,6 +255,7 @@ int launch_router(const RouterArgs &a, size_t smem, hipStream_t s) {
   return QMOE_OK;
 }
 
+static_assert(BUCKET_BLOCK_ROWS == PF_MT, "one matrix-core pass per bucket block");
 static_assert((size_t)(DEC_SYNC_WORD + SY_LINES * SY_LINE) * 4 <= COUNTER_BYTES,
               "decode sync area inside the counter area");
 
@@ -353,7 +354,7 @@ static int launch_d(FfnArgs a, bool with_shared, hipStream_t s) {
 // bracket the gate/up kernel.
 static int launch_pf(const FfnArgs &a, hipStream_t s) {
   int rc;
-  const int n_gu = (a.shared ? (a.Is / GROUP) * ((a.T + GU_MT - 1) / GU_MT) : 0) +
+  const int n_gu = (a.shared ? (a.Is / GROUP) * ((a.T + PF_MT - 1) / PF_MT) : 0) +
                    a.n_slots * (a.I / GROUP);
   if (g_prof_start && (rc = record_event(g_prof_start, s))) return rc;
   if (n_gu > 0) {
@@ -362,7 +363,7 @@ static int launch_pf(const FfnArgs &a, hipStream_t s) {
   }
   if (g_prof_stop && (rc = record_event(g_prof_stop, s))) return rc;
   const int tgroups = (a.H / TILE_ROWS + PF_W - 1) / PF_W;
-  const int n_d = (a.shared ? tgroups * ((a.T + D_MT - 1) / D_MT) : 0) + a.n_slots * tgroups;
+  const int n_d = (a.shared ? tgroups * ((a.T + PF_MT - 1) / PF_MT) : 0) + a.n_slots * tgroups;
   if (n_d > 0) {
     hipLaunchKernelGGL(d_pf_kernel, dim3(n_d), dim3(PF_THREADS), 0, s, a);
     QMOE_LAUNCHED();
@@ -653,6 +654,7 @@ int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16
     FfnArgs fa = make_ffn_args(L, xc, Tc, ra.offsets, ra.sorted, ra.active, ra.n_active,
                                at<float>(ws, wl.y), nullptr, ws, Tc_max);
     fa.slot_tab = ra.slot_tab;
+    fa.n_slots = bucket_max_blocks(Tc * k, d->n_experts);
     ra.n_slots = fa.n_slots;
     const bool mfma = !valu_ffn(Tc);
     if (mfma) ra.gsum = at<float>(ws, wl.gx);

@@ -43,7 +43,8 @@ struct RouterArgs {
   int n_tb, n_eb;             // token blocks, expert blocks
   // optional fused bucketing (layer path); null counts -> skip
   int32_t *counts, *offsets, *sorted, *active, *n_active;
-  int32_t *slot_tab;          // [n_slots][4] {expert, first bucket position, rows, first flat id}
+  int32_t *slot_tab;          // [n_slots][4] block table {expert, first bucket position, rows,
+                              //   first flat id or -1} (bucket_offsets)
   float *gsum;                // [T, H/64] sums of every 64-column group of x, or null
   int n_slots;
 };
@@ -142,67 +143,83 @@ QMOE_DEV void topk_wave(const float *lrow, int E, int k, const float *pes, uint6
 // ---------------------------------------------------------------- bucketing (one workgroup)
 // Stable counting sort of N = T*k assignments by expert (ids outside [0, E) are dropped):
 // position of assignment f = (first position of its expert) + (number of assignments f' < f
-// with the same expert).  Optionally also writes the slot table used by the expert kernels:
-// entry s = {expert, first bucket position, rows, first flat id} of the s-th active expert,
-// zero rows for s in [n_active, n_slots).  get(f) returns the expert id of assignment f.
+// with the same expert).  Optionally also writes the block table used by the expert kernels
+// (bucket_offsets).  get(f) returns the expert id of assignment f.
 
-// Per-expert totals -> counts, offsets, active list, slot table; cnt[e] becomes the expert's
-// first position.  first[e]: smallest flat id of the expert.
+// Per-expert totals -> counts, offsets, active list, block table; cnt[e] becomes the
+// expert's first position.  first[e]: smallest flat id of the expert.  The block table cuts
+// the rows of every active expert, in expert order, into blocks of BUCKET_BLOCK_ROWS: entry b
+// = {expert, bucket position of the block's first row, rows, flat id of that row for the
+// expert's first block, else -1}; entries from the number of blocks up to n_slots have zero
+// rows.
+constexpr int BUCKET_BLOCK_ROWS = 16;
+inline __host__ __device__ int bucket_max_blocks(int N, int E) {
+  return N / BUCKET_BLOCK_ROWS + (N < E ? N : E);
+}
+
 template <int NT>
 QMOE_DEV void bucket_offsets(int *cnt, const int *first, int E, int32_t *counts, int32_t *offsets,
                              int32_t *active, int32_t *n_active, int32_t *slot_tab, int n_slots) {
-  constexpr int NW = NT / WAVE;
+  constexpr int NW = NT / WAVE, BB = BUCKET_BLOCK_ROWS;
   const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
-  // exclusive scan of counts and of (count > 0) flags, E <= MAX_EXPERTS
+  // exclusive scan of (rows, blocks, active flags) packed as rows << 40 | blocks << 20 | flags
+  // (at most 2^21 assignments), E <= MAX_EXPERTS
   const int per = (E + NT - 1) / NT;
   const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
-  int s_cnt = 0, s_act = 0;
-  for (int e = e0; e < e1; ++e) { s_cnt += cnt[e]; s_act += cnt[e] > 0; }
-  // inclusive wave scan of the pair (count total in the high bits, active flags in the low 16)
-  long long pair = ((long long)s_cnt << 16) | s_act;
+  long long own = 0;
+  for (int e = e0; e < e1; ++e) {
+    const long long c = cnt[e];
+    own += (c << 40) | (((c + BB - 1) / BB) << 20) | (c > 0 ? 1 : 0);
+  }
+  long long pack = own;
   for (int o = 1; o < WAVE; o <<= 1) {
-    const long long up = __shfl_up(pair, o, WAVE);
-    if (lane >= o) pair += up;
+    const long long up = __shfl_up(pack, o, WAVE);
+    if (lane >= o) pack += up;
   }
   __shared__ long long wtot[NW];
-  if (lane == WAVE - 1) wtot[wv] = pair;
+  if (lane == WAVE - 1) wtot[wv] = pack;
   __syncthreads();
   long long before = 0, tot = 0;
   for (int w = 0; w < NW; ++w) {
     if (w < wv) before += wtot[w];
     tot += wtot[w];
   }
-  long long excl = before + pair - (((long long)s_cnt << 16) | s_act);
-  int run_cnt = (int)(excl >> 16), run_act = (int)(excl & 0xFFFF);
+  const long long excl = before + pack - own;
+  int run_cnt = (int)(excl >> 40), run_blk = (int)((excl >> 20) & 0xFFFFF),
+      run_act = (int)(excl & 0xFFFFF);
   for (int e = e0; e < e1; ++e) {
     const int c = cnt[e];
     counts[e] = c;
     offsets[e] = run_cnt;
     if (c > 0) {
       active[run_act] = e;
-      if (slot_tab && run_act < n_slots)
-        *(qmoe_u32x4 *)(slot_tab + 4 * run_act) =
-            qmoe_u32x4{(uint32_t)e, (uint32_t)run_cnt, (uint32_t)c, (uint32_t)first[e]};
+      if (slot_tab)
+        for (int b = 0; b * BB < c && run_blk + b < n_slots; ++b)
+          *(qmoe_u32x4 *)(slot_tab + 4 * (run_blk + b)) =
+              qmoe_u32x4{(uint32_t)e, (uint32_t)(run_cnt + b * BB), (uint32_t)min(BB, c - b * BB),
+                         b == 0 ? (uint32_t)first[e] : 0xFFFFFFFFu};
+      run_blk += (c + BB - 1) / BB;
       ++run_act;
     }
     cnt[e] = run_cnt;
     run_cnt += c;
   }
-  const int na = (int)(tot & 0xFFFF);
+  const int na = (int)(tot & 0xFFFFF), nb = (int)((tot >> 20) & 0xFFFFF);
   if (tid == NT - 1) {
-    offsets[E] = (int)(tot >> 16);
+    offsets[E] = (int)(tot >> 40);
     *n_active = na;
   }
   if (slot_tab)
-    for (int sl = na + tid; sl < n_slots; sl += NT)
+    for (int sl = nb + tid; sl < n_slots; sl += NT)
       *(qmoe_u32x4 *)(slot_tab + 4 * sl) = qmoe_u32x4{0u, 0u, 0u, 0u};
   __syncthreads();
 }
 
 // Segmented form, for up to BUCKET_SEG_N assignments with segments x experts <=
 // BUCKET_SEG_CELLS: the assignments are cut into 64-long segments (one wave each); an
-// assignment's rank among the same expert's earlier ones is its rank inside its segment (64
-// broadcast compares) plus the expert's counts in the earlier segments (a prefix per expert).
+// assignment's rank among the same expert's earlier ones is its rank inside its segment (one
+// ballot per bit of the expert id) plus the expert's counts in the earlier segments (a prefix
+// per expert).
 // Every step is parallel.  lds: bucket_lds_bytes(N, E).
 constexpr int BUCKET_SEG_N = 4096, BUCKET_SEG_CELLS = 16384;
 inline __host__ __device__ bool bucket_seg_ok(int N, int E) {
@@ -241,18 +258,24 @@ QMOE_DEV void bucket_block_seg(Get get, int N, int E, int32_t *counts, int32_t *
     }
   }
   __syncthreads();
+  // lanes of a segment with the same expert: AND over the id bits of the ballot of that bit
+  // (or of its complement), restricted to valid lanes
+  const int bits = 32 - __builtin_clz((unsigned)max(E - 1, 1));
   for (int sg = wv; sg < S; sg += NW) {
     const int f = sg * WAVE + lane;
     const int e = (f < N) ? er[f] : -1;
     const bool valid = (f < N) && ((unsigned)e < (unsigned)E);
-    int rank = 0;
-    const int *seg = er + sg * WAVE;
-    const int n = min(WAVE, N - sg * WAVE);
-    for (int j = 0; j < n; ++j) rank += (j < lane && seg[j] == e) ? 1 : 0;
-    __builtin_amdgcn_wave_barrier();
+    unsigned long long same = __ballot(valid);
+    for (int b = 0; b < bits; ++b) {
+      const bool set = (e >> b) & 1;
+      const unsigned long long m = __ballot(set);
+      same &= set ? m : ~m;
+    }
+    const int rank = __popcll(same & ((1ull << lane) - 1ull));
     if (f < N) er[f] = valid ? ((e << 8) | rank) : -1;
-    if (valid) {
-      atomicAdd(&cnt[sg * E + e], 1);
+    if (valid && rank == 0) {
+      // the first lane of each expert in the segment holds its count and smallest flat id
+      cnt[sg * E + e] = __popcll(same);
       atomicMin(&first[e], f);
     }
   }
@@ -416,7 +439,8 @@ QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *sme
               float4{x0 * rsv[j].x, x1 * rsv[j].y, x2 * rsv[j].z, x3 * rsv[j].w};
         }
         if (GSUM && a.gsum && eb == 0) {
-          // group sums of the raw x: 16 consecutive threads hold one 64-column group
+          // group sums of the raw x: 16 consecutive threads hold one 64-column group (a
+          // balanced pairwise tree over its 64 elements)
           float g = 0.f;
           if (c < n4)
             g = (bf16lo(xv[i][j].x) + bf16hi(xv[i][j].x)) + (bf16lo(xv[i][j].y) + bf16hi(xv[i][j].y));
