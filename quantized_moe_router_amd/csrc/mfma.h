@@ -23,9 +23,10 @@
 // G of lane l holds, for tile row 16 (G % 2) + l % 16, the columns 32 (G / 2) + 8 (l / 16) +
 // [0, 8): exactly the B operand of weight block G % 2 for column half G / 2.
 //
-// A wave owns one weight tile (32 rows) and runs over all of its k-steps; its activation rows
-// are read straight from memory (every wave of a bucket reads the same rows at the same
-// k-steps, so they hit in L1/L2), nothing is staged in LDS.  The bias term needs the sum of
+// A wave owns a few weight tiles (32 rows each) and runs over all of their k-steps, so one
+// load of its activation rows serves all of them; the rows are read straight from memory
+// (every wave of a bucket reads the same rows at the same k-steps, so they hit in L1/L2),
+// nothing is staged in LDS.  The bias term needs the sum of
 // each 64-column group of every activation row: for x they are computed once per chunk (by
 // the router pass or gsum_kernel), for h by the gate/up kernel that writes h (the four waves
 // of a gate/up workgroup own exactly one 64-column group of h).
@@ -38,11 +39,13 @@ namespace qmoe {
 typedef __bf16 qmoe_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float qmoe_f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int PF_W = 4;                 // waves per workgroup
-constexpr int PF_THREADS = PF_W * WAVE;
 constexpr int PF_MT = 16;               // activation rows per pass (MFMA rows)
-constexpr int GU_KB = 4;                // k-steps per load batch: gate/up (one plane)
-constexpr int D_KB = 3;                 //                          down (hi and lo planes)
+constexpr int GU_NT = 2;                // gate/up: tiles per wave (a workgroup of 2 waves owns
+constexpr int GU_WAVES = 4 / GU_NT;     //   the 4 tiles of one 64-column group of h)
+constexpr int GU_KB = 2;                //   k-steps per load batch
+constexpr int D_NT = 2;                 // down: tiles per wave
+constexpr int D_WAVES = 4;              //   waves per workgroup
+constexpr int D_KB = 2;                 //   k-steps per load batch
 
 // B operand: the 8 codes of word w as bf16 (128 + q), element order
 QMOE_DEV qmoe_bf16x8 q4_operand(uint32_t w) {
@@ -55,55 +58,62 @@ QMOE_DEV qmoe_f32x4 mfma16(qmoe_u32x4 a, uint32_t w, qmoe_f32x4 c) {
                                                  q4_operand(w), c, 0, 0, 0);
 }
 
-// One k-step of a 32-row tile: acc0 (tile rows 0..15) and acc1 (rows 16..31) for the 16
-// activation rows.  xa[p][h]: plane p, column half h of the lane's row; s0/s1: scale|bias of
-// the lane's column in each block; g: group sum of the lane's row (used where gmask).
-template <int NP>
-QMOE_DEV void pf_kstep(qmoe_f32x4 &acc0, qmoe_f32x4 &acc1, qmoe_u32x4 cv,
-                       const qmoe_u32x4 (&xa)[NP][2], uint32_t s0, uint32_t s1, float g,
+// One k-step of NT 32-row tiles against the wave's 16 activation rows: acc[j][0] (tile j rows
+// 0..15) and acc[j][1] (rows 16..31).  xa[p][h]: plane p, column half h of the lane's row;
+// sb[j][b]: scale|bias of the lane's column in block b of tile j; g: group sum of the lane's
+// row (used where gmask).
+template <int NP, int NT>
+QMOE_DEV void pf_kstep(qmoe_f32x4 (&acc)[NT][2], const qmoe_u32x4 (&cv)[NT],
+                       const qmoe_u32x4 (&xa)[NP][2], const uint32_t (&sb)[NT][2], float g,
                        bool gmask) {
-  const auto x02 = __builtin_amdgcn_permlane32_swap(cv.x, cv.z, false, false);
-  const auto x13 = __builtin_amdgcn_permlane32_swap(cv.y, cv.w, false, false);
-  const auto y01 = __builtin_amdgcn_permlane16_swap(x02[0], x13[0], false, false);
-  const auto y23 = __builtin_amdgcn_permlane16_swap(x02[1], x13[1], false, false);
-  qmoe_f32x4 t0 = {}, t1 = {};
-#pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    t0 = mfma16(xa[p][0], y01[0], t0);
-    t1 = mfma16(xa[p][0], y01[1], t1);
-    t0 = mfma16(xa[p][1], y23[0], t0);
-    t1 = mfma16(xa[p][1], y23[1], t1);
-  }
-  const float sc0 = bf16lo(s0), c0 = fmaf(-128.f, sc0, bf16hi(s0));
-  const float sc1 = bf16lo(s1), c1 = fmaf(-128.f, sc1, bf16hi(s1));
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    acc0[i] = fmaf(sc0, t0[i], acc0[i]);
-    acc1[i] = fmaf(sc1, t1[i], acc1[i]);
-  }
   const float gv = gmask ? g : 0.f;
-  acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(gv, c0, acc0, 0, 0, 0);
-  acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(gv, c1, acc1, 0, 0, 0);
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const auto x02 = __builtin_amdgcn_permlane32_swap(cv[j].x, cv[j].z, false, false);
+    const auto x13 = __builtin_amdgcn_permlane32_swap(cv[j].y, cv[j].w, false, false);
+    const auto y01 = __builtin_amdgcn_permlane16_swap(x02[0], x13[0], false, false);
+    const auto y23 = __builtin_amdgcn_permlane16_swap(x02[1], x13[1], false, false);
+    qmoe_f32x4 t0 = {}, t1 = {};
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      t0 = mfma16(xa[p][0], y01[0], t0);
+      t1 = mfma16(xa[p][0], y01[1], t1);
+      t0 = mfma16(xa[p][1], y23[0], t0);
+      t1 = mfma16(xa[p][1], y23[1], t1);
+    }
+    const float sc0 = bf16lo(sb[j][0]), c0 = fmaf(-128.f, sc0, bf16hi(sb[j][0]));
+    const float sc1 = bf16lo(sb[j][1]), c1 = fmaf(-128.f, sc1, bf16hi(sb[j][1]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[j][0][i] = fmaf(sc0, t0[i], acc[j][0][i]);
+      acc[j][1][i] = fmaf(sc1, t1[i], acc[j][1][i]);
+    }
+    acc[j][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(gv, c0, acc[j][0], 0, 0, 0);
+    acc[j][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(gv, c1, acc[j][1], 0, 0, 0);
+  }
 }
 
-// KB consecutive k-steps from ks0 (with TAIL only those below nks; the loads past the end
-// re-read the last k-step and are not used), all loads issued before any product.  ap[p]:
-// the lane's row of plane p, offset to its 8-column piece (k-step ks, half h at
-// ap[p] + 64 ks + 32 h); grow: the row's group sums.
-template <int NP, int KB, bool TAIL>
-QMOE_DEV void pf_batch(qmoe_f32x4 &acc0, qmoe_f32x4 &acc1, const uint8_t *tbase, int ks0,
-                       int nks, const uint16_t *const (&ap)[NP], const float *grow, bool gmask) {
+// KB consecutive k-steps from ks0 of NT tiles (tile j at tb[j]) (with TAIL only those below
+// nks; the loads past the end re-read the last k-step and are not used), all loads issued
+// before any product.  ap[p]: the lane's row of plane p, offset to its 8-column piece
+// (k-step ks, half h at ap[p] + 64 ks + 32 h); grow: the row's group sums.
+template <int NP, int NT, int KB, bool TAIL>
+QMOE_DEV void pf_batch(qmoe_f32x4 (&acc)[NT][2], const uint8_t *const (&tb)[NT], int ks0, int nks,
+                       const uint16_t *const (&ap)[NP], const float *grow, bool gmask) {
   const int lane = threadIdx.x % WAVE, n = lane % 16;
-  qmoe_u32x4 cv[KB], xa[KB][NP][2];
-  uint32_t s0[KB], s1[KB];
+  qmoe_u32x4 cv[KB][NT], xa[KB][NP][2];
+  uint32_t sb[KB][NT][2];
   float g[KB];
 #pragma unroll
   for (int u = 0; u < KB; ++u) {
     const int ks = TAIL ? min(ks0 + u, nks - 1) : ks0 + u;
-    const uint8_t *st = tbase + (size_t)ks * KSTEP_BYTES;
-    cv[u] = *(const qmoe_u32x4 *)(st + 16 * lane);
-    s0[u] = *(const uint32_t *)(st + 1024 + 4 * n);
-    s1[u] = *(const uint32_t *)(st + 1024 + 64 + 4 * n);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const uint8_t *st = tb[j] + (size_t)ks * KSTEP_BYTES;
+      cv[u][j] = *(const qmoe_u32x4 *)(st + 16 * lane);
+      sb[u][j][0] = *(const uint32_t *)(st + 1024 + 4 * n);
+      sb[u][j][1] = *(const uint32_t *)(st + 1024 + 64 + 4 * n);
+    }
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
       xa[u][p][0] = *(const qmoe_u32x4 *)(ap[p] + GROUP * ks);
@@ -113,28 +123,32 @@ QMOE_DEV void pf_batch(qmoe_f32x4 &acc0, qmoe_f32x4 &acc1, const uint8_t *tbase,
   }
 #pragma unroll
   for (int u = 0; u < KB; ++u)
-    if (!TAIL || ks0 + u < nks) pf_kstep<NP>(acc0, acc1, cv[u], xa[u], s0[u], s1[u], g[u], gmask);
+    if (!TAIL || ks0 + u < nks) pf_kstep<NP, NT>(acc, cv[u], xa[u], sb[u], g[u], gmask);
 }
 
-template <int NP, int KB>
-QMOE_DEV void pf_tile(qmoe_f32x4 &acc0, qmoe_f32x4 &acc1, const uint8_t *tbase, int nks,
-                      const uint16_t *const (&ap)[NP], const float *grow, bool gmask) {
-  acc0 = qmoe_f32x4{0.f, 0.f, 0.f, 0.f};
-  acc1 = qmoe_f32x4{0.f, 0.f, 0.f, 0.f};
+template <int NP, int NT, int KB>
+QMOE_DEV void pf_tiles(qmoe_f32x4 (&acc)[NT][2], const uint8_t *const (&tb)[NT], int nks,
+                       const uint16_t *const (&ap)[NP], const float *grow, bool gmask) {
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    acc[j][0] = qmoe_f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[j][1] = qmoe_f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   int k0 = 0;
-  for (; k0 + KB <= nks; k0 += KB) pf_batch<NP, KB, false>(acc0, acc1, tbase, k0, nks, ap, grow, gmask);
-  if (k0 < nks) pf_batch<NP, KB, true>(acc0, acc1, tbase, k0, nks, ap, grow, gmask);
+  for (; k0 + KB <= nks; k0 += KB) pf_batch<NP, NT, KB, false>(acc, tb, k0, nks, ap, grow, gmask);
+  if (k0 < nks) pf_batch<NP, NT, KB, true>(acc, tb, k0, nks, ap, grow, gmask);
 }
 
 // ---------------------------------------------------------------- gate/up + SwiGLU
 // grid: shared workgroups first (h group, block of PF_MT tokens), then routed (slot, h
-// group).  Wave w computes tile 4 group + w: gate rows 16 tile + [0, 16) in acc0 and the
-// matching up rows in acc1, so lane l holds gate and up of the same (row, h column
-// 16 tile + l % 16).  A routed workgroup loops over its bucket PF_MT rows at a time.
-// h = silu(gate) up goes to the hi/lo planes (routed rows in bucket order), and the group
-// sums of hi + lo to gh_r / gh_s.
-__global__ void __launch_bounds__(PF_THREADS) gu_pf_kernel(FfnArgs a) {
-  __shared__ float gpart[PF_W][PF_MT];
+// group); a workgroup of GU_WAVES waves owns the four tiles of one 64-column group of h, wave
+// w the tiles 4 group + GU_NT w + j.  Tile j's gate rows 16 tile + [0, 16) are acc[j][0] and
+// the matching up rows acc[j][1], so lane l holds gate and up of the same (row, h column
+// 16 tile + l % 16).  A workgroup loops over its rows PF_MT at a time.  h = silu(gate) up goes
+// to the hi/lo planes (routed rows in bucket order), and the group sums of hi + lo to gh_r /
+// gh_s.
+__global__ void __launch_bounds__(GU_WAVES * WAVE) gu_pf_kernel(FfnArgs a) {
+  __shared__ float gpart[GU_WAVES][PF_MT];
   const int H = a.H, KS = H / GROUP;
   const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE, n = lane % 16, lg = lane / 16;
   const int grp_s = a.shared ? a.Is / GROUP : 0;
@@ -156,8 +170,10 @@ __global__ void __launch_bounds__(PF_THREADS) gu_pf_kernel(FfnArgs a) {
     m1 = sr.m;
   }
   const int I = sr.shared ? a.Is : a.I, KI = I / GROUP;
-  const int tile = PF_W * grp + wv;
-  const uint8_t *tbase = sr.blk + (size_t)tile * KS * KSTEP_BYTES;
+  const int tile0 = 4 * grp + GU_NT * wv;
+  const uint8_t *tb[GU_NT];
+#pragma unroll
+  for (int j = 0; j < GU_NT; ++j) tb[j] = sr.blk + (size_t)(tile0 + j) * KS * KSTEP_BYTES;
   uint16_t *hhi = sr.shared ? a.hs_hi : a.hr_hi;
   uint16_t *hlo = sr.shared ? a.hs_lo : a.hr_lo;
   float *gh = sr.shared ? a.gh_s : a.gh_r;
@@ -167,24 +183,26 @@ __global__ void __launch_bounds__(PF_THREADS) gu_pf_kernel(FfnArgs a) {
     const int r = min(n, mt - 1);  // padding lanes repeat the last row
     const int tok = sr.shared ? p0 + r : flat_of(a, sr, p0 + r) / a.k;
     const uint16_t *const ap[1] = {a.x + (size_t)tok * H + 8 * lg};
-    qmoe_f32x4 gate, up;
-    pf_tile<1, GU_KB>(gate, up, tbase, KS, ap, a.gx + (size_t)tok * KS, lg == 0);
-    float hs[4];
+    qmoe_f32x4 acc[GU_NT][2];
+    pf_tiles<1, GU_NT, GU_KB>(acc, tb, KS, ap, a.gx + (size_t)tok * KS, lg == 0);
+    float hs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 4 * lg + i;
-      hs[i] = 0.f;
-      if (m < mt) {
-        const float h = silu(gate[i]) * up[i];
-        const uint32_t hi = f32_to_bf16_bits(h);
-        const uint32_t lo = f32_to_bf16_bits(h - __uint_as_float(hi << 16));
-        const size_t row = (size_t)(pos0 + p0 + m);
-        hhi[row * I + 16 * tile + n] = (uint16_t)hi;
-        hlo[row * I + 16 * tile + n] = (uint16_t)lo;
-        hs[i] = __uint_as_float(hi << 16) + __uint_as_float(lo << 16);
+    for (int j = 0; j < GU_NT; ++j) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * lg + i;
+        if (m < mt) {
+          const float h = silu(acc[j][0][i]) * acc[j][1][i];
+          const uint32_t hi = f32_to_bf16_bits(h);
+          const uint32_t lo = f32_to_bf16_bits(h - __uint_as_float(hi << 16));
+          const size_t at = (size_t)(pos0 + p0 + m) * I + 16 * (tile0 + j) + n;
+          hhi[at] = (uint16_t)hi;
+          hlo[at] = (uint16_t)lo;
+          hs[i] += __uint_as_float(hi << 16) + __uint_as_float(lo << 16);
+        }
       }
     }
-    // group sums: over the 16 lanes of each lane group, then over the four waves
+    // group sums: over the 16 lanes of each lane group, then over the waves
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       hs[i] += __shfl_xor(hs[i], 1, WAVE);
@@ -199,8 +217,10 @@ __global__ void __launch_bounds__(PF_THREADS) gu_pf_kernel(FfnArgs a) {
     __syncthreads();
     if ((int)threadIdx.x < mt) {
       const int m = threadIdx.x;
-      gh[(size_t)(pos0 + p0 + m) * KI + grp] =
-          (gpart[0][m] + gpart[1][m]) + (gpart[2][m] + gpart[3][m]);
+      float t = 0.f;
+#pragma unroll
+      for (int w = 0; w < GU_WAVES; ++w) t += gpart[w][m];
+      gh[(size_t)(pos0 + p0 + m) * KI + grp] = t;
     }
     __syncthreads();
   }
@@ -208,11 +228,12 @@ __global__ void __launch_bounds__(PF_THREADS) gu_pf_kernel(FfnArgs a) {
 
 // ---------------------------------------------------------------- down projection
 // grid: shared workgroups first (tile group, block of PF_MT tokens), then routed (slot, tile
-// group).  Wave w computes output tile 4 group + w (32 rows of H: acc0 rows 0..15, acc1 rows
-// 16..31) over all of K, with the h hi and lo planes of PF_MT tokens as the activation rows.
-// Routed rows go to y by flat assignment id, shared rows to y_sh.
-__global__ void __launch_bounds__(PF_THREADS) d_pf_kernel(FfnArgs a) {
-  const int H = a.H, tiles = H / TILE_ROWS, tgroups = (tiles + PF_W - 1) / PF_W;
+// group); a tile group is D_WAVES * D_NT output tiles, wave w computing D_NT of them (32 rows
+// of H each: acc[j][0] rows 0..15, acc[j][1] rows 16..31) over all of K, with the h hi and lo
+// planes of PF_MT tokens as the activation rows.  Routed rows go to y by flat assignment id,
+// shared rows to y_sh.
+__global__ void __launch_bounds__(D_WAVES * WAVE) d_pf_kernel(FfnArgs a) {
+  const int H = a.H, tiles = H / TILE_ROWS, tgroups = (tiles + D_WAVES * D_NT - 1) / (D_WAVES * D_NT);
   const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE, n = lane % 16, lg = lane / 16;
   const int n_sh = a.shared ? tgroups * ((a.T + PF_MT - 1) / PF_MT) : 0;
   int bid = blockIdx.x;
@@ -230,10 +251,14 @@ __global__ void __launch_bounds__(PF_THREADS) d_pf_kernel(FfnArgs a) {
     m0 = 0;
     m1 = sr.m;
   }
-  const int tile = PF_W * tg + wv;
-  if (tile >= tiles) return;  // no barrier in this kernel
+  const int tile0 = (D_WAVES * tg + wv) * D_NT;
+  if (tile0 >= tiles) return;  // no barrier in this kernel
   const int K = sr.shared ? a.Is : a.I, KSd = K / GROUP;
-  const uint8_t *tbase = sr.blk + block_geom(H, K).gu_bytes + (size_t)tile * KSd * KSTEP_BYTES;
+  const uint8_t *dbase = sr.blk + block_geom(H, K).gu_bytes;
+  const uint8_t *tb[D_NT];
+#pragma unroll
+  for (int j = 0; j < D_NT; ++j)  // tiles past the end re-read the last one (not stored)
+    tb[j] = dbase + (size_t)min(tile0 + j, tiles - 1) * KSd * KSTEP_BYTES;
   const uint16_t *phi = sr.shared ? a.hs_hi : a.hr_hi;
   const uint16_t *plo = sr.shared ? a.hs_lo : a.hr_lo;
   const float *gh = sr.shared ? a.gh_s : a.gh_r;
@@ -242,8 +267,8 @@ __global__ void __launch_bounds__(PF_THREADS) d_pf_kernel(FfnArgs a) {
     const int mt = min(PF_MT, m1 - p0);
     const size_t pos = (size_t)(pos0 + p0 + min(n, mt - 1));  // padding lanes repeat the last row
     const uint16_t *const ap[2] = {phi + pos * K + 8 * lg, plo + pos * K + 8 * lg};
-    qmoe_f32x4 y0, y1;
-    pf_tile<2, D_KB>(y0, y1, tbase, KSd, ap, gh + pos * KSd, lg == 0);
+    qmoe_f32x4 acc[D_NT][2];
+    pf_tiles<2, D_NT, D_KB>(acc, tb, KSd, ap, gh + pos * KSd, lg == 0);
     int flat = 0;
     if (!sr.shared && lane < mt) flat = flat_of(a, sr, p0 + lane);
 #pragma unroll
@@ -252,8 +277,13 @@ __global__ void __launch_bounds__(PF_THREADS) d_pf_kernel(FfnArgs a) {
       const int fm = __shfl(flat, m, WAVE);
       if (m < mt) {
         float *dst = sr.shared ? a.y_sh + (size_t)(p0 + m) * H : a.y + (size_t)fm * H;
-        dst[TILE_ROWS * tile + n] = y0[i];
-        dst[TILE_ROWS * tile + 16 + n] = y1[i];
+#pragma unroll
+        for (int j = 0; j < D_NT; ++j) {
+          if (tile0 + j < tiles) {
+            dst[TILE_ROWS * (tile0 + j) + n] = acc[j][0][i];
+            dst[TILE_ROWS * (tile0 + j) + 16 + n] = acc[j][1][i];
+          }
+        }
       }
     }
   }

@@ -358,14 +358,14 @@ static int launch_pf(const FfnArgs &a, hipStream_t s) {
                    a.n_slots * (a.I / GROUP);
   if (g_prof_start && (rc = record_event(g_prof_start, s))) return rc;
   if (n_gu > 0) {
-    hipLaunchKernelGGL(gu_pf_kernel, dim3(n_gu), dim3(PF_THREADS), 0, s, a);
+    hipLaunchKernelGGL(gu_pf_kernel, dim3(n_gu), dim3(GU_WAVES * WAVE), 0, s, a);
     QMOE_LAUNCHED();
   }
   if (g_prof_stop && (rc = record_event(g_prof_stop, s))) return rc;
-  const int tgroups = (a.H / TILE_ROWS + PF_W - 1) / PF_W;
+  const int tgroups = (a.H / TILE_ROWS + D_WAVES * D_NT - 1) / (D_WAVES * D_NT);
   const int n_d = (a.shared ? tgroups * ((a.T + PF_MT - 1) / PF_MT) : 0) + a.n_slots * tgroups;
   if (n_d > 0) {
-    hipLaunchKernelGGL(d_pf_kernel, dim3(n_d), dim3(PF_THREADS), 0, s, a);
+    hipLaunchKernelGGL(d_pf_kernel, dim3(n_d), dim3(D_WAVES * WAVE), 0, s, a);
     QMOE_LAUNCHED();
   }
   return QMOE_OK;
