@@ -12,5 +12,6 @@ brute force, textbook special cases and hand-built fixtures (tests/golden).
 from .qmoe_oracle import (  # noqa: F401
     EPS, bf16_to_f64, bf16_rne_bits, unpack_nibbles, dequant, dequant_int4,
     dequant_int8, rmsnorm_no_scale, router_logits, topk_select, topk_weights,
-    router, bucket, expert_ffn, combine, layer_forward, near_tie_mask,
+    router, bucket, expert_ffn, combine, post_combine, combine_post, layer_forward,
+    near_tie_mask,
 )

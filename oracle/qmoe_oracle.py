@@ -25,8 +25,13 @@ project's design notes):
   * The expert FFN is SwiGLU: h = silu(x W_g^T) * (x W_u^T), y = h W_d^T,
     silu(z) = z / (1 + exp(-z)); no biases.  The shared expert uses the same
     form and format and is added with weight 1.
-  * The layer output is x + shared + sum_j w_j y_j; the post-combine norm and
-    layer scalar of cb2 are not part of this layer.
+  * The layer output is x + m with m = shared + sum_j w_j y_j.  When a layer
+    carries cb2's post-combine steps, they run in the order the post lists
+    them -- normalisation, residual, layer scalar:
+        out = (x + gain * m / sqrt(mean(m^2) + 1e-6)) * scalar
+    (RMS over the hidden axis, a per-channel gain multiplying the normalised
+    value directly, one scalar per layer).  Without a gain the norm step is
+    skipped; without a scalar it is 1.
   * Top-k order: descending logit; exact ties go to the lower expert index.
   * Optional per-expert logit bias (absent on the pages) is added to the
     logits before top-k and enters the softmax.
@@ -212,13 +217,42 @@ def combine(x_bits, y_routed, w, y_shared):
     return out, bf16_rne_bits(out)
 
 
+def post_combine(x_bits, m, gain=None, scalar=None, eps=EPS):
+    """cb2's last steps on the combined branches m [T, H] (fp64): normalisation, residual,
+    layer scalar, in that order ([TF-struct] cb2).
+
+        n   = gain * m / sqrt(mean_h(m^2) + eps)     (gain None: n = m, no norm)
+        out = (x + n) * scalar                       (scalar None: 1)
+    Returns the fp64 result and its bf16 rounding.
+    """
+    x = bf16_to_f64(x_bits)
+    m = np.asarray(m, np.float64)
+    n = m
+    if gain is not None:
+        rms = np.sqrt(np.mean(m * m, axis=-1, keepdims=True) + eps)
+        n = np.asarray(gain, np.float64) * (m / rms)
+    out = x + n
+    if scalar is not None:
+        out = out * float(scalar)
+    return out, bf16_rne_bits(out)
+
+
+def combine_post(x_bits, y_routed, w, y_shared, gain=None, scalar=None, eps=EPS):
+    """m = y_shared + sum_j w_j y_routed_j, then post_combine (fp64)."""
+    m = np.einsum("tk,tkh->th", np.asarray(w, np.float64), np.asarray(y_routed, np.float64))
+    if y_shared is not None:
+        m = m + y_shared
+    return post_combine(x_bits, m, gain, scalar, eps)
+
+
 # ------------------------------------------------------------------ whole layer
 
 def layer_forward(x_bits, layer, k, eps=EPS, top_override=None):
     """One routed MoE layer on bf16 input rows x_bits [T, H].
 
     ``layer`` provides router_q/s/b, router_scale, pes, bias, expert(e) and
-    shared() (or None for no shared expert).  ``top_override`` replaces the
+    shared() (or None for no shared expert), and optionally post_gain [H] and
+    layer_scalar for cb2's post-combine steps.  ``top_override`` replaces the
     router's selection (used to re-evaluate near-tied tokens with another
     valid selection); the weights are then recomputed from the logits.
     Returns a dict of every intermediate.
@@ -241,6 +275,10 @@ def layer_forward(x_bits, layer, k, eps=EPS, top_override=None):
         h_rows[int(e)] = he
     sh = layer.shared() if hasattr(layer, "shared") else None
     y_sh = expert_ffn(x, sh) if sh is not None else None
-    out64, out_bf16 = combine(x_bits, y.reshape(T, k, H), w, y_sh)
+    gain, scalar = getattr(layer, "post_gain", None), getattr(layer, "layer_scalar", None)
+    if gain is None and scalar is None:
+        out64, out_bf16 = combine(x_bits, y.reshape(T, k, H), w, y_sh)
+    else:
+        out64, out_bf16 = combine_post(x_bits, y.reshape(T, k, H), w, y_sh, gain, scalar, eps)
     return dict(logits=logits, top=top, w=w, counts=counts, offsets=offsets, sorted=sorted_ids,
                 active=active, y=y, y_shared=y_sh, h=h_rows, out=out64, out_bf16=out_bf16)

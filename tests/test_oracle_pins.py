@@ -307,6 +307,73 @@ def test_combine_closed_form():
     assert np.array_equal(O.bf16_to_f64(out_b[0]), np.array(d["out"]))
 
 
+# ------------------------------------------------------------------ post-combine steps (cb2)
+
+def _post_case():
+    d = {p[0]: [float(v) for v in p[1:]] for p in golden_lines("post_combine_example.txt")}
+    xb = O.bf16_rne_bits(np.array([d["x"]]))
+    y = np.array([[d["y0"]]])
+    return d, xb, y
+
+
+def test_post_combine_hand_example():
+    """Order (norm of the combined branches, then residual, then scalar) and the gain."""
+    d, xb, y = _post_case()
+    out, out_b = O.combine_post(xb, y, np.array([d["w"]]), np.array([d["yshared"]]),
+                                np.array(d["gain"]), d["scalar"][0])
+    assert np.allclose(out[0], d["out"], rtol=1e-15, atol=0)
+    assert np.array_equal(out_b, O.bf16_rne_bits(out))
+
+
+def test_post_combine_without_steps_is_combine():
+    d, xb, y = _post_case()
+    a, ab = O.combine_post(xb, y, np.array([d["w"]]), np.array([d["yshared"]]))
+    b, bb = O.combine(xb, y, np.array([d["w"]]), np.array([d["yshared"]]))
+    assert np.array_equal(a, b) and np.array_equal(ab, bb)
+
+
+def test_post_norm_unit_gain_has_unit_rms():
+    """gain 1, scalar 1: the added term has RMS sqrt(ms / (ms + eps)) over the hidden axis."""
+    rng = np.random.default_rng(7)
+    T, H = 5, 256
+    xb = O.bf16_rne_bits(rng.standard_normal((T, H)))
+    m = rng.standard_normal((T, H)) * np.array([[0.01], [0.1], [1.0], [10.0], [100.0]])
+    out, _ = O.post_combine(xb, m, np.ones(H), None)
+    added = out - O.bf16_to_f64(xb)
+    ms = np.mean(m * m, axis=1)
+    want = np.sqrt(ms / (ms + O.EPS))
+    assert np.allclose(np.sqrt(np.mean(added * added, axis=1)), want, rtol=1e-12)
+
+
+def test_post_norm_scale_invariance_and_scalar_linearity():
+    rng = np.random.default_rng(8)
+    T, H = 3, 128
+    xb = O.bf16_rne_bits(rng.standard_normal((T, H)))
+    m = rng.standard_normal((T, H))
+    g = 1.0 + 0.1 * rng.standard_normal(H)
+    a, _ = O.post_combine(xb, m, g, None)
+    b, _ = O.post_combine(xb, 1000.0 * m, g, None, eps=1e6 * O.EPS)   # scale m by c, eps by c^2
+    assert np.allclose(a, b, rtol=1e-13, atol=1e-14)
+    c1, _ = O.post_combine(xb, m, g, 1.0)
+    c3, _ = O.post_combine(xb, m, g, 0.75)
+    assert np.allclose(c3, 0.75 * c1, rtol=1e-15, atol=0)
+    z, _ = O.post_combine(xb, m, np.zeros(H), 0.5)       # zero gain: scaled residual only
+    assert np.array_equal(z, 0.5 * O.bf16_to_f64(xb))
+
+
+def test_layer_forward_post_steps_match_post_combine():
+    cfg = G.config("tiny")
+    li = G.make_layer_small(cfg, 0)
+    xb = G.make_hidden(cfg, 0)
+    plain = O.layer_forward(xb, li, cfg.top_k)
+    li.post_gain, li.layer_scalar = G.make_post(cfg, 0)
+    post = O.layer_forward(xb, li, cfg.top_k)
+    m = plain["out"] - O.bf16_to_f64(xb)
+    want, _ = O.post_combine(xb, m, li.post_gain, li.layer_scalar)
+    assert np.array_equal(post["top"], plain["top"])
+    assert np.allclose(post["out"], want, rtol=1e-12, atol=1e-12)
+
+
 def test_zero_input_routes_to_first_k_experts():
     cfg = G.config("tiny")
     li = G.make_layer_small(cfg, 0)

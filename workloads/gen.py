@@ -46,6 +46,8 @@ class Tag:
     PES = 2
     HIDDEN = 3
     ZIPF = 4
+    POST_GAIN = 5
+    POST_SCALAR = 6
     SHARED = 8          # + 0 gate, 1 up, 2 down
     EXPERT = 16         # + 3*e + m, m: 0 gate, 1 up, 2 down
 
@@ -284,6 +286,15 @@ def make_router(cfg, layer):
     pes = uniform_f32(layer_key(cfg, layer), Tag.PES, E, cfg.pes_lo, cfg.pes_hi)
     bias = zipf_bias(cfg, layer) if cfg.zipf_s else None
     return LayerInputs(cfg, layer, q, s, b, np.ones(H, np.float32), pes, bias)
+
+
+def make_post(cfg, layer):
+    """Post-combine norm gain (fp32 [H], 1 + N(0, 0.1^2)) and layer scalar (fp32,
+    U(0.5, 1.0)) of one layer."""
+    g = normal_f32(layer_key(cfg, layer), Tag.POST_GAIN, cfg.hidden, 0.1)
+    gain = (np.float32(1.0) + g).astype(np.float32)
+    scalar = uniform_f32(layer_key(cfg, layer), Tag.POST_SCALAR, 1, 0.5, 1.0)[0]
+    return gain, np.float32(scalar)
 
 
 def make_hidden(cfg, step, tokens=None, std=None):
