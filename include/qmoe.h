@@ -101,11 +101,16 @@ typedef struct {
     const void *experts;     /* base of E blocks, block e at experts + e * expert_stride */
     size_t expert_stride;    /* >= qmoe_expert_stride(&d, d.inter), multiple of 256 */
     const void *shared;      /* one block packed with inter = shared_inter, or NULL */
+    /* cb2's post-combine steps ([TF-struct] cb2: normalisation, residual, layer scalar), both
+     * optional; with both NULL the layer ends at the residual add. */
+    const float *post_norm_gain; /* [H] fp32 (16-byte aligned) gain of the RMS norm of the
+                                    combined branches, or NULL: no norm */
+    const float *layer_scalar;   /* [1] fp32 multiplier of the layer output, or NULL: 1 */
 } qmoe_layer;
 
 /* ---------------------------------------------------------------- host-only queries */
 
-/* Library ABI version (major*10000 + minor*100 + patch). */
+/* Library ABI version (major*10000 + minor*100 + patch): 200 = 0.2.0. */
 int qmoe_version(void);
 
 /* Thread-local text of the last error (empty string if none). Never NULL. */
@@ -199,19 +204,34 @@ int qmoe_combine(const qmoe_dims *d, const uint16_t *x, const float *y, const fl
                  const float *y_shared_or_null, int32_t T, uint16_t *out,
                  float *out_f32_or_null, qmoe_stream_t stream);
 
-/* The whole layer (steps 1-4) with no host round trip.  A one-token call runs as a single
- * launch whose workgroups take the roles router, shared gate/up, routed gate/up, shared down
- * and routed down, handing data to each other through the workspace (each role starts loading
- * its weights as soon as it knows them).  Larger calls run as three launches:
- *   kernel 1: router logits, then (last workgroup) top-k, softmax and bucketing, while other
- *             workgroups of the same launch run the shared expert's gate/up projection;
- *   kernel 2: routed gate/up projection + SwiGLU over the buckets;
- *   kernel 3: routed and shared down projection; the last workgroup of each output row tile
- *             adds the router-weighted routed rows, the shared row and the residual.
+/* Step 4 with cb2's post-combine steps ([TF-struct] cb2, in the order listed there:
+ * normalisation, residual, layer scalar):
+ *   m[t, :]   = y_shared[t] + sum_j topk_w[t, j] * y[t*k + j]         (fp32, j ascending, then
+ *                                                                      the shared branch)
+ *   n[t, :]   = gain * m[t] / sqrt(mean(m[t]^2) + 1e-6)                (gain NULL: n = m)
+ *   out[t, :] = bf16_rne( (x[t] + n[t]) * layer_scalar )               (layer_scalar NULL: 1)
+ * gain: fp32 [H], 16-byte aligned; layer_scalar: fp32 [1]; both device pointers.  With both
+ * NULL the result equals qmoe_combine's bit for bit. */
+int qmoe_combine_post(const qmoe_dims *d, const uint16_t *x, const float *y, const float *topk_w,
+                      const float *y_shared_or_null, const float *post_norm_gain_or_null,
+                      const float *layer_scalar_or_null, int32_t T, uint16_t *out,
+                      float *out_f32_or_null, qmoe_stream_t stream);
+
+/* The whole layer (steps 1-4, plus the layer's post-combine steps when it carries them) with
+ * no host round trip.  A one-token call runs as a single launch whose workgroups take the
+ * roles router, shared gate/up, routed gate/up, shared down and routed down, handing data to
+ * each other through the workspace (each role starts loading its weights as soon as it knows
+ * them); the routed-down workgroups of the last slot combine.  Larger calls run per chunk of
+ * at most 128 tokens as four launches:
+ *   kernel 1: router logits and the 64-column group sums of x, then (last workgroups) top-k,
+ *             softmax and bucketing into a table of 16-row blocks;
+ *   kernel 2: routed and shared gate/up projection + SwiGLU on the matrix cores;
+ *   kernel 3: routed and shared down projection on the matrix cores;
+ *   kernel 4: combine (qmoe_combine / qmoe_combine_post arithmetic).
  * out: bf16 [T, H]; out_f32_or_null: fp32 [T, H]; topk_idx_or_null / topk_w_or_null receive
  * the routing ([T, k]).  Results equal qmoe_router_topk -> qmoe_bucket -> qmoe_expert_ffn ->
- * qmoe_combine up to fp32 summation order.  T may exceed 128; callers that follow the pages'
- * chunked prefill pass chunks of at most 128 tokens. */
+ * qmoe_combine_post up to fp32 summation order.  T may exceed 128; callers that follow the
+ * pages' chunked prefill pass chunks of at most 128 tokens. */
 int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16_t *out,
                        float *out_f32_or_null, int32_t *topk_idx_or_null,
                        float *topk_w_or_null, void *ws, size_t ws_bytes,

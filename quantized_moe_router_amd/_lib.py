@@ -15,7 +15,7 @@ ERRORS = {-1: "QMOE_ERR_ARG", -2: "QMOE_ERR_SHAPE", -3: "QMOE_ERR_WORKSPACE",
 EXPORTS = [
     "qmoe_version", "qmoe_last_error", "qmoe_expert_stride", "qmoe_workspace_bytes",
     "qmoe_workspace_init", "qmoe_pack_expert", "qmoe_unpack_expert", "qmoe_router_topk",
-    "qmoe_bucket", "qmoe_expert_ffn", "qmoe_combine", "qmoe_layer_forward",
+    "qmoe_bucket", "qmoe_expert_ffn", "qmoe_combine", "qmoe_combine_post", "qmoe_layer_forward",
     "qmoe_event_create", "qmoe_event_destroy", "qmoe_event_record", "qmoe_event_elapsed_ms",
     "qmoe_set_profile_events", "qmoe_workspace_status",
 ]
@@ -41,7 +41,8 @@ class Router(ctypes.Structure):
 
 class Layer(ctypes.Structure):
     _fields_ = [("d", Dims), ("r", Router), ("experts", ctypes.c_void_p),
-                ("expert_stride", ctypes.c_size_t), ("shared", ctypes.c_void_p)]
+                ("expert_stride", ctypes.c_size_t), ("shared", ctypes.c_void_p),
+                ("post_norm_gain", ctypes.c_void_p), ("layer_scalar", ctypes.c_void_p)]
 
 
 _lib = None
@@ -72,6 +73,7 @@ def lib():
         "qmoe_bucket": (ctypes.c_int, [pd, P, I32, P, P, P, P, P, P, SZ, P]),
         "qmoe_expert_ffn": (ctypes.c_int, [ctypes.POINTER(Layer), P, I32, P, P, P, P, P, P, P, SZ, P]),
         "qmoe_combine": (ctypes.c_int, [pd, P, P, P, P, I32, P, P, P]),
+        "qmoe_combine_post": (ctypes.c_int, [pd, P, P, P, P, P, P, I32, P, P, P]),
         "qmoe_layer_forward": (ctypes.c_int, [ctypes.POINTER(Layer), P, I32, P, P, P, P, P, SZ, P]),
         "qmoe_event_create": (ctypes.c_int, [ctypes.POINTER(ctypes.c_void_p)]),
         "qmoe_event_destroy": (ctypes.c_int, [P]),

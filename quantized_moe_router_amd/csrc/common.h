@@ -16,6 +16,7 @@ constexpr int KSTEP_BYTES = 1152;  // one k-step of a 32-row tile: 1024 B codes 
 constexpr int TILE_ROWS = 32;      // rows per store tile
 constexpr int MAX_TOPK = 32;
 constexpr int MAX_EXPERTS = 1024;
+constexpr float RMS_EPS = 1e-6f;   // epsilon of every RMS norm of the layer
 constexpr int CHUNK_TOKENS = 128;  // layer_forward processes at most this many tokens per pass
 
 // ---------------------------------------------------------------- bf16 <-> fp32

@@ -68,13 +68,17 @@ struct DecodeArgs {
   float *topk_w;                // [k]
   uint16_t *out;                // [H]
   float *out_f32;               // [H] or null
+  const float *gain;            // [H] post-combine norm gain, or null (no norm)
+  const float *lscale;          // [1] layer scalar, or null (1)
+  uint64_t *nrm;                // [combining workgroups] tagged partial sums of m^2
+  uint64_t *mrow;               // [H] tagged combined branches m (post-combine norm only)
   int nR, nSG, nRG, nSD, nRD;
 };
 
 // LDS map (bytes) shared by every role: [top-k ranking][per-expert scales][reduction]
 // [union: staged x | staged h + combine rows]
 struct DecLds {
-  size_t tk, pes, red, x, xs, hf, hh, hl, hs, comb, total;
+  size_t tk, pes, red, nrm, x, xs, hf, hh, hl, hs, comb, total;
 };
 inline __host__ __device__ size_t al16(size_t v) { return (v + 15) & ~(size_t)15; }
 inline __host__ __device__ int dec_tiles_per_wg(int wpt) { return DEC_W / wpt; }
@@ -84,6 +88,7 @@ inline __host__ __device__ DecLds dec_lds(int H, int E, int k, int I, int Kc_sh,
   L.tk = o; o = al16(o + topk_lds_bytes(E, k));
   L.pes = o; o = al16(o + (size_t)E * 4 + 16);
   L.red = o; o = al16(o + (size_t)DEC_W * 32 * 4);
+  L.nrm = o; o = al16(o + (size_t)(DEC_W + H / TILE_ROWS) * 4);
   const size_t u = o;
   L.x = u;
   L.xs = al16(L.x + (size_t)H * 2);
@@ -395,15 +400,48 @@ QMOE_DEV void dec_routed_down(const DecodeArgs &a, int b, unsigned ep, char *sme
                                        : a.y_sh + (size_t)(s - (a.k - 1)) * a.H + row0 + rw;
                 },
                 [&](int i, float v) { comb[i] = v; });
+  float m = 0.f;  // routed rows (router-weighted) + shared row
   if (mine) {
-    float acc = yv;
-    for (int s = 0; s < a.k - 1; ++s) acc += comb[s * nr + r];
+    m = yv;
+    for (int s = 0; s < a.k - 1; ++s) m += comb[s * nr + r];
     float sh = 0.f;
     for (int s = a.k - 1; s < nsrc; ++s) sh += comb[s * nr + r];
-    acc += sh;
-    acc += bf16_to_f32(a.x[row0 + r]);
-    a.out[row0 + r] = (uint16_t)f32_to_bf16_bits(acc);
-    if (a.out_f32) a.out_f32[row0 + r] = acc;
+    m += sh;
+  }
+  if (a.gain) {
+    // post-combine norm: every combining workgroup publishes m for its rows and the sum of
+    // m^2 over them; the last one to arrive normalises the whole row (waiting on no one).
+    float *nr_lds = (float *)(smem + L.nrm);  // [DEC_W] wave sums, then [groups] partials
+    if (mine) st_tag(a.mrow + row0 + r, ep, m);
+    const float ss = wave_sum(mine ? m * m : 0.f);
+    if (tid % WAVE == 0) nr_lds[wv] = ss;
+    __syncthreads();
+    if (tid == 0) {
+      float p = 0.f;
+      for (int i = 0; i < DEC_W; ++i) p += nr_lds[i];
+      st_tag(a.nrm + g, ep, p);
+    }
+    if (!arrive_last(sy(a, SY_DONE), (unsigned)groups)) return;
+    float *part = nr_lds + DEC_W;
+    fetch_tags<1>(a, groups, ep, [&](int i) { return a.nrm + i; },
+                  [&](int i, float v) { part[i] = v; });
+    float tot = 0.f;
+    for (int i = 0; i < groups; ++i) tot += part[i];
+    const float rs = 1.f / sqrtf(tot / (float)a.H + RMS_EPS);
+    const float al = a.lscale ? *a.lscale : 1.f;
+    fetch_tags<12>(a, a.H, ep, [&](int i) { return a.mrow + i; }, [&](int i, float v) {
+      const float o = (bf16_to_f32(a.x[i]) + a.gain[i] * (v * rs)) * al;
+      a.out[i] = (uint16_t)f32_to_bf16_bits(o);
+      if (a.out_f32) a.out_f32[i] = o;
+    });
+    if (tid == 0) st_sys_u(sy(a, SY_EPOCH), ep);
+    return;
+  }
+  if (mine) {
+    float o = bf16_to_f32(a.x[row0 + r]) + m;
+    if (a.lscale) o *= *a.lscale;
+    a.out[row0 + r] = (uint16_t)f32_to_bf16_bits(o);
+    if (a.out_f32) a.out_f32[row0 + r] = o;
   }
   // the last combining workgroup advances the epoch
   if (arrive_last(sy(a, SY_DONE), (unsigned)groups) && tid == 0) st_sys_u(sy(a, SY_EPOCH), ep);

@@ -346,4 +346,75 @@ __global__ void __launch_bounds__(256) combine_pf_kernel(const uint16_t *x, cons
   }
 }
 
+// cb2 with its post-combine steps (normalisation, residual, layer scalar), one workgroup per
+// token row t:
+//   m   = sum_j w[t,j] y[t*k+j] + y_sh[t]          fp32, j ascending, then the shared row
+//   n   = gain * m / sqrt(mean(m^2) + RMS_EPS)      (gain null: n = m)
+//   out = (x + n) * scalar                          (scalar null: 1)
+// With neither step the arithmetic is combine_pf_kernel's.  H <= 4 * POST_THREADS * POST_V.
+constexpr int POST_THREADS = 256, POST_V = 8;
+__global__ void __launch_bounds__(POST_THREADS) combine_post_kernel(
+    const uint16_t *x, const float *y, const float *w, const float *y_sh, const float *gain,
+    const float *scalar, int H, int k, uint16_t *out, float *out_f32) {
+  __shared__ float red[POST_THREADS / WAVE];
+  const int t = blockIdx.x, tid = threadIdx.x, n4 = H / 4;
+  float4 m[POST_V];
+  float ss = 0.f;
+#pragma unroll
+  for (int v = 0; v < POST_V; ++v) {
+    const int c = tid + POST_THREADS * v;
+    float4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (c < n4) {
+      for (int j = 0; j < k; ++j) {
+        const float wj = w[(size_t)t * k + j];
+        const float4 yv = *(const float4 *)(y + ((size_t)t * k + j) * H + 4 * c);
+        acc.x = fmaf(wj, yv.x, acc.x);
+        acc.y = fmaf(wj, yv.y, acc.y);
+        acc.z = fmaf(wj, yv.z, acc.z);
+        acc.w = fmaf(wj, yv.w, acc.w);
+      }
+      if (y_sh) {
+        const float4 s4 = *(const float4 *)(y_sh + (size_t)t * H + 4 * c);
+        acc.x += s4.x; acc.y += s4.y; acc.z += s4.z; acc.w += s4.w;
+      }
+      ss = fmaf(acc.x, acc.x, ss);
+      ss = fmaf(acc.y, acc.y, ss);
+      ss = fmaf(acc.z, acc.z, ss);
+      ss = fmaf(acc.w, acc.w, ss);
+    }
+    m[v] = acc;
+  }
+  float r = 1.f;
+  if (gain) {
+    ss = wave_sum(ss);
+    if (tid % WAVE == 0) red[tid / WAVE] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int i = 0; i < POST_THREADS / WAVE; ++i) tot += red[i];
+    r = 1.f / sqrtf(tot / (float)H + RMS_EPS);
+  }
+  const float al = scalar ? *scalar : 1.f;
+#pragma unroll
+  for (int v = 0; v < POST_V; ++v) {
+    const int c = tid + POST_THREADS * v;
+    if (c >= n4) continue;
+    float4 n = m[v];
+    if (gain) {
+      const float4 g = *(const float4 *)(gain + 4 * c);
+      n.x = g.x * (n.x * r); n.y = g.y * (n.y * r); n.z = g.z * (n.z * r); n.w = g.w * (n.w * r);
+    }
+    const uint2 xb = *(const uint2 *)(x + (size_t)t * H + 4 * c);
+    float4 o;
+    o.x = (bf16lo(xb.x) + n.x) * al;
+    o.y = (bf16hi(xb.x) + n.y) * al;
+    o.z = (bf16lo(xb.y) + n.z) * al;
+    o.w = (bf16hi(xb.y) + n.w) * al;
+    const uint2 ob = {f32_to_bf16_bits(o.x) | (f32_to_bf16_bits(o.y) << 16),
+                      f32_to_bf16_bits(o.z) | (f32_to_bf16_bits(o.w) << 16)};
+    *(uint2 *)(out + (size_t)t * H + 4 * c) = ob;
+    if (out_f32) *(float4 *)(out_f32 + (size_t)t * H + 4 * c) = o;
+  }
+}
+
 }  // namespace qmoe

@@ -22,7 +22,7 @@ using namespace qmoe;
 
 namespace {
 
-constexpr int VERSION = 100;               // 0.1.0
+constexpr int VERSION = 200;               // 0.2.0
 constexpr size_t COUNTER_BYTES = 512 * 1024;
 constexpr int GU_W = 8;     // waves per routed gate/up workgroup (split-K)
 constexpr int D_W = 8;      // waves per down workgroup (split-K)
@@ -133,7 +133,7 @@ inline int dec_shared_chunks(const qmoe_dims *d) {
 struct WsLayout {
   size_t cnt, logits, tidx, tw, counts, offsets, sorted, active, nact, slot_tab;
   size_t hr_hi, hr_lo, hs_hi, hs_lo, y, ysh, gx, ghr, ghs;
-  size_t dec_logits, dec_hr, dec_hsh, dec_yr, dec_ysh, total;
+  size_t dec_logits, dec_hr, dec_hsh, dec_yr, dec_ysh, dec_nrm, dec_m, total;
 };
 
 WsLayout ws_layout(const qmoe_dims *d, int Tmax) {
@@ -165,6 +165,8 @@ WsLayout ws_layout(const qmoe_dims *d, int Tmax) {
   w.dec_hsh = o; o += (size_t)H_COPIES * dec_copy_stride((size_t)d->shared_inter);
   w.dec_yr = o; o += al((k - 1) * H * 8);
   w.dec_ysh = o; o += al((size_t)dec_shared_chunks(d) * H * 8);
+  w.dec_nrm = o; o += al((H / TILE_ROWS) * 8);
+  w.dec_m = o; o += al(H * 8);
   w.total = o;
   return w;
 }
@@ -203,6 +205,8 @@ int check_layer(const qmoe_layer *L) {
     return fail(QMOE_ERR_ARG, "shared block given but shared_inter is 0");
   if (L->shared && !aligned(L->shared, 256))
     return fail(QMOE_ERR_ARG, "shared block must be 256-byte aligned");
+  if (L->post_norm_gain && !aligned(L->post_norm_gain, 16))
+    return fail(QMOE_ERR_ARG, "post_norm_gain must be 16-byte aligned");
   return QMOE_OK;
 }
 
@@ -383,6 +387,15 @@ static int launch_gsum(const uint16_t *x, int T, int H, float *g, hipStream_t s)
   return QMOE_OK;
 }
 
+static int launch_combine_post(const uint16_t *x, const float *y, const float *w,
+                               const float *y_sh, const float *gain, const float *scalar, int T,
+                               int H, int k, uint16_t *out, float *out_f32, hipStream_t s) {
+  hipLaunchKernelGGL(combine_post_kernel, dim3(T), dim3(POST_THREADS), 0, s, x, y, w, y_sh, gain,
+                     scalar, H, k, out, out_f32);
+  QMOE_LAUNCHED();
+  return QMOE_OK;
+}
+
 static int launch_combine_pf(const uint16_t *x, const float *y, const float *w, const float *y_sh,
                              int T, int H, int k, uint16_t *out, float *out_f32, hipStream_t s) {
   const size_t n4 = (size_t)T * H / 4;
@@ -441,6 +454,9 @@ static int launch_decode(const qmoe_layer *L, const uint16_t *x, uint16_t *out, 
   a.y_r = at<uint64_t>(ws, wl.dec_yr);
   a.y_sh = at<uint64_t>(ws, wl.dec_ysh);
   a.topk_idx = idx; a.topk_w = w; a.out = out; a.out_f32 = out_f32;
+  a.gain = L->post_norm_gain; a.lscale = L->layer_scalar;
+  a.nrm = at<uint64_t>(ws, wl.dec_nrm);
+  a.mrow = at<uint64_t>(ws, wl.dec_m);
   const int tiles_d = a.H / TILE_ROWS, tpw = dec_tiles_per_wg(a.wpt);
   a.nR = (a.E + ROUTER_WAVES - 1) / ROUTER_WAVES;   // one expert per wave
   a.nSG = sh ? a.Is / 16 : 0;
@@ -615,6 +631,24 @@ int qmoe_combine(const qmoe_dims *d, const uint16_t *x, const float *y, const fl
   return ok();
 }
 
+int qmoe_combine_post(const qmoe_dims *d, const uint16_t *x, const float *y, const float *topk_w,
+                      const float *y_shared_or_null, const float *post_norm_gain_or_null,
+                      const float *layer_scalar_or_null, int32_t T, uint16_t *out,
+                      float *out_f32_or_null, qmoe_stream_t stream) {
+  int rc = check_dims(d);
+  if (rc || (rc = check_T(T))) return rc;
+  if (T == 0) return ok();
+  if (!x || !y || !topk_w || !out) return fail(QMOE_ERR_ARG, "combine_post: NULL pointer");
+  if (post_norm_gain_or_null && !aligned(post_norm_gain_or_null, 16))
+    return fail(QMOE_ERR_ARG, "post_norm_gain must be 16-byte aligned");
+  if ((rc = check_arch())) return rc;
+  if ((rc = launch_combine_post(x, y, topk_w, y_shared_or_null, post_norm_gain_or_null,
+                                layer_scalar_or_null, T, d->hidden, d->top_k, out,
+                                out_f32_or_null, (hipStream_t)stream)))
+    return rc;
+  return ok();
+}
+
 int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16_t *out,
                        float *out_f32_or_null, int32_t *topk_idx_or_null, float *topk_w_or_null,
                        void *ws, size_t ws_bytes, qmoe_stream_t stream) {
@@ -630,6 +664,7 @@ int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16
   const WsLayout wl = ws_layout(d, Tc_max);
   const int H = d->hidden, k = d->top_k;
   const bool sh = L->shared != nullptr;
+  const bool post = L->post_norm_gain || L->layer_scalar;
   if (T == 1 && decode_fits(d)) {
     int32_t *idx = topk_idx_or_null ? topk_idx_or_null : at<int32_t>(ws, wl.tidx);
     float *w = topk_w_or_null ? topk_w_or_null : at<float>(ws, wl.tw);
@@ -666,7 +701,10 @@ int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16
       fa.y_sh = sh ? at<float>(ws, wl.ysh) : nullptr;
       if (!sh) fa.shared = nullptr;
       if ((rc = launch_pf(fa, s))) return rc;
-      if ((rc = launch_combine_pf(xc, fa.y, w, fa.y_sh, Tc, H, k, oc, oc32, s))) return rc;
+      if (post) rc = launch_combine_post(xc, fa.y, w, fa.y_sh, L->post_norm_gain, L->layer_scalar,
+                                         Tc, H, k, oc, oc32, s);
+      else rc = launch_combine_pf(xc, fa.y, w, fa.y_sh, Tc, H, k, oc, oc32, s);
+      if (rc) return rc;
     } else {
       // VALU kernels: gate/up (routed + shared), down (routed + shared, one chunk), combine
       fa.y_sh = sh ? at<float>(ws, wl.ysh) : nullptr;
@@ -675,11 +713,17 @@ int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16
       if ((rc = launch_gu(fa, s))) return rc;
       if (g_prof_stop && (rc = record_event(g_prof_stop, s))) return rc;
       if ((rc = launch_d(fa, sh, s))) return rc;
-      const size_t n = (size_t)Tc * H;
-      const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
-      hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, s, xc, fa.y, w, fa.y_sh, Tc,
-                         H, k, oc, oc32);
-      QMOE_LAUNCHED();
+      if (post) {
+        if ((rc = launch_combine_post(xc, fa.y, w, fa.y_sh, L->post_norm_gain, L->layer_scalar,
+                                      Tc, H, k, oc, oc32, s)))
+          return rc;
+      } else {
+        const size_t n = (size_t)Tc * H;
+        const unsigned blocks = (unsigned)std::min<size_t>((n + 255) / 256, 4096);
+        hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, s, xc, fa.y, w, fa.y_sh,
+                           Tc, H, k, oc, oc32);
+        QMOE_LAUNCHED();
+      }
     }
   }
   return ok();

@@ -19,7 +19,6 @@ constexpr int ROUTER_EPW = 4;    // experts per wave (multi-token router)
 constexpr int ROUTER_WAVES = 4;
 constexpr int ROUTER_EPB = ROUTER_EPW * ROUTER_WAVES;  // experts per router workgroup
 constexpr int ROUTER_THREADS = ROUTER_WAVES * WAVE;
-constexpr float RMS_EPS = 1e-6f;
 
 struct RouterArgs {
   const uint16_t *x;          // [T, H] bf16

@@ -87,11 +87,19 @@ class RouterWeights:
 class LayerWeights:
     """A layer: router + packed expert store (+ shared block)."""
 
-    def __init__(self, dims, router, experts, stride, shared=None, experts_offset=0):
+    def __init__(self, dims, router, experts, stride, shared=None, experts_offset=0,
+                 post_norm_gain=None, layer_scalar=None):
         self.dims, self.router, self.experts, self.shared = dims, router, experts, shared
+        if post_norm_gain is not None:
+            _need(post_norm_gain, torch.float32, "post_norm_gain")
+        if layer_scalar is not None:
+            _need(layer_scalar, torch.float32, "layer_scalar")
+        self.post = (post_norm_gain, layer_scalar)
         base = _ptr(experts, 1, "experts").value + int(experts_offset)
         self.struct = Layer(dims, router.struct, base, int(stride),
-                            _ptr(shared, 1, "shared").value if shared is not None else None)
+                            _ptr(shared, 1, "shared").value if shared is not None else None,
+                            _ptr(post_norm_gain, 4).value if post_norm_gain is not None else None,
+                            _ptr(layer_scalar, 4).value if layer_scalar is not None else None)
 
 
 def router_topk(dims, router, x, ws, topk_idx=None, topk_w=None, logits=None):
@@ -147,6 +155,19 @@ def combine(dims, x, y, topk_w, y_shared=None, out=None, out_f32=None):
     check(lib().qmoe_combine(
         ctypes.byref(dims), _ptr(x, 2, "x"), _ptr(y, 4, "y"), _ptr(topk_w, 4, "topk_w"),
         _ptr(y_shared, 4, allow_none=True), T, _ptr(out, 2, "out"),
+        _ptr(out_f32, 4, allow_none=True), _stream()))
+    return out
+
+
+def combine_post(dims, x, y, topk_w, y_shared=None, post_norm_gain=None, layer_scalar=None,
+                 out=None, out_f32=None):
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty(T, dims.hidden, dtype=torch.bfloat16, device=x.device)
+    check(lib().qmoe_combine_post(
+        ctypes.byref(dims), _ptr(x, 2, "x"), _ptr(y, 4, "y"), _ptr(topk_w, 4, "topk_w"),
+        _ptr(y_shared, 4, allow_none=True), _ptr(post_norm_gain, 4, allow_none=True),
+        _ptr(layer_scalar, 4, allow_none=True), T, _ptr(out, 2, "out"),
         _ptr(out_f32, 4, allow_none=True), _stream()))
     return out
 

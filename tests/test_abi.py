@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_last_error():
     L = _lib()
-    assert L.lib().qmoe_version() == 100
+    assert L.lib().qmoe_version() == 200
     assert isinstance(L.last_error(), str)
 
 
@@ -115,6 +115,13 @@ def test_argument_errors_do_not_touch_the_device():
     assert lib.qmoe_pack_expert(ctypes.byref(d), 96, *([fake] * 9), fake, None) == -2
     # combine / bucket nulls
     assert lib.qmoe_combine(ctypes.byref(d), fake, None, fake, None, 4, fake, None, None) == -1
+    assert lib.qmoe_combine_post(ctypes.byref(d), fake, None, fake, None, None, None, 4, fake,
+                                 None, None) == -1
+    assert lib.qmoe_combine_post(ctypes.byref(d), fake, fake, fake, None, ctypes.c_void_p(4100), None, 4, fake,
+                                 None, None) == -1              # misaligned gain
+    lay = L.Layer(d, r, 4096, 65536, None, 4104, None)
+    assert lib.qmoe_layer_forward(ctypes.byref(lay), fake, 4, fake, None, None, None, fake,
+                                  1 << 30, None) == -1          # misaligned post-norm gain
     assert lib.qmoe_bucket(ctypes.byref(d), None, 4, fake, fake, fake, fake, fake, None, 0, None) == -1
     # events
     assert lib.qmoe_set_profile_events(None, None) == 0       # profiling off

@@ -359,6 +359,108 @@ def test_one_token_calls_repeat_and_report_no_timeout(name):
     check_out_bf16(np16(fresh)[0], o32.cpu().numpy()[0], ref["out"][0], "one-token out")
 
 
+# ------------------------------------------------------------------ post-combine steps (cb2)
+
+class _WithPost:
+    """Oracle view of a layer that carries the post-combine norm gain and layer scalar."""
+
+    def __init__(self, li, gain, scalar):
+        self._li, self.post_gain, self.layer_scalar = li, gain, scalar
+
+    def __getattr__(self, name):
+        return getattr(self._li, name)
+
+
+def post_layer(name, steps="both"):
+    """(LayerWeights with the post steps, oracle layer view) sharing layer(name)'s store."""
+    ops = _ops()
+    cfg = G.config(name)
+    pl, li = layer(name)
+    gain, scalar = G.make_post(cfg, 0)
+    g = torch.from_numpy(gain).to(DEV) if steps in ("both", "gain") else None
+    sc = torch.tensor([scalar], dtype=torch.float32, device=DEV) if steps in ("both", "scalar") else None
+    lw = ops.LayerWeights(pl.dims, pl.router, pl.store, pl.stride, pl.shared,
+                          post_norm_gain=g, layer_scalar=sc)
+    view = _WithPost(li, gain if g is not None else None, scalar if sc is not None else None)
+    return pl, lw, view
+
+
+@pytest.mark.parametrize("name,T,sample,steps", [
+    ("tiny", 4, None, "both"), ("tiny", 1, None, "both"), ("tiny", 1, None, "scalar"),
+    ("tiny", 64, None, "gain"), ("tiny", 37, None, "scalar"),
+    ("gemma4_26b_a4b_decode", 1, None, "both"), ("gemma4_26b_a4b_decode", 128, [3, 100], "both"),
+    ("qwen3_next_80b_a3b_decode_b1", 1, None, "both"),
+    ("qwen3_6_35b_a3b_long_prefill", 128, [10], "gain")])
+def test_layer_forward_post_parity(name, T, sample, steps):
+    """The layer with cb2's post-combine steps (one-token kernel and chunked path)."""
+    ops = _ops()
+    cfg = G.config(name)
+    pl, lw, view = post_layer(name, steps)
+    xb, x = _stacks().hidden(cfg, 5, T)
+    ws = ops.workspace(pl.dims, T)
+    out_f32 = torch.empty(T, cfg.hidden, dtype=torch.float32, device=DEV)
+    idx = torch.empty(T, cfg.top_k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, cfg.top_k, dtype=torch.float32, device=DEV)
+    out = ops.layer_forward(lw, x, ws, out_f32=out_f32, topk_idx=idx, topk_w=w)
+    torch.cuda.synchronize()
+    assert ops.workspace_status(ws) == 0
+    toks = range(T) if sample is None else sample
+    ties, nd, flips = _layer_check(cfg, view, xb, out, out_f32, idx, w, toks)
+    print(f"{name} T={T} post={steps}: near ties {ties}, re-evaluated {nd}, bf16 flips {flips}")
+
+
+def test_combine_post_against_oracle_and_plain_combine():
+    ops = _ops()
+    cfg = G.config("gemma4_26b_a4b_prefill")
+    T, H, k = 9, cfg.hidden, cfg.top_k
+    rng = np.random.default_rng(11)
+    xb = O.bf16_rne_bits(rng.standard_normal((T, H)))
+    x = _stacks().t16(xb, DEV)
+    y = torch.from_numpy(rng.standard_normal((T * k, H)).astype(np.float32)).to(DEV)
+    ysh = torch.from_numpy(rng.standard_normal((T, H)).astype(np.float32)).to(DEV)
+    w = torch.from_numpy(rng.uniform(0.05, 0.3, (T, k)).astype(np.float32)).to(DEV)
+    gain, scalar = G.make_post(cfg, 3)
+    g = torch.from_numpy(gain).to(DEV)
+    sc = torch.tensor([scalar], dtype=torch.float32, device=DEV)
+    dims = layer("gemma4_26b_a4b_decode")[0].dims
+    o32 = torch.empty(T, H, dtype=torch.float32, device=DEV)
+    out = ops.combine_post(dims, x, y, w, ysh, g, sc, out_f32=o32)
+    p32 = torch.empty_like(o32)
+    plain = ops.combine_post(dims, x, y, w, ysh, out_f32=p32)
+    c32 = torch.empty_like(o32)
+    ref_plain = ops.combine(dims, x, y, w, ysh, out_f32=c32)
+    torch.cuda.synchronize()
+    assert torch.equal(plain.view(torch.int16), ref_plain.view(torch.int16))
+    assert torch.equal(p32, c32)
+    want, _ = O.combine_post(xb, y.cpu().numpy().astype(np.float64).reshape(T, k, H),
+                             w.cpu().numpy(), ysh.cpu().numpy().astype(np.float64), gain, scalar)
+    o_n = o32.cpu().numpy()
+    for t in range(T):
+        assert_close_f32(o_n[t], want[t], f"combine_post out_f32 token {t}")
+        check_out_bf16(np16(out)[t], o_n[t], want[t], f"combine_post out token {t}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "gemma4_26b_a4b_decode"])
+def test_one_token_post_calls_repeat(name):
+    """Back-to-back one-token calls with the post-combine norm give the same bits as a fresh
+    workspace and report no timed-out wait."""
+    ops = _ops()
+    cfg = G.config(name)
+    pl, lw, view = post_layer(name)
+    xb, x = _stacks().hidden(cfg, 8, 1)
+    ws = ops.workspace(pl.dims, 1)
+    outs = [ops.layer_forward(lw, x, ws) for _ in range(4)]
+    plain = ops.layer_forward(pl.weights, x, ws)
+    outs.append(ops.layer_forward(lw, x, ws))
+    ws2 = ops.workspace(pl.dims, 1)
+    fresh = ops.layer_forward(lw, x, ws2)
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o.view(torch.int16), fresh.view(torch.int16))
+    assert not torch.equal(plain.view(torch.int16), fresh.view(torch.int16))
+    assert ops.workspace_status(ws) == 0 and ops.workspace_status(ws2) == 0
+
+
 @pytest.mark.parametrize("T", [1, 128])
 def test_graph_replays_match_eager(T):
     """A captured layer call replayed several times, with eager work in between, reproduces the
