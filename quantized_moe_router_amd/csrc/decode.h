@@ -85,7 +85,7 @@ inline __host__ __device__ int dec_tiles_per_wg(int wpt) { return DEC_W / wpt; }
 inline __host__ __device__ DecLds dec_lds(int H, int E, int k, int I, int Kc_sh, int nc, int wpt) {
   DecLds L;
   size_t o = 0;
-  L.tk = o; o = al16(o + topk_lds_bytes(E, k));
+  L.tk = o; o = al16(o + (size_t)topk_chunks(E) * WAVE * 4);
   L.pes = o; o = al16(o + (size_t)E * 4 + 16);
   L.red = o; o = al16(o + (size_t)DEC_W * 32 * 4);
   L.nrm = o; o = al16(o + (size_t)(DEC_W + H / TILE_ROWS) * 4);
@@ -170,19 +170,16 @@ QMOE_DEV void dec_router(const DecodeArgs &a, int rb, unsigned ep, char *smem) {
   router_logits_block<1, 1, false>(ra, 0, rb, smem);
 }
 
-// ---------------------------------------------------------------- top-k (whole workgroup)
+// ---------------------------------------------------------------- top-k (every wave)
 // Expert and weight of `slot` (returned to every thread); with `publish`, the top-k outputs
-// are written too.  The E logits are fetched (tagged) into keys; chunks are ranked by the
-// four waves in parallel, the survivors by wave 0.
+// are written too.  The E logits are fetched (tagged) into LDS as ordered bits, then every
+// wave runs the selection on its own copy in registers (same result in each wave).
 QMOE_DEV void dec_topk(const DecodeArgs &a, unsigned ep, int slot, bool publish, int &e_out,
                        float &w_out, char *smem, const DecLds &L) {
   const int tid = threadIdx.x, wv = tid / WAVE, lane = tid % WAVE;
   const int E = a.E, k = a.k, nch = topk_chunks(E);
-  uint64_t *keys = (uint64_t *)(smem + L.tk);
-  uint64_t *surv = keys + nch * WAVE, *sel = surv + nch * k;
+  uint32_t *ord = (uint32_t *)(smem + L.tk);
   float *pes = (float *)(smem + L.pes);
-  int *se = (int *)(pes + E);
-  float *sw = (float *)(se + 1);
   // per-expert scales into LDS (loads in flight while the logits are fetched)
   constexpr int PJ = MAX_EXPERTS / DEC_THREADS;
   float pv[PJ];
@@ -191,32 +188,26 @@ QMOE_DEV void dec_topk(const DecodeArgs &a, unsigned ep, int slot, bool publish,
     const int i = tid + j * DEC_THREADS;
     pv[j] = (i < E) ? a.pes[i] : 0.f;
   }
-  for (int i = E + tid; i < nch * WAVE; i += DEC_THREADS) keys[i] = topk_pad_key(i);
+  for (int i = E + tid; i < nch * WAVE; i += DEC_THREADS) ord[i] = 0u;
   const uint64_t *lg = a.logits + (size_t)(blockIdx.x % LOGIT_COPIES) * a.logit_copy;
   fetch_tags<PJ>(a, E, ep, [&](int i) { return lg + i; },
-                 [&](int i, float v) { keys[i] = topk_key(v, i); });
+                 [&](int i, float v) { ord[i] = topk_ord(v); });
 #pragma unroll
   for (int j = 0; j < PJ; ++j) {
     const int i = tid + j * DEC_THREADS;
     if (i < E) pes[i] = pv[j];
   }
-  for (int c = wv; c < nch; c += DEC_W) topk_rank_chunk(keys + c * WAVE, k, surv + c * k);
   __syncthreads();
-  if (wv == 0) {
-    topk_rank_survivors(surv, nch * k, k, sel);
-    __builtin_amdgcn_wave_barrier();
-    int myi;
-    float myw;
-    topk_weights(sel, k, pes, myi, myw);
-    if (publish && lane < k) {
-      a.topk_idx[lane] = myi;
-      a.topk_w[lane] = myw;
-    }
-    if (lane == slot) { *se = myi; *sw = myw; }
+  int my_e;
+  float my_l;
+  topk_select(nch, [&](int c) { return c < nch ? ord[c * WAVE + lane] : 0u; }, k, my_e, my_l);
+  const float my_w = topk_weight(my_e, my_l, k, pes);
+  if (publish && wv == 0 && lane < k) {
+    a.topk_idx[lane] = my_e;
+    a.topk_w[lane] = my_w;
   }
-  __syncthreads();
-  e_out = min(max(*se, 0), E - 1);
-  w_out = *sw;
+  e_out = min(max(__builtin_amdgcn_readlane(my_e, slot), 0), E - 1);
+  w_out = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), slot));
 }
 
 // ---------------------------------------------------------------- gate/up of one tile, one token

@@ -230,8 +230,7 @@ int set_lds(K kernel, size_t bytes) {
 }
 
 size_t router_smem(const qmoe_dims *d, int T) {
-  return std::max({router_lds_bytes(d->hidden), bucket_lds_bytes(T * d->top_k, d->n_experts),
-                   ROUTER_WAVES * topk_lds_bytes(d->n_experts, d->top_k)});
+  return std::max(router_lds_bytes(d->hidden), bucket_lds_bytes(T * d->top_k, d->n_experts));
 }
 
 RouterArgs make_router_args(const qmoe_dims *d, const qmoe_router *r, const uint16_t *x, int T,

@@ -49,94 +49,105 @@ struct RouterArgs {
 };
 
 
-// ---------------------------------------------------------------- top-k by exact ranking
+// ---------------------------------------------------------------- top-k selection (one wave)
 // Order: larger logit first, equal logits -> lower expert index.  A NaN logit ranks as -inf
 // (so every selected index is a valid expert id whatever the logits hold) and -0 as +0.
-// Each (logit, expert) pair becomes one 64-bit key whose unsigned order is exactly that
-// order; all keys are distinct, so the selection is a rank computation with no branches:
-//   1. the keys are cut into chunks of 64; a lane ranks its key inside its chunk with 64
-//      broadcast LDS reads, and the keys of rank < k ("survivors") go to slot rank of their
-//      chunk's k survivor slots (every global top-k key survives its chunk);
-//   2. each survivor is ranked among all survivors; rank r < k is the r-th selected expert.
-// Padding keys (chunk positions >= E) sort below every real key.
-QMOE_DEV uint64_t topk_key(float l, int e) {
+// A logit becomes 32 bits whose unsigned order is its numeric order; 0 lies below every
+// logit and marks padding and taken entries.  Lane l holds experts l + 64 c (c < chunks) in
+// registers; each of the k rounds takes the wave maximum (a rotate-max inside each 16-lane
+// row by DPP, then the four row results read as scalars), and one ballot per chunk finds the
+// lowest expert index holding it, which is then removed.  No LDS, no barrier.  The chunk
+// count is compiled in (1, 2, 4, 8 or 16) so that the rounds have no runtime guards.
+constexpr int TOPK_NCH = MAX_EXPERTS / WAVE;   // register chunks per lane
+
+QMOE_DEV uint32_t topk_ord(float l) {
   if (!(l == l)) l = -INFINITY;
   if (l == 0.f) l = 0.f;
-  uint32_t u = __float_as_uint(l);
-  u ^= (u & 0x80000000u) ? 0xFFFFFFFFu : 0x80000000u;
-  return ((uint64_t)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+  const uint32_t u = __float_as_uint(l);
+  return u ^ ((u & 0x80000000u) ? 0xFFFFFFFFu : 0x80000000u);
 }
-QMOE_DEV uint64_t topk_pad_key(int e) { return (uint64_t)(0xFFFFFFFFu - (uint32_t)e); }
-QMOE_DEV int key_expert(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
-QMOE_DEV float key_logit(uint64_t key) {
-  uint32_t u = (uint32_t)(key >> 32);
-  u ^= (u & 0x80000000u) ? 0x80000000u : 0xFFFFFFFFu;
-  return __uint_as_float(u);
+QMOE_DEV float topk_ord_logit(uint32_t v) {
+  return __uint_as_float(v ^ ((v & 0x80000000u) ? 0x80000000u : 0xFFFFFFFFu));
 }
-
 inline __host__ __device__ int topk_chunks(int E) { return (E + WAVE - 1) / WAVE; }
-// LDS of one ranking: keys [chunks*64], survivors [chunks*k], result [k] (64-bit each)
-inline __host__ __device__ size_t topk_lds_bytes(int E, int k) {
-  return (size_t)8 * (topk_chunks(E) * WAVE + topk_chunks(E) * k + k);
+
+QMOE_DEV uint32_t dpp_ror_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121, 0xF, 0xF, false));  // ror 1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x122, 0xF, 0xF, false));  // ror 2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x124, 0xF, 0xF, false));  // ror 4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128, 0xF, 0xF, false));  // ror 8
+  return v;
+}
+QMOE_DEV uint32_t wave_max_uniform(uint32_t v) {
+  v = dpp_ror_max(v);
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return max(max(a, b), max(c, d));
 }
 
-// Step 1 for one chunk, by one wave: ck = the chunk's 64 keys.
-QMOE_DEV void topk_rank_chunk(const uint64_t *ck, int k, uint64_t *surv) {
+// The selection over NCH register chunks; load(c) gives the lane's ordered logit of expert
+// lane + 64 c (0 for padding).  Lane j < k receives the j-th selection (expert, logit); the
+// others receive (0, 0).
+template <int NCH, class Load>
+QMOE_DEV void topk_run(Load load, int k, int &my_e, float &my_l) {
   const int lane = threadIdx.x % WAVE;
-  const uint64_t K = ck[lane];
-  int r = 0;
-#pragma unroll 16
-  for (int j = 0; j < WAVE; ++j) r += (ck[j] > K) ? 1 : 0;
-  if (r < k) surv[r] = K;
-}
-
-// Step 2, by one wave: sel[r] = the key of rank r < k among the n survivors.
-QMOE_DEV void topk_rank_survivors(const uint64_t *surv, int n, int k, uint64_t *sel) {
-  for (int i = threadIdx.x % WAVE; i < n; i += WAVE) {
-    const uint64_t K = surv[i];
-    int r = 0;
-    for (int j = 0; j < n; ++j) r += (surv[j] > K) ? 1 : 0;
-    if (r < k) sel[r] = K;
+  uint32_t u[NCH];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) u[c] = load(c);
+  my_e = 0;
+  my_l = 0.f;
+  for (int j = 0; j < k; ++j) {
+    uint32_t lm = u[0];
+#pragma unroll
+    for (int c = 1; c < NCH; ++c) lm = max(lm, u[c]);
+    const uint32_t M = wave_max_uniform(lm);
+    int e = -1;
+#pragma unroll
+    for (int c = NCH - 1; c >= 0; --c) {
+      const unsigned long long m = __ballot(u[c] == M);
+      if (m) e = WAVE * c + __builtin_ctzll(m);
+    }
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+      if (WAVE * c + lane == e) u[c] = 0;
+    if (lane == j) {
+      my_e = e;
+      my_l = topk_ord_logit(M);
+    }
   }
 }
 
-// Lane j < k of the wave gets the j-th selected expert and its weight: softmax over the kept
-// logits, times per_expert_scale (pes, global or LDS) of that expert.  Other lanes get 0, 0.
-QMOE_DEV void topk_weights(const uint64_t *sel, int k, const float *pes, int &myi, float &myw) {
+// nch = topk_chunks(E) chunks, rounded up to a compiled width (load(c) must give 0 past nch).
+template <class Load>
+QMOE_DEV void topk_select(int nch, Load load, int k, int &my_e, float &my_l) {
+  if (nch <= 1) topk_run<1>(load, k, my_e, my_l);
+  else if (nch <= 2) topk_run<2>(load, k, my_e, my_l);
+  else if (nch <= 4) topk_run<4>(load, k, my_e, my_l);
+  else if (nch <= 8) topk_run<8>(load, k, my_e, my_l);
+  else topk_run<TOPK_NCH>(load, k, my_e, my_l);
+}
+
+// Softmax over the k selected logits (lane j < k holds the j-th, the largest in lane 0), times
+// per_expert_scale (global or LDS).  Lanes >= k get 0.
+QMOE_DEV float topk_weight(int my_e, float my_l, int k, const float *pes) {
   const int lane = threadIdx.x % WAVE;
-  const uint64_t K = sel[min(lane, k - 1)];
-  const float lv = key_logit(K);
-  const float vmax = __shfl(lv, 0, WAVE);
-  const float z = (lane < k) ? expf(lv - vmax) : 0.f;
+  const float vmax = __shfl(my_l, 0, WAVE);
+  const float z = (lane < k) ? expf(my_l - vmax) : 0.f;
   const float zsum = wave_sum(z);
-  myi = (lane < k) ? key_expert(K) : 0;
-  myw = (lane < k) ? (z / zsum) * pes[myi] : 0.f;
+  return (lane < k) ? (z / zsum) * pes[my_e] : 0.f;
 }
 
 // The whole selection by one wave for one token.  lrow: E logits written by other
-// workgroups of the launch (system-scope loads).  lds: topk_lds_bytes(E, k) bytes owned by
-// this wave.
-QMOE_DEV void topk_wave(const float *lrow, int E, int k, const float *pes, uint64_t *lds,
-                        int &myi, float &myw) {
-  const int lane = threadIdx.x % WAVE, nch = topk_chunks(E);
-  uint64_t *keys = lds, *surv = lds + nch * WAVE, *sel = surv + nch * k;
-  float v[MAX_EXPERTS / WAVE];
-#pragma unroll
-  for (int c = 0; c < MAX_EXPERTS / WAVE; ++c) {
+// workgroups of the launch (system-scope loads).  Lane j < k gets the j-th expert and weight.
+QMOE_DEV void topk_wave(const float *lrow, int E, int k, const float *pes, int &myi, float &myw) {
+  const int lane = threadIdx.x % WAVE;
+  float l;
+  topk_select(topk_chunks(E), [&](int c) {
     const int e = c * WAVE + lane;
-    v[c] = (c < nch && e < E) ? ld_sys(lrow + e) : 0.f;
-  }
-#pragma unroll
-  for (int c = 0; c < MAX_EXPERTS / WAVE; ++c) {
-    const int e = c * WAVE + lane;
-    if (c < nch) keys[e] = (e < E) ? topk_key(v[c], e) : topk_pad_key(e);
-  }
-  __builtin_amdgcn_wave_barrier();
-  for (int c = 0; c < nch; ++c) topk_rank_chunk(keys + c * WAVE, k, surv + c * k);
-  __builtin_amdgcn_wave_barrier();
-  topk_rank_survivors(surv, nch * k, k, sel);
-  __builtin_amdgcn_wave_barrier();
-  topk_weights(sel, k, pes, myi, myw);
+    return e < E ? topk_ord(ld_sys(lrow + e)) : 0u;
+  }, k, myi, l);
+  myw = topk_weight(myi, l, k, pes);
+  if (lane >= k) myi = 0;
 }
 
 // ---------------------------------------------------------------- bucketing (one workgroup)
@@ -532,12 +543,11 @@ QMOE_DEV void router_finish(const RouterArgs &a, int tb, char *smem) {
   const int wv = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
   const int t0 = tb * ROUTER_TB;
   const int nt = min(ROUTER_TB, a.T - t0);
-  uint64_t *lds = (uint64_t *)(smem + (size_t)wv * topk_lds_bytes(a.E, a.k));
   for (int i = wv; i < nt; i += ROUTER_WAVES) {
     const int t = t0 + i;
     int myi;
     float myw;
-    topk_wave(a.logits + (size_t)t * a.E, a.E, a.k, a.pes, lds, myi, myw);
+    topk_wave(a.logits + (size_t)t * a.E, a.E, a.k, a.pes, myi, myw);
     if (lane < a.k) {
       st_sys(a.topk_idx + (size_t)t * a.k + lane, myi);
       st_sys(a.topk_w + (size_t)t * a.k + lane, myw);
