@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--layers", type=int, default=0, help="0 = the workload's full stack")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-extra", action="store_true",
+                   help="skip the post-norm stack and the other workload shapes")
     p.add_argument("--cpu-sample", type=int, default=8, help="token-layers timed on the oracle")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (reads MIB, writes MIB) a few "
@@ -233,8 +235,9 @@ def run_decode(args, cfg, layers):
         kern_bytes = all_bytes
         traffic = stored_traffic(f"decode_layer_kernel_{cfg.name}")
     else:
-        kernel = "gu_kernel (routed gate/up + SwiGLU)"
-        kern_bytes = n_dist * 2 * G.matrix_bytes(cfg.inter, H)
+        kernel = "gu_pf_kernel (routed and shared gate/up + SwiGLU, matrix cores)"
+        kern_bytes = (n_dist * 2 * G.matrix_bytes(cfg.inter, H)
+                      + 2 * G.matrix_bytes(cfg.shared_inter, H))
         traffic = None
     tok_s_layer = T * L / (ms_step / 1e3)
     layer_s = ms_step / 1e3 / L
@@ -247,6 +250,66 @@ def run_decode(args, cfg, layers):
         credited=credited, all_bytes=all_bytes, distinct=n_dist, timing_src=timing_src,
         traffic=traffic,
     )
+
+
+def time_stack(ops, weights, xs, ws, steps):
+    """Seconds per layer call of one graph replaying the stack (xs[l] -> its own output)."""
+    import torch
+    outs = [torch.empty_like(x) for x in xs]
+    for w, x, o in zip(weights, xs, outs):
+        ops.layer_forward(w, x, ws, out=o)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for w, x, o in zip(weights, xs, outs):
+            ops.layer_forward(w, x, ws, out=o)
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps / len(weights)
+
+
+def run_post(layers, cfg, steps):
+    """The decode stack with the post-combine norm and layer scalar switched on."""
+    import torch
+    from quantized_moe_router_amd import ops
+    from workloads import gen as G
+    weights, keep = [], []
+    for l, (pl, _) in enumerate(layers):
+        gain, scalar = G.make_post(cfg, l)
+        g = torch.from_numpy(gain).cuda()
+        sc = torch.tensor([scalar], dtype=torch.float32, device="cuda")
+        keep += [g, sc]
+        weights.append(ops.LayerWeights(pl.dims, pl.router, pl.store, pl.stride, pl.shared,
+                                        post_norm_gain=g, layer_scalar=sc))
+    xs = [x for x in layer_inputs(cfg, 0, len(layers), cfg.tokens)]
+    ws = ops.workspace(layers[0][0].dims, cfg.tokens)
+    return time_stack(ops, weights, xs, ws, steps)
+
+
+def run_other_configs(n_layers, steps):
+    """Per-layer time of the other workload shapes on a short stack of their own layers."""
+    from quantized_moe_router_amd import ops
+    from workloads import gen as G
+    res = {}
+    for name, src in [("qwen3_next_80b_a3b_decode_b1", None),
+                      ("qwen3_next_80b_a3b_decode_b16", "qwen3_next_80b_a3b_decode_b1"),
+                      ("qwen3_6_35b_a3b_long_prefill", None)]:
+        cfg = G.config(name)
+        layers = build_stack(G.config(src or name), n_layers)
+        xs = [x for x in layer_inputs(cfg, 0, n_layers, cfg.tokens)]
+        ws = ops.workspace(layers[0][0].dims, cfg.tokens)
+        sec = time_stack(ops, [pl.weights for pl, _ in layers], xs, ws, steps)
+        res[name] = {"tokens_per_call": cfg.tokens, "us_per_layer_call": round(sec * 1e6, 2),
+                     "tokens_per_s_per_layer": round(cfg.tokens / sec, 1),
+                     "stack": f"{n_layers} layers of this shape (of {cfg.layers})"}
+        del layers, xs, ws
+        import torch
+        torch.cuda.empty_cache()
+    return res
 
 
 def run_prefill(layers, cfg_pf, reps=3):
@@ -337,6 +400,13 @@ def main():
     if not args.no_prefill and cfg.name == "gemma4_26b_a4b_decode":
         log("prefill timing")
         pf = run_prefill(layers, G.config("gemma4_26b_a4b_prefill"))
+    post = other = None
+    if not args.no_extra and cfg.tokens == 1:
+        log("post-combine norm stack timing")
+        post = run_post(layers, cfg, args.steps)
+        if cfg.name == "gemma4_26b_a4b_decode":
+            log("other workload shapes (4-layer stacks)")
+            other = run_other_configs(4, args.steps)
     cb = None
     if not args.no_cpu_baseline:
         log("cpu oracle timing")
@@ -389,6 +459,13 @@ def main():
             "credited_GBps": round(pf["credited_gbps"], 1),
             "distinct_experts_per_chunk": round(pf["distinct_mean"], 2),
         }
+    if post:
+        out["post_combine_norm"] = {
+            "workload": f"{cfg.name} with the post-combine RMS norm (gain) and layer scalar",
+            "us_per_layer": round(post * 1e6, 3),
+        }
+    if other:
+        out["other_workloads"] = other
     if cb:
         out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)

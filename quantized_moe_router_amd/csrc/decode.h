@@ -71,7 +71,6 @@ struct DecodeArgs {
   const float *gain;            // [H] post-combine norm gain, or null (no norm)
   const float *lscale;          // [1] layer scalar, or null (1)
   uint64_t *nrm;                // [combining workgroups] tagged partial sums of m^2
-  uint64_t *mrow;               // [H] tagged combined branches m (post-combine norm only)
   int nR, nSG, nRG, nSD, nRD;
 };
 
@@ -400,10 +399,14 @@ QMOE_DEV void dec_routed_down(const DecodeArgs &a, int b, unsigned ep, char *sme
     m += sh;
   }
   if (a.gain) {
-    // post-combine norm: every combining workgroup publishes m for its rows and the sum of
-    // m^2 over them; the last one to arrive normalises the whole row (waiting on no one).
+    // post-combine norm: every combining workgroup publishes the sum of m^2 over its rows,
+    // reads all of them (summed in the same order everywhere) and finishes its rows.  These
+    // are the only waits on higher workgroup indices in the launch; they cannot block, because
+    // the combining workgroups are far fewer than the workgroups the device holds at once and
+    // every other role finishes without waiting on them.
     float *nr_lds = (float *)(smem + L.nrm);  // [DEC_W] wave sums, then [groups] partials
-    if (mine) st_tag(a.mrow + row0 + r, ep, m);
+    const float xr = mine ? bf16_to_f32(a.x[row0 + r]) : 0.f;
+    const float gr = mine ? a.gain[row0 + r] : 0.f;
     const float ss = wave_sum(mine ? m * m : 0.f);
     if (tid % WAVE == 0) nr_lds[wv] = ss;
     __syncthreads();
@@ -412,23 +415,18 @@ QMOE_DEV void dec_routed_down(const DecodeArgs &a, int b, unsigned ep, char *sme
       for (int i = 0; i < DEC_W; ++i) p += nr_lds[i];
       st_tag(a.nrm + g, ep, p);
     }
-    if (!arrive_last(sy(a, SY_DONE), (unsigned)groups)) return;
     float *part = nr_lds + DEC_W;
     fetch_tags<1>(a, groups, ep, [&](int i) { return a.nrm + i; },
                   [&](int i, float v) { part[i] = v; });
     float tot = 0.f;
     for (int i = 0; i < groups; ++i) tot += part[i];
-    const float rs = 1.f / sqrtf(tot / (float)a.H + RMS_EPS);
-    const float al = a.lscale ? *a.lscale : 1.f;
-    fetch_tags<12>(a, a.H, ep, [&](int i) { return a.mrow + i; }, [&](int i, float v) {
-      const float o = (bf16_to_f32(a.x[i]) + a.gain[i] * (v * rs)) * al;
-      a.out[i] = (uint16_t)f32_to_bf16_bits(o);
-      if (a.out_f32) a.out_f32[i] = o;
-    });
-    if (tid == 0) st_sys_u(sy(a, SY_EPOCH), ep);
-    return;
-  }
-  if (mine) {
+    if (mine) {
+      float o = xr + gr * (m * (1.f / sqrtf(tot / (float)a.H + RMS_EPS)));
+      if (a.lscale) o *= *a.lscale;
+      a.out[row0 + r] = (uint16_t)f32_to_bf16_bits(o);
+      if (a.out_f32) a.out_f32[row0 + r] = o;
+    }
+  } else if (mine) {
     float o = bf16_to_f32(a.x[row0 + r]) + m;
     if (a.lscale) o *= *a.lscale;
     a.out[row0 + r] = (uint16_t)f32_to_bf16_bits(o);

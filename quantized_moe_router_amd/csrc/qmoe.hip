@@ -133,7 +133,7 @@ inline int dec_shared_chunks(const qmoe_dims *d) {
 struct WsLayout {
   size_t cnt, logits, tidx, tw, counts, offsets, sorted, active, nact, slot_tab;
   size_t hr_hi, hr_lo, hs_hi, hs_lo, y, ysh, gx, ghr, ghs;
-  size_t dec_logits, dec_hr, dec_hsh, dec_yr, dec_ysh, dec_nrm, dec_m, total;
+  size_t dec_logits, dec_hr, dec_hsh, dec_yr, dec_ysh, dec_nrm, total;
 };
 
 WsLayout ws_layout(const qmoe_dims *d, int Tmax) {
@@ -166,7 +166,6 @@ WsLayout ws_layout(const qmoe_dims *d, int Tmax) {
   w.dec_yr = o; o += al((k - 1) * H * 8);
   w.dec_ysh = o; o += al((size_t)dec_shared_chunks(d) * H * 8);
   w.dec_nrm = o; o += al((H / TILE_ROWS) * 8);
-  w.dec_m = o; o += al(H * 8);
   w.total = o;
   return w;
 }
@@ -455,7 +454,6 @@ static int launch_decode(const qmoe_layer *L, const uint16_t *x, uint16_t *out, 
   a.topk_idx = idx; a.topk_w = w; a.out = out; a.out_f32 = out_f32;
   a.gain = L->post_norm_gain; a.lscale = L->layer_scalar;
   a.nrm = at<uint64_t>(ws, wl.dec_nrm);
-  a.mrow = at<uint64_t>(ws, wl.dec_m);
   const int tiles_d = a.H / TILE_ROWS, tpw = dec_tiles_per_wg(a.wpt);
   a.nR = (a.E + ROUTER_WAVES - 1) / ROUTER_WAVES;   // one expert per wave
   a.nSG = sh ? a.Is / 16 : 0;
