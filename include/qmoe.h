@@ -39,8 +39,7 @@
  *    they use different workspaces and outputs.  Outputs must not alias inputs.
  *  - T = 0 (no tokens) is a valid no-op that returns QMOE_OK.
  *  - Shape limits: hidden, inter and shared_inter are multiples of 64; hidden <= 8192,
- *    inter and shared_inter <= 4096 (so that one workgroup stages a block of activations in
- *    LDS); group == 64; 1 <= top_k <= min(n_experts, 32); 1 <= n_experts <= 1024;
+ *    inter and shared_inter <= 4096; group == 64; expert_bits 0, 4 or 8; 1 <= top_k <= min(n_experts, 32); 1 <= n_experts <= 1024;
  *    T <= 65536 per call.  Store base pointers and strides are 256-byte aligned.
  *
  * Quantised formats (canonical, as the pages describe them)
@@ -51,6 +50,10 @@
  *  bias bf16 [E, H/64], value = s * q + b.
  *  An expert is gate [I, H], up [I, H] and down [H, I] int4 matrices (SwiGLU:
  *  h = silu(x gate^T) * (x up^T), y = h down^T, silu(z) = z / (1 + exp(-z))).
+ *  With qmoe_dims.expert_bits = 8 the expert matrices are int8 like the router (codes
+ *  uint8 [R, K], MLX int8 group quantisation as in [SW-mem]'s runtime): the store then
+ *  holds every 64-weight group as two 4-bit k-steps (high nibbles with scale 16*s and bias
+ *  b, low nibbles with scale s and bias 0), twice the k-steps of a 4-bit block.
  */
 #ifndef QMOE_H
 #define QMOE_H
@@ -81,6 +84,8 @@ typedef struct {
     int32_t inter;         /* I, routed expert width */
     int32_t shared_inter;  /* Is, shared expert width (0: none) */
     int32_t group;         /* 64 */
+    int32_t expert_bits;   /* bits of the routed and shared expert codes: 0 or 4 (MLX int4),
+                              8 (MLX int8, [SW-mem]); the router is always 8-bit */
 } qmoe_dims;
 
 /* Router weights of one layer [TF-struct] router listing, [TF-mem] 8-bit projection. */
@@ -136,8 +141,8 @@ int qmoe_workspace_init(void *ws, size_t ws_bytes, qmoe_stream_t stream);
 
 /* ---------------------------------------------------------------- expert store */
 
-/* Copy one expert from the canonical int4 arrays (gate/up [inter, H], down [H, inter], see the
- * format above; all device pointers) into `dst_block` (device, qmoe_expert_stride bytes,
+/* Copy one expert from the canonical int4 (or, with d->expert_bits = 8, int8) arrays (gate/up
+ * [inter, H], down [H, inter], see the formats above; all device pointers) into `dst_block` (device, qmoe_expert_stride bytes,
  * 256-byte aligned) in the store's tiled order.  Layout change only: every code, scale and
  * bias bit is copied, nothing is dequantised or requantised [TF-inst].  `inter` is d->inter
  * for a routed expert or d->shared_inter for the shared block. */

@@ -186,14 +186,16 @@ def bucket(top, n_experts):
 # ------------------------------------------------------------------ expert FFN
 
 def expert_ffn(x, weights, return_h=False):
-    """SwiGLU expert on fp64 rows x [m, H]; weights dequantised on the fly.
+    """SwiGLU expert on fp64 rows x [m, H]; weights dequantised on the fly (int4 codes, or
+    int8 codes when weights.bits == 8: the MLX 8-bit group format of [SW-mem]'s runtime).
 
     g = x W_g^T, v = x W_u^T, h = silu(g) * v, y = h W_d^T with W = s*q + b.
     """
     x = np.asarray(x, dtype=np.float64)
-    Wg = dequant_int4(weights.gate_q, weights.gate_s, weights.gate_b)   # [I, H]
-    Wu = dequant_int4(weights.up_q, weights.up_s, weights.up_b)         # [I, H]
-    Wd = dequant_int4(weights.down_q, weights.down_s, weights.down_b)   # [H, I]
+    deq = dequant_int8 if getattr(weights, "bits", 4) == 8 else dequant_int4
+    Wg = deq(weights.gate_q, weights.gate_s, weights.gate_b)   # [I, H]
+    Wu = deq(weights.up_q, weights.up_s, weights.up_b)         # [I, H]
+    Wd = deq(weights.down_q, weights.down_s, weights.down_b)   # [H, I]
     g = x @ Wg.T
     v = x @ Wu.T
     with np.errstate(over="ignore"):

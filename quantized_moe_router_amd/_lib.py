@@ -30,7 +30,8 @@ class QmoeError(RuntimeError):
 class Dims(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("inter", ctypes.c_int32),
-                ("shared_inter", ctypes.c_int32), ("group", ctypes.c_int32)]
+                ("shared_inter", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("expert_bits", ctypes.c_int32)]
 
 
 class Router(ctypes.Structure):
@@ -100,5 +101,5 @@ def check(rc):
     return rc
 
 
-def make_dims(hidden, n_experts, top_k, inter, shared_inter=0, group=64):
-    return Dims(hidden, n_experts, top_k, inter, shared_inter, group)
+def make_dims(hidden, n_experts, top_k, inter, shared_inter=0, group=64, expert_bits=4):
+    return Dims(hidden, n_experts, top_k, inter, shared_inter, group, expert_bits)

@@ -54,6 +54,7 @@ struct DecodeArgs {
   size_t stride;
   const uint8_t *shared;        // null: no shared expert
   int H, E, k, I, Is;
+  int kshift;                   // k-steps per expert-code group: 0 (4-bit) or 1 (8-bit)
   int nc;                       // shared down K chunks per output tile
   int wpt;                      // waves per routed down tile (1, 2 or 4)
   float inv_sqrt_h;
@@ -220,7 +221,7 @@ QMOE_DEV void dec_stage_x(const DecodeArgs &a, char *smem, const DecLds &L) {
 // each of the H_COPIES copies.
 QMOE_DEV void dec_gate_up(const DecodeArgs &a, const uint8_t *blk, int tile, uint64_t *h_out,
                           size_t copy_stride, unsigned ep, char *smem, const DecLds &L) {
-  const int H = a.H, KS = H / GROUP;
+  const int H = a.H, KS = (H / GROUP) << a.kshift;
   const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
   const int rr = lane % 32, half = lane / 32;
   const uint16_t *xl = (const uint16_t *)(smem + L.x);
@@ -236,7 +237,7 @@ QMOE_DEV void dec_gate_up(const DecodeArgs &a, const uint8_t *blk, int tile, uin
 #pragma unroll
     for (int u = 0; u < KB_DEC; ++u)
       if (kc + u < nk) {
-        const int col = (ks0 + kc + u) * GROUP + half * 32;
+        const int col = ((ks0 + kc + u) >> a.kshift) * GROUP + half * 32;
         acc += kstep_bf16(cv[u], sb[u], xl + col, xs[col / 32]);
       }
   }
@@ -263,8 +264,8 @@ struct DownRegs {
 QMOE_DEV void dec_down_load(const DecodeArgs &a, const uint8_t *blk, int K, int tile, int kb0,
                             int nk, DownRegs &d) {
   const int lane = threadIdx.x % WAVE;
-  const BlockGeom geo = block_geom(a.H, K);
-  const uint8_t *tbase = blk + geo.gu_bytes + (size_t)tile * (K / GROUP) * KSTEP_BYTES;
+  const BlockGeom geo = block_geom(a.H, K, a.kshift);
+  const uint8_t *tbase = blk + geo.gu_bytes + (size_t)tile * geo.d_ks * KSTEP_BYTES;
   d.nk = nk;
   if (nk > 0) load_batch<KB_DEC>(tbase, kb0, 0, nk, lane, lane % 32, d.cv, d.sb);
 }
@@ -303,8 +304,10 @@ QMOE_DEV void dec_stage_h(const DecodeArgs &a, const uint64_t *src, int n, unsig
 }
 
 // This wave's partial dot products for its 32 rows over its loaded k-steps; local k-step u
-// of the wave is column block kb0 + u of the staged h.  The 32 sums go to red[wave][row].
-QMOE_DEV void dec_down_dot(const DownRegs &d, int kb0, char *smem, const DecLds &L) {
+// of the wave is k-step kb0 + u, whose activations are column block ((kb0 + u) >> kshift) -
+// g0 of the staged h (staged from group g0 on).  The 32 sums go to red[wave][row].
+QMOE_DEV void dec_down_dot(const DownRegs &d, int kb0, int g0, int kshift, char *smem,
+                           const DecLds &L) {
   const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
   const int rr = lane % 32, half = lane / 32;
   const uint16_t *hh = (const uint16_t *)(smem + L.hh), *hl = (const uint16_t *)(smem + L.hl);
@@ -314,7 +317,7 @@ QMOE_DEV void dec_down_dot(const DownRegs &d, int kb0, char *smem, const DecLds 
 #pragma unroll
   for (int u = 0; u < KB_DEC; ++u)
     if (u < d.nk) {
-      const int col = (kb0 + u) * GROUP + half * 32;
+      const int col = (((kb0 + u) >> kshift) - g0) * GROUP + half * 32;
       acc += kstep_hilo(d.cv[u], d.sb[u], hh + col, hl + col, hs[col / 32]);
     }
   acc += __shfl_xor(acc, 32, WAVE);
@@ -325,8 +328,9 @@ QMOE_DEV void dec_down_dot(const DownRegs &d, int kb0, char *smem, const DecLds 
 QMOE_DEV void dec_shared_down(const DecodeArgs &a, int b, unsigned ep, char *smem, const DecLds &L) {
   const int tiles_d = a.H / TILE_ROWS;
   const int tile = b % tiles_d, c = b / tiles_d;
-  const int KS = a.Is / GROUP;
-  const int kb0 = (KS * c) / a.nc, kb1 = (KS * (c + 1)) / a.nc;
+  const int NG = a.Is / GROUP;
+  const int g0 = (NG * c) / a.nc, g1 = (NG * (c + 1)) / a.nc;   // this chunk's groups
+  const int kb0 = g0 << a.kshift, kb1 = g1 << a.kshift;        // and its k-steps
   const int wv = threadIdx.x / WAVE;
   const int n = kb1 - kb0;
   const int w0 = (n * wv) / DEC_W, w1 = (n * (wv + 1)) / DEC_W;
@@ -335,9 +339,9 @@ QMOE_DEV void dec_shared_down(const DecodeArgs &a, int b, unsigned ep, char *sme
   wait_tags(a, a.logits + (size_t)(blockIdx.x % LOGIT_COPIES) * a.logit_copy + (a.E - 1), 1, 1, ep);
   DownRegs d;
   dec_down_load(a, a.shared, a.Is, tile, kb0 + w0, w1 - w0, d);
-  dec_stage_h(a, a.h_sh + (size_t)(tile % H_COPIES) * a.hsh_copy + (size_t)kb0 * GROUP, n * GROUP,
-              ep, smem, L);
-  dec_down_dot(d, w0, smem, L);
+  dec_stage_h(a, a.h_sh + (size_t)(tile % H_COPIES) * a.hsh_copy + (size_t)g0 * GROUP,
+              (g1 - g0) * GROUP, ep, smem, L);
+  dec_down_dot(d, kb0 + w0, g0, a.kshift, smem, L);
   __syncthreads();
   if (threadIdx.x < 32) {
     const float *red = (const float *)(smem + L.red);
@@ -355,14 +359,14 @@ QMOE_DEV void dec_routed_down(const DecodeArgs &a, int b, unsigned ep, char *sme
   int e;
   float w;
   dec_topk(a, ep, slot, false, e, w, smem, L);
-  const int KS = a.I / GROUP;
+  const int KS = (a.I / GROUP) << a.kshift;
   const int tile = g * tpw + wv / a.wpt, part = wv % a.wpt;
   const int kb0 = (KS * part) / a.wpt, kb1 = (KS * (part + 1)) / a.wpt;
   DownRegs d;
   dec_down_load(a, a.experts + (size_t)e * a.stride, a.I, min(tile, tiles_d - 1), kb0,
                 tile < tiles_d ? kb1 - kb0 : 0, d);
   dec_stage_h(a, a.h_r + (size_t)(g % H_COPIES) * a.hr_copy + (size_t)slot * a.I, a.I, ep, smem, L);
-  dec_down_dot(d, kb0, smem, L);
+  dec_down_dot(d, kb0, 0, a.kshift, smem, L);
   __syncthreads();
   // row r of this group (tile r / 32 of the group): the wpt waves of its tile add up
   const float *red = (const float *)(smem + L.red);

@@ -20,6 +20,7 @@ struct FfnArgs {
   size_t stride;
   const uint8_t *shared;      // shared block or null
   int H, I, Is, k, T, n_experts;
+  int kshift;                 // k-steps per group: 0 (4-bit experts) or 1 (8-bit, two planes)
   const uint16_t *x;          // [T, H] bf16
   const int32_t *offsets, *sorted, *active, *n_active;
   int n_slots;                // routed slots in the grid: active experts (no slot table) or
@@ -177,7 +178,7 @@ template <int W, int MB, int KB>
 QMOE_DEV void gu_tile(const FfnArgs &a, const SlotRows &sr, int tile, char *smem) {
   const int H = a.H;
   const int I = sr.shared ? a.Is : a.I;
-  const int KS = H / GROUP;
+  const int KS = (H / GROUP) << a.kshift;
   const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
   const int rr = lane % 32, half = lane / 32;
   uint16_t *xl = (uint16_t *)smem;                              // [MB][H]
@@ -202,7 +203,7 @@ QMOE_DEV void gu_tile(const FfnArgs &a, const SlotRows &sr, int tile, char *smem
 #pragma unroll
       for (int u = 0; u < KB; ++u) {
         if (kc + u < nk) {
-          const int col = (ks0 + kc + u) * GROUP + half * 32;
+          const int col = ((ks0 + kc + u) >> a.kshift) * GROUP + half * 32;
 #pragma unroll
           for (int i = 0; i < MB; ++i)
             if (i < mb)
@@ -263,14 +264,15 @@ inline __host__ __device__ size_t d_lds_bytes(int Kc) {
   return (size_t)MB * Kc * 4 + (size_t)MB * (Kc / 32) * 4 + (size_t)W * MB * 32 * 4;
 }
 
-// k-steps [kb0, kb0 + nks) of one 32-row output tile of the down projection of slot `sr`
-// (K = the block's width).  Output rows go to dst (row of token r0+i = ysel(r0+i)).
+// Groups [kb0, kb0 + nks) of one 32-row output tile of the down projection of slot `sr`
+// (K = the block's width; a group is 1 << kshift k-steps).  Output rows go to dst (row of
+// token r0+i = ysel(r0+i)).
 template <int W, int MB, int KB, class YSel>
 QMOE_DEV void d_tile(const FfnArgs &a, const SlotRows &sr, int tile, int kb0, int nks,
                      float *dst, YSel ysel, char *smem) {
   const int H = a.H;
   const int K = sr.shared ? a.Is : a.I;
-  const int KS = K / GROUP;
+  const int KS = (K / GROUP) << a.kshift, nkk = nks << a.kshift;
   const int Kc = nks * GROUP;
   const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
   const int rr = lane % 32, half = lane / 32;
@@ -278,9 +280,10 @@ QMOE_DEV void d_tile(const FfnArgs &a, const SlotRows &sr, int tile, int kb0, in
   uint16_t *hl = hh + (size_t)MB * Kc;                          // [MB][Kc]
   float *hs = (float *)(hl + (size_t)MB * Kc);                  // [MB][Kc/32]
   float *red = hs + MB * (Kc / 32);                             // [W][MB][32]
-  const BlockGeom geo = block_geom(H, K);
-  const uint8_t *tbase = sr.blk + geo.gu_bytes + ((size_t)tile * KS + kb0) * KSTEP_BYTES;
-  const int ks0 = (nks * wv) / W, nk = (nks * (wv + 1)) / W - ks0;
+  const BlockGeom geo = block_geom(H, K, a.kshift);
+  const uint8_t *tbase =
+      sr.blk + geo.gu_bytes + ((size_t)tile * KS + ((size_t)kb0 << a.kshift)) * KSTEP_BYTES;
+  const int ks0 = (nkk * wv) / W, nk = (nkk * (wv + 1)) / W - ks0;
   const uint16_t *src_hi = (sr.shared ? a.hs_hi : a.hr_hi) + (size_t)kb0 * GROUP;
   const uint16_t *src_lo = (sr.shared ? a.hs_lo : a.hr_lo) + (size_t)kb0 * GROUP;
   qmoe_u32x4 cv[KB];
@@ -314,7 +317,7 @@ QMOE_DEV void d_tile(const FfnArgs &a, const SlotRows &sr, int tile, int kb0, in
 #pragma unroll
       for (int u = 0; u < KB; ++u) {
         if (kc + u < nk) {
-          const int col = (ks0 + kc + u) * GROUP + half * 32;
+          const int col = ((ks0 + kc + u) >> a.kshift) * GROUP + half * 32;
 #pragma unroll
           for (int i = 0; i < MB; ++i)
             if (i < mb)

@@ -96,10 +96,12 @@ QMOE_DEV void pf_kstep(qmoe_f32x4 (&acc)[NT][2], const qmoe_u32x4 (&cv)[NT],
 // KB consecutive k-steps from ks0 of NT tiles (tile j at tb[j]) (with TAIL only those below
 // nks; the loads past the end re-read the last k-step and are not used), all loads issued
 // before any product.  ap[p]: the lane's row of plane p, offset to its 8-column piece
-// (k-step ks, half h at ap[p] + 64 ks + 32 h); grow: the row's group sums.
+// (group g, half h at ap[p] + 64 g + 32 h; k-step ks reads group ks >> kshift); grow: the
+// row's group sums.
 template <int NP, int NT, int KB, bool TAIL>
 QMOE_DEV void pf_batch(qmoe_f32x4 (&acc)[NT][2], const uint8_t *const (&tb)[NT], int ks0, int nks,
-                       const uint16_t *const (&ap)[NP], const float *grow, bool gmask) {
+                       const uint16_t *const (&ap)[NP], const float *grow, bool gmask,
+                       int kshift) {
   const int lane = threadIdx.x % WAVE, n = lane % 16;
   qmoe_u32x4 cv[KB][NT], xa[KB][NP][2];
   uint32_t sb[KB][NT][2];
@@ -114,12 +116,13 @@ QMOE_DEV void pf_batch(qmoe_f32x4 (&acc)[NT][2], const uint8_t *const (&tb)[NT],
       sb[u][j][0] = *(const uint32_t *)(st + 1024 + 4 * n);
       sb[u][j][1] = *(const uint32_t *)(st + 1024 + 64 + 4 * n);
     }
+    const int grp = ks >> kshift;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-      xa[u][p][0] = *(const qmoe_u32x4 *)(ap[p] + GROUP * ks);
-      xa[u][p][1] = *(const qmoe_u32x4 *)(ap[p] + GROUP * ks + 32);
+      xa[u][p][0] = *(const qmoe_u32x4 *)(ap[p] + GROUP * grp);
+      xa[u][p][1] = *(const qmoe_u32x4 *)(ap[p] + GROUP * grp + 32);
     }
-    g[u] = grow[ks];
+    g[u] = grow[grp];
   }
 #pragma unroll
   for (int u = 0; u < KB; ++u)
@@ -128,15 +131,17 @@ QMOE_DEV void pf_batch(qmoe_f32x4 (&acc)[NT][2], const uint8_t *const (&tb)[NT],
 
 template <int NP, int NT, int KB>
 QMOE_DEV void pf_tiles(qmoe_f32x4 (&acc)[NT][2], const uint8_t *const (&tb)[NT], int nks,
-                       const uint16_t *const (&ap)[NP], const float *grow, bool gmask) {
+                       const uint16_t *const (&ap)[NP], const float *grow, bool gmask,
+                       int kshift) {
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     acc[j][0] = qmoe_f32x4{0.f, 0.f, 0.f, 0.f};
     acc[j][1] = qmoe_f32x4{0.f, 0.f, 0.f, 0.f};
   }
   int k0 = 0;
-  for (; k0 + KB <= nks; k0 += KB) pf_batch<NP, NT, KB, false>(acc, tb, k0, nks, ap, grow, gmask);
-  if (k0 < nks) pf_batch<NP, NT, KB, true>(acc, tb, k0, nks, ap, grow, gmask);
+  for (; k0 + KB <= nks; k0 += KB)
+    pf_batch<NP, NT, KB, false>(acc, tb, k0, nks, ap, grow, gmask, kshift);
+  if (k0 < nks) pf_batch<NP, NT, KB, true>(acc, tb, k0, nks, ap, grow, gmask, kshift);
 }
 
 // ---------------------------------------------------------------- gate/up + SwiGLU
@@ -149,7 +154,7 @@ QMOE_DEV void pf_tiles(qmoe_f32x4 (&acc)[NT][2], const uint8_t *const (&tb)[NT],
 // gh_s.
 __global__ void __launch_bounds__(GU_WAVES * WAVE) gu_pf_kernel(FfnArgs a) {
   __shared__ float gpart[GU_WAVES][PF_MT];
-  const int H = a.H, KS = H / GROUP;
+  const int H = a.H, KG = H / GROUP, KS = KG << a.kshift;
   const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE, n = lane % 16, lg = lane / 16;
   const int grp_s = a.shared ? a.Is / GROUP : 0;
   const int n_sh = grp_s * ((a.T + PF_MT - 1) / PF_MT);
@@ -184,7 +189,7 @@ __global__ void __launch_bounds__(GU_WAVES * WAVE) gu_pf_kernel(FfnArgs a) {
     const int tok = sr.shared ? p0 + r : flat_of(a, sr, p0 + r) / a.k;
     const uint16_t *const ap[1] = {a.x + (size_t)tok * H + 8 * lg};
     qmoe_f32x4 acc[GU_NT][2];
-    pf_tiles<1, GU_NT, GU_KB>(acc, tb, KS, ap, a.gx + (size_t)tok * KS, lg == 0);
+    pf_tiles<1, GU_NT, GU_KB>(acc, tb, KS, ap, a.gx + (size_t)tok * KG, lg == 0, a.kshift);
     float hs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < GU_NT; ++j) {
@@ -253,8 +258,8 @@ __global__ void __launch_bounds__(D_WAVES * WAVE) d_pf_kernel(FfnArgs a) {
   }
   const int tile0 = (D_WAVES * tg + wv) * D_NT;
   if (tile0 >= tiles) return;  // no barrier in this kernel
-  const int K = sr.shared ? a.Is : a.I, KSd = K / GROUP;
-  const uint8_t *dbase = sr.blk + block_geom(H, K).gu_bytes;
+  const int K = sr.shared ? a.Is : a.I, KGd = K / GROUP, KSd = KGd << a.kshift;
+  const uint8_t *dbase = sr.blk + block_geom(H, K, a.kshift).gu_bytes;
   const uint8_t *tb[D_NT];
 #pragma unroll
   for (int j = 0; j < D_NT; ++j)  // tiles past the end re-read the last one (not stored)
@@ -268,7 +273,7 @@ __global__ void __launch_bounds__(D_WAVES * WAVE) d_pf_kernel(FfnArgs a) {
     const size_t pos = (size_t)(pos0 + p0 + min(n, mt - 1));  // padding lanes repeat the last row
     const uint16_t *const ap[2] = {phi + pos * K + 8 * lg, plo + pos * K + 8 * lg};
     qmoe_f32x4 acc[D_NT][2];
-    pf_tiles<2, D_NT, D_KB>(acc, tb, KSd, ap, gh + pos * KSd, lg == 0);
+    pf_tiles<2, D_NT, D_KB>(acc, tb, KSd, ap, gh + pos * KGd, lg == 0, a.kshift);
     int flat = 0;
     if (!sr.shared && lane < mt) flat = flat_of(a, sr, p0 + lane);
 #pragma unroll

@@ -77,8 +77,13 @@ int check_dims(const qmoe_dims *d) {
     return fail(QMOE_ERR_SHAPE, "n_experts must be in [1, %d] (got %d)", MAX_EXPERTS, d->n_experts);
   if (d->top_k < 1 || d->top_k > MAX_TOPK || d->top_k > d->n_experts)
     return fail(QMOE_ERR_SHAPE, "top_k must be in [1, min(n_experts, 32)] (got %d)", d->top_k);
+  if (d->expert_bits != 0 && d->expert_bits != 4 && d->expert_bits != 8)
+    return fail(QMOE_ERR_SHAPE, "expert_bits must be 0 or 4 (4-bit) or 8 (got %d)", d->expert_bits);
   return QMOE_OK;
 }
+
+// k-steps per quantisation group of the expert store: 1 for 4-bit experts, 2 for 8-bit ones
+inline int kshift_of(const qmoe_dims *d) { return d->expert_bits == 8 ? 1 : 0; }
 
 int check_T(int32_t T) {
   if (T < 0 || T > MAX_T) return fail(QMOE_ERR_SHAPE, "T must be in [0, %d] (got %d)", MAX_T, T);
@@ -126,8 +131,8 @@ inline int shared_chunks(const qmoe_dims *d) {
 // tile's k-steps over their four waves (at most DEC_W * KB_DEC k-steps per chunk).
 inline int dec_shared_chunks(const qmoe_dims *d) {
   if (d->shared_inter == 0) return 0;
-  const int ks = d->shared_inter / GROUP;
-  return (ks + DEC_W * KB_DEC - 1) / (DEC_W * KB_DEC);
+  const int groups = d->shared_inter / GROUP, per = (DEC_W * KB_DEC) >> kshift_of(d);
+  return (groups + per - 1) / per;
 }
 
 struct WsLayout {
@@ -197,9 +202,9 @@ int check_layer(const qmoe_layer *L) {
   if (!L->experts) return fail(QMOE_ERR_ARG, "expert store is NULL");
   if (!aligned(L->experts, 256) || L->expert_stride % 256)
     return fail(QMOE_ERR_ARG, "expert store base and stride must be 256-byte aligned");
-  if (L->expert_stride < block_stride_bytes(L->d.hidden, L->d.inter))
+  if (L->expert_stride < block_stride_bytes(L->d.hidden, L->d.inter, kshift_of(&L->d)))
     return fail(QMOE_ERR_ARG, "expert_stride %zu smaller than the packed block (%zu)",
-                L->expert_stride, block_stride_bytes(L->d.hidden, L->d.inter));
+                L->expert_stride, block_stride_bytes(L->d.hidden, L->d.inter, kshift_of(&L->d)));
   if (L->shared && L->d.shared_inter == 0)
     return fail(QMOE_ERR_ARG, "shared block given but shared_inter is 0");
   if (L->shared && !aligned(L->shared, 256))
@@ -297,6 +302,7 @@ static FfnArgs make_ffn_args(const qmoe_layer *L, const uint16_t *x, int T, cons
   a.x = x;
   a.offsets = offsets; a.sorted = sorted; a.active = active; a.n_active = n_active;
   a.n_slots = std::min(L->d.n_experts, T * L->d.top_k);
+  a.kshift = kshift_of(&L->d);
   a.hr_hi = at<uint16_t>(ws, wl.hr_hi); a.hr_lo = at<uint16_t>(ws, wl.hr_lo);
   a.hs_hi = at<uint16_t>(ws, wl.hs_hi); a.hs_lo = at<uint16_t>(ws, wl.hs_lo);
   a.y = y; a.y_sh = y_sh;
@@ -410,7 +416,7 @@ static int launch_combine_pf(const uint16_t *x, const float *y, const float *w, 
 // the critical path), else the fewest that fit KB_DEC; the shared down width is cut into
 // chunks of at most DEC_W * KB_DEC k-steps.
 static int dec_wpt(const qmoe_dims *d) {
-  const int ks = d->inter / GROUP;
+  const int ks = (d->inter / GROUP) << kshift_of(d);
   for (int lim : {KB_DEC / 2, KB_DEC})
     for (int w = 1; w <= DEC_W; w *= 2)
       if ((ks + w - 1) / w <= lim) return w;
@@ -438,6 +444,7 @@ static int launch_decode(const qmoe_layer *L, const uint16_t *x, uint16_t *out, 
   a.experts = (const uint8_t *)L->experts; a.stride = L->expert_stride;
   a.shared = sh ? (const uint8_t *)L->shared : nullptr;
   a.H = d->hidden; a.E = d->n_experts; a.k = d->top_k; a.I = d->inter;
+  a.kshift = kshift_of(d);
   a.Is = sh ? d->shared_inter : 0;
   a.nc = sh ? dec_shared_chunks(d) : 0;
   a.wpt = dec_wpt(d);
@@ -484,7 +491,7 @@ size_t qmoe_expert_stride(const qmoe_dims *d, int32_t inter) {
     fail(QMOE_ERR_SHAPE, "inter must be a positive multiple of 64 <= 4096 (got %d)", inter);
     return 0;
   }
-  return block_stride_bytes(d->hidden, inter);
+  return block_stride_bytes(d->hidden, inter, kshift_of(d));
 }
 
 size_t qmoe_workspace_bytes(const qmoe_dims *d, int32_t max_tokens) {
@@ -520,10 +527,10 @@ int qmoe_pack_expert(const qmoe_dims *d, int32_t inter, const uint8_t *gate_q,
   if (!aligned(dst_block, 256)) return fail(QMOE_ERR_ARG, "dst_block must be 256-byte aligned");
   if ((rc = check_arch())) return rc;
   CanonExpert c{gate_q, up_q, down_q, gate_s, gate_b, up_s, up_b, down_s, down_b};
-  const BlockGeom g = block_geom(d->hidden, inter);
+  const BlockGeom g = block_geom(d->hidden, inter, kshift_of(d));
   const long n = (long)(g.gu_tiles * g.gu_ks + g.d_tiles * g.d_ks) * 64;
   hipLaunchKernelGGL(pack_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                     (hipStream_t)stream, c, d->hidden, inter, (uint8_t *)dst_block);
+                     (hipStream_t)stream, c, d->hidden, inter, kshift_of(d), (uint8_t *)dst_block);
   QMOE_LAUNCHED();
   return ok();
 }
@@ -542,10 +549,11 @@ int qmoe_unpack_expert(const qmoe_dims *d, int32_t inter, const void *src_block,
   if (!aligned(src_block, 256)) return fail(QMOE_ERR_ARG, "src_block must be 256-byte aligned");
   if ((rc = check_arch())) return rc;
   CanonExpertOut c{gate_q, up_q, down_q, gate_s, gate_b, up_s, up_b, down_s, down_b};
-  const BlockGeom g = block_geom(d->hidden, inter);
+  const BlockGeom g = block_geom(d->hidden, inter, kshift_of(d));
   const long n = (long)(g.gu_tiles * g.gu_ks + g.d_tiles * g.d_ks) * 64;
   hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-                     (hipStream_t)stream, (const uint8_t *)src_block, d->hidden, inter, c);
+                     (hipStream_t)stream, (const uint8_t *)src_block, d->hidden, inter,
+                     kshift_of(d), c);
   QMOE_LAUNCHED();
   return ok();
 }

@@ -16,6 +16,14 @@
 // element 8d+2i+1 in nibble i+4 (i = 0..3), so that one AND-OR yields a bf16 pair aligned
 // with an activation pair.  Wave lane l of a kernel reads chunk l of each k-step: one
 // contiguous 1 KiB load per wave.
+//
+// 8-bit experts (MLX int8 group quantisation, the Swiftlet article, section "같은 모델을 왜
+// 이렇게 적은 메모리로 돌릴 수 있나"): a code q = 16 qh + ql splits into two 4-bit codes, and
+// s q + b = (16 s) qh + s ql + b, so each quantisation group becomes two consecutive k-steps
+// of the layout above -- the high nibbles with scale 16 s (exact in bf16) and bias b, then the
+// low nibbles with scale s and bias 0 -- that multiply the same 64 activations.  Every kernel
+// runs on it unchanged except that k-step ks reads the activations of group ks >> kshift
+// (kshift = 1 for 8-bit experts, 0 for 4-bit ones).  Packing stays exactly invertible.
 #pragma once
 #include "common.h"
 
@@ -23,26 +31,26 @@ namespace qmoe {
 
 struct BlockGeom {
   int H, I;
-  int gu_tiles, gu_ks;   // I/16 tiles, H/64 k-steps each
-  int d_tiles, d_ks;     // H/32 tiles, I/64 k-steps each
+  int gu_tiles, gu_ks;   // I/16 tiles, (H/64) << kshift k-steps each
+  int d_tiles, d_ks;     // H/32 tiles, (I/64) << kshift k-steps each
   size_t gu_bytes, d_bytes;
 };
 
-inline __host__ __device__ BlockGeom block_geom(int H, int I) {
+inline __host__ __device__ BlockGeom block_geom(int H, int I, int kshift) {
   BlockGeom g;
   g.H = H;
   g.I = I;
   g.gu_tiles = I / 16;
-  g.gu_ks = H / GROUP;
+  g.gu_ks = (H / GROUP) << kshift;
   g.d_tiles = H / TILE_ROWS;
-  g.d_ks = I / GROUP;
+  g.d_ks = (I / GROUP) << kshift;
   g.gu_bytes = (size_t)g.gu_tiles * g.gu_ks * KSTEP_BYTES;
   g.d_bytes = (size_t)g.d_tiles * g.d_ks * KSTEP_BYTES;
   return g;
 }
 
-inline size_t block_stride_bytes(int H, int I) {
-  BlockGeom g = block_geom(H, I);
+inline size_t block_stride_bytes(int H, int I, int kshift) {
+  BlockGeom g = block_geom(H, I, kshift);
   size_t b = g.gu_bytes + g.d_bytes;
   return (b + 4095) & ~(size_t)4095;
 }
@@ -59,86 +67,110 @@ struct CanonExpertOut {
   uint16_t *gs, *gb, *us, *ub, *ds, *db;
 };
 
-// one thread per 16-byte chunk of the block (GU chunks first, then D chunks)
-__global__ void pack_kernel(CanonExpert c, int H, int I, uint8_t *dst) {
-  const BlockGeom g = block_geom(H, I);
+// Where chunk `id` of a block (GU chunks first, then D chunks) comes from.
+struct ChunkPos {
+  bool gu;
+  long kst;          // tile * k-steps per tile + ks
+  int chunk, rr, half, row, K, ks, group, plane;
+};
+QMOE_DEV bool chunk_pos(long id, int H, int I, int kshift, ChunkPos &c) {
+  const BlockGeom g = block_geom(H, I, kshift);
   const long n_gu = (long)g.gu_tiles * g.gu_ks * 64;
   const long n_all = n_gu + (long)g.d_tiles * g.d_ks * 64;
-  const long id = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (id >= n_all) return;
-  const bool gu = id < n_gu;
-  const long local = gu ? id : id - n_gu;
-  const int chunk = (int)(local % 64);
-  const long kst = local / 64;  // tile * ks_per_tile + ks
-  const int ks_per = gu ? g.gu_ks : g.d_ks;
-  const int tile = (int)(kst / ks_per);
-  const int ks = (int)(kst % ks_per);
-  const int rr = chunk % 32, half = chunk / 32;
-  const uint8_t *q;
-  const uint16_t *s, *b;
-  int row, K;
-  if (gu) {
-    K = H;
-    if (rr < 16) { q = c.gq; s = c.gs; b = c.gb; row = 16 * tile + rr; }
-    else         { q = c.uq; s = c.us; b = c.ub; row = 16 * tile + rr - 16; }
+  if (id >= n_all) return false;
+  c.gu = id < n_gu;
+  const long local = c.gu ? id : id - n_gu;
+  c.chunk = (int)(local % 64);
+  c.kst = local / 64;
+  const int ks_per = c.gu ? g.gu_ks : g.d_ks;
+  const int tile = (int)(c.kst / ks_per);
+  c.ks = (int)(c.kst % ks_per);
+  c.group = c.ks >> kshift;
+  c.plane = kshift ? (c.ks & 1) : 0;   // 8-bit: 0 high nibbles, 1 low nibbles
+  c.rr = c.chunk % 32;
+  c.half = c.chunk / 32;
+  if (c.gu) {
+    c.K = H;
+    c.row = 16 * tile + (c.rr & 15);
   } else {
-    K = I; q = c.dq; s = c.ds; b = c.db; row = 32 * tile + rr;
+    c.K = I;
+    c.row = 32 * tile + c.rr;
   }
-  const int e0 = ks * GROUP + half * 32;
-  const uint8_t *src = q + (size_t)row * (K / 2) + e0 / 2;  // 16 canonical bytes
+  return true;
+}
+
+// one thread per 16-byte chunk of the block
+__global__ void pack_kernel(CanonExpert c, int H, int I, int kshift, uint8_t *dst) {
+  ChunkPos p;
+  if (!chunk_pos((long)blockIdx.x * blockDim.x + threadIdx.x, H, I, kshift, p)) return;
+  const BlockGeom g = block_geom(H, I, kshift);
+  const bool up = p.gu && p.rr >= 16;
+  const uint8_t *q = p.gu ? (up ? c.uq : c.gq) : c.dq;
+  const uint16_t *s = p.gu ? (up ? c.us : c.gs) : c.ds;
+  const uint16_t *b = p.gu ? (up ? c.ub : c.gb) : c.db;
+  const int e0 = p.group * GROUP + p.half * 32;
   uint32_t w[4] = {0, 0, 0, 0};
   for (int j = 0; j < 32; ++j) {
-    const uint32_t code = (src[j >> 1] >> ((j & 1) * 4)) & 0xFu;
+    uint32_t code;
+    if (kshift) {
+      const uint32_t q8 = q[(size_t)p.row * p.K + e0 + j];
+      code = p.plane ? (q8 & 0xFu) : (q8 >> 4);
+    } else {
+      const uint8_t *src = q + (size_t)p.row * (p.K / 2) + e0 / 2;
+      code = (src[j >> 1] >> ((j & 1) * 4)) & 0xFu;
+    }
     w[j >> 3] |= code << (4 * nibble_slot(j & 7));
   }
-  uint8_t *base = dst + (gu ? 0 : g.gu_bytes) + (size_t)kst * KSTEP_BYTES;
-  *(qmoe_u32x4 *)(base + chunk * 16) = qmoe_u32x4{w[0], w[1], w[2], w[3]};
-  if (half == 0) {
-    const size_t gi = (size_t)row * (K / GROUP) + ks;
-    *(uint32_t *)(base + 1024 + rr * 4) = (uint32_t)s[gi] | ((uint32_t)b[gi] << 16);
+  uint8_t *base = dst + (p.gu ? 0 : g.gu_bytes) + (size_t)p.kst * KSTEP_BYTES;
+  *(qmoe_u32x4 *)(base + p.chunk * 16) = qmoe_u32x4{w[0], w[1], w[2], w[3]};
+  if (p.half == 0) {
+    const size_t gi = (size_t)p.row * (p.K / GROUP) + p.group;
+    uint32_t sw = s[gi], bw = b[gi];
+    if (kshift && p.plane == 0) sw = f32_to_bf16_bits(bf16_to_f32((uint16_t)sw) * 16.f);  // exact
+    if (kshift && p.plane == 1) bw = 0u;
+    *(uint32_t *)(base + 1024 + p.rr * 4) = sw | (bw << 16);
   }
 }
 
-__global__ void unpack_kernel(const uint8_t *srcb, int H, int I, CanonExpertOut c) {
-  const BlockGeom g = block_geom(H, I);
-  const long n_gu = (long)g.gu_tiles * g.gu_ks * 64;
-  const long n_all = n_gu + (long)g.d_tiles * g.d_ks * 64;
-  const long id = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (id >= n_all) return;
-  const bool gu = id < n_gu;
-  const long local = gu ? id : id - n_gu;
-  const int chunk = (int)(local % 64);
-  const long kst = local / 64;
-  const int ks_per = gu ? g.gu_ks : g.d_ks;
-  const int tile = (int)(kst / ks_per);
-  const int ks = (int)(kst % ks_per);
-  const int rr = chunk % 32, half = chunk / 32;
-  uint8_t *q;
-  uint16_t *s, *b;
-  int row, K;
-  if (gu) {
-    K = H;
-    if (rr < 16) { q = c.gq; s = c.gs; b = c.gb; row = 16 * tile + rr; }
-    else         { q = c.uq; s = c.us; b = c.ub; row = 16 * tile + rr - 16; }
-  } else {
-    K = I; q = c.dq; s = c.ds; b = c.db; row = 32 * tile + rr;
-  }
-  const uint8_t *base = srcb + (gu ? 0 : g.gu_bytes) + (size_t)kst * KSTEP_BYTES;
-  const qmoe_u32x4 v = *(const qmoe_u32x4 *)(base + chunk * 16);
+__global__ void unpack_kernel(const uint8_t *srcb, int H, int I, int kshift, CanonExpertOut c) {
+  ChunkPos p;
+  if (!chunk_pos((long)blockIdx.x * blockDim.x + threadIdx.x, H, I, kshift, p)) return;
+  const BlockGeom g = block_geom(H, I, kshift);
+  const bool up = p.gu && p.rr >= 16;
+  uint8_t *q = p.gu ? (up ? c.uq : c.gq) : c.dq;
+  uint16_t *s = p.gu ? (up ? c.us : c.gs) : c.ds;
+  uint16_t *b = p.gu ? (up ? c.ub : c.gb) : c.db;
+  const uint8_t *base = srcb + (p.gu ? 0 : g.gu_bytes) + (size_t)p.kst * KSTEP_BYTES;
+  const qmoe_u32x4 v = *(const qmoe_u32x4 *)(base + p.chunk * 16);
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  const int e0 = ks * GROUP + half * 32;
-  uint8_t *dstq = q + (size_t)row * (K / 2) + e0 / 2;
-  for (int m = 0; m < 16; ++m) {
-    const int j0 = 2 * m, j1 = 2 * m + 1;
-    const uint32_t c0 = (w[j0 >> 3] >> (4 * nibble_slot(j0 & 7))) & 0xFu;
-    const uint32_t c1 = (w[j1 >> 3] >> (4 * nibble_slot(j1 & 7))) & 0xFu;
-    dstq[m] = (uint8_t)(c0 | (c1 << 4));
+  const int e0 = p.group * GROUP + p.half * 32;
+  auto code_at = [&](int j) { return (w[j >> 3] >> (4 * nibble_slot(j & 7))) & 0xFu; };
+  if (kshift) {
+    // the high-nibble k-step writes bits 7..4 of each code, the low one bits 3..0: both
+    // k-steps of a group own the same bytes, so the high one writes the whole byte from both
+    // (reading the low k-step's chunk, which is the next one)
+    if (p.plane == 0) {
+      const qmoe_u32x4 v2 = *(const qmoe_u32x4 *)(base + KSTEP_BYTES + p.chunk * 16);
+      const uint32_t w2[4] = {v2.x, v2.y, v2.z, v2.w};
+      uint8_t *dq = q + (size_t)p.row * p.K + e0;
+      for (int j = 0; j < 32; ++j)
+        dq[j] = (uint8_t)((code_at(j) << 4) | ((w2[j >> 3] >> (4 * nibble_slot(j & 7))) & 0xFu));
+    }
+  } else {
+    uint8_t *dq = q + (size_t)p.row * (p.K / 2) + e0 / 2;
+    for (int m = 0; m < 16; ++m) dq[m] = (uint8_t)(code_at(2 * m) | (code_at(2 * m + 1) << 4));
   }
-  if (half == 0) {
-    const uint32_t sb = *(const uint32_t *)(base + 1024 + rr * 4);
-    const size_t gi = (size_t)row * (K / GROUP) + ks;
-    s[gi] = (uint16_t)(sb & 0xFFFFu);
-    b[gi] = (uint16_t)(sb >> 16);
+  if (p.half == 0) {
+    const uint32_t sb = *(const uint32_t *)(base + 1024 + p.rr * 4);
+    const size_t gi = (size_t)p.row * (p.K / GROUP) + p.group;
+    if (!kshift) {
+      s[gi] = (uint16_t)(sb & 0xFFFFu);
+      b[gi] = (uint16_t)(sb >> 16);
+    } else if (p.plane == 0) {
+      b[gi] = (uint16_t)(sb >> 16);
+    } else {
+      s[gi] = (uint16_t)(sb & 0xFFFFu);
+    }
   }
 }
 

@@ -45,5 +45,5 @@ class PackedLayer:
         return cls(dims, router, store, stride, shared)
 
 
-def dims_of(hidden, n_experts, top_k, inter, shared_inter=0):
-    return make_dims(hidden, n_experts, top_k, inter, shared_inter)
+def dims_of(hidden, n_experts, top_k, inter, shared_inter=0, expert_bits=4):
+    return make_dims(hidden, n_experts, top_k, inter, shared_inter, expert_bits=expert_bits)

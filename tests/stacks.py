@@ -16,7 +16,8 @@ from quantized_moe_router_amd._lib import make_dims
 
 
 def dims_of(cfg):
-    return make_dims(cfg.hidden, cfg.experts, cfg.top_k, cfg.inter, cfg.shared_inter)
+    return make_dims(cfg.hidden, cfg.experts, cfg.top_k, cfg.inter, cfg.shared_inter,
+                     expert_bits=cfg.expert_bits)
 
 
 def t16(a, dev):

@@ -47,12 +47,16 @@ def test_stride_and_workspace_queries():
     d2 = L.make_dims(2048, 512, 10, 512, 512)
     assert lib.qmoe_expert_stride(ctypes.byref(d2), 512) == 1769472     # already a 4 KiB multiple
     assert lib.qmoe_workspace_bytes(ctypes.byref(d), 128) > lib.qmoe_workspace_bytes(ctypes.byref(d), 1) > 0
+    # 8-bit experts: two 4-bit k-steps per group, 6,690,816 B -> 4 KiB multiple
+    d8 = L.make_dims(2816, 128, 8, 704, 2112, expert_bits=8)
+    assert lib.qmoe_expert_stride(ctypes.byref(d8), 704) == 6692864
 
 
 @pytest.mark.parametrize("field,value", [("group", 32), ("hidden", 100), ("hidden", 16384),
                                          ("inter", 0), ("inter", 8192), ("n_experts", 0),
                                          ("n_experts", 2048), ("top_k", 0), ("top_k", 33),
-                                         ("shared_inter", 65)])
+                                         ("shared_inter", 65), ("expert_bits", 5),
+                                         ("expert_bits", 16)])
 def test_bad_dims_are_rejected(field, value):
     L = _lib()
     d = L.make_dims(256, 16, 2, 128, 128)

@@ -48,7 +48,9 @@ def np16(t):
 # ------------------------------------------------------------------ generator and store
 
 @pytest.mark.parametrize("name,experts", [("tiny", [0, 7, 15]), ("gemma4_26b_a4b_decode", [0, 77]),
-                                          ("qwen3_next_80b_a3b_decode_b1", [511])])
+                                          ("qwen3_next_80b_a3b_decode_b1", [511]),
+                                          ("tiny_int8", [0, 7, 15]),
+                                          ("gemma4_26b_a4b_int8_decode", [5])])
 def test_device_generator_matches_host(name, experts):
     from workloads import device as D
     cfg = G.config(name)
@@ -61,7 +63,8 @@ def test_device_generator_matches_host(name, experts):
             assert np.array_equal(g, w), (name, e)
 
 
-@pytest.mark.parametrize("name", ["tiny", "gemma4_26b_a4b_decode"])
+@pytest.mark.parametrize("name", ["tiny", "gemma4_26b_a4b_decode", "tiny_int8",
+                                  "gemma4_26b_a4b_int8_decode"])
 def test_pack_unpack_round_trip(name):
     ops = _ops()
     cfg = G.config(name)
@@ -208,13 +211,15 @@ def _bucket_of(ops, dims, idx):
 
 # T <= 128 takes the matrix-core kernels, T = 200 the VALU ones
 @pytest.mark.parametrize("name,T,sample", [("tiny", 4, None), ("tiny", 37, None), ("tiny", 200, None),
+                                           ("tiny_int8", 1, None), ("tiny_int8", 37, None),
+                                           ("gemma4_26b_a4b_int8_decode", 1, None),
                                            ("gemma4_26b_a4b_decode", 1, None),
                                            ("gemma4_26b_a4b_prefill", 128, [0, 77]),
                                            ("qwen3_next_80b_a3b_decode_b16", 16, [3, 15])])
 def test_expert_ffn_and_combine_parity(name, T, sample):
     ops = _ops()
     cfg = G.config(name)
-    pl, li = layer(name) if "gemma" not in name else layer("gemma4_26b_a4b_decode")
+    pl, li = layer({"gemma4_26b_a4b_prefill": "gemma4_26b_a4b_decode"}.get(name, name))
     xb, x = _stacks().hidden(cfg, 1, T)
     ws = ops.workspace(pl.dims, T)
     idx, w = ops.router_topk(pl.dims, pl.router, x, ws)
@@ -269,7 +274,11 @@ def _layer_check(cfg, li, xb, out, out_f32, idx, w, toks):
                                            ("gemma4_26b_a4b_prefill", 128, [5, 127]),
                                            ("qwen3_next_80b_a3b_decode_b1", 1, None),
                                            ("qwen3_next_80b_a3b_decode_b16", 16, [0, 9]),
-                                           ("qwen3_6_35b_a3b_long_prefill", 128, [64])])
+                                           ("qwen3_6_35b_a3b_long_prefill", 128, [64]),
+                                           ("tiny_int8", 1, None), ("tiny_int8", 4, None),
+                                           ("tiny_int8", 64, None),
+                                           ("gemma4_26b_a4b_int8_decode", 1, None),
+                                           ("gemma4_26b_a4b_int8_decode", 128, [7, 120])])
 def test_layer_forward_parity(name, T, sample):
     ops = _ops()
     cfg = G.config(name)
@@ -337,7 +346,8 @@ def test_zero_tokens_is_noop():
 
 # ------------------------------------------------------------------ one-token launches and graphs
 
-@pytest.mark.parametrize("name", ["tiny", "gemma4_26b_a4b_decode", "qwen3_next_80b_a3b_decode_b1"])
+@pytest.mark.parametrize("name", ["tiny", "gemma4_26b_a4b_decode", "qwen3_next_80b_a3b_decode_b1",
+                                  "gemma4_26b_a4b_int8_decode"])
 def test_one_token_calls_repeat_and_report_no_timeout(name):
     """Back-to-back one-token calls on one workspace (each advances its epoch) give the same
     bits as a fresh workspace, and the workspace status reports no timed-out wait."""

@@ -290,6 +290,45 @@ def test_swiglu_identity_closed_form():
     assert np.allclose(y[0], want, rtol=1e-14, atol=1e-15)
 
 
+def _identity_expert_int8():
+    """The same closed-form expert with 8-bit codes that use both nibbles and a bias:
+    gate codes 192 on the diagonal and 64 elsewhere with s = 1/128, b = -0.5 (so W_g = I);
+    up 192 / 64 with s = 1/64, b = -1 (W_u = 2 I); down 160 on the shifted diagonal and 32
+    elsewhere with s = 1/128, b = -0.25 (the permutation)."""
+    H = 64
+    shift = int([p for p in golden_lines("swiglu_identity.txt") if p[0] == "down_shift"][0][1])
+    diag = np.where(np.eye(H, dtype=bool), 192, 64).astype(np.uint8)
+    perm = np.full((H, H), 32, np.uint8)
+    perm[np.arange(H), (np.arange(H) + shift) % H] = 160
+
+    def col(v):
+        return np.full((H, 1), v, np.uint16)
+
+    return G.ExpertWeights(diag, col(0x3C00), col(0xBF00), diag, col(0x3C80), col(0xBF80),
+                           perm, col(0x3C00), col(0xBE80), bits=8)
+
+
+def test_swiglu_identity_closed_form_int8_experts():
+    lines = golden_lines("swiglu_identity.txt")
+    x = np.zeros((1, 64))
+    for p in lines:
+        if p[0] == "x":
+            x[0, int(p[1])] = float(p[2])
+    want = np.zeros(64)
+    for p in lines:
+        if p[0] == "y":
+            want[int(p[1])] = float(p[2])
+    y = O.expert_ffn(x, _identity_expert_int8())
+    assert np.allclose(y[0], want, rtol=1e-14, atol=1e-15)
+
+
+def test_int8_expert_generator_codes_span_the_range():
+    cfg = G.config("tiny_int8")
+    ew = G.make_expert(cfg, 0, 3)
+    assert ew.bits == 8 and ew.gate_q.shape == (cfg.inter, cfg.hidden)
+    assert ew.gate_q.min() == 0 and ew.gate_q.max() == 255
+
+
 def test_expert_ffn_zero_input_is_zero():
     cfg = G.config("tiny")
     y = O.expert_ffn(np.zeros((2, cfg.hidden)), G.make_expert(cfg, 0, 3))

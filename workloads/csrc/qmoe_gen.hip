@@ -86,9 +86,72 @@ __global__ void gen_int4_kernel(uint32_t k0, uint32_t tag0, uint32_t tag_step, i
   b[(size_t)m * mat_groups + (size_t)row * gpr + g] = (uint16_t)b16;
 }
 
+// The 8-bit form of the same recipe: one thread per group, unpacked codes [rows, cols].  The
+// code is the nearest integer to t / s with ties to even, found from fp32 floor(t / s) with
+// exact corrections (q * s and (q + 0.5) * s are exact in fp32: at most 17 significant bits).
+__global__ void gen_int8_kernel(uint32_t k0, uint32_t tag0, uint32_t tag_step, int n_mat, int rows,
+                                int cols, float c, float inv_qmax, uint8_t *q, uint16_t *s,
+                                uint16_t *b) {
+  const int gpr = cols / 64;
+  const long n_groups = (long)n_mat * rows * gpr;
+  const long id = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= n_groups) return;
+  const int m = (int)(id / ((long)rows * gpr));
+  const long rem = id % ((long)rows * gpr);
+  const int row = (int)(rem / gpr), g = (int)(rem % gpr);
+  const uint32_t k1 = tag0 + (uint32_t)m * tag_step;
+  const unsigned long long pair0 = ((unsigned long long)row * cols + (unsigned long long)g * 64) / 2;
+  float w[64];
+  float wmin = INFINITY, wmax = -INFINITY;
+#pragma unroll 4
+  for (int i = 0; i < 32; ++i) {
+    const unsigned long long p = pair0 + i;
+    uint32_t ctr[4] = {(uint32_t)p, (uint32_t)(p >> 32), 0u, 0u};
+    philox10(ctr, k0, k1);
+    const float a = __fmul_rn((float)ih4(ctr[0], ctr[1]), c);
+    const float bb = __fmul_rn((float)ih4(ctr[2], ctr[3]), c);
+    w[2 * i] = a;
+    w[2 * i + 1] = bb;
+    wmin = fminf(wmin, fminf(a, bb));
+    wmax = fmaxf(wmax, fmaxf(a, bb));
+  }
+  const float s32 = __fmul_rn(__fsub_rn(wmax, wmin), inv_qmax);
+  const uint32_t s16 = bf16_rne_bits(s32), b16 = bf16_rne_bits(wmin);
+  const float sf = __uint_as_float(s16 << 16), bf = __uint_as_float(b16 << 16);
+  const size_t mat_groups = (size_t)rows * gpr;
+  uint8_t *qo = q + (size_t)m * rows * cols + (size_t)row * cols + g * 64;
+  for (int j = 0; j < 64; ++j) {
+    const float t = __fsub_rn(w[j], bf);
+    int qq = 0;
+    if (sf > 0.f) {
+      float f = floorf(__fdiv_rn(t, sf));
+      if (t < __fmul_rn(f, sf)) f -= 1.f;
+      if (t >= __fmul_rn(f + 1.f, sf)) f += 1.f;
+      const float mid = __fmul_rn(f + 0.5f, sf);
+      const int fi = (int)f;
+      if (t > mid || (t == mid && (fi & 1))) f += 1.f;
+      qq = (int)fminf(fmaxf(f, 0.f), 255.f);
+    }
+    qo[j] = (uint8_t)qq;
+  }
+  s[(size_t)m * mat_groups + (size_t)row * gpr + g] = (uint16_t)s16;
+  b[(size_t)m * mat_groups + (size_t)row * gpr + g] = (uint16_t)b16;
+}
+
 }  // namespace
 
 extern "C" {
+
+// Draw n_mat int8 matrices [rows, cols] (codes unpacked: q holds n_mat * rows * cols bytes).
+int qmoe_gen_int8(uint32_t k0, uint32_t tag0, uint32_t tag_step, int n_mat, int rows, int cols,
+                  float c, float inv_qmax, uint8_t *q, uint16_t *s, uint16_t *b, void *stream) {
+  if (n_mat <= 0 || rows <= 0 || cols <= 0 || cols % 64 || !q || !s || !b) return -1;
+  const long n = (long)n_mat * rows * (cols / 64);
+  hipLaunchKernelGGL(gen_int8_kernel, dim3((unsigned)((n + 127) / 128)), dim3(128), 0,
+                     (hipStream_t)stream, k0, tag0, tag_step, n_mat, rows, cols, c, inv_qmax, q, s,
+                     b);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
 
 // Draw n_mat int4 matrices [rows, cols] for layer key k0 and tags tag0 + m * tag_step.
 // q: n_mat * rows * cols/2 bytes; s, b: n_mat * rows * cols/64 bf16 (device pointers).

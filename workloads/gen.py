@@ -77,6 +77,7 @@ class Config:
     hidden_std: float = 1.0
     pes_lo: float = 0.5
     pes_hi: float = 1.5
+    expert_bits: int = 4        # routed and shared expert codes: 4 or 8 (MLX int8 groups)
     desc: str = ""
 
 
@@ -96,6 +97,11 @@ CONFIGS = {
                zipf_s=1.1, prompt=10240,
                desc="Qwen3.6-35B-A3B-shaped long prefill, 10,240 tokens in 128-token "
                     "chunks, Zipf(1.1) router bias, 40 stacked layers"),
+        Config("tiny_int8", 256, 16, 2, 128, 128, layers=1, tokens=4, expert_bits=8,
+               desc="tiny single MoE layer with int8 experts, 4 tokens"),
+        Config("gemma4_26b_a4b_int8_decode", 2816, 128, 8, 704, 2112, layers=30, tokens=1,
+               expert_bits=8,
+               desc="Gemma-4-26B-A4B-shaped decode with int8 experts, 1 token/step"),
     ]
 }
 
@@ -191,7 +197,8 @@ def pack_nibbles(q):
 
 @dataclass
 class ExpertWeights:
-    """Canonical MLX-style int4 expert: codes packed two per byte (low nibble first)."""
+    """Canonical MLX-style expert: int4 codes packed two per byte (low nibble first), or
+    int8 codes one per byte when bits == 8 (shapes [I, H] and [H, I] then)."""
     gate_q: np.ndarray   # uint8 [I, H/2]
     gate_s: np.ndarray   # uint16 bf16 bits [I, H/64]
     gate_b: np.ndarray
@@ -201,6 +208,7 @@ class ExpertWeights:
     down_q: np.ndarray   # uint8 [H, I/2]
     down_s: np.ndarray   # uint16 [H, I/64]
     down_b: np.ndarray
+    bits: int = 4
 
     def arrays(self):
         return (self.gate_q, self.gate_s, self.gate_b, self.up_q, self.up_s, self.up_b,
@@ -235,18 +243,18 @@ def layer_key(cfg, layer):
     return (cfg.seed + layer) & 0xFFFFFFFF
 
 
-def _int4_matrix(cfg, layer, tag, rows, cols):
+def _expert_matrix(cfg, layer, tag, rows, cols):
     w = normal_f32(layer_key(cfg, layer), tag, rows * cols, cfg.weight_std).reshape(rows, cols)
-    q, s, b = quantize_groups(w, 4)
-    return pack_nibbles(q), s, b
+    q, s, b = quantize_groups(w, cfg.expert_bits)
+    return (q if cfg.expert_bits == 8 else pack_nibbles(q)), s, b
 
 
 def _ffn_block(cfg, layer, tags, inter):
     H = cfg.hidden
-    gq, gs, gb = _int4_matrix(cfg, layer, tags[0], inter, H)
-    uq, us, ub = _int4_matrix(cfg, layer, tags[1], inter, H)
-    dq, ds, db = _int4_matrix(cfg, layer, tags[2], H, inter)
-    return ExpertWeights(gq, gs, gb, uq, us, ub, dq, ds, db)
+    gq, gs, gb = _expert_matrix(cfg, layer, tags[0], inter, H)
+    uq, us, ub = _expert_matrix(cfg, layer, tags[1], inter, H)
+    dq, ds, db = _expert_matrix(cfg, layer, tags[2], H, inter)
+    return ExpertWeights(gq, gs, gb, uq, us, ub, dq, ds, db, bits=cfg.expert_bits)
 
 
 def make_expert(cfg, layer, e):
@@ -324,7 +332,8 @@ def matrix_bytes(rows, cols, bits=4):
 def expert_bytes(cfg, inter=None):
     """Bytes of one routed expert (gate, up, down) in the canonical format."""
     I = cfg.inter if inter is None else inter
-    return 2 * matrix_bytes(I, cfg.hidden) + matrix_bytes(cfg.hidden, I)
+    b = cfg.expert_bits
+    return 2 * matrix_bytes(I, cfg.hidden, b) + matrix_bytes(cfg.hidden, I, b)
 
 
 def credited_expert_bytes(cfg, n_distinct):
