@@ -297,7 +297,8 @@ def run_other_configs(n_layers, steps):
     res = {}
     for name, src in [("qwen3_next_80b_a3b_decode_b1", None),
                       ("qwen3_next_80b_a3b_decode_b16", "qwen3_next_80b_a3b_decode_b1"),
-                      ("qwen3_6_35b_a3b_long_prefill", None)]:
+                      ("qwen3_6_35b_a3b_long_prefill", None),
+                      ("gemma4_26b_a4b_int8_decode", None)]:
         cfg = G.config(name)
         layers = build_stack(G.config(src or name), n_layers)
         xs = [x for x in layer_inputs(cfg, 0, n_layers, cfg.tokens)]
@@ -305,6 +306,7 @@ def run_other_configs(n_layers, steps):
         sec = time_stack(ops, [pl.weights for pl, _ in layers], xs, ws, steps)
         res[name] = {"tokens_per_call": cfg.tokens, "us_per_layer_call": round(sec * 1e6, 2),
                      "tokens_per_s_per_layer": round(cfg.tokens / sec, 1),
+                     "expert_bits": cfg.expert_bits,
                      "stack": f"{n_layers} layers of this shape (of {cfg.layers})"}
         del layers, xs, ws
         import torch
