@@ -242,6 +242,51 @@ int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16
                        float *topk_w_or_null, void *ws, size_t ws_bytes,
                        qmoe_stream_t stream);
 
+/* ---------------------------------------------------------------- tiered expert residency */
+
+/* For layers whose routed experts do not all stay in device memory: the experts live in host
+ * memory in the store's block layout (the cold tier; the pages keep them on SSD and read one
+ * fixed-stride block per expert [TF-struct] io phase, [SW-mem]), and `slots` device blocks
+ * cache the ones in use, replaced LFU with recency as the pages describe: a hit adds one use
+ * and refreshes the last use; a miss takes an empty slot, else the slot not used by the same
+ * call with the fewest uses, then the oldest last use, then the lowest index, and starts at one
+ * use.  Counts belong to the slot (no ageing). */
+typedef struct qmoe_expert_cache qmoe_expert_cache;
+
+/* host_store: host memory (pinned for full copy speed) with expert e's block at
+ * host_store + e * host_stride; device_slots: device memory with slot s at
+ * device_slots + s * slot_stride.  Both strides >= qmoe_expert_stride(d, d->inter) and multiples
+ * of 256; slots in [top_k, n_experts].  The cache object is host memory owned by the library
+ * (the pointers are kept, nothing is touched until a forward call). */
+int qmoe_cache_create(const qmoe_dims *d, const void *host_store, size_t host_stride,
+                      void *device_slots, size_t slot_stride, int32_t slots,
+                      qmoe_expert_cache **cache_out);
+int qmoe_cache_destroy(qmoe_expert_cache *cache);
+
+/* Host only: the cache's decision for one call naming the expert ids ids[0..n) -- the slot of
+ * every id (slot_of_out[n]) and the blocks to copy (fill_expert_out / fill_slot_out, at most
+ * `slots` entries, count in *n_fills_out).  Updates the cache state exactly as a forward call
+ * does.  Fails (QMOE_ERR_ARG) on an id outside [0, E) or more distinct ids than slots. */
+int qmoe_cache_plan(qmoe_expert_cache *cache, const int32_t *ids, int32_t n, int32_t *slot_of_out,
+                    int32_t *fill_expert_out, int32_t *fill_slot_out, int32_t *n_fills_out);
+
+/* Lookups so far (hits + misses = distinct experts per call, summed over calls). */
+int qmoe_cache_stats(const qmoe_expert_cache *cache, int64_t *hits_out, int64_t *misses_out);
+
+/* The layer with its routed experts streamed through the cache, per chunk of at most 128
+ * tokens: router and top-k on the GPU; the ids copied to the host (the one synchronisation of
+ * `stream`, where the pages' CPU reads the router's choice); the cache plan; one host-to-device
+ * copy per missing expert block; the slot ids copied back; bucketing, expert FFN (routed
+ * experts from the slots, shared block from L->shared) and combine (with L's post-combine
+ * steps if set) as in qmoe_layer_forward.  L->experts and L->expert_stride are not used.  The
+ * chunk's distinct experts must fit in the slots.  Not for use under graph capture.  Results
+ * equal qmoe_router_topk -> qmoe_bucket -> qmoe_expert_ffn -> qmoe_combine_post on a resident
+ * store bit for bit. */
+int qmoe_layer_forward_tiered(const qmoe_layer *L, qmoe_expert_cache *cache, const uint16_t *x,
+                              int32_t T, uint16_t *out, float *out_f32_or_null,
+                              int32_t *topk_idx_or_null, float *topk_w_or_null, void *ws,
+                              size_t ws_bytes, qmoe_stream_t stream);
+
 /* Diagnostic: copy the workspace's status word to *status_out (0 = no fault; 1 = a one-token
  * layer call gave up waiting for another workgroup, so its results are not valid).
  * Synchronises `stream`; not for use under graph capture. */

@@ -17,7 +17,8 @@ EXPORTS = [
     "qmoe_workspace_init", "qmoe_pack_expert", "qmoe_unpack_expert", "qmoe_router_topk",
     "qmoe_bucket", "qmoe_expert_ffn", "qmoe_combine", "qmoe_combine_post", "qmoe_layer_forward",
     "qmoe_event_create", "qmoe_event_destroy", "qmoe_event_record", "qmoe_event_elapsed_ms",
-    "qmoe_set_profile_events", "qmoe_workspace_status",
+    "qmoe_set_profile_events", "qmoe_workspace_status", "qmoe_cache_create", "qmoe_cache_destroy",
+    "qmoe_cache_plan", "qmoe_cache_stats", "qmoe_layer_forward_tiered",
 ]
 
 
@@ -82,6 +83,13 @@ def lib():
         "qmoe_event_elapsed_ms": (ctypes.c_int, [P, P, ctypes.POINTER(ctypes.c_float)]),
         "qmoe_set_profile_events": (ctypes.c_int, [P, P]),
         "qmoe_workspace_status": (ctypes.c_int, [P, SZ, ctypes.POINTER(ctypes.c_int32), P]),
+        "qmoe_cache_create": (ctypes.c_int, [pd, P, SZ, P, SZ, I32, ctypes.POINTER(ctypes.c_void_p)]),
+        "qmoe_cache_destroy": (ctypes.c_int, [P]),
+        "qmoe_cache_plan": (ctypes.c_int, [P, P, I32, P, P, P, ctypes.POINTER(ctypes.c_int32)]),
+        "qmoe_cache_stats": (ctypes.c_int, [P, ctypes.POINTER(ctypes.c_int64),
+                                            ctypes.POINTER(ctypes.c_int64)]),
+        "qmoe_layer_forward_tiered": (ctypes.c_int, [ctypes.POINTER(Layer), P, P, I32, P, P, P, P, P,
+                                                     SZ, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)

@@ -17,6 +17,7 @@
 #include "router.h"
 #include "ffn.h"
 #include "decode.h"
+#include "cache.h"
 
 using namespace qmoe;
 
@@ -137,7 +138,7 @@ inline int dec_shared_chunks(const qmoe_dims *d) {
 
 struct WsLayout {
   size_t cnt, logits, tidx, tw, counts, offsets, sorted, active, nact, slot_tab;
-  size_t hr_hi, hr_lo, hs_hi, hs_lo, y, ysh, gx, ghr, ghs;
+  size_t hr_hi, hr_lo, hs_hi, hs_lo, y, ysh, gx, ghr, ghs, slot_ids;
   size_t dec_logits, dec_hr, dec_hsh, dec_yr, dec_ysh, dec_nrm, total;
 };
 
@@ -156,6 +157,7 @@ WsLayout ws_layout(const qmoe_dims *d, int Tmax) {
   w.active = o; o += al(E * 4);
   w.nact = o; o += al(4);
   w.slot_tab = o; o += al((size_t)bucket_max_blocks((int)(Tc * k), (int)E) * 16);
+  w.slot_ids = o; o += al(Tc * k * 4);
   w.hr_hi = o; o += al(T * k * d->inter * 2);
   w.hr_lo = o; o += al(T * k * d->inter * 2);
   w.hs_hi = o; o += al(T * (size_t)d->shared_inter * 2);
@@ -478,6 +480,21 @@ static int launch_decode(const qmoe_layer *L, const uint16_t *x, uint16_t *out, 
 
 }  // namespace
 
+// The tiered-residency cache object behind the opaque qmoe_expert_cache handle.
+struct qmoe_expert_cache {
+  qmoe_dims d;
+  const uint8_t *host_store;
+  size_t host_stride;
+  uint8_t *slots_mem;
+  size_t slot_stride;
+  int n_slots;
+  qmoe::ExpertCachePolicy policy;
+  int32_t *h_ids = nullptr, *h_slots = nullptr;   // pinned staging, made on first forward call
+  qmoe_expert_cache(const qmoe_dims &dd, const void *hs, size_t hst, void *ds, size_t dst, int n)
+      : d(dd), host_store((const uint8_t *)hs), host_stride(hst), slots_mem((uint8_t *)ds),
+        slot_stride(dst), n_slots(n), policy(dd.n_experts, n) {}
+};
+
 // ====================================================================== exported entry points
 extern "C" {
 
@@ -730,6 +747,144 @@ int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16
         QMOE_LAUNCHED();
       }
     }
+  }
+  return ok();
+}
+
+int qmoe_cache_create(const qmoe_dims *d, const void *host_store, size_t host_stride,
+                      void *device_slots, size_t slot_stride, int32_t slots,
+                      qmoe_expert_cache **cache_out) {
+  int rc = check_dims(d);
+  if (rc) return rc;
+  if (!cache_out) return fail(QMOE_ERR_ARG, "cache_out is NULL");
+  *cache_out = nullptr;
+  if (!host_store || !device_slots) return fail(QMOE_ERR_ARG, "cache: NULL store or slots");
+  const size_t blk = block_stride_bytes(d->hidden, d->inter, kshift_of(d));
+  if (host_stride < blk || slot_stride < blk || host_stride % 256 || slot_stride % 256)
+    return fail(QMOE_ERR_ARG, "cache strides must be multiples of 256 and >= %zu", blk);
+  if (!aligned(device_slots, 256)) return fail(QMOE_ERR_ARG, "device_slots must be 256-byte aligned");
+  if (slots < d->top_k || slots > d->n_experts)
+    return fail(QMOE_ERR_SHAPE, "slots must be in [top_k, n_experts] (got %d)", slots);
+  *cache_out = new qmoe_expert_cache(*d, host_store, host_stride, device_slots, slot_stride, slots);
+  return ok();
+}
+
+int qmoe_cache_destroy(qmoe_expert_cache *cache) {
+  if (!cache) return ok();
+  if (cache->h_ids) (void)hipHostFree(cache->h_ids);
+  if (cache->h_slots) (void)hipHostFree(cache->h_slots);
+  delete cache;
+  return ok();
+}
+
+int qmoe_cache_plan(qmoe_expert_cache *cache, const int32_t *ids, int32_t n, int32_t *slot_of_out,
+                    int32_t *fill_expert_out, int32_t *fill_slot_out, int32_t *n_fills_out) {
+  if (!cache || (!ids && n > 0) || (!slot_of_out && n > 0) || !fill_expert_out || !fill_slot_out ||
+      !n_fills_out)
+    return fail(QMOE_ERR_ARG, "cache_plan: NULL pointer");
+  if (n < 0) return fail(QMOE_ERR_ARG, "cache_plan: n < 0");
+  CachePlan p;
+  if (!cache->policy.plan(ids, n, p))
+    return fail(QMOE_ERR_ARG, "cache_plan: an id outside [0, %d) or more distinct ids than the %d slots",
+                cache->d.n_experts, cache->n_slots);
+  for (int i = 0; i < n; ++i) slot_of_out[i] = p.slot_of[i];
+  for (size_t j = 0; j < p.fill_slot.size(); ++j) {
+    fill_expert_out[j] = p.fill_expert[j];
+    fill_slot_out[j] = p.fill_slot[j];
+  }
+  *n_fills_out = (int32_t)p.fill_slot.size();
+  return ok();
+}
+
+int qmoe_cache_stats(const qmoe_expert_cache *cache, int64_t *hits_out, int64_t *misses_out) {
+  if (!cache || !hits_out || !misses_out) return fail(QMOE_ERR_ARG, "cache_stats: NULL pointer");
+  *hits_out = cache->policy.hits();
+  *misses_out = cache->policy.misses();
+  return ok();
+}
+
+int qmoe_layer_forward_tiered(const qmoe_layer *L, qmoe_expert_cache *C, const uint16_t *x,
+                              int32_t T, uint16_t *out, float *out_f32_or_null,
+                              int32_t *topk_idx_or_null, float *topk_w_or_null, void *ws,
+                              size_t ws_bytes, qmoe_stream_t stream) {
+  if (!L) return fail(QMOE_ERR_ARG, "layer is NULL");
+  int rc = check_dims(&L->d);
+  if (rc || (rc = check_router(&L->r)) || (rc = check_T(T))) return rc;
+  if (!C) return fail(QMOE_ERR_ARG, "cache is NULL");
+  const qmoe_dims *d = &L->d;
+  if (C->d.hidden != d->hidden || C->d.n_experts != d->n_experts || C->d.top_k != d->top_k ||
+      C->d.inter != d->inter || kshift_of(&C->d) != kshift_of(d))
+    return fail(QMOE_ERR_ARG, "cache was made for other layer dims");
+  if (L->shared && (d->shared_inter == 0 || !aligned(L->shared, 256)))
+    return fail(QMOE_ERR_ARG, "shared block needs shared_inter > 0 and 256-byte alignment");
+  if (L->post_norm_gain && !aligned(L->post_norm_gain, 16))
+    return fail(QMOE_ERR_ARG, "post_norm_gain must be 16-byte aligned");
+  if (T == 0) return ok();
+  if (!x || !out) return fail(QMOE_ERR_ARG, "layer_forward_tiered: x/out must not be NULL");
+  const int Tc_max = std::min<int>(T, CHUNK_TOKENS);
+  if ((rc = check_ws(d, Tc_max, ws, ws_bytes))) return rc;
+  if ((rc = check_arch())) return rc;
+  if (!C->h_ids) {
+    QMOE_HIP(hipHostMalloc((void **)&C->h_ids, (size_t)CHUNK_TOKENS * MAX_TOPK * 4));
+    QMOE_HIP(hipHostMalloc((void **)&C->h_slots, (size_t)CHUNK_TOKENS * MAX_TOPK * 4));
+  }
+  hipStream_t s = (hipStream_t)stream;
+  const WsLayout wl = ws_layout(d, Tc_max);
+  const int H = d->hidden, k = d->top_k;
+  const bool sh = L->shared != nullptr;
+  const bool post = L->post_norm_gain || L->layer_scalar;
+  const size_t blk = block_stride_bytes(d->hidden, d->inter, kshift_of(d));
+  for (int c0 = 0; c0 < T; c0 += CHUNK_TOKENS) {
+    const int Tc = std::min(CHUNK_TOKENS, T - c0), N = Tc * k;
+    const uint16_t *xc = x + (size_t)c0 * H;
+    int32_t *idx = topk_idx_or_null ? topk_idx_or_null + (size_t)c0 * k : at<int32_t>(ws, wl.tidx);
+    float *w = topk_w_or_null ? topk_w_or_null + (size_t)c0 * k : at<float>(ws, wl.tw);
+    // router and top-k, then the ids to the host
+    RouterArgs ra = make_router_args(d, &L->r, xc, Tc, at<float>(ws, wl.logits), idx, w, ws);
+    if ((rc = launch_router(ra, router_smem(d, Tc), s))) return rc;
+    QMOE_HIP(hipMemcpyAsync(C->h_ids, idx, (size_t)N * 4, hipMemcpyDeviceToHost, s));
+    QMOE_HIP(hipStreamSynchronize(s));
+    CachePlan p;
+    if (!C->policy.plan(C->h_ids, N, p))
+      return fail(QMOE_ERR_ARG, "a chunk names more distinct experts than the cache's %d slots",
+                  C->n_slots);
+    // one copy per missing block, then the slot ids
+    for (size_t j = 0; j < p.fill_slot.size(); ++j)
+      QMOE_HIP(hipMemcpyAsync(C->slots_mem + (size_t)p.fill_slot[j] * C->slot_stride,
+                              C->host_store + (size_t)p.fill_expert[j] * C->host_stride, blk,
+                              hipMemcpyHostToDevice, s));
+    for (int i = 0; i < N; ++i) C->h_slots[i] = p.slot_of[i];
+    int32_t *slot_ids = at<int32_t>(ws, wl.slot_ids);
+    QMOE_HIP(hipMemcpyAsync(slot_ids, C->h_slots, (size_t)N * 4, hipMemcpyHostToDevice, s));
+    // bucketing over the slots, FFN from the slots, combine
+    int32_t *counts = at<int32_t>(ws, wl.counts), *offsets = at<int32_t>(ws, wl.offsets);
+    int32_t *sorted = at<int32_t>(ws, wl.sorted), *active = at<int32_t>(ws, wl.active);
+    int32_t *nact = at<int32_t>(ws, wl.nact);
+    const size_t lds = bucket_lds_bytes(N, C->n_slots);
+    if ((rc = set_lds(bucket_kernel, lds))) return rc;
+    hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(256), lds, s, (const int32_t *)slot_ids, N,
+                       C->n_slots, counts, offsets, sorted, active, nact);
+    QMOE_LAUNCHED();
+    FfnArgs fa = make_ffn_args(L, xc, Tc, offsets, sorted, active, nact, at<float>(ws, wl.y),
+                               sh ? at<float>(ws, wl.ysh) : nullptr, ws, Tc_max);
+    fa.experts = C->slots_mem;
+    fa.stride = C->slot_stride;
+    fa.n_experts = C->n_slots;
+    fa.n_slots = std::min(C->n_slots, N);
+    if (!sh) fa.shared = nullptr;
+    uint16_t *oc = out + (size_t)c0 * H;
+    float *oc32 = out_f32_or_null ? out_f32_or_null + (size_t)c0 * H : nullptr;
+    if (valu_ffn(Tc)) {
+      if ((rc = launch_gu(fa, s))) return rc;
+      if ((rc = launch_d(fa, sh, s))) return rc;
+    } else {
+      if ((rc = launch_gsum(xc, Tc, H, at<float>(ws, wl.gx), s))) return rc;
+      if ((rc = launch_pf(fa, s))) return rc;
+    }
+    if (post) rc = launch_combine_post(xc, fa.y, w, fa.y_sh, L->post_norm_gain, L->layer_scalar, Tc,
+                                       H, k, oc, oc32, s);
+    else rc = launch_combine_pf(xc, fa.y, w, fa.y_sh, Tc, H, k, oc, oc32, s);
+    if (rc) return rc;
   }
   return ok();
 }

@@ -184,6 +184,62 @@ def layer_forward(layer, x, ws, out=None, out_f32=None, topk_idx=None, topk_w=No
     return out
 
 
+class ExpertCache:
+    """Tiered residency: routed expert blocks in host memory (`host_store`, a CPU uint8 tensor,
+    pinned for full copy speed), `slots` of them cached in the device tensor `slot_store`."""
+
+    def __init__(self, dims, host_store, host_stride, slot_store, slot_stride, slots):
+        if not isinstance(host_store, torch.Tensor) or host_store.device.type != "cpu":
+            raise ValueError("host_store must be a CPU tensor")
+        if not host_store.is_contiguous():
+            raise ValueError("host_store must be contiguous")
+        self.keep = (host_store, slot_store)
+        self.dims = dims
+        h = ctypes.c_void_p()
+        check(lib().qmoe_cache_create(ctypes.byref(dims), ctypes.c_void_p(host_store.data_ptr()),
+                                      int(host_stride), _ptr(slot_store, 1, "slot_store"),
+                                      int(slot_stride), int(slots), ctypes.byref(h)))
+        self.h = h
+
+    def plan(self, ids):
+        """Host-only slot decision for the expert ids of one call: (slot of every id, list of
+        (expert, slot) blocks to copy)."""
+        import numpy as np
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        n = ids.size
+        slot_of = np.empty(max(n, 1), np.int32)
+        fe = np.empty(max(n, 1), np.int32)
+        fs = np.empty(max(n, 1), np.int32)
+        nf = ctypes.c_int32()
+        check(lib().qmoe_cache_plan(self.h, ids.ctypes.data, n, slot_of.ctypes.data, fe.ctypes.data,
+                                    fs.ctypes.data, ctypes.byref(nf)))
+        return slot_of[:n], list(zip(fe[:nf.value].tolist(), fs[:nf.value].tolist()))
+
+    def stats(self):
+        h, m = ctypes.c_int64(), ctypes.c_int64()
+        check(lib().qmoe_cache_stats(self.h, ctypes.byref(h), ctypes.byref(m)))
+        return h.value, m.value
+
+    def __del__(self):
+        try:
+            if self.h:
+                lib().qmoe_cache_destroy(self.h)
+        except Exception:
+            pass
+
+
+def layer_forward_tiered(layer, cache, x, ws, out=None, out_f32=None, topk_idx=None, topk_w=None):
+    T = x.shape[0]
+    d = layer.dims
+    if out is None:
+        out = torch.empty(T, d.hidden, dtype=torch.bfloat16, device=x.device)
+    check(lib().qmoe_layer_forward_tiered(
+        ctypes.byref(layer.struct), cache.h, _ptr(x, 2, "x"), T, _ptr(out, 2, "out"),
+        _ptr(out_f32, 4, allow_none=True), _ptr(topk_idx, 4, allow_none=True),
+        _ptr(topk_w, 4, allow_none=True), _ptr(ws, 1, "ws"), ws.numel(), _stream()))
+    return out
+
+
 class Event:
     """A HIP event created by the library (for timing kernels on the stream they run on)."""
 

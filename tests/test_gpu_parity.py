@@ -471,6 +471,77 @@ def test_one_token_post_calls_repeat(name):
     assert ops.workspace_status(ws) == 0 and ops.workspace_status(ws2) == 0
 
 
+# ------------------------------------------------------------------ tiered residency
+
+def _tiered(name, slots):
+    ops = _ops()
+    pl, li = layer(name)
+    host = torch.empty(pl.store.numel(), dtype=torch.uint8, pin_memory=True)
+    host.copy_(pl.store)
+    slot_store = torch.empty(slots * pl.stride, dtype=torch.uint8, device=DEV)
+    cache = ops.ExpertCache(pl.dims, host, pl.stride, slot_store, pl.stride, slots)
+    return pl, li, cache
+
+
+@pytest.mark.parametrize("name,T,slots,steps", [("tiny", 4, 8, 6), ("tiny", 1, 2, 8),
+                                                ("tiny", 130, 16, 2), ("tiny_int8", 4, 8, 3),
+                                                ("gemma4_26b_a4b_decode", 1, 16, 6),
+                                                ("gemma4_26b_a4b_decode", 128, 128, 2)])
+def test_tiered_layer_equals_resident_stepwise(name, T, slots, steps):
+    """Experts streamed from host memory through the device cache give the bits of the
+    resident step-by-step path, and the cache counts follow the replacement rule."""
+    from cache_model import Model
+    ops = _ops()
+    cfg = G.config(name)
+    pl, li, cache = _tiered(name, slots)
+    ws = ops.workspace(pl.dims, T)
+    ws2 = ops.workspace(pl.dims, T)
+    model = Model(cfg.experts, slots)
+    for step in range(steps):
+        xb, x = _stacks().hidden(cfg, 20 + step, T)
+        o32t = torch.empty(T, cfg.hidden, dtype=torch.float32, device=DEV)
+        idx_t = torch.empty(T, cfg.top_k, dtype=torch.int32, device=DEV)
+        w_t = torch.empty(T, cfg.top_k, dtype=torch.float32, device=DEV)
+        out_t = ops.layer_forward_tiered(pl.weights, cache, x, ws, out_f32=o32t, topk_idx=idx_t,
+                                         topk_w=w_t)
+        idx, w = ops.router_topk(pl.dims, pl.router, x, ws2)
+        counts, offsets, srt, active, n_active = ops.bucket(pl.dims, idx)
+        y, ysh = ops.expert_ffn(pl.weights, x, offsets, srt, active, n_active, ws2)
+        o32r = torch.empty_like(o32t)
+        out_r = ops.combine(pl.dims, x, y, w, ysh, out_f32=o32r)
+        torch.cuda.synchronize()
+        assert torch.equal(idx_t, idx) and torch.equal(w_t, w)
+        assert torch.equal(out_t.view(torch.int16), out_r.view(torch.int16))
+        assert torch.equal(o32t, o32r)
+        ids = idx.cpu().numpy()
+        for c0 in range(0, T, 128):
+            model.plan(ids[c0:c0 + 128].ravel())
+    assert cache.stats() == (model.hits, model.misses)
+    print(f"{name} T={T} slots={slots}: hits {model.hits}, misses {model.misses}")
+
+
+def test_tiered_layer_with_post_steps_and_too_few_slots():
+    ops = _ops()
+    cfg = G.config("tiny")
+    pl, lw, view = post_layer("tiny")
+    _, _, cache = _tiered("tiny", 4)
+    xb, x = _stacks().hidden(cfg, 31, 1)
+    ws = ops.workspace(pl.dims, 4)
+    o32 = torch.empty(1, cfg.hidden, dtype=torch.float32, device=DEV)
+    out = ops.layer_forward_tiered(lw, cache, x, ws, out_f32=o32)
+    torch.cuda.synchronize()
+    ref = O.layer_forward(xb, view, cfg.top_k)
+    assert_close_f32(o32.cpu().numpy()[0], ref["out"][0], "tiered post out_f32")
+    check_out_bf16(np16(out)[0], o32.cpu().numpy()[0], ref["out"][0], "tiered post out")
+    # four tokens name up to eight experts: more than the four slots
+    _, _, small = _tiered("tiny", 2)
+    xb4, x4 = _stacks().hidden(cfg, 32, 4)
+    from quantized_moe_router_amd import QmoeError
+    with pytest.raises(QmoeError):
+        ops.layer_forward_tiered(pl.weights, small, x4, ws)
+    torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("T", [1, 128])
 def test_graph_replays_match_eager(T):
     """A captured layer call replayed several times, with eager work in between, reproduces the
