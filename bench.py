@@ -314,6 +314,43 @@ def run_other_configs(n_layers, steps):
     return res
 
 
+def run_tiered(layers, cfg, slots, steps):
+    """One-token steps through the first layers of the stack with their routed experts in pinned
+    host memory and `slots` device slots per layer: per-layer time, hit rate, copy rate."""
+    import torch
+    from quantized_moe_router_amd import ops
+    from workloads import gen as G
+    caches, keep = [], []
+    for pl, _ in layers:
+        host = torch.empty(pl.store.numel(), dtype=torch.uint8, pin_memory=True)
+        host.copy_(pl.store)
+        slot_store = torch.empty(slots * pl.stride, dtype=torch.uint8, device="cuda")
+        keep += [host, slot_store]
+        caches.append(ops.ExpertCache(pl.dims, host, pl.stride, slot_store, pl.stride, slots))
+    ws = ops.workspace(layers[0][0].dims, 1)
+    xs = [layer_inputs(cfg, s, len(layers), 1) for s in range(steps + 2)]
+    out = torch.empty(1, cfg.hidden, dtype=torch.bfloat16, device="cuda")
+    for s in range(2):      # warm-up: fills the caches
+        for l, (pl, _) in enumerate(layers):
+            ops.layer_forward_tiered(pl.weights, caches[l], xs[s][l], ws, out=out)
+    torch.cuda.synchronize()
+    h0 = [c.stats() for c in caches]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        for l, (pl, _) in enumerate(layers):
+            ops.layer_forward_tiered(pl.weights, caches[l], xs[s + 2][l], ws, out=out)
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / steps / len(layers)
+    hits = sum(c.stats()[0] - h[0] for c, h in zip(caches, h0))
+    misses = sum(c.stats()[1] - h[1] for c, h in zip(caches, h0))
+    copied = misses * G.expert_bytes(cfg) / (steps * len(layers))
+    return dict(us_per_layer=round(sec * 1e6, 1), slots_per_layer=slots,
+                hit_rate=round(hits / max(hits + misses, 1), 3),
+                copied_MB_per_layer=round(copied / 1e6, 2),
+                host_to_device_GBps=round(copied / sec / 1e9, 1),
+                stack=f"first {len(layers)} layers, 1 token per step, {steps} steps")
+
+
 def run_prefill(layers, cfg_pf, reps=3):
     """One 128-token chunk per layer through the same stack (prefill shape)."""
     import numpy as np
@@ -402,11 +439,13 @@ def main():
     if not args.no_prefill and cfg.name == "gemma4_26b_a4b_decode":
         log("prefill timing")
         pf = run_prefill(layers, G.config("gemma4_26b_a4b_prefill"))
-    post = other = None
+    post = other = tiered = None
     if not args.no_extra and cfg.tokens == 1:
         log("post-combine norm stack timing")
         post = run_post(layers, cfg, args.steps)
         if cfg.name == "gemma4_26b_a4b_decode":
+            log("tiered residency (16 slots per layer)")
+            tiered = run_tiered(layers[:4], cfg, 16, args.steps)
             log("other workload shapes (4-layer stacks)")
             other = run_other_configs(4, args.steps)
     cb = None
@@ -466,6 +505,9 @@ def main():
             "workload": f"{cfg.name} with the post-combine RMS norm (gain) and layer scalar",
             "us_per_layer": round(post * 1e6, 3),
         }
+    if tiered:
+        out["tiered_residency"] = dict(tiered, workload=f"{cfg.name}: routed experts in pinned host "
+                                       "memory, LFU-with-recency device cache per layer")
     if other:
         out["other_workloads"] = other
     if cb:
