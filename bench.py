@@ -272,22 +272,76 @@ def time_stack(ops, weights, xs, ws, steps):
     return (time.perf_counter() - t0) / steps / len(weights)
 
 
-def run_post(layers, cfg, steps):
-    """The decode stack with the post-combine norm and layer scalar switched on."""
+def post_weights(layers, cfg):
+    """The stack's layers with the post-combine norm and layer scalar switched on (the
+    LayerWeights keep their gain and scalar tensors alive)."""
     import torch
     from quantized_moe_router_amd import ops
     from workloads import gen as G
-    weights, keep = [], []
+    weights = []
     for l, (pl, _) in enumerate(layers):
         gain, scalar = G.make_post(cfg, l)
         g = torch.from_numpy(gain).cuda()
         sc = torch.tensor([scalar], dtype=torch.float32, device="cuda")
-        keep += [g, sc]
         weights.append(ops.LayerWeights(pl.dims, pl.router, pl.store, pl.stride, pl.shared,
                                         post_norm_gain=g, layer_scalar=sc))
+    return weights
+
+
+def run_post(layers, cfg, steps):
+    """The decode stack with the post-combine norm and layer scalar switched on."""
+    from quantized_moe_router_amd import ops
+    weights = post_weights(layers, cfg)
     xs = [x for x in layer_inputs(cfg, 0, len(layers), cfg.tokens)]
     ws = ops.workspace(layers[0][0].dims, cfg.tokens)
     return time_stack(ops, weights, xs, ws, steps)
+
+
+def time_graph(fn, steps):
+    """Seconds per replay of a graph holding fn()."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / steps
+
+
+def run_chain(layers, cfg, steps):
+    """One token through the whole stack with each layer's input the previous layer's output:
+    as one chained launch (qmoe_decode_stack) and as one-token layer calls in a graph.  The
+    layers carry the post-combine norm and layer scalar, which keep the chained residual
+    stream of the synthetic weights in range."""
+    import torch
+    from quantized_moe_router_amd import ops
+    weights = post_weights(layers, cfg)
+    L, H = len(weights), cfg.hidden
+    x = layer_inputs(cfg, 0, 1, 1)[0]
+    ws = ops.workspace(layers[0][0].dims, 1)
+    out_s = torch.empty(L, H, dtype=torch.bfloat16, device="cuda")
+    out_c = torch.empty(L, H, dtype=torch.bfloat16, device="cuda")
+
+    def chained_calls():
+        cur = x
+        for l, w in enumerate(weights):
+            ops.layer_forward(w, cur, ws, out=out_c[l:l + 1])
+            cur = out_c[l:l + 1]
+
+    t_stack = time_graph(lambda: ops.decode_stack(weights, x, ws, out=out_s), steps)
+    t_calls = time_graph(chained_calls, steps)
+    same = bool(torch.equal(out_s.view(torch.int16), out_c.view(torch.int16)))
+    finite = bool(torch.isfinite(out_s.float()).all())
+    return {"us_per_layer": round(t_stack * 1e6 / L, 3), "outputs_finite": finite,
+            "tokens_per_s_per_layer": round(L / t_stack, 1),
+            "chained_layer_calls_us_per_layer": round(t_calls * 1e6 / L, 3),
+            "outputs_equal_chained_calls": same, "layers": L}
 
 
 def run_other_configs(n_layers, steps):
@@ -439,10 +493,14 @@ def main():
     if not args.no_prefill and cfg.name == "gemma4_26b_a4b_decode":
         log("prefill timing")
         pf = run_prefill(layers, G.config("gemma4_26b_a4b_prefill"))
-    post = other = tiered = None
+    post = other = tiered = chain = None
     if not args.no_extra and cfg.tokens == 1:
         log("post-combine norm stack timing")
         post = run_post(layers, cfg, args.steps)
+        log("chained launch over the stack")
+        chain = run_chain(layers, cfg, args.steps)
+        log(f"chained launch: {chain['us_per_layer']} us/layer "
+            f"(chained layer calls {chain['chained_layer_calls_us_per_layer']})")
         if cfg.name == "gemma4_26b_a4b_decode":
             log("tiered residency (16 slots per layer)")
             tiered = run_tiered(layers[:4], cfg, 16, args.steps)
@@ -505,6 +563,11 @@ def main():
             "workload": f"{cfg.name} with the post-combine RMS norm (gain) and layer scalar",
             "us_per_layer": round(post * 1e6, 3),
         }
+    if chain:
+        out["chained_stack"] = dict(chain, workload=f"{cfg.name} with the post-combine norm and "
+                                    f"layer scalar: one token through all {chain['layers']} "
+                                    "layers, x of each layer the bf16 output of the one before, "
+                                    "in one launch (qmoe_decode_stack)")
     if tiered:
         out["tiered_residency"] = dict(tiered, workload=f"{cfg.name}: routed experts in pinned host "
                                        "memory, LFU-with-recency device cache per layer")

@@ -242,6 +242,30 @@ int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16
                        float *topk_w_or_null, void *ws, size_t ws_bytes,
                        qmoe_stream_t stream);
 
+/* ---------------------------------------------------------------- chained one-token layers */
+
+#define QMOE_MAX_STACK 64
+
+/* One token through n_layers layers in one launch, each layer's input being the bf16 output of
+ * the one before: x_0 = x, x_{l+1} = out[l].  The per-layer arithmetic is that of a one-token
+ * qmoe_layer_forward call (results equal n_layers such calls chained, bit for bit); the chain
+ * overlaps the layers' phases as the pages' decode loop does ([TF-struct]: the next layer's
+ * resident work starts while the current one's routed work is still running): workgroups of
+ * layer l + 1 start loading their weights while layer l runs and wait only for its output.
+ *   layers: host array of n_layers descriptors (read during the call), all with the same dims
+ *           and either all or none with a shared block; the one-token launch must fit the
+ *           shape (routed inter and bits as for qmoe_layer_forward's single launch, else
+ *           QMOE_ERR_SHAPE).  n_layers in [0, QMOE_MAX_STACK]; 0 is a no-op.
+ *   x: bf16 [H] device; out: bf16 [n_layers, H] device (every layer's output; the last row is
+ *   the chain's result); out_f32_or_null: fp32 [n_layers, H]; topk_idx_or_null /
+ *   topk_w_or_null: [n_layers, k], both or neither.
+ *   ws: a workspace for one token (qmoe_workspace_bytes(d, >= 1)); calls that share it must
+ *   run on one stream in order, as for qmoe_layer_forward.
+ * Capturable in a graph (the per-layer table is written by kernels whose arguments carry it). */
+int qmoe_decode_stack(const qmoe_layer *layers, int32_t n_layers, const uint16_t *x,
+                      uint16_t *out, float *out_f32_or_null, int32_t *topk_idx_or_null,
+                      float *topk_w_or_null, void *ws, size_t ws_bytes, qmoe_stream_t stream);
+
 /* ---------------------------------------------------------------- tiered expert residency */
 
 /* For layers whose routed experts do not all stay in device memory: the experts live in host

@@ -18,8 +18,9 @@ EXPORTS = [
     "qmoe_bucket", "qmoe_expert_ffn", "qmoe_combine", "qmoe_combine_post", "qmoe_layer_forward",
     "qmoe_event_create", "qmoe_event_destroy", "qmoe_event_record", "qmoe_event_elapsed_ms",
     "qmoe_set_profile_events", "qmoe_workspace_status", "qmoe_cache_create", "qmoe_cache_destroy",
-    "qmoe_cache_plan", "qmoe_cache_stats", "qmoe_layer_forward_tiered",
+    "qmoe_cache_plan", "qmoe_cache_stats", "qmoe_layer_forward_tiered", "qmoe_decode_stack",
 ]
+MAX_STACK = 64
 
 
 class QmoeError(RuntimeError):
@@ -90,6 +91,7 @@ def lib():
                                             ctypes.POINTER(ctypes.c_int64)]),
         "qmoe_layer_forward_tiered": (ctypes.c_int, [ctypes.POINTER(Layer), P, P, I32, P, P, P, P, P,
                                                      SZ, P]),
+        "qmoe_decode_stack": (ctypes.c_int, [ctypes.POINTER(Layer), I32, P, P, P, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)

@@ -22,6 +22,21 @@
 // A workgroup only ever waits for words written by workgroups with smaller block indices, and
 // the hardware dispatches workgroups of a launch in index order, so every wait ends; each wait
 // is also bounded and reports a timeout in the status word instead of spinning on.
+//
+// Layer chain (decode_stack_kernel): one launch runs a token through several layers of the
+// same shape, x of layer l + 1 being the bf16 output of layer l.  Block b belongs to layer
+// b / (blocks per layer), with the roles above in the same order inside each layer, so the
+// argument above still holds: a layer's router, shared and routed gate/up workgroups wait for
+// the previous layer's output, which comes from workgroups of smaller index.  Layer l's words
+// carry tag epoch + l; its combining workgroups publish the output as tagged bf16 pairs (two
+// buffers, alternating by layer), which readers poll through the first word of each
+// combining workgroup's rows before fetching them all.  Workgroups of layer l + 1
+// are dispatched while layer l still runs and issue their weight loads before they wait, which
+// takes the router's cold loads and the launch gap off the chain between layers (the overlap
+// of the pages' cb1 / io / cb2 phases, TurboFieldfare post, section "TurboFieldfare의 전문가
+// 스트리밍 구조").  Every hand-off buffer of a layer is reused by the next one only after all
+// of its readers are done: each of them feeds, through the chain of waits, the output that
+// the next layer waits for.
 #pragma once
 #include "common.h"
 #include "store.h"
@@ -33,6 +48,7 @@ namespace qmoe {
 // Sync area of the workspace (zero-initialised, one 256-byte line each)
 constexpr int SY_LINE = 64;                    // words per line
 enum : int { SY_EPOCH = 0, SY_STATUS = 1, SY_DONE = 2, SY_LINES = 3 };
+constexpr int MAX_STACK = 64;                  // layers of one chained launch
 constexpr unsigned WAIT_LIMIT = 1u << 20;      // polls: well over a second
 constexpr int DEC_W = 4;                       // waves per workgroup (every role)
 constexpr int KB_DEC = 12;                     // k-steps a wave holds in registers
@@ -40,7 +56,7 @@ constexpr int DEC_THREADS = DEC_W * WAVE;
 // Values that many workgroups wait for are published in several copies, each on its own
 // memory pages, and a reader polls one of them, so that polling does not pile onto a few
 // memory lines: the logits in LOGIT_COPIES copies, h (routed and shared) in H_COPIES.
-constexpr int LOGIT_COPIES = 32, H_COPIES = 4;
+constexpr int LOGIT_COPIES = 32, H_COPIES = 4, X_COPIES = 8;
 inline __host__ __device__ size_t dec_copy_stride(size_t words) {
   return ((words * 8 + 4095) / 4096) * 4096;   // bytes
 }
@@ -73,12 +89,30 @@ struct DecodeArgs {
   const float *lscale;          // [1] layer scalar, or null (1)
   uint64_t *nrm;                // [combining workgroups] tagged partial sums of m^2
   int nR, nSG, nRG, nSD, nRD;
+  // layer chain
+  const uint64_t *xin;          // [X_COPIES] tagged x (bf16 pairs) from the previous layer, or null
+  uint64_t *xout;               // [X_COPIES] tagged output for the next layer, or null
+  size_t x_copy;                // words between x copies
+  unsigned *lcnt;               // arrival counter of the combining workgroups (the SY_DONE line)
+  int advance;                  // this layer's combining workgroups count their arrivals, and
+                                // the last of them advances the epoch (the launch's last layer)
 };
+
+// Per-layer pointers of a chained launch (a table in device memory).
+struct DecLayer {
+  const uint8_t *rq;
+  const uint16_t *rs, *rb;
+  const float *rscale, *pes, *lbias;
+  const uint8_t *experts, *shared;
+  const float *gain, *lscale;
+};
+
+inline __host__ __device__ size_t dec_x_copy_bytes(int H) { return dec_copy_stride((size_t)H / 2); }
 
 // LDS map (bytes) shared by every role: [top-k ranking][per-expert scales][reduction]
 // [union: staged x | staged h + combine rows]
 struct DecLds {
-  size_t tk, pes, red, nrm, x, xs, hf, hh, hl, hs, comb, total;
+  size_t tk, tks, pes, red, nrm, xw, x, xs, hf, hh, hl, hs, comb, total;
 };
 inline __host__ __device__ size_t al16(size_t v) { return (v + 15) & ~(size_t)15; }
 inline __host__ __device__ int dec_tiles_per_wg(int wpt) { return DEC_W / wpt; }
@@ -86,9 +120,11 @@ inline __host__ __device__ DecLds dec_lds(int H, int E, int k, int I, int Kc_sh,
   DecLds L;
   size_t o = 0;
   L.tk = o; o = al16(o + (size_t)topk_chunks(E) * WAVE * 4);
+  L.tks = o; o = al16(o + (size_t)2 * MAX_TOPK * 4);
   L.pes = o; o = al16(o + (size_t)E * 4 + 16);
   L.red = o; o = al16(o + (size_t)DEC_W * 32 * 4);
   L.nrm = o; o = al16(o + (size_t)(DEC_W + H / TILE_ROWS) * 4);
+  L.xw = o; o = al16(o + (size_t)TILE_ROWS * DEC_W / 2 * 4);
   const size_t u = o;
   L.x = u;
   L.xs = al16(L.x + (size_t)H * 2);
@@ -156,7 +192,19 @@ QMOE_DEV void fetch_tags(const DecodeArgs &a, int n, unsigned ep, Addr addr, F f
   }
 }
 
+// Whole workgroup: wait until the first word of every combining workgroup of the previous
+// layer carries its tag (ep - 1), then fetch the H bf16 outputs into dst.
+QMOE_DEV void dec_fetch_x(const DecodeArgs &a, unsigned ep, uint16_t *dst) {
+  const uint64_t *src = a.xin + (size_t)(blockIdx.x % X_COPIES) * a.x_copy;
+  const unsigned tg = ep - 1u;
+  const int rows = TILE_ROWS * dec_tiles_per_wg(a.wpt);
+  wait_tags(a, src, (a.H + rows - 1) / rows, rows / 2, tg);
+  fetch_tags<6>(a, a.H / 2, tg, [&](int i) { return src + i; },
+                [&](int i, float v) { ((uint32_t *)dst)[i] = __float_as_uint(v); });
+}
+
 // ---------------------------------------------------------------- R: router
+template <bool ST>
 QMOE_DEV void dec_router(const DecodeArgs &a, int rb, unsigned ep, char *smem) {
   RouterArgs ra;
   ra.x = a.x; ra.rq = a.rq; ra.rs = a.rs; ra.rb = a.rb; ra.rscale = a.rscale; ra.pes = a.pes;
@@ -167,13 +215,22 @@ QMOE_DEV void dec_router(const DecodeArgs &a, int rb, unsigned ep, char *smem) {
   ra.cnt_all = nullptr; ra.n_tb = 1; ra.n_eb = a.nR; ra.counts = nullptr; ra.offsets = nullptr;
   ra.sorted = nullptr; ra.active = nullptr; ra.n_active = nullptr; ra.slot_tab = nullptr;
   ra.n_slots = 0; ra.gsum = nullptr;
-  router_logits_block<1, 1, false>(ra, 0, rb, smem);
+  if (ST && a.xin) {
+    // x staged after the router's own LDS, fetched once the codes are in flight
+    uint16_t *xs = (uint16_t *)(smem + al16(router_lds_bytes(a.H, 1)));
+    ra.x = xs;
+    router_logits_block<1, 1, false>(ra, 0, rb, smem, [&]() { dec_fetch_x(a, ep, xs); });
+  } else {
+    router_logits_block<1, 1, false>(ra, 0, rb, smem);
+  }
 }
 
 // ---------------------------------------------------------------- top-k (every wave)
 // Expert and weight of `slot` (returned to every thread); with `publish`, the top-k outputs
-// are written too.  The E logits are fetched (tagged) into LDS as ordered bits, then every
-// wave runs the selection on its own copy in registers (same result in each wave).
+// are written too.  The E logits are fetched (tagged) into LDS as ordered bits, then one wave
+// of the workgroup runs the selection in registers and hands the result to the others through
+// LDS (the consumers of a layer all select at the same moment: one wave each, on a SIMD that
+// varies with the block index, keeps the SIMDs free for the waves that have other work).
 QMOE_DEV void dec_topk(const DecodeArgs &a, unsigned ep, int slot, bool publish, int &e_out,
                        float &w_out, char *smem, const DecLds &L) {
   const int tid = threadIdx.x, wv = tid / WAVE, lane = tid % WAVE;
@@ -198,22 +255,38 @@ QMOE_DEV void dec_topk(const DecodeArgs &a, unsigned ep, int slot, bool publish,
     if (i < E) pes[i] = pv[j];
   }
   __syncthreads();
-  int my_e;
-  float my_l;
-  topk_select(nch, [&](int c) { return c < nch ? ord[c * WAVE + lane] : 0u; }, k, my_e, my_l);
-  const float my_w = topk_weight(my_e, my_l, k, pes);
-  if (publish && wv == 0 && lane < k) {
-    a.topk_idx[lane] = my_e;
-    a.topk_w[lane] = my_w;
+  int32_t *tk_e = (int32_t *)(smem + L.tks);
+  float *tk_w = (float *)(tk_e + MAX_TOPK);
+  if (__builtin_amdgcn_readfirstlane(wv) == (int)(blockIdx.x % DEC_W)) {
+    int my_e;
+    float my_l;
+    topk_select(nch, [&](int c) { return c < nch ? ord[c * WAVE + lane] : 0u; }, k, my_e, my_l);
+    const float my_w = topk_weight(my_e, my_l, k, pes);
+    if (lane < k) {
+      tk_e[lane] = my_e;
+      tk_w[lane] = my_w;
+      if (publish) {
+        a.topk_idx[lane] = my_e;
+        a.topk_w[lane] = my_w;
+      }
+    }
   }
-  e_out = min(max(__builtin_amdgcn_readlane(my_e, slot), 0), E - 1);
-  w_out = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), slot));
+  __syncthreads();
+  e_out = min(max(tk_e[slot], 0), E - 1);
+  w_out = tk_w[slot];
 }
 
 // ---------------------------------------------------------------- gate/up of one tile, one token
-QMOE_DEV void dec_stage_x(const DecodeArgs &a, char *smem, const DecLds &L) {
-  stage_rows_bf16<DEC_THREADS>(a.x, a.H, 1, [](int) { return 0; }, (uint16_t *)(smem + L.x),
-                               (float *)(smem + L.xs));
+template <bool ST>
+QMOE_DEV void dec_stage_x(const DecodeArgs &a, unsigned ep, char *smem, const DecLds &L) {
+  uint16_t *xl = (uint16_t *)(smem + L.x);
+  if (ST && a.xin) {
+    dec_fetch_x(a, ep, xl);
+    // in place: the same 32-column sums as for x read from memory
+    stage_rows_bf16<DEC_THREADS>(xl, a.H, 1, [](int) { return 0; }, xl, (float *)(smem + L.xs));
+  } else {
+    stage_rows_bf16<DEC_THREADS>(a.x, a.H, 1, [](int) { return 0; }, xl, (float *)(smem + L.xs));
+  }
 }
 
 // 16 gate + 16 up rows of store tile `tile` of block `blk` against the staged x (split-K over
@@ -351,6 +424,7 @@ QMOE_DEV void dec_shared_down(const DecodeArgs &a, int b, unsigned ep, char *sme
   }
 }
 
+template <bool ST>
 QMOE_DEV void dec_routed_down(const DecodeArgs &a, int b, unsigned ep, char *smem, const DecLds &L) {
   const int tiles_d = a.H / TILE_ROWS, tpw = dec_tiles_per_wg(a.wpt);
   const int groups = (tiles_d + tpw - 1) / tpw;
@@ -402,6 +476,19 @@ QMOE_DEV void dec_routed_down(const DecodeArgs &a, int b, unsigned ep, char *sme
     for (int s = a.k - 1; s < nsrc; ++s) sh += comb[s * nr + r];
     m += sh;
   }
+  // residual rows: from memory, or from the previous layer's tagged output (complete by now:
+  // this workgroup's inputs depend on all of it)
+  float xr = 0.f;
+  if (ST && a.xin) {
+    uint32_t *xw = (uint32_t *)(smem + L.xw);
+    const uint64_t *src = a.xin + (size_t)(blockIdx.x % X_COPIES) * a.x_copy + row0 / 2;
+    fetch_tags<1>(a, nr / 2, ep - 1u, [&](int i) { return src + i; },
+                  [&](int i, float v) { xw[i] = __float_as_uint(v); });
+    if (mine) xr = bf16_to_f32((uint16_t)(xw[r / 2] >> (16 * (r & 1))));
+  } else if (mine) {
+    xr = bf16_to_f32(a.x[row0 + r]);
+  }
+  float o = 0.f;
   if (a.gain) {
     // post-combine norm: every combining workgroup publishes the sum of m^2 over its rows,
     // reads all of them (summed in the same order everywhere) and finishes its rows.  These
@@ -409,7 +496,6 @@ QMOE_DEV void dec_routed_down(const DecodeArgs &a, int b, unsigned ep, char *sme
     // the combining workgroups are far fewer than the workgroups the device holds at once and
     // every other role finishes without waiting on them.
     float *nr_lds = (float *)(smem + L.nrm);  // [DEC_W] wave sums, then [groups] partials
-    const float xr = mine ? bf16_to_f32(a.x[row0 + r]) : 0.f;
     const float gr = mine ? a.gain[row0 + r] : 0.f;
     const float ss = wave_sum(mine ? m * m : 0.f);
     if (tid % WAVE == 0) nr_lds[wv] = ss;
@@ -424,32 +510,36 @@ QMOE_DEV void dec_routed_down(const DecodeArgs &a, int b, unsigned ep, char *sme
                   [&](int i, float v) { part[i] = v; });
     float tot = 0.f;
     for (int i = 0; i < groups; ++i) tot += part[i];
-    if (mine) {
-      float o = xr + gr * (m * (1.f / sqrtf(tot / (float)a.H + RMS_EPS)));
-      if (a.lscale) o *= *a.lscale;
-      a.out[row0 + r] = (uint16_t)f32_to_bf16_bits(o);
-      if (a.out_f32) a.out_f32[row0 + r] = o;
-    }
-  } else if (mine) {
-    float o = bf16_to_f32(a.x[row0 + r]) + m;
-    if (a.lscale) o *= *a.lscale;
-    a.out[row0 + r] = (uint16_t)f32_to_bf16_bits(o);
+    o = xr + gr * (m * (1.f / sqrtf(tot / (float)a.H + RMS_EPS)));
+  } else {
+    o = xr + m;
+  }
+  if (a.lscale) o *= *a.lscale;
+  const uint32_t ob = mine ? f32_to_bf16_bits(o) : 0u;
+  if (mine) {
+    a.out[row0 + r] = (uint16_t)ob;
     if (a.out_f32) a.out_f32[row0 + r] = o;
   }
-  // the last combining workgroup advances the epoch
-  if (arrive_last(sy(a, SY_DONE), (unsigned)groups) && tid == 0) st_sys_u(sy(a, SY_EPOCH), ep);
+  if (ST && a.xout) {
+    // rows r, r + 1 (same wave) as one tagged pair in every copy
+    const uint32_t hi = (uint32_t)__shfl_down((int)ob, 1, WAVE);
+    if (mine && (r & 1) == 0)
+      for (int c = 0; c < X_COPIES; ++c)
+        st_tag(a.xout + (size_t)c * a.x_copy + (row0 + r) / 2, ep, __uint_as_float(ob | (hi << 16)));
+  }
+  // the last combining workgroup of the launch advances the epoch
+  if (a.advance && arrive_last(a.lcnt, (unsigned)groups) && tid == 0) st_sys_u(sy(a, SY_EPOCH), ep);
 }
 
-__global__ void __launch_bounds__(DEC_THREADS) decode_layer_kernel(DecodeArgs a) {
-  extern __shared__ __align__(16) char smem[];
-  const unsigned ep = ld_sys_u(sy(a, SY_EPOCH)) + 1u;
+// Block b (of one layer) with tag ep.
+template <bool ST>
+QMOE_DEV void decode_block(const DecodeArgs &a, int b, unsigned ep, char *smem) {
   const int Kc_sh = a.shared ? GROUP * ((a.Is / GROUP + a.nc - 1) / a.nc) : 0;
   const DecLds L = dec_lds(a.H, a.E, a.k, a.I, Kc_sh, a.nc, a.wpt);
-  int b = blockIdx.x;
-  if (b < a.nR) { dec_router(a, b, ep, smem); return; }
+  if (b < a.nR) { dec_router<ST>(a, b, ep, smem); return; }
   b -= a.nR;
   if (b < a.nSG) {
-    dec_stage_x(a, smem, L);
+    dec_stage_x<ST>(a, ep, smem, L);
     wait_tags(a, a.logits + (size_t)(blockIdx.x % LOGIT_COPIES) * a.logit_copy + (a.E - 1), 1, 1, ep);
     dec_gate_up(a, a.shared, b, a.h_sh, a.hsh_copy, ep, smem, L);
     return;
@@ -458,7 +548,7 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_layer_kernel(DecodeArgs a)
   if (b < a.nRG) {
     const int tiles_r = a.I / 16;
     const int slot = b / tiles_r, tile = b % tiles_r;
-    dec_stage_x(a, smem, L);
+    dec_stage_x<ST>(a, ep, smem, L);
     int e;
     float w;
     dec_topk(a, ep, slot, b == 0, e, w, smem, L);
@@ -469,7 +559,46 @@ __global__ void __launch_bounds__(DEC_THREADS) decode_layer_kernel(DecodeArgs a)
   b -= a.nRG;
   if (b < a.nSD) { dec_shared_down(a, b, ep, smem, L); return; }
   b -= a.nSD;
-  if (b < a.nRD) dec_routed_down(a, b, ep, smem, L);
+  if (b < a.nRD) dec_routed_down<ST>(a, b, ep, smem, L);
+}
+
+// One layer (a.lcnt = the SY_DONE line, a.advance = 1; a.xin, a.xout unused).
+__global__ void __launch_bounds__(DEC_THREADS) decode_layer_kernel(DecodeArgs a) {
+  extern __shared__ __align__(16) char smem[];
+  const unsigned ep = ld_sys_u(sy(a, SY_EPOCH)) + 1u;
+  decode_block<false>(a, blockIdx.x, ep, smem);
+}
+
+// n_layers chained layers of one token; a holds the shared shape and hand-off buffers, tab the
+// per-layer pointers, xb[0..1] the two tagged x buffers.  out, out_f32 are [n_layers][H]; the
+// top-k outputs are [n_layers][k] when tk_per_layer, else one scratch row for every layer.
+__global__ void __launch_bounds__(DEC_THREADS)
+decode_stack_kernel(DecodeArgs a, const DecLayer *tab, uint64_t *xb0, uint64_t *xb1, int n_layers,
+                    int tk_per_layer) {
+  extern __shared__ __align__(16) char smem[];
+  const int per = a.nR + a.nSG + a.nRG + a.nSD + a.nRD;
+  const int l = blockIdx.x / per;
+  const unsigned ep = ld_sys_u(sy(a, SY_EPOCH)) + 1u + (unsigned)l;
+  const DecLayer D = tab[l];
+  a.rq = D.rq; a.rs = D.rs; a.rb = D.rb; a.rscale = D.rscale; a.pes = D.pes; a.lbias = D.lbias;
+  a.experts = D.experts; a.shared = D.shared; a.gain = D.gain; a.lscale = D.lscale;
+  a.out += (size_t)l * a.H;
+  if (a.out_f32) a.out_f32 += (size_t)l * a.H;
+  if (tk_per_layer) { a.topk_idx += (size_t)l * a.k; a.topk_w += (size_t)l * a.k; }
+  a.xin = l > 0 ? ((l - 1) & 1 ? xb1 : xb0) : nullptr;
+  a.xout = l + 1 < n_layers ? (l & 1 ? xb1 : xb0) : nullptr;
+  a.lcnt = sy(a, SY_DONE);
+  a.advance = l == n_layers - 1;
+  decode_block<true>(a, blockIdx.x % per, ep, smem);
+}
+
+// Writes entries [first, first + n) of the per-layer table (n <= DEC_TAB_CHUNK).
+constexpr int DEC_TAB_CHUNK = 32;
+struct DecTabChunk {
+  DecLayer L[DEC_TAB_CHUNK];
+};
+__global__ void dec_table_kernel(DecTabChunk c, DecLayer *tab, int first, int n) {
+  if ((int)threadIdx.x < n) tab[first + threadIdx.x] = c.L[threadIdx.x];
 }
 
 }  // namespace qmoe

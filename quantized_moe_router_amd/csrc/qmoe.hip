@@ -139,7 +139,7 @@ inline int dec_shared_chunks(const qmoe_dims *d) {
 struct WsLayout {
   size_t cnt, logits, tidx, tw, counts, offsets, sorted, active, nact, slot_tab;
   size_t hr_hi, hr_lo, hs_hi, hs_lo, y, ysh, gx, ghr, ghs, slot_ids;
-  size_t dec_logits, dec_hr, dec_hsh, dec_yr, dec_ysh, dec_nrm, total;
+  size_t dec_logits, dec_hr, dec_hsh, dec_yr, dec_ysh, dec_nrm, dec_x, dec_tab, total;
 };
 
 WsLayout ws_layout(const qmoe_dims *d, int Tmax) {
@@ -173,6 +173,8 @@ WsLayout ws_layout(const qmoe_dims *d, int Tmax) {
   w.dec_yr = o; o += al((k - 1) * H * 8);
   w.dec_ysh = o; o += al((size_t)dec_shared_chunks(d) * H * 8);
   w.dec_nrm = o; o += al((H / TILE_ROWS) * 8);
+  w.dec_x = o; o += 2 * (size_t)X_COPIES * dec_x_copy_bytes((int)H);
+  w.dec_tab = o; o += al((size_t)MAX_STACK * sizeof(DecLayer));
   w.total = o;
   return w;
 }
@@ -435,8 +437,9 @@ static DecLds dec_lds_of(const qmoe_dims *d, bool sh) {
   return dec_lds(d->hidden, d->n_experts, d->top_k, d->inter, kc, nc, dec_wpt(d));
 }
 
-static int launch_decode(const qmoe_layer *L, const uint16_t *x, uint16_t *out, float *out_f32,
-                         int32_t *idx, float *w, void *ws, const WsLayout &wl, hipStream_t s) {
+static DecodeArgs make_decode_args(const qmoe_layer *L, const uint16_t *x, uint16_t *out,
+                                   float *out_f32, int32_t *idx, float *w, void *ws,
+                                   const WsLayout &wl) {
   const qmoe_dims *d = &L->d;
   const bool sh = L->shared != nullptr;
   DecodeArgs a;
@@ -469,11 +472,54 @@ static int launch_decode(const qmoe_layer *L, const uint16_t *x, uint16_t *out, 
   a.nRG = a.k * (a.I / 16);
   a.nSD = sh ? tiles_d * a.nc : 0;
   a.nRD = a.k * ((tiles_d + tpw - 1) / tpw);
-  const size_t lds = std::max(router_lds_bytes(a.H, 1), dec_lds_of(d, sh).total);
+  a.lcnt = a.sync + (size_t)SY_DONE * SY_LINE;
+  a.advance = 1;
+  return a;
+}
+
+static int launch_decode(const qmoe_layer *L, const uint16_t *x, uint16_t *out, float *out_f32,
+                         int32_t *idx, float *w, void *ws, const WsLayout &wl, hipStream_t s) {
+  const DecodeArgs a = make_decode_args(L, x, out, out_f32, idx, w, ws, wl);
+  const size_t lds = std::max(router_lds_bytes(a.H, 1), dec_lds_of(&L->d, a.shared != nullptr).total);
   int rc = set_lds(decode_layer_kernel, lds);
   if (rc) return rc;
   const int n = a.nR + a.nSG + a.nRG + a.nSD + a.nRD;
   hipLaunchKernelGGL(decode_layer_kernel, dim3(n), dim3(DEC_THREADS), lds, s, a);
+  QMOE_LAUNCHED();
+  return QMOE_OK;
+}
+
+// Layer chain of one token in one launch (decode.h): the per-layer table is written by small
+// kernels whose arguments carry it (so that the call can be captured in a graph), then the
+// chained kernel runs every layer.
+static int launch_decode_stack(const qmoe_layer *layers, int n, const uint16_t *x, uint16_t *out,
+                               float *out_f32, int32_t *idx, float *w, bool tk_per_layer, void *ws,
+                               const WsLayout &wl, hipStream_t s) {
+  DecLayer *tab = at<DecLayer>(ws, wl.dec_tab);
+  for (int f = 0; f < n; f += DEC_TAB_CHUNK) {
+    DecTabChunk c;
+    memset(&c, 0, sizeof c);
+    const int m = std::min(DEC_TAB_CHUNK, n - f);
+    for (int i = 0; i < m; ++i) {
+      const qmoe_layer &Li = layers[f + i];
+      c.L[i] = DecLayer{Li.r.codes, Li.r.scales, Li.r.biases, Li.r.router_scale,
+                        Li.r.per_expert_scale, Li.r.logit_bias, (const uint8_t *)Li.experts,
+                        (const uint8_t *)Li.shared, Li.post_norm_gain, Li.layer_scalar};
+    }
+    hipLaunchKernelGGL(dec_table_kernel, dim3(1), dim3(DEC_TAB_CHUNK), 0, s, c, tab, f, m);
+    QMOE_LAUNCHED();
+  }
+  DecodeArgs a = make_decode_args(&layers[0], x, out, out_f32, idx, w, ws, wl);
+  a.x_copy = dec_x_copy_bytes(a.H) / 8;
+  uint64_t *xb0 = at<uint64_t>(ws, wl.dec_x);
+  uint64_t *xb1 = xb0 + (size_t)X_COPIES * a.x_copy;
+  const size_t lds = std::max(al16(router_lds_bytes(a.H, 1)) + (size_t)a.H * 2,
+                              dec_lds_of(&layers[0].d, a.shared != nullptr).total);
+  int rc = set_lds(decode_stack_kernel, lds);
+  if (rc) return rc;
+  const int per = a.nR + a.nSG + a.nRG + a.nSD + a.nRD;
+  hipLaunchKernelGGL(decode_stack_kernel, dim3((unsigned)(per * n)), dim3(DEC_THREADS), lds, s, a,
+                     (const DecLayer *)tab, xb0, xb1, n, tk_per_layer ? 1 : 0);
   QMOE_LAUNCHED();
   return QMOE_OK;
 }
@@ -800,6 +846,43 @@ int qmoe_cache_stats(const qmoe_expert_cache *cache, int64_t *hits_out, int64_t 
   if (!cache || !hits_out || !misses_out) return fail(QMOE_ERR_ARG, "cache_stats: NULL pointer");
   *hits_out = cache->policy.hits();
   *misses_out = cache->policy.misses();
+  return ok();
+}
+
+int qmoe_decode_stack(const qmoe_layer *layers, int32_t n_layers, const uint16_t *x,
+                      uint16_t *out, float *out_f32_or_null, int32_t *topk_idx_or_null,
+                      float *topk_w_or_null, void *ws, size_t ws_bytes, qmoe_stream_t stream) {
+  if (!layers) return fail(QMOE_ERR_ARG, "decode_stack: layers is NULL");
+  if (n_layers < 0 || n_layers > QMOE_MAX_STACK)
+    return fail(QMOE_ERR_SHAPE, "decode_stack: n_layers must be in [0, %d] (got %d)", QMOE_MAX_STACK,
+                n_layers);
+  if (n_layers == 0) return ok();
+  int rc;
+  for (int i = 0; i < n_layers; ++i) {
+    if ((rc = check_layer(&layers[i]))) return rc;
+    if (memcmp(&layers[i].d, &layers[0].d, sizeof(qmoe_dims)) != 0)
+      return fail(QMOE_ERR_SHAPE, "decode_stack: dims of layer %d differ from layer 0", i);
+    if ((layers[i].shared != nullptr) != (layers[0].shared != nullptr))
+      return fail(QMOE_ERR_ARG, "decode_stack: every layer or none must have a shared block");
+  }
+  if (!x || !out) return fail(QMOE_ERR_ARG, "decode_stack: x/out must not be NULL");
+  if ((topk_idx_or_null == nullptr) != (topk_w_or_null == nullptr))
+    return fail(QMOE_ERR_ARG, "decode_stack: give both top-k outputs or neither");
+  const qmoe_dims *d = &layers[0].d;
+  if (!decode_fits(d))
+    return fail(QMOE_ERR_SHAPE, "decode_stack: inter %d with %d-bit experts is too wide for the "
+                "one-token launch", d->inter, d->expert_bits == 8 ? 8 : 4);
+  if ((rc = check_ws(d, 1, ws, ws_bytes))) return rc;
+  if ((rc = check_arch())) return rc;
+  const WsLayout wl = ws_layout(d, 1);
+  const bool tk = topk_idx_or_null != nullptr;
+  int32_t *idx = tk ? topk_idx_or_null : at<int32_t>(ws, wl.tidx);
+  float *w = tk ? topk_w_or_null : at<float>(ws, wl.tw);
+  hipStream_t s = (hipStream_t)stream;
+  if (g_prof_start && (rc = record_event(g_prof_start, s))) return rc;
+  if ((rc = launch_decode_stack(layers, n_layers, x, out, out_f32_or_null, idx, w, tk, ws, wl, s)))
+    return rc;
+  if (g_prof_stop && (rc = record_event(g_prof_stop, s))) return rc;
   return ok();
 }
 

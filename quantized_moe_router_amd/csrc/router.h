@@ -381,8 +381,15 @@ inline __host__ __device__ size_t router_lds_bytes(int H, int nt = ROUTER_TB) {
   return (size_t)nt * H * 4 + 64;
 }
 
-template <int TB, int EPW, bool GSUM>
-QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *smem) {
+struct NoWait {
+  QMOE_DEV void operator()() const {}
+};
+
+// xwait() is called by the whole workgroup after the first batch of codes was issued and
+// before x is read (a caller whose x is produced inside the same launch waits there).
+template <int TB, int EPW, bool GSUM, class XW = NoWait>
+QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *smem,
+                                  XW xwait = XW()) {
   constexpr int EPB = EPW * ROUTER_WAVES;
   const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
   const int H = a.H;
@@ -412,9 +419,20 @@ QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *sme
 #pragma unroll
   for (int x = 0; x < EPW; ++x) lb[x] = a.lbias ? a.lbias[min(e_first + x, a.E - 1)] : 0.f;
   // activations: thread tid stages elements 4 (tid + 256 j) .. + 3 of each token, XB chunks
-  // per batch (one batch for H <= 3072)
+  // per batch (one batch for H <= 3072); the router scales of the first batch are loaded
+  // before xwait()
   constexpr int XB = 3;
   const int n4 = H / 4;
+  float4 rsv[XB];
+  auto load_rs = [&](int j0) {
+#pragma unroll
+    for (int j = 0; j < XB; ++j) {
+      const int c = min(tid + ROUTER_THREADS * (j0 + j), n4 - 1);
+      rsv[j] = a.rscale ? *(const float4 *)(a.rscale + 4 * c) : float4{1.f, 1.f, 1.f, 1.f};
+    }
+  };
+  load_rs(0);
+  xwait();
   float *z = (float *)smem;                                  // [nt][H]
   float *fac = z + nt * H;                                   // [TB]
   __shared__ float red[ROUTER_WAVES][TB];
@@ -423,11 +441,10 @@ QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *sme
   for (int i = 0; i < TB; ++i) ss[i] = 0.f;
   for (int j0 = 0; j0 * ROUTER_THREADS < n4; j0 += XB) {
     uint2 xv[TB][XB];
-    float4 rsv[XB];
+    if (j0 > 0) load_rs(j0);
 #pragma unroll
     for (int j = 0; j < XB; ++j) {
       const int c = min(tid + ROUTER_THREADS * (j0 + j), n4 - 1);
-      rsv[j] = a.rscale ? *(const float4 *)(a.rscale + 4 * c) : float4{1.f, 1.f, 1.f, 1.f};
 #pragma unroll
       for (int i = 0; i < TB; ++i)
         xv[i][j] = *(const uint2 *)(a.x + (size_t)(t0 + min(i, nt - 1)) * H + 4 * c);

@@ -184,6 +184,21 @@ def layer_forward(layer, x, ws, out=None, out_f32=None, topk_idx=None, topk_w=No
     return out
 
 
+def decode_stack(layers, x, ws, out=None, out_f32=None, topk_idx=None, topk_w=None):
+    """One token through the chained layers in one launch: x [1, H] (or [H]) bf16; returns
+    out [n_layers, H] bf16, every layer's output (the last row is the chain's result)."""
+    n = len(layers)
+    d = layers[0].dims if n else None
+    if out is None:
+        out = torch.empty(max(n, 1), d.hidden if d else 1, dtype=torch.bfloat16, device=x.device)
+    arr = (Layer * max(n, 1))(*[l.struct for l in layers])
+    check(lib().qmoe_decode_stack(
+        arr, n, _ptr(x, 2, "x"), _ptr(out, 2, "out"), _ptr(out_f32, 4, allow_none=True),
+        _ptr(topk_idx, 4, allow_none=True), _ptr(topk_w, 4, allow_none=True), _ptr(ws, 1, "ws"),
+        ws.numel(), _stream()))
+    return out
+
+
 class ExpertCache:
     """Tiered residency: routed expert blocks in host memory (`host_store`, a CPU uint8 tensor,
     pinned for full copy speed), `slots` of them cached in the device tensor `slot_store`."""

@@ -127,6 +127,25 @@ def test_argument_errors_do_not_touch_the_device():
     assert lib.qmoe_layer_forward(ctypes.byref(lay), fake, 4, fake, None, None, None, fake,
                                   1 << 30, None) == -1          # misaligned post-norm gain
     assert lib.qmoe_bucket(ctypes.byref(d), None, 4, fake, fake, fake, fake, fake, None, 0, None) == -1
+    # chained one-token layers
+    lays = (L.Layer * 2)(L.Layer(d, r, 4096, 65536, None), L.Layer(d, r, 4096, 65536, None))
+    assert lib.qmoe_decode_stack(None, 2, fake, fake, None, None, None, fake, 1 << 30, None) == -1
+    assert lib.qmoe_decode_stack(lays, 65, fake, fake, None, None, None, fake, 1 << 30, None) == -2
+    assert lib.qmoe_decode_stack(lays, -1, fake, fake, None, None, None, fake, 1 << 30, None) == -2
+    assert lib.qmoe_decode_stack(lays, 0, None, None, None, None, None, None, 0, None) == 0
+    assert lib.qmoe_decode_stack(lays, 2, None, fake, None, None, None, fake, 1 << 30, None) == -1
+    assert lib.qmoe_decode_stack(lays, 2, fake, fake, None, fake, None, fake, 1 << 30,
+                                 None) == -1                    # one of the two top-k outputs
+    assert lib.qmoe_decode_stack(lays, 2, fake, fake, None, None, None, fake, 16, None) == -3
+    d2 = L.make_dims(256, 16, 2, 192, 128)
+    lays[1] = L.Layer(d2, r, 4096, 1 << 20, None)
+    assert lib.qmoe_decode_stack(lays, 2, fake, fake, None, None, None, fake, 1 << 30,
+                                 None) == -2                    # dims differ
+    assert "differ" in L.last_error()
+    lays[1] = L.Layer(d, r, 4096, 65536, 8192)
+    assert lib.qmoe_decode_stack(lays, 2, fake, fake, None, None, None, fake, 1 << 30,
+                                 None) == -1                    # shared block in one layer only
+    assert L.MAX_STACK == 64
     # events
     assert lib.qmoe_set_profile_events(None, None) == 0       # profiling off
     assert lib.qmoe_event_create(None) == -1
