@@ -55,8 +55,10 @@ constexpr int KB_DEC = 12;                     // k-steps a wave holds in regist
 constexpr int DEC_THREADS = DEC_W * WAVE;
 // Values that many workgroups wait for are published in several copies, each on its own
 // memory pages, and a reader polls one of them, so that polling does not pile onto a few
-// memory lines: the logits in LOGIT_COPIES copies, h (routed and shared) in H_COPIES.
-constexpr int LOGIT_COPIES = 32, H_COPIES = 4, X_COPIES = 8;
+// memory lines: the logits in LOGIT_COPIES copies, h (routed and shared) in H_COPIES.  More
+// copies spread the polling but cost the router more stores before its logits are all out;
+// eight copies measured fastest for the logits (32 and 64 were slower, as were 1 to 4).
+constexpr int LOGIT_COPIES = 8, H_COPIES = 4, X_COPIES = 8;
 inline __host__ __device__ size_t dec_copy_stride(size_t words) {
   return ((words * 8 + 4095) / 4096) * 4096;   // bytes
 }
@@ -540,6 +542,8 @@ QMOE_DEV void decode_block(const DecodeArgs &a, int b, unsigned ep, char *smem) 
   b -= a.nR;
   if (b < a.nSG) {
     dec_stage_x<ST>(a, ep, smem, L);
+    // once the last router workgroup has published (so that the router's loads go first);
+    // the wait's barrier also makes the staged x visible to every wave
     wait_tags(a, a.logits + (size_t)(blockIdx.x % LOGIT_COPIES) * a.logit_copy + (a.E - 1), 1, 1, ep);
     dec_gate_up(a, a.shared, b, a.h_sh, a.hsh_copy, ep, smem, L);
     return;
