@@ -68,15 +68,56 @@ QMOE_DEV float dot32_q4_bf16(const uint32_t w[4], const uint32_t x[16]) {
   return a0 + a1;
 }
 
-// ---------------------------------------------------------------- wave reductions
+// ---------------------------------------------------------------- lane exchanges in registers
+// Values of other lanes through lane swaps (v_permlane32_swap, v_permlane16_swap) and DPP
+// inside 16-lane rows, instead of LDS permutes (each of which is a round trip through the LDS
+// unit, and a reduction is a chain of them).
+// xor32 / xor16: the value of lane l ^ 32 / l ^ 16.
+QMOE_DEV float xor32(float v) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? p[0] : p[1]);
+}
+QMOE_DEV float xor16(float v) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float((threadIdx.x & 16) ? p[0] : p[1]);
+}
+template <int CTRL>
+QMOE_DEV float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+QMOE_DEV float xor1(float v) { return dpp<0xB1>(v); }   // quad_perm [1, 0, 3, 2]
+QMOE_DEV float xor2(float v) { return dpp<0x4E>(v); }   // quad_perm [2, 3, 0, 1]
+
+// Sum over the 16 lanes of each row, as the xor butterfly 1, 2, 4, 8 adds them: after the
+// quad steps the value is the same in the four lanes of a quad, so the half-row mirror gives
+// the xor-4 partner's value, and after that the row mirror the xor-8 partner's.
+QMOE_DEV float row_sum16(float v) {
+  v += xor1(v);
+  v += xor2(v);
+  v += dpp<0x141>(v);   // row_half_mirror
+  v += dpp<0x140>(v);   // row_mirror
+  return v;
+}
+
+// Sum over the wave, as the xor butterfly 32, 16, 8, 4, 2, 1 adds them (the same bits in
+// every lane): after the xor-32 and xor-16 steps the value repeats every 16 lanes, so the
+// rotation of a row by 8 gives the xor-8 partner's value, and so on down to 1.
 QMOE_DEV float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+  v += xor32(v);
+  v += xor16(v);
+  v += dpp<0x128>(v);   // row_ror 8
+  v += dpp<0x124>(v);   // row_ror 4
+  v += dpp<0x122>(v);   // row_ror 2
+  v += dpp<0x121>(v);   // row_ror 1
   return v;
 }
 QMOE_DEV float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+  v = fmaxf(v, xor32(v));
+  v = fmaxf(v, xor16(v));
+  v = fmaxf(v, dpp<0x128>(v));
+  v = fmaxf(v, dpp<0x124>(v));
+  v = fmaxf(v, dpp<0x122>(v));
+  v = fmaxf(v, dpp<0x121>(v));
   return v;
 }
 

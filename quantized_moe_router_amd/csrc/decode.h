@@ -316,7 +316,7 @@ QMOE_DEV void dec_gate_up(const DecodeArgs &a, const uint8_t *blk, int tile, uin
         acc += kstep_bf16(cv[u], sb[u], xl + col, xs[col / 32]);
       }
   }
-  acc += __shfl_xor(acc, 32, WAVE);
+  acc += xor32(acc);
   if (half == 0) red[wv * 32 + rr] = acc;
   __syncthreads();
   if (tid < 16 * H_COPIES) {
@@ -371,8 +371,8 @@ QMOE_DEV void dec_stage_h(const DecodeArgs &a, const uint64_t *src, int n, unsig
     }
     *(qmoe_u32x4 *)(hh + 8 * c) = qmoe_u32x4{hi2[0], hi2[1], hi2[2], hi2[3]};
     *(qmoe_u32x4 *)(hl + 8 * c) = qmoe_u32x4{lo2[0], lo2[1], lo2[2], lo2[3]};
-    p += __shfl_xor(p, 1, WAVE);
-    p += __shfl_xor(p, 2, WAVE);
+    p += xor1(p);
+    p += xor2(p);
     if ((c & 3) == 0) hs[c / 4] = p;
   }
   __syncthreads();
@@ -395,7 +395,7 @@ QMOE_DEV void dec_down_dot(const DownRegs &d, int kb0, int g0, int kshift, char 
       const int col = (((kb0 + u) >> kshift) - g0) * GROUP + half * 32;
       acc += kstep_hilo(d.cv[u], d.sb[u], hh + col, hl + col, hs[col / 32]);
     }
-  acc += __shfl_xor(acc, 32, WAVE);
+  acc += xor32(acc);
   if (half == 0) red[wv * 32 + rr] = acc;
 }
 

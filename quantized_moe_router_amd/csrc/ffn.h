@@ -92,8 +92,8 @@ QMOE_DEV void stage_rows_bf16(const uint16_t *src, int K, int mb, RowSel rowsel,
     *(qmoe_u32x4 *)(dst + (size_t)i * K + 8 * cc) = v;
     float p = bf16lo(v.x) + bf16hi(v.x) + bf16lo(v.y) + bf16hi(v.y) + bf16lo(v.z) +
               bf16hi(v.z) + bf16lo(v.w) + bf16hi(v.w);
-    p += __shfl_xor(p, 1, WAVE);
-    p += __shfl_xor(p, 2, WAVE);
+    p += xor1(p);
+    p += xor2(p);
     if ((cc & 3) == 0) sums[i * (K / 32) + cc / 4] = p;
   }
 }
@@ -114,8 +114,8 @@ QMOE_DEV void stage_rows_hilo(const uint16_t *src_hi, const uint16_t *src_lo, in
               (bf16lo(vh.y) + bf16lo(vl.y)) + (bf16hi(vh.y) + bf16hi(vl.y)) +
               (bf16lo(vh.z) + bf16lo(vl.z)) + (bf16hi(vh.z) + bf16hi(vl.z)) +
               (bf16lo(vh.w) + bf16lo(vl.w)) + (bf16hi(vh.w) + bf16hi(vl.w));
-    p += __shfl_xor(p, 1, WAVE);
-    p += __shfl_xor(p, 2, WAVE);
+    p += xor1(p);
+    p += xor2(p);
     if ((cc & 3) == 0) sums[i * (K / 32) + cc / 4] = p;
   }
 }
@@ -213,7 +213,7 @@ QMOE_DEV void gu_tile(const FfnArgs &a, const SlotRows &sr, int tile, char *smem
     }
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
-      const float tot = acc[i] + __shfl_xor(acc[i], 32, WAVE);
+      const float tot = acc[i] + xor32(acc[i]);
       if (half == 0) red[(wv * MB + i) * 32 + rr] = tot;
     }
     __syncthreads();
@@ -304,8 +304,8 @@ QMOE_DEV void d_tile(const FfnArgs &a, const SlotRows &sr, int tile, int kb0, in
                 (bf16lo(vh.y) + bf16lo(vl.y)) + (bf16hi(vh.y) + bf16hi(vl.y)) +
                 (bf16lo(vh.z) + bf16lo(vl.z)) + (bf16hi(vh.z) + bf16hi(vl.z)) +
                 (bf16lo(vh.w) + bf16lo(vl.w)) + (bf16hi(vh.w) + bf16hi(vl.w));
-      p += __shfl_xor(p, 1, WAVE);
-      p += __shfl_xor(p, 2, WAVE);
+      p += xor1(p);
+      p += xor2(p);
       if ((cc & 3) == 0) hs[i * (Kc / 32) + cc / 4] = p;
     }
     __syncthreads();
@@ -328,7 +328,7 @@ QMOE_DEV void d_tile(const FfnArgs &a, const SlotRows &sr, int tile, int kb0, in
     }
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
-      const float tot = acc[i] + __shfl_xor(acc[i], 32, WAVE);
+      const float tot = acc[i] + xor32(acc[i]);
       if (half == 0) red[(wv * MB + i) * 32 + rr] = tot;
     }
     __syncthreads();

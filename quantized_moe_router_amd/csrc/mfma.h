@@ -210,10 +210,7 @@ __global__ void __launch_bounds__(GU_WAVES * WAVE) gu_pf_kernel(FfnArgs a) {
     // group sums: over the 16 lanes of each lane group, then over the waves
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      hs[i] += __shfl_xor(hs[i], 1, WAVE);
-      hs[i] += __shfl_xor(hs[i], 2, WAVE);
-      hs[i] += __shfl_xor(hs[i], 4, WAVE);
-      hs[i] += __shfl_xor(hs[i], 8, WAVE);
+      hs[i] = row_sum16(hs[i]);
     }
     if (n == 0) {
 #pragma unroll

@@ -131,7 +131,7 @@ QMOE_DEV void topk_select(int nch, Load load, int k, int &my_e, float &my_l) {
 // per_expert_scale (global or LDS).  Lanes >= k get 0.
 QMOE_DEV float topk_weight(int my_e, float my_l, int k, const float *pes) {
   const int lane = threadIdx.x % WAVE;
-  const float vmax = __shfl(my_l, 0, WAVE);
+  const float vmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_l), 0));
   const float z = (lane < k) ? expf(my_l - vmax) : 0.f;
   const float zsum = wave_sum(z);
   return (lane < k) ? (z / zsum) * pes[my_e] : 0.f;
@@ -471,10 +471,7 @@ QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *sme
           float g = 0.f;
           if (c < n4)
             g = (bf16lo(xv[i][j].x) + bf16hi(xv[i][j].x)) + (bf16lo(xv[i][j].y) + bf16hi(xv[i][j].y));
-          g += __shfl_xor(g, 1, WAVE);
-          g += __shfl_xor(g, 2, WAVE);
-          g += __shfl_xor(g, 4, WAVE);
-          g += __shfl_xor(g, 8, WAVE);
+          g = row_sum16(g);
           if (c < n4 && (c & 15) == 0) a.gsum[(size_t)(t0 + i) * (H / GROUP) + c / 16] = g;
         }
       }
