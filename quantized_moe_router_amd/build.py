@@ -13,7 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libqmoe.so")
 SOURCES = ["qmoe.hip"]
-HEADERS = ["common.h", "store.h", "router.h", "ffn.h", "mfma.h", "decode.h"]
+HEADERS = ["common.h", "store.h", "router.h", "router_mf.h", "ffn.h", "mfma.h", "decode.h"]
 
 
 def hipcc():

@@ -17,6 +17,7 @@
 #include "router.h"
 #include "ffn.h"
 #include "decode.h"
+#include "router_mf.h"
 #include "cache.h"
 
 using namespace qmoe;
@@ -139,7 +140,7 @@ inline int dec_shared_chunks(const qmoe_dims *d) {
 struct WsLayout {
   size_t cnt, logits, tidx, tw, counts, offsets, sorted, active, nact, slot_tab;
   size_t hr_hi, hr_lo, hs_hi, hs_lo, y, ysh, gx, ghr, ghs, slot_ids;
-  size_t dec_logits, dec_hr, dec_hsh, dec_yr, dec_ysh, dec_nrm, dec_x, dec_tab, total;
+  size_t dec_logits, dec_hr, dec_hsh, dec_yr, dec_ysh, dec_nrm, dec_x, dec_tab, rpart, rss, total;
 };
 
 WsLayout ws_layout(const qmoe_dims *d, int Tmax) {
@@ -175,6 +176,8 @@ WsLayout ws_layout(const qmoe_dims *d, int Tmax) {
   w.dec_nrm = o; o += al((H / TILE_ROWS) * 8);
   w.dec_x = o; o += 2 * (size_t)X_COPIES * dec_x_copy_bytes((int)H);
   w.dec_tab = o; o += al((size_t)MAX_STACK * sizeof(DecLayer));
+  w.rpart = o; o += al((size_t)rmf_splits((int)H) * Tc * E * 4);   // router partial tiles
+  w.rss = o; o += al((size_t)rmf_splits((int)H) * Tc * 4);         // and sums of x^2
   w.total = o;
   return w;
 }
@@ -194,6 +197,7 @@ int check_ws(const qmoe_dims *d, int T, void *ws, size_t ws_bytes) {
 int check_router(const qmoe_router *r) {
   if (!r || !r->codes || !r->scales || !r->biases || !r->per_expert_scale)
     return fail(QMOE_ERR_ARG, "router codes/scales/biases/per_expert_scale must not be NULL");
+  if (!aligned(r->codes, 16)) return fail(QMOE_ERR_ARG, "router codes must be 16-byte aligned");
   if (r->router_scale && !aligned(r->router_scale, 16))
     return fail(QMOE_ERR_ARG, "router_scale must be 16-byte aligned");
   return QMOE_OK;
@@ -237,8 +241,9 @@ int set_lds(K kernel, size_t bytes) {
   return QMOE_OK;
 }
 
+// dynamic LDS of the top-k / bucketing launch
 size_t router_smem(const qmoe_dims *d, int T) {
-  return std::max(router_lds_bytes(d->hidden), bucket_lds_bytes(T * d->top_k, d->n_experts));
+  return bucket_lds_bytes(T * d->top_k, d->n_experts);
 }
 
 RouterArgs make_router_args(const qmoe_dims *d, const qmoe_router *r, const uint16_t *x, int T,
@@ -258,10 +263,20 @@ RouterArgs make_router_args(const qmoe_dims *d, const qmoe_router *r, const uint
   return a;
 }
 
-int launch_router(const RouterArgs &a, size_t smem, hipStream_t s) {
-  int rc = set_lds(router_kernel, smem);
+// Router of a call of T tokens (router_mf.h): logits on the matrix cores, then top-k (and, with
+// a.counts set, bucketing) in a second launch.
+// (a.T <= CHUNK_TOKENS: the partial tiles live in the workspace regions rpart / rss)
+int launch_router(const RouterArgs &a, size_t smem, void *ws, const WsLayout &wl, hipStream_t s) {
+  float *part = at<float>(ws, wl.rpart), *ssq = at<float>(ws, wl.rss);
+  const unsigned nb = (unsigned)(((a.T + RMF_ROWS - 1) / RMF_ROWS) *
+                                 ((a.E + RMF_COLS - 1) / RMF_COLS) * rmf_splits(a.H));
+  hipLaunchKernelGGL(router_mf_kernel, dim3(nb), dim3(RMF_THREADS), 0, s, a, part, ssq);
+  QMOE_LAUNCHED();
+  if (!a.counts) smem = 0;
+  int rc = set_lds(router_topk_kernel, smem);
   if (rc) return rc;
-  hipLaunchKernelGGL(router_kernel, dim3(a.n_tb * a.n_eb), dim3(ROUTER_THREADS), smem, s, a);
+  hipLaunchKernelGGL(router_topk_kernel, dim3((unsigned)((a.T + ROUTER_WAVES - 1) / ROUTER_WAVES)),
+                     dim3(ROUTER_THREADS), smem, s, a, (const float *)part, (const float *)ssq);
   QMOE_LAUNCHED();
   return QMOE_OK;
 }
@@ -628,12 +643,19 @@ int qmoe_router_topk(const qmoe_dims *d, const qmoe_router *r, const uint16_t *x
   if (rc || (rc = check_T(T)) || (rc = check_router(r))) return rc;
   if (T == 0) return ok();
   if (!x || !topk_idx || !topk_w) return fail(QMOE_ERR_ARG, "x/topk_idx/topk_w must not be NULL");
+  if (!aligned(x, 16)) return fail(QMOE_ERR_ARG, "x must be 16-byte aligned");
   if ((rc = check_ws(d, T, ws, ws_bytes))) return rc;
   if ((rc = check_arch())) return rc;
   const WsLayout wl = ws_layout(d, T);
   float *logits = logits_or_null ? logits_or_null : at<float>(ws, wl.logits);
-  RouterArgs a = make_router_args(d, r, x, T, logits, topk_idx, topk_w, ws);
-  if ((rc = launch_router(a, router_smem(d, T), (hipStream_t)stream))) return rc;
+  // per chunk of at most CHUNK_TOKENS tokens (the partial tiles of the router are sized for one)
+  for (int c0 = 0; c0 < T; c0 += CHUNK_TOKENS) {
+    const int Tc = std::min(CHUNK_TOKENS, T - c0);
+    RouterArgs a = make_router_args(d, r, x + (size_t)c0 * d->hidden, Tc,
+                                    logits + (size_t)c0 * d->n_experts, topk_idx + (size_t)c0 * d->top_k,
+                                    topk_w + (size_t)c0 * d->top_k, ws);
+    if ((rc = launch_router(a, router_smem(d, Tc), ws, wl, (hipStream_t)stream))) return rc;
+  }
   return ok();
 }
 
@@ -666,6 +688,7 @@ int qmoe_expert_ffn(const qmoe_layer *L, const uint16_t *x, int32_t T, const int
   if (T == 0) return ok();
   if (!x || !offsets || !sorted || !active || !n_active || !y)
     return fail(QMOE_ERR_ARG, "expert_ffn: NULL pointer");
+  if (!aligned(x, 16)) return fail(QMOE_ERR_ARG, "x must be 16-byte aligned");
   if ((rc = check_ws(&L->d, T, ws, ws_bytes))) return rc;
   if ((rc = check_arch())) return rc;
   FfnArgs a = make_ffn_args(L, x, T, offsets, sorted, active, n_active, y, y_shared_or_null, ws, T);
@@ -724,6 +747,7 @@ int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16
   if (rc || (rc = check_T(T))) return rc;
   if (T == 0) return ok();
   if (!x || !out) return fail(QMOE_ERR_ARG, "layer_forward: x/out must not be NULL");
+  if (!aligned(x, 16)) return fail(QMOE_ERR_ARG, "x must be 16-byte aligned");
   const int Tc_max = std::min<int>(T, CHUNK_TOKENS);
   if ((rc = check_ws(&L->d, Tc_max, ws, ws_bytes))) return rc;
   if ((rc = check_arch())) return rc;
@@ -761,7 +785,7 @@ int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16
     ra.n_slots = fa.n_slots;
     const bool mfma = !valu_ffn(Tc);
     if (mfma) ra.gsum = at<float>(ws, wl.gx);
-    if ((rc = launch_router(ra, router_smem(d, Tc), s))) return rc;
+    if ((rc = launch_router(ra, router_smem(d, Tc), ws, wl, s))) return rc;
     uint16_t *oc = out + (size_t)c0 * H;
     float *oc32 = out_f32_or_null ? out_f32_or_null + (size_t)c0 * H : nullptr;
     if (mfma) {
@@ -866,6 +890,7 @@ int qmoe_decode_stack(const qmoe_layer *layers, int32_t n_layers, const uint16_t
       return fail(QMOE_ERR_ARG, "decode_stack: every layer or none must have a shared block");
   }
   if (!x || !out) return fail(QMOE_ERR_ARG, "decode_stack: x/out must not be NULL");
+  if (!aligned(x, 16)) return fail(QMOE_ERR_ARG, "x must be 16-byte aligned");
   if ((topk_idx_or_null == nullptr) != (topk_w_or_null == nullptr))
     return fail(QMOE_ERR_ARG, "decode_stack: give both top-k outputs or neither");
   const qmoe_dims *d = &layers[0].d;
@@ -904,6 +929,7 @@ int qmoe_layer_forward_tiered(const qmoe_layer *L, qmoe_expert_cache *C, const u
     return fail(QMOE_ERR_ARG, "post_norm_gain must be 16-byte aligned");
   if (T == 0) return ok();
   if (!x || !out) return fail(QMOE_ERR_ARG, "layer_forward_tiered: x/out must not be NULL");
+  if (!aligned(x, 16)) return fail(QMOE_ERR_ARG, "x must be 16-byte aligned");
   const int Tc_max = std::min<int>(T, CHUNK_TOKENS);
   if ((rc = check_ws(d, Tc_max, ws, ws_bytes))) return rc;
   if ((rc = check_arch())) return rc;
@@ -924,7 +950,7 @@ int qmoe_layer_forward_tiered(const qmoe_layer *L, qmoe_expert_cache *C, const u
     float *w = topk_w_or_null ? topk_w_or_null + (size_t)c0 * k : at<float>(ws, wl.tw);
     // router and top-k, then the ids to the host
     RouterArgs ra = make_router_args(d, &L->r, xc, Tc, at<float>(ws, wl.logits), idx, w, ws);
-    if ((rc = launch_router(ra, router_smem(d, Tc), s))) return rc;
+    if ((rc = launch_router(ra, router_smem(d, Tc), ws, wl, s))) return rc;
     QMOE_HIP(hipMemcpyAsync(C->h_ids, idx, (size_t)N * 4, hipMemcpyDeviceToHost, s));
     QMOE_HIP(hipStreamSynchronize(s));
     CachePlan p;

@@ -549,44 +549,6 @@ QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *sme
   }
 }
 
-// After a router workgroup has written its logits: the last workgroup of a token block runs
-// top-k for that block; with bucketing requested, the last of those (or that workgroup
-// itself when there is a single token block) runs the bucketing.
-QMOE_DEV void router_finish(const RouterArgs &a, int tb, char *smem) {
-  if (!arrive_last(&a.cnt_tb[tb], (unsigned)a.n_eb)) return;
-  const int wv = threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
-  const int t0 = tb * ROUTER_TB;
-  const int nt = min(ROUTER_TB, a.T - t0);
-  for (int i = wv; i < nt; i += ROUTER_WAVES) {
-    const int t = t0 + i;
-    int myi;
-    float myw;
-    topk_wave(a.logits + (size_t)t * a.E, a.E, a.k, a.pes, myi, myw);
-    if (lane < a.k) {
-      st_sys(a.topk_idx + (size_t)t * a.k + lane, myi);
-      st_sys(a.topk_w + (size_t)t * a.k + lane, myw);
-    }
-  }
-  __syncthreads();
-  if (a.counts == nullptr) return;
-  if (a.n_tb == 1) {
-    drain_memory();    // this workgroup wrote every assignment
-    __syncthreads();
-  } else if (!arrive_last(a.cnt_all, (unsigned)a.n_tb)) {
-    return;
-  }
-  bucket_block<ROUTER_THREADS>([&](int f) { return ld_sys(a.topk_idx + f); }, a.T * a.k, a.E,
-                               a.counts, a.offsets, a.sorted, a.active, a.n_active, a.slot_tab,
-                               a.n_slots, (int *)smem);
-}
-
-__global__ void __launch_bounds__(ROUTER_THREADS) router_kernel(RouterArgs a) {
-  extern __shared__ __align__(16) char smem[];
-  const int tb = blockIdx.x / a.n_eb, eb = blockIdx.x % a.n_eb;
-  router_logits_block<ROUTER_TB, ROUTER_EPW, true>(a, tb, eb, smem);
-  router_finish(a, tb, smem);
-}
-
 __global__ void __launch_bounds__(256) bucket_kernel(const int32_t *idx, int N, int E,
                                                      int32_t *counts, int32_t *offsets,
                                                      int32_t *sorted, int32_t *active,
