@@ -40,7 +40,8 @@
  *  - T = 0 (no tokens) is a valid no-op that returns QMOE_OK.
  *  - Shape limits: hidden, inter and shared_inter are multiples of 64; hidden <= 8192,
  *    inter and shared_inter <= 4096; group == 64; expert_bits 0, 4 or 8; 1 <= top_k <= min(n_experts, 32); 1 <= n_experts <= 1024;
- *    T <= 65536 per call.  Store base pointers and strides are 256-byte aligned.
+ *    T <= 65536 per call.  Store base pointers and strides are 256-byte aligned; x and the
+ *    router codes are 16-byte aligned (the kernels read them with 16-byte loads).
  *
  * Quantised formats (canonical, as the pages describe them)
  * ---------------------------------------------------------
@@ -168,7 +169,11 @@ int qmoe_unpack_expert(const qmoe_dims *d, int32_t inter, const void *src_block,
  *   topk_idx[t, :] = the k largest logits, descending; equal logits -> lower expert index
  *   topk_w[t, j] = softmax over the k kept logits, times per_expert_scale[topk_idx[t, j]]
  * Outputs: topk_idx int32 [T, k], topk_w fp32 [T, k], logits fp32 [T, E] (optional, may be
- * NULL).  ws: device workspace of qmoe_workspace_bytes(d, T) bytes. */
+ * NULL).  ws: device workspace of qmoe_workspace_bytes(d, T) bytes.  Runs per chunk of at most
+ * 128 tokens, two launches each: the logits on the matrix cores (fp32 products of
+ * x*router_scale with s*q+b over tiles of 16 tokens x 16 experts, the hidden axis split over
+ * workgroups), then the partial tiles summed in a fixed order, the norm factor and bias
+ * applied, and the top-k selected, one wave per token. */
 int qmoe_router_topk(const qmoe_dims *d, const qmoe_router *r, const uint16_t *x, int32_t T,
                      int32_t *topk_idx, float *topk_w, float *logits_or_null,
                      void *ws, size_t ws_bytes, qmoe_stream_t stream);
@@ -227,12 +232,12 @@ int qmoe_combine_post(const qmoe_dims *d, const uint16_t *x, const float *y, con
  * roles router, shared gate/up, routed gate/up, shared down and routed down, handing data to
  * each other through the workspace (each role starts loading its weights as soon as it knows
  * them); the routed-down workgroups of the last slot combine.  Larger calls run per chunk of
- * at most 128 tokens as four launches:
- *   kernel 1: router logits and the 64-column group sums of x, then (last workgroups) top-k,
- *             softmax and bucketing into a table of 16-row blocks;
- *   kernel 2: routed and shared gate/up projection + SwiGLU on the matrix cores;
- *   kernel 3: routed and shared down projection on the matrix cores;
- *   kernel 4: combine (qmoe_combine / qmoe_combine_post arithmetic).
+ * at most 128 tokens as five launches:
+ *   kernels 1-2: router logits (as qmoe_router_topk) and the 64-column group sums of x, then
+ *             top-k, softmax and (last workgroup) bucketing into a table of 16-row blocks;
+ *   kernel 3: routed and shared gate/up projection + SwiGLU on the matrix cores;
+ *   kernel 4: routed and shared down projection on the matrix cores;
+ *   kernel 5: combine (qmoe_combine / qmoe_combine_post arithmetic).
  * out: bf16 [T, H]; out_f32_or_null: fp32 [T, H]; topk_idx_or_null / topk_w_or_null receive
  * the routing ([T, k]).  Results equal qmoe_router_topk -> qmoe_bucket -> qmoe_expert_ffn ->
  * qmoe_combine_post up to fp32 summation order.  T may exceed 128; callers that follow the
