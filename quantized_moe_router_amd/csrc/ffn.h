@@ -375,7 +375,18 @@ __global__ void __launch_bounds__(256) combine_kernel(const uint16_t *x, const f
        o += (size_t)gridDim.x * blockDim.x) {
     const size_t t = o / H, col = o % H;
     float acc = 0.f;
-    for (int j = 0; j < k; ++j) acc = fmaf(w[t * k + j], y[(t * k + j) * H + col], acc);
+    for (int j0 = 0; j0 < k; j0 += 8) {   // eight rows' loads in flight, summed j ascending
+      float v[8], wj[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int j = min(j0 + q, k - 1);
+        wj[q] = w[t * k + j];
+        v[q] = y[(t * k + j) * H + col];
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (j0 + q < k) acc = fmaf(wj[q], v[q], acc);
+    }
     if (y_sh) acc += y_sh[o];
     acc += bf16_to_f32(x[o]);
     out[o] = (uint16_t)f32_to_bf16_bits(acc);

@@ -315,6 +315,31 @@ __global__ void __launch_bounds__(256) gsum_kernel(const uint16_t *x, int n_grou
   g[i] = v[0];
 }
 
+// sum_j w[j] y[j * H + off .. + 4) over j = 0..k-1 in ascending order (fp32 FMAs); the loads of
+// eight rows are in flight together (a loop of dependent round trips otherwise)
+QMOE_DEV float4 routed_sum4(const float *y, const float *w, int k, int H, size_t off) {
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    float4 v[8];
+    float wj[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int j = min(j0 + q, k - 1);   // rows past k re-read the last one (not used)
+      wj[q] = w[j];
+      v[q] = *(const float4 *)(y + (size_t)j * H + off);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (j0 + q < k) {
+        acc.x = fmaf(wj[q], v[q].x, acc.x);
+        acc.y = fmaf(wj[q], v[q].y, acc.y);
+        acc.z = fmaf(wj[q], v[q].z, acc.z);
+        acc.w = fmaf(wj[q], v[q].w, acc.w);
+      }
+  }
+  return acc;
+}
+
 // out[t, :] = bf16( x[t, :] + sum_j w[t,j] y[t*k+j, :] + y_sh[t, :] ) in fp32, j ascending,
 // then the shared row, then the residual (the order of combine_kernel); four columns per
 // thread.
@@ -326,15 +351,7 @@ __global__ void __launch_bounds__(256) combine_pf_kernel(const uint16_t *x, cons
   for (size_t o = (size_t)blockIdx.x * blockDim.x + threadIdx.x; o < n4;
        o += (size_t)gridDim.x * blockDim.x) {
     const size_t t = (o * 4) / H, col = (o * 4) % H;
-    float4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const float wj = w[t * k + j];
-      const float4 v = *(const float4 *)(y + (t * k + j) * H + col);
-      acc.x = fmaf(wj, v.x, acc.x);
-      acc.y = fmaf(wj, v.y, acc.y);
-      acc.z = fmaf(wj, v.z, acc.z);
-      acc.w = fmaf(wj, v.w, acc.w);
-    }
+    float4 acc = routed_sum4(y + t * k * H, w + t * k, k, H, col);
     if (y_sh) {
       const float4 v = *(const float4 *)(y_sh + t * H + col);
       acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
@@ -367,14 +384,7 @@ __global__ void __launch_bounds__(POST_THREADS) combine_post_kernel(
     const int c = tid + POST_THREADS * v;
     float4 acc = {0.f, 0.f, 0.f, 0.f};
     if (c < n4) {
-      for (int j = 0; j < k; ++j) {
-        const float wj = w[(size_t)t * k + j];
-        const float4 yv = *(const float4 *)(y + ((size_t)t * k + j) * H + 4 * c);
-        acc.x = fmaf(wj, yv.x, acc.x);
-        acc.y = fmaf(wj, yv.y, acc.y);
-        acc.z = fmaf(wj, yv.z, acc.z);
-        acc.w = fmaf(wj, yv.w, acc.w);
-      }
+      acc = routed_sum4(y + (size_t)t * k * H, w + (size_t)t * k, k, H, (size_t)4 * c);
       if (y_sh) {
         const float4 s4 = *(const float4 *)(y_sh + (size_t)t * H + 4 * c);
         acc.x += s4.x; acc.y += s4.y; acc.z += s4.z; acc.w += s4.w;
