@@ -179,7 +179,13 @@ __global__ void __launch_bounds__(ROUTER_THREADS) router_topk_kernel(RouterArgs 
   const int n_ks = rmf_splits(a.H);
   if (t < a.T) {
     float tot = 0.f;
-    for (int ks = 0; ks < n_ks; ++ks) tot += ssq[(size_t)ks * a.T + t];
+    for (int k0 = 0; k0 < n_ks; k0 += 16) {   // sixteen splits' loads in flight, added in order
+      float pv[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) pv[q] = k0 + q < n_ks ? ssq[(size_t)(k0 + q) * a.T + t] : 0.f;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) tot += pv[q];
+    }
     const float fac = a.inv_sqrt_h / sqrtf(tot / (float)a.H + RMS_EPS);
     const int nch = topk_chunks(a.E);
     if (nch <= 1) rmf_token<1>(a, part, t, fac);
