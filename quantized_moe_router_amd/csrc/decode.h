@@ -213,17 +213,17 @@ QMOE_DEV void dec_router(const DecodeArgs &a, int rb, unsigned ep, char *smem) {
   ra.lbias = a.lbias; ra.T = 1; ra.H = a.H; ra.E = a.E; ra.k = a.k; ra.inv_sqrt_h = a.inv_sqrt_h;
   ra.logits = nullptr; ra.logits_tag = a.logits; ra.tag = ep;
   ra.tag_copies = LOGIT_COPIES; ra.tag_copy_stride = a.logit_copy;
-  ra.topk_idx = nullptr; ra.topk_w = nullptr; ra.cnt_tb = nullptr;
-  ra.cnt_all = nullptr; ra.n_tb = 1; ra.n_eb = a.nR; ra.counts = nullptr; ra.offsets = nullptr;
+  ra.topk_idx = nullptr; ra.topk_w = nullptr;
+  ra.cnt_all = nullptr; ra.counts = nullptr; ra.offsets = nullptr;
   ra.sorted = nullptr; ra.active = nullptr; ra.n_active = nullptr; ra.slot_tab = nullptr;
   ra.n_slots = 0; ra.gsum = nullptr;
   if (ST && a.xin) {
     // x staged after the router's own LDS, fetched once the codes are in flight
     uint16_t *xs = (uint16_t *)(smem + al16(router_lds_bytes(a.H, 1)));
     ra.x = xs;
-    router_logits_block<1, 1, false>(ra, 0, rb, smem, [&]() { dec_fetch_x(a, ep, xs); });
+    router_logits_block<1, 1>(ra, 0, rb, smem, [&]() { dec_fetch_x(a, ep, xs); });
   } else {
-    router_logits_block<1, 1, false>(ra, 0, rb, smem);
+    router_logits_block<1, 1>(ra, 0, rb, smem);
   }
 }
 

@@ -257,9 +257,6 @@ RouterArgs make_router_args(const qmoe_dims *d, const qmoe_router *r, const uint
   a.logits = logits; a.topk_idx = idx; a.topk_w = w;
   const WsLayout wl = ws_layout(d, T);
   a.cnt_all = at<unsigned>(ws, wl.cnt);
-  a.cnt_tb = at<unsigned>(ws, wl.cnt) + 64;
-  a.n_tb = (T + ROUTER_TB - 1) / ROUTER_TB;
-  a.n_eb = (d->n_experts + ROUTER_EPB - 1) / ROUTER_EPB;
   return a;
 }
 

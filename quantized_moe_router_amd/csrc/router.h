@@ -14,10 +14,7 @@
 
 namespace qmoe {
 
-constexpr int ROUTER_TB = 4;     // tokens per router workgroup (multi-token router)
-constexpr int ROUTER_EPW = 4;    // experts per wave (multi-token router)
 constexpr int ROUTER_WAVES = 4;
-constexpr int ROUTER_EPB = ROUTER_EPW * ROUTER_WAVES;  // experts per router workgroup
 constexpr int ROUTER_THREADS = ROUTER_WAVES * WAVE;
 
 struct RouterArgs {
@@ -37,9 +34,7 @@ struct RouterArgs {
   size_t tag_copy_stride;
   int32_t *topk_idx;          // [T, k]
   float *topk_w;              // [T, k]
-  unsigned *cnt_tb;           // [n_tb] completion counters (zero on entry, zero on exit)
-  unsigned *cnt_all;          // [1]
-  int n_tb, n_eb;             // token blocks, expert blocks
+  unsigned *cnt_all;          // [1] completion counter (zero on entry, zero on exit)
   // optional fused bucketing (layer path); null counts -> skip
   int32_t *counts, *offsets, *sorted, *active, *n_active;
   int32_t *slot_tab;          // [n_slots][4] block table {expert, first bucket position, rows,
@@ -135,19 +130,6 @@ QMOE_DEV float topk_weight(int my_e, float my_l, int k, const float *pes) {
   const float z = (lane < k) ? expf(my_l - vmax) : 0.f;
   const float zsum = wave_sum(z);
   return (lane < k) ? (z / zsum) * pes[my_e] : 0.f;
-}
-
-// The whole selection by one wave for one token.  lrow: E logits written by other
-// workgroups of the launch (system-scope loads).  Lane j < k gets the j-th expert and weight.
-QMOE_DEV void topk_wave(const float *lrow, int E, int k, const float *pes, int &myi, float &myw) {
-  const int lane = threadIdx.x % WAVE;
-  float l;
-  topk_select(topk_chunks(E), [&](int c) {
-    const int e = c * WAVE + lane;
-    return e < E ? topk_ord(ld_sys(lrow + e)) : 0u;
-  }, k, myi, l);
-  myw = topk_weight(myi, l, k, pes);
-  if (lane >= k) myi = 0;
 }
 
 // ---------------------------------------------------------------- bucketing (one workgroup)
@@ -365,7 +347,9 @@ QMOE_DEV void bucket_block(Get get, int N, int E, int32_t *counts, int32_t *offs
   }
 }
 
-// ---------------------------------------------------------------- router logits
+// ---------------------------------------------------------------- router logits (VALU)
+// The one-token layer's router role (TB = 1, EPW = 1: one expert per wave); calls of several
+// tokens use the matrix-core router (router_mf.h).
 // Workgroup (tb, eb): tokens [TB tb, TB tb + TB) x experts [EPB eb, EPB eb + EPB), EPW
 // experts per wave.  Per token the input is staged in LDS as z = x * router_scale (fp32);
 // the token's norm factor f = (1/sqrt(H)) / sqrt(mean(x^2) + eps) multiplies the finished
@@ -377,7 +361,7 @@ QMOE_DEV void bucket_block(Get get, int N, int E, int32_t *counts, int32_t *offs
 constexpr int ROUTER_MAX_H = 8192;
 constexpr int ROUTER_RB = 11;          // 256-element blocks of codes a wave loads per batch
 
-inline __host__ __device__ size_t router_lds_bytes(int H, int nt = ROUTER_TB) {
+inline __host__ __device__ size_t router_lds_bytes(int H, int nt) {
   return (size_t)nt * H * 4 + 64;
 }
 
@@ -387,7 +371,7 @@ struct NoWait {
 
 // xwait() is called by the whole workgroup after the first batch of codes was issued and
 // before x is read (a caller whose x is produced inside the same launch waits there).
-template <int TB, int EPW, bool GSUM, class XW = NoWait>
+template <int TB, int EPW, class XW = NoWait>
 QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *smem,
                                   XW xwait = XW()) {
   constexpr int EPB = EPW * ROUTER_WAVES;
@@ -464,15 +448,6 @@ QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *sme
           ss[i] = fmaf(x3, x3, ss[i]);
           *(float4 *)(z + i * H + 4 * c) =
               float4{x0 * rsv[j].x, x1 * rsv[j].y, x2 * rsv[j].z, x3 * rsv[j].w};
-        }
-        if (GSUM && a.gsum && eb == 0) {
-          // group sums of the raw x: 16 consecutive threads hold one 64-column group (a
-          // balanced pairwise tree over its 64 elements)
-          float g = 0.f;
-          if (c < n4)
-            g = (bf16lo(xv[i][j].x) + bf16hi(xv[i][j].x)) + (bf16lo(xv[i][j].y) + bf16hi(xv[i][j].y));
-          g = row_sum16(g);
-          if (c < n4 && (c & 15) == 0) a.gsum[(size_t)(t0 + i) * (H / GROUP) + c / 16] = g;
         }
       }
     }
