@@ -98,6 +98,15 @@ def test_argument_errors_do_not_touch_the_device():
     # T = 0 is a no-op
     assert lib.qmoe_router_topk(ctypes.byref(d), ctypes.byref(r), fake, 0, fake, fake, None,
                                 None, 0, None) == 0
+    # x and the router codes are read with 16-byte loads
+    odd = ctypes.c_void_p(4100)
+    assert lib.qmoe_router_topk(ctypes.byref(d), ctypes.byref(r), odd, 4, fake, fake, None,
+                                fake, 1 << 30, None) == -1
+    assert "aligned" in L.last_error()
+    rodd = L.Router(4100, 4096, 4096, None, 4096, None)
+    assert lib.qmoe_router_topk(ctypes.byref(d), ctypes.byref(rodd), fake, 4, fake, fake, None,
+                                fake, 1 << 30, None) == -1
+    assert "codes" in L.last_error()
     # layer checks
     lay = L.Layer(d, r, 4096, 4096, None)
     assert lib.qmoe_layer_forward(ctypes.byref(lay), fake, 4, fake, None, None, None, fake,
@@ -108,6 +117,8 @@ def test_argument_errors_do_not_touch_the_device():
     lay = L.Layer(d, r, 4096, 65536, None)
     assert lib.qmoe_layer_forward(ctypes.byref(lay), None, 4, fake, None, None, None, fake,
                                   1 << 30, None) == -1          # null x
+    assert lib.qmoe_layer_forward(ctypes.byref(lay), odd, 4, fake, None, None, None, fake,
+                                  1 << 30, None) == -1          # misaligned x
     assert lib.qmoe_layer_forward(ctypes.byref(lay), None, 0, None, None, None, None, None,
                                   0, None) == 0                 # T = 0: pointers unused
     d0 = L.make_dims(256, 16, 2, 128, 0)
