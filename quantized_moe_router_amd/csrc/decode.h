@@ -58,7 +58,7 @@ constexpr int DEC_THREADS = DEC_W * WAVE;
 // memory lines: the logits in LOGIT_COPIES copies, h (routed and shared) in H_COPIES.  More
 // copies spread the polling but cost the router more stores before its logits are all out;
 // eight copies measured fastest for the logits (32 and 64 were slower, as were 1 to 4).
-constexpr int LOGIT_COPIES = 8, H_COPIES = 4, X_COPIES = 8;
+constexpr int LOGIT_COPIES = 8, H_COPIES = 4, X_COPIES = 8, TK_COPIES = 8;
 inline __host__ __device__ size_t dec_copy_stride(size_t words) {
   return ((words * 8 + 4095) / 4096) * 4096;   // bytes
 }
@@ -90,6 +90,8 @@ struct DecodeArgs {
   const float *gain;            // [H] post-combine norm gain, or null (no norm)
   const float *lscale;          // [1] layer scalar, or null (1)
   uint64_t *nrm;                // [combining workgroups] tagged partial sums of m^2
+  uint64_t *tk;                 // [TK_COPIES][2 MAX_TOPK] tagged top-k (expert bits, weight) of
+                                //   the layer, published by the first routed gate/up workgroup
   int nR, nSG, nRG, nSD, nRD;
   // layer chain
   const uint64_t *xin;          // [X_COPIES] tagged x (bf16 pairs) from the previous layer, or null
@@ -270,6 +272,11 @@ QMOE_DEV void dec_topk(const DecodeArgs &a, unsigned ep, int slot, bool publish,
       if (publish) {
         a.topk_idx[lane] = my_e;
         a.topk_w[lane] = my_w;
+        // and for the routed down workgroups, which take their expert from these words
+        for (int c = 0; c < TK_COPIES; ++c) {
+          st_tag(a.tk + (size_t)c * 2 * MAX_TOPK + lane, ep, __int_as_float(my_e));
+          st_tag(a.tk + (size_t)c * 2 * MAX_TOPK + MAX_TOPK + lane, ep, my_w);
+        }
       }
     }
   }
@@ -432,9 +439,19 @@ QMOE_DEV void dec_routed_down(const DecodeArgs &a, int b, unsigned ep, char *sme
   const int groups = (tiles_d + tpw - 1) / tpw;
   const int slot = b / groups, g = b % groups;
   const int tid = threadIdx.x, wv = tid / WAVE;
-  int e;
-  float w;
-  dec_topk(a, ep, slot, false, e, w, smem, L);
+  // expert and weight of the slot from the top-k the first routed gate/up workgroup published
+  // (selected from the same logits by the same code: these workgroups have time to spare and
+  // leave the SIMDs to the gate/up workgroups, whose selection is on the critical path)
+  int32_t *tk_e = (int32_t *)(smem + L.tks);
+  float *tk_w = (float *)(tk_e + MAX_TOPK);
+  const uint64_t *tks = a.tk + (size_t)(blockIdx.x % TK_COPIES) * 2 * MAX_TOPK;
+  fetch_tags<1>(a, 2 * a.k, ep,
+                [&](int i) { return tks + (i < a.k ? i : MAX_TOPK + i - a.k); },
+                [&](int i, float v) {
+                  if (i < a.k) tk_e[i] = __float_as_int(v); else tk_w[i - a.k] = v;
+                });
+  const int e = min(max(tk_e[slot], 0), a.E - 1);
+  const float w = tk_w[slot];
   const int KS = (a.I / GROUP) << a.kshift;
   const int tile = g * tpw + wv / a.wpt, part = wv % a.wpt;
   const int kb0 = (KS * part) / a.wpt, kb1 = (KS * (part + 1)) / a.wpt;

@@ -140,7 +140,8 @@ inline int dec_shared_chunks(const qmoe_dims *d) {
 struct WsLayout {
   size_t cnt, logits, tidx, tw, counts, offsets, sorted, active, nact, slot_tab;
   size_t hr_hi, hr_lo, hs_hi, hs_lo, y, ysh, gx, ghr, ghs, slot_ids;
-  size_t dec_logits, dec_hr, dec_hsh, dec_yr, dec_ysh, dec_nrm, dec_x, dec_tab, rpart, rss, total;
+  size_t dec_logits, dec_hr, dec_hsh, dec_yr, dec_ysh, dec_nrm, dec_tk, dec_x, dec_tab, rpart, rss,
+      total;
 };
 
 WsLayout ws_layout(const qmoe_dims *d, int Tmax) {
@@ -174,6 +175,7 @@ WsLayout ws_layout(const qmoe_dims *d, int Tmax) {
   w.dec_yr = o; o += al((k - 1) * H * 8);
   w.dec_ysh = o; o += al((size_t)dec_shared_chunks(d) * H * 8);
   w.dec_nrm = o; o += al((H / TILE_ROWS) * 8);
+  w.dec_tk = o; o += al((size_t)TK_COPIES * 2 * MAX_TOPK * 8);
   w.dec_x = o; o += 2 * (size_t)X_COPIES * dec_x_copy_bytes((int)H);
   w.dec_tab = o; o += al((size_t)MAX_STACK * sizeof(DecLayer));
   w.rpart = o; o += al((size_t)rmf_splits((int)H) * Tc * E * 4);   // router partial tiles
@@ -478,6 +480,7 @@ static DecodeArgs make_decode_args(const qmoe_layer *L, const uint16_t *x, uint1
   a.topk_idx = idx; a.topk_w = w; a.out = out; a.out_f32 = out_f32;
   a.gain = L->post_norm_gain; a.lscale = L->layer_scalar;
   a.nrm = at<uint64_t>(ws, wl.dec_nrm);
+  a.tk = at<uint64_t>(ws, wl.dec_tk);
   const int tiles_d = a.H / TILE_ROWS, tpw = dec_tiles_per_wg(a.wpt);
   a.nR = (a.E + ROUTER_WAVES - 1) / ROUTER_WAVES;   // one expert per wave
   a.nSG = sh ? a.Is / 16 : 0;
