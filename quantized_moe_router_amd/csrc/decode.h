@@ -559,9 +559,7 @@ QMOE_DEV void decode_block(const DecodeArgs &a, int b, unsigned ep, char *smem) 
   b -= a.nR;
   if (b < a.nSG) {
     dec_stage_x<ST>(a, ep, smem, L);
-    // once the last router workgroup has published (so that the router's loads go first);
-    // the wait's barrier also makes the staged x visible to every wave
-    wait_tags(a, a.logits + (size_t)(blockIdx.x % LOGIT_COPIES) * a.logit_copy + (a.E - 1), 1, 1, ep);
+    __syncthreads();   // (no wait for the router: measured slightly faster than letting it go first)
     dec_gate_up(a, a.shared, b, a.h_sh, a.hsh_copy, ep, smem, L);
     return;
   }
