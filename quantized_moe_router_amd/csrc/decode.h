@@ -123,7 +123,7 @@ inline __host__ __device__ int dec_tiles_per_wg(int wpt) { return DEC_W / wpt; }
 inline __host__ __device__ DecLds dec_lds(int H, int E, int k, int I, int Kc_sh, int nc, int wpt) {
   DecLds L;
   size_t o = 0;
-  L.tk = o; o = al16(o + (size_t)topk_chunks(E) * WAVE * 4);
+  L.tk = o; o = al16(o + (size_t)topk_chunks(E) * WAVE * (topk_chunks(E) <= 2 ? 8 : 4));
   L.tks = o; o = al16(o + (size_t)2 * MAX_TOPK * 4);
   L.pes = o; o = al16(o + (size_t)E * 4 + 16);
   L.red = o; o = al16(o + (size_t)DEC_W * 32 * 4);
@@ -230,17 +230,44 @@ QMOE_DEV void dec_router(const DecodeArgs &a, int rb, unsigned ep, char *smem) {
 }
 
 // ---------------------------------------------------------------- top-k (every wave)
-// Expert and weight of `slot` (returned to every thread); with `publish`, the top-k outputs
-// are written too.  The E logits are fetched (tagged) into LDS as ordered bits, then one wave
-// of the workgroup runs the selection in registers and hands the result to the others through
-// LDS (the consumers of a layer all select at the same moment: one wave each, on a SIMD that
-// varies with the block index, keeps the SIMDs free for the waves that have other work).
+// Top-k of the workgroup's routed gate/up (all waves), for E <= 128, by rank: expert i gets
+// the 64-bit key (ordered logit << 32) | ~i.  The keys are distinct and their order is the
+// order in which the round-by-round selection takes the experts (larger logit first, the
+// lower index first among equal logits), so the expert whose key has r keys above it is the
+// r-th selection.  Each wave ranks E_pad / 4 experts, every lane of it against one of the
+// E_pad / (E_pad / 4) equal parts of the keys (broadcast LDS reads), and the parts' counts are
+// added by lane swaps; the experts of rank < k write themselves to their place.  Every wave
+// then forms the k weights itself.
+template <int NCH>
+QMOE_DEV void dec_rank_select(const uint64_t *key, int k, int32_t *tk_e, float *tk_l) {
+  constexpr int EP = NCH * WAVE, CPW = EP / DEC_W, PP = WAVE / CPW, SPAN = EP / PP;
+  const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
+  const int c = CPW * wv + lane % CPW, part = lane / CPW;
+  const uint64_t mine = key[c];
+  const uint64_t *kp = key + SPAN * part;
+  uint32_t r = 0;
+#pragma unroll
+  for (int j = 0; j < SPAN; ++j) r += kp[j] > mine ? 1u : 0u;
+  if (PP == 4) r += (uint32_t)__float_as_int(xor16(__int_as_float((int)r)));
+  r += (uint32_t)__float_as_int(xor32(__int_as_float((int)r)));
+  if (part == 0 && mine != 0 && r < (uint32_t)k) {
+    tk_e[r] = c;
+    tk_l[r] = topk_ord_logit((uint32_t)(mine >> 32));
+  }
+}
+
+// The workgroup's expert and weight for routing slot `slot`, returned to every thread (and,
+// with publish, the top-k written out for the routed down workgroups and the caller).  The E
+// logits are fetched (tagged) into LDS; for E <= 128 the whole workgroup ranks them as above,
+// otherwise one wave runs the round-by-round selection in registers (on a SIMD that varies
+// with the block index) and hands the result to the others through LDS.
 QMOE_DEV void dec_topk(const DecodeArgs &a, unsigned ep, int slot, bool publish, int &e_out,
                        float &w_out, char *smem, const DecLds &L) {
   const int tid = threadIdx.x, wv = tid / WAVE, lane = tid % WAVE;
   const int E = a.E, k = a.k, nch = topk_chunks(E);
-  uint32_t *ord = (uint32_t *)(smem + L.tk);
   float *pes = (float *)(smem + L.pes);
+  int32_t *tk_e = (int32_t *)(smem + L.tks);
+  float *tk_w = (float *)(tk_e + MAX_TOPK);
   // per-expert scales into LDS (loads in flight while the logits are fetched)
   constexpr int PJ = MAX_EXPERTS / DEC_THREADS;
   float pv[PJ];
@@ -249,40 +276,65 @@ QMOE_DEV void dec_topk(const DecodeArgs &a, unsigned ep, int slot, bool publish,
     const int i = tid + j * DEC_THREADS;
     pv[j] = (i < E) ? a.pes[i] : 0.f;
   }
-  for (int i = E + tid; i < nch * WAVE; i += DEC_THREADS) ord[i] = 0u;
   const uint64_t *lg = a.logits + (size_t)(blockIdx.x % LOGIT_COPIES) * a.logit_copy;
-  fetch_tags<PJ>(a, E, ep, [&](int i) { return lg + i; },
-                 [&](int i, float v) { ord[i] = topk_ord(v); });
+  const bool by_rank = nch <= 2;
+  int my_e;
+  float my_l, my_w;
+  if (by_rank) {
+    uint64_t *key = (uint64_t *)(smem + L.tk);
+    for (int i = E + tid; i < nch * WAVE; i += DEC_THREADS) key[i] = 0u;
+    fetch_tags<PJ>(a, E, ep, [&](int i) { return lg + i; }, [&](int i, float v) {
+      key[i] = ((uint64_t)topk_ord(v) << 32) | (uint32_t)~i;
+    });
 #pragma unroll
-  for (int j = 0; j < PJ; ++j) {
-    const int i = tid + j * DEC_THREADS;
-    if (i < E) pes[i] = pv[j];
-  }
-  __syncthreads();
-  int32_t *tk_e = (int32_t *)(smem + L.tks);
-  float *tk_w = (float *)(tk_e + MAX_TOPK);
-  if (__builtin_amdgcn_readfirstlane(wv) == (int)(blockIdx.x % DEC_W)) {
-    int my_e;
-    float my_l;
-    topk_select(nch, [&](int c) { return c < nch ? ord[c * WAVE + lane] : 0u; }, k, my_e, my_l);
-    const float my_w = topk_weight(my_e, my_l, k, pes);
-    if (lane < k) {
-      tk_e[lane] = my_e;
-      tk_w[lane] = my_w;
-      if (publish) {
-        a.topk_idx[lane] = my_e;
-        a.topk_w[lane] = my_w;
-        // and for the routed down workgroups, which take their expert from these words
-        for (int c = 0; c < TK_COPIES; ++c) {
-          st_tag(a.tk + (size_t)c * 2 * MAX_TOPK + lane, ep, __int_as_float(my_e));
-          st_tag(a.tk + (size_t)c * 2 * MAX_TOPK + MAX_TOPK + lane, ep, my_w);
-        }
+    for (int j = 0; j < PJ; ++j) {
+      const int i = tid + j * DEC_THREADS;
+      if (i < E) pes[i] = pv[j];
+    }
+    __syncthreads();
+    if (nch <= 1) dec_rank_select<1>(key, k, tk_e, tk_w);
+    else dec_rank_select<2>(key, k, tk_e, tk_w);
+    __syncthreads();
+    my_e = lane < k ? tk_e[lane] : 0;
+    my_l = lane < k ? tk_w[lane] : 0.f;
+    my_w = topk_weight(my_e, my_l, k, pes);
+    e_out = min(max(tk_e[slot], 0), E - 1);
+    w_out = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w),
+                                                     __builtin_amdgcn_readfirstlane(slot)));
+    if (!publish || __builtin_amdgcn_readfirstlane(wv) != (int)(blockIdx.x % DEC_W)) return;
+  } else {
+    uint32_t *ord = (uint32_t *)(smem + L.tk);
+    for (int i = E + tid; i < nch * WAVE; i += DEC_THREADS) ord[i] = 0u;
+    fetch_tags<PJ>(a, E, ep, [&](int i) { return lg + i; },
+                   [&](int i, float v) { ord[i] = topk_ord(v); });
+#pragma unroll
+    for (int j = 0; j < PJ; ++j) {
+      const int i = tid + j * DEC_THREADS;
+      if (i < E) pes[i] = pv[j];
+    }
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(wv) == (int)(blockIdx.x % DEC_W)) {
+      topk_select(nch, [&](int c) { return c < nch ? ord[c * WAVE + lane] : 0u; }, k, my_e, my_l);
+      my_w = topk_weight(my_e, my_l, k, pes);
+      if (lane < k) {
+        tk_e[lane] = my_e;
+        tk_w[lane] = my_w;
       }
     }
+    __syncthreads();
+    e_out = min(max(tk_e[slot], 0), E - 1);
+    w_out = tk_w[slot];
+    if (!publish || __builtin_amdgcn_readfirstlane(wv) != (int)(blockIdx.x % DEC_W)) return;
   }
-  __syncthreads();
-  e_out = min(max(tk_e[slot], 0), E - 1);
-  w_out = tk_w[slot];
+  if (lane < k) {
+    a.topk_idx[lane] = my_e;
+    a.topk_w[lane] = my_w;
+    // and for the routed down workgroups, which take their expert from these words
+    for (int c = 0; c < TK_COPIES; ++c) {
+      st_tag(a.tk + (size_t)c * 2 * MAX_TOPK + lane, ep, __int_as_float(my_e));
+      st_tag(a.tk + (size_t)c * 2 * MAX_TOPK + MAX_TOPK + lane, ep, my_w);
+    }
+  }
 }
 
 // ---------------------------------------------------------------- gate/up of one tile, one token
