@@ -529,26 +529,10 @@ QMOE_DEV void dec_routed_down(const DecodeArgs &a, int b, unsigned ep, char *sme
     if (mine) st_tag(a.y_r + (size_t)slot * a.H + row0 + r, ep, yv);
     return;
   }
-  // last slot: combine the rows of this group
-  const int nsrc = a.k - 1 + (a.shared ? a.nc : 0);
-  float *comb = (float *)(smem + L.comb);
-  fetch_tags<4>(a, nsrc * nr, ep,
-                [&](int i) {
-                  const int s = i / nr, rw = i % nr;
-                  return (s < a.k - 1) ? a.y_r + (size_t)s * a.H + row0 + rw
-                                       : a.y_sh + (size_t)(s - (a.k - 1)) * a.H + row0 + rw;
-                },
-                [&](int i, float v) { comb[i] = v; });
-  float m = 0.f;  // routed rows (router-weighted) + shared row
-  if (mine) {
-    m = yv;
-    for (int s = 0; s < a.k - 1; ++s) m += comb[s * nr + r];
-    float sh = 0.f;
-    for (int s = a.k - 1; s < nsrc; ++s) sh += comb[s * nr + r];
-    m += sh;
-  }
-  // residual rows: from memory, or from the previous layer's tagged output (complete by now:
-  // this workgroup's inputs depend on all of it)
+  // last slot: combine the rows of this group.  The residual rows, the gain and the layer
+  // scalar are read first, so that their loads overlap the wait for the other slots' rows.
+  // Residual rows: from memory, or from the previous layer's tagged output (complete by now:
+  // this workgroup's h depends on all of it).
   float xr = 0.f;
   if (ST && a.xin) {
     uint32_t *xw = (uint32_t *)(smem + L.xw);
@@ -559,6 +543,33 @@ QMOE_DEV void dec_routed_down(const DecodeArgs &a, int b, unsigned ep, char *sme
   } else if (mine) {
     xr = bf16_to_f32(a.x[row0 + r]);
   }
+  const float gr = (a.gain && mine) ? a.gain[row0 + r] : 0.f;
+  const float lsc = a.lscale ? *a.lscale : 1.f;
+  const int nsrc = a.k - 1 + (a.shared ? a.nc : 0);
+  float *comb = (float *)(smem + L.comb);
+  fetch_tags<4>(a, nsrc * nr, ep,
+                [&](int i) {
+                  const int s = i / nr, rw = i % nr;
+                  return (s < a.k - 1) ? a.y_r + (size_t)s * a.H + row0 + rw
+                                       : a.y_sh + (size_t)(s - (a.k - 1)) * a.H + row0 + rw;
+                },
+                [&](int i, float v) { comb[i] = v; });
+  // Arrival of this combining workgroup, issued now and read at the end.  Once every
+  // combining workgroup has its inputs, every workgroup of the launch has published its part
+  // and so has read the epoch: the last to arrive may advance it.  (No drain first: the
+  // launch's outputs reach the next launch through the kernel boundary, not through the
+  // epoch.)
+  unsigned old = 0u;
+  if (a.advance && tid == 0)
+    old = __hip_atomic_fetch_add(a.lcnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  float m = 0.f;  // routed rows (router-weighted) + shared row
+  if (mine) {
+    m = yv;
+    for (int s = 0; s < a.k - 1; ++s) m += comb[s * nr + r];
+    float sh = 0.f;
+    for (int s = a.k - 1; s < nsrc; ++s) sh += comb[s * nr + r];
+    m += sh;
+  }
   float o = 0.f;
   if (a.gain) {
     // post-combine norm: every combining workgroup publishes the sum of m^2 over its rows,
@@ -567,7 +578,6 @@ QMOE_DEV void dec_routed_down(const DecodeArgs &a, int b, unsigned ep, char *sme
     // the combining workgroups are far fewer than the workgroups the device holds at once and
     // every other role finishes without waiting on them.
     float *nr_lds = (float *)(smem + L.nrm);  // [DEC_W] wave sums, then [groups] partials
-    const float gr = mine ? a.gain[row0 + r] : 0.f;
     const float ss = wave_sum(mine ? m * m : 0.f);
     if (tid % WAVE == 0) nr_lds[wv] = ss;
     __syncthreads();
@@ -585,7 +595,7 @@ QMOE_DEV void dec_routed_down(const DecodeArgs &a, int b, unsigned ep, char *sme
   } else {
     o = xr + m;
   }
-  if (a.lscale) o *= *a.lscale;
+  if (a.lscale) o *= lsc;
   const uint32_t ob = mine ? f32_to_bf16_bits(o) : 0u;
   if (mine) {
     a.out[row0 + r] = (uint16_t)ob;
@@ -598,8 +608,11 @@ QMOE_DEV void dec_routed_down(const DecodeArgs &a, int b, unsigned ep, char *sme
       for (int c = 0; c < X_COPIES; ++c)
         st_tag(a.xout + (size_t)c * a.x_copy + (row0 + r) / 2, ep, __uint_as_float(ob | (hi << 16)));
   }
-  // the last combining workgroup of the launch advances the epoch
-  if (a.advance && arrive_last(a.lcnt, (unsigned)groups) && tid == 0) st_sys_u(sy(a, SY_EPOCH), ep);
+  // the last combining workgroup of the launch to arrive advances the epoch
+  if (a.advance && tid == 0 && old == (unsigned)groups - 1u) {
+    __hip_atomic_store(a.lcnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    st_sys_u(sy(a, SY_EPOCH), ep);
+  }
 }
 
 // Block b (of one layer) with tag ep.
