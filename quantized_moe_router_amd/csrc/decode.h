@@ -468,9 +468,10 @@ QMOE_DEV void dec_shared_down(const DecodeArgs &a, int b, unsigned ep, char *sme
   const int wv = threadIdx.x / WAVE;
   const int n = kb1 - kb0;
   const int w0 = (n * wv) / DEC_W, w1 = (n * (wv + 1)) / DEC_W;
-  // once the last router workgroup has published (so that the router's loads go first),
-  // load the weights, then wait for h_shared
-  wait_tags(a, a.logits + (size_t)(blockIdx.x % LOGIT_COPIES) * a.logit_copy + (a.E - 1), 1, 1, ep);
+  // once the first router workgroup has published (so that the router's loads go first; the
+  // last one's word comes later and then leaves these loads to compete with the routed gate/up
+  // stream), load the weights, then wait for h_shared
+  wait_tags(a, a.logits + (size_t)(blockIdx.x % LOGIT_COPIES) * a.logit_copy, 1, 1, ep);
   DownRegs d;
   dec_down_load(a, a.shared, a.Is, tile, kb0 + w0, w1 - w0, d);
   dec_stage_h(a, a.h_sh + (size_t)(tile % H_COPIES) * a.hsh_copy + (size_t)g0 * GROUP,
