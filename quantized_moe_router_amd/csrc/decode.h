@@ -42,6 +42,7 @@
 #include "store.h"
 #include "router.h"
 #include "ffn.h"
+#include "mfma.h"
 
 namespace qmoe {
 
@@ -437,25 +438,77 @@ QMOE_DEV void dec_stage_h(const DecodeArgs &a, const uint64_t *src, int n, unsig
   __syncthreads();
 }
 
-// This wave's partial dot products for its 32 rows over its loaded k-steps; local k-step u
-// of the wave is k-step kb0 + u, whose activations are column block ((kb0 + u) >> kshift) -
-// g0 of the staged h (staged from group g0 on).  The 32 sums go to red[wave][row].
+// This wave's partial dot products for its 32 rows over its loaded k-steps, on the matrix
+// cores; local k-step u of the wave is k-step kb0 + u, whose activations are column block
+// ((kb0 + u) >> kshift) - g0 of the staged h (staged from group g0 on).  The A operand holds
+// the one token's h as two rows, the hi plane in row 0 and the lo plane in row 1 (the other
+// 14 rows zero); the B operand is the k-step's codes, re-laid by four lane swaps as in the
+// multi-token kernels (mfma.h).  Per k-step and 16-row block the products of the two column
+// halves are scaled by the row's scale, and (b - 128 s) times the group's sum of hi + lo is
+// added to row 0; rows 0 and 1 added give the 32 sums, which go to red[wave][row].
+QMOE_DEV void dec_down_step(const DownRegs &d, int u, int nk, int kb0, int g0, int kshift,
+                            const uint16_t *arow, const float *hs, bool zero_a,
+                            qmoe_f32x4 &acc0, qmoe_f32x4 &acc1) {
+  // steps past the wave's count re-read the last one and are scaled by 0
+  const bool valid = u < nk;
+  const int col = (((kb0 + min(u, nk - 1)) >> kshift) - g0) * GROUP;
+  qmoe_u32x4 xa0 = *(const qmoe_u32x4 *)(arow + col);
+  qmoe_u32x4 xa1 = *(const qmoe_u32x4 *)(arow + col + 32);
+  if (zero_a) {
+    xa0 = qmoe_u32x4{0u, 0u, 0u, 0u};
+    xa1 = qmoe_u32x4{0u, 0u, 0u, 0u};
+  }
+  const qmoe_u32x4 cv = d.cv[u];
+  const auto x02 = __builtin_amdgcn_permlane32_swap(cv.x, cv.z, false, false);
+  const auto x13 = __builtin_amdgcn_permlane32_swap(cv.y, cv.w, false, false);
+  const auto y01 = __builtin_amdgcn_permlane16_swap(x02[0], x13[0], false, false);
+  const auto y23 = __builtin_amdgcn_permlane16_swap(x02[1], x13[1], false, false);
+  qmoe_f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
+  t0 = mfma16(xa0, y01[0], t0);
+  t1 = mfma16(xa0, y01[1], t1);
+  t0 = mfma16(xa1, y23[0], t0);
+  t1 = mfma16(xa1, y23[1], t1);
+  // lane l < 16 holds rows 0, 1 of output column l: tile row l (block 0) and 16 + l
+  // (block 1), whose scale|bias word lane l + 16 loaded
+  const uint32_t sb0 = d.sb[u], sb1 = __float_as_uint(xor16(__uint_as_float(sb0)));
+  const float s0 = valid ? bf16lo(sb0) : 0.f, s1 = valid ? bf16lo(sb1) : 0.f;
+  const float c0 = valid ? fmaf(-128.f, bf16lo(sb0), bf16hi(sb0)) : 0.f;
+  const float c1 = valid ? fmaf(-128.f, bf16lo(sb1), bf16hi(sb1)) : 0.f;
+  const float g = hs[col / 32] + hs[col / 32 + 1];
+  acc0[0] = fmaf(s0, t0[0], acc0[0]);
+  acc0[1] = fmaf(s0, t0[1], acc0[1]);
+  acc1[0] = fmaf(s1, t1[0], acc1[0]);
+  acc1[1] = fmaf(s1, t1[1], acc1[1]);
+  acc0[0] = fmaf(c0, g, acc0[0]);
+  acc1[0] = fmaf(c1, g, acc1[0]);
+}
+
 QMOE_DEV void dec_down_dot(const DownRegs &d, int kb0, int g0, int kshift, char *smem,
                            const DecLds &L) {
   const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
-  const int rr = lane % 32, half = lane / 32;
+  const int m = lane % 16, kc = lane / 16;
   const uint16_t *hh = (const uint16_t *)(smem + L.hh), *hl = (const uint16_t *)(smem + L.hl);
+  const uint16_t *arow = (m == 1 ? hl : hh) + 8 * kc;   // rows >= 2 read row 0 and zero it
   const float *hs = (const float *)(smem + L.hs);
   float *red = (float *)(smem + L.red);
-  float acc = 0.f;
+  const int nk = __builtin_amdgcn_readfirstlane(d.nk);
+  qmoe_f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  if (nk > 0) {
+    // straight-line code for the first half of the batch (the usual count), so that the
+    // steps' products overlap; the second half only where a wave has more
 #pragma unroll
-  for (int u = 0; u < KB_DEC; ++u)
-    if (u < d.nk) {
-      const int col = (((kb0 + u) >> kshift) - g0) * GROUP + half * 32;
-      acc += kstep_hilo(d.cv[u], d.sb[u], hh + col, hl + col, hs[col / 32]);
+    for (int u = 0; u < KB_DEC / 2; ++u)
+      dec_down_step(d, u, nk, kb0, g0, kshift, arow, hs, m >= 2, acc0, acc1);
+    if (nk > KB_DEC / 2) {
+#pragma unroll
+      for (int u = KB_DEC / 2; u < KB_DEC; ++u)
+        dec_down_step(d, u, nk, kb0, g0, kshift, arow, hs, m >= 2, acc0, acc1);
     }
-  acc += xor32(acc);
-  if (half == 0) red[wv * 32 + rr] = acc;
+  }
+  if (lane < 16) {
+    red[wv * 32 + lane] = acc0[0] + acc0[1];
+    red[wv * 32 + 16 + lane] = acc1[0] + acc1[1];
+  }
 }
 
 // ---------------------------------------------------------------- roles
