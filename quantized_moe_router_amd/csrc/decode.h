@@ -257,76 +257,75 @@ QMOE_DEV void dec_rank_select(const uint64_t *key, int k, int32_t *tk_e, float *
   }
 }
 
-// The workgroup's expert and weight for routing slot `slot`, returned to every thread (and,
-// with publish, the top-k written out for the routed down workgroups and the caller).  The E
-// logits are fetched (tagged) into LDS; for E <= 128 the whole workgroup ranks them as above,
-// otherwise one wave runs the round-by-round selection in registers (on a SIMD that varies
-// with the block index) and hands the result to the others through LDS.
-QMOE_DEV void dec_topk(const DecodeArgs &a, unsigned ep, int slot, bool publish, int &e_out,
-                       float &w_out, char *smem, const DecLds &L) {
+// The workgroup's expert for routing slot `slot`, returned to every thread (its routing
+// weight is applied by the routed down workgroups); with publish, the top-k ids and weights
+// are also written out for the routed down workgroups and the caller.  The E logits are
+// fetched (tagged) into LDS; for E <= 128 the whole workgroup ranks them as above, otherwise
+// one wave runs the round-by-round selection in registers (on a SIMD that varies with the
+// block index) and hands the result to the others through LDS.
+QMOE_DEV int dec_topk(const DecodeArgs &a, unsigned ep, int slot, bool publish, char *smem,
+                      const DecLds &L) {
   const int tid = threadIdx.x, wv = tid / WAVE, lane = tid % WAVE;
   const int E = a.E, k = a.k, nch = topk_chunks(E);
   float *pes = (float *)(smem + L.pes);
   int32_t *tk_e = (int32_t *)(smem + L.tks);
-  float *tk_w = (float *)(tk_e + MAX_TOPK);
-  // per-expert scales into LDS (loads in flight while the logits are fetched)
+  float *tk_l = (float *)(tk_e + MAX_TOPK);
+  const bool chosen = __builtin_amdgcn_readfirstlane(wv) == (int)(blockIdx.x % DEC_W);
+  // per-expert scales into LDS (loads in flight while the logits are fetched; only the
+  // publishing workgroup forms weights)
   constexpr int PJ = MAX_EXPERTS / DEC_THREADS;
   float pv[PJ];
 #pragma unroll
   for (int j = 0; j < PJ; ++j) {
     const int i = tid + j * DEC_THREADS;
-    pv[j] = (i < E) ? a.pes[i] : 0.f;
+    pv[j] = (publish && i < E) ? a.pes[i] : 0.f;
   }
   const uint64_t *lg = a.logits + (size_t)(blockIdx.x % LOGIT_COPIES) * a.logit_copy;
-  const bool by_rank = nch <= 2;
-  int my_e;
-  float my_l, my_w;
-  if (by_rank) {
+  int my_e = 0;
+  float my_l = 0.f;
+  if (nch <= 2) {
     uint64_t *key = (uint64_t *)(smem + L.tk);
     for (int i = E + tid; i < nch * WAVE; i += DEC_THREADS) key[i] = 0u;
     fetch_tags<PJ>(a, E, ep, [&](int i) { return lg + i; }, [&](int i, float v) {
       key[i] = ((uint64_t)topk_ord(v) << 32) | (uint32_t)~i;
     });
+    if (publish) {
 #pragma unroll
-    for (int j = 0; j < PJ; ++j) {
-      const int i = tid + j * DEC_THREADS;
-      if (i < E) pes[i] = pv[j];
+      for (int j = 0; j < PJ; ++j) {
+        const int i = tid + j * DEC_THREADS;
+        if (i < E) pes[i] = pv[j];
+      }
     }
     __syncthreads();
-    if (nch <= 1) dec_rank_select<1>(key, k, tk_e, tk_w);
-    else dec_rank_select<2>(key, k, tk_e, tk_w);
+    if (nch <= 1) dec_rank_select<1>(key, k, tk_e, tk_l);
+    else dec_rank_select<2>(key, k, tk_e, tk_l);
     __syncthreads();
+    const int e_out = min(max(tk_e[slot], 0), E - 1);
+    if (!publish || !chosen) return e_out;
     my_e = lane < k ? tk_e[lane] : 0;
-    my_l = lane < k ? tk_w[lane] : 0.f;
-    my_w = topk_weight(my_e, my_l, k, pes);
-    e_out = min(max(tk_e[slot], 0), E - 1);
-    w_out = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w),
-                                                     __builtin_amdgcn_readfirstlane(slot)));
-    if (!publish || __builtin_amdgcn_readfirstlane(wv) != (int)(blockIdx.x % DEC_W)) return;
+    my_l = lane < k ? tk_l[lane] : 0.f;
   } else {
     uint32_t *ord = (uint32_t *)(smem + L.tk);
     for (int i = E + tid; i < nch * WAVE; i += DEC_THREADS) ord[i] = 0u;
     fetch_tags<PJ>(a, E, ep, [&](int i) { return lg + i; },
                    [&](int i, float v) { ord[i] = topk_ord(v); });
+    if (publish) {
 #pragma unroll
-    for (int j = 0; j < PJ; ++j) {
-      const int i = tid + j * DEC_THREADS;
-      if (i < E) pes[i] = pv[j];
-    }
-    __syncthreads();
-    if (__builtin_amdgcn_readfirstlane(wv) == (int)(blockIdx.x % DEC_W)) {
-      topk_select(nch, [&](int c) { return c < nch ? ord[c * WAVE + lane] : 0u; }, k, my_e, my_l);
-      my_w = topk_weight(my_e, my_l, k, pes);
-      if (lane < k) {
-        tk_e[lane] = my_e;
-        tk_w[lane] = my_w;
+      for (int j = 0; j < PJ; ++j) {
+        const int i = tid + j * DEC_THREADS;
+        if (i < E) pes[i] = pv[j];
       }
     }
     __syncthreads();
-    e_out = min(max(tk_e[slot], 0), E - 1);
-    w_out = tk_w[slot];
-    if (!publish || __builtin_amdgcn_readfirstlane(wv) != (int)(blockIdx.x % DEC_W)) return;
+    if (chosen) {
+      topk_select(nch, [&](int c) { return c < nch ? ord[c * WAVE + lane] : 0u; }, k, my_e, my_l);
+      if (lane < k) tk_e[lane] = my_e;
+    }
+    __syncthreads();
+    const int e_out = min(max(tk_e[slot], 0), E - 1);
+    if (!publish || !chosen) return e_out;
   }
+  const float my_w = topk_weight(my_e, my_l, k, pes);
   if (lane < k) {
     a.topk_idx[lane] = my_e;
     a.topk_w[lane] = my_w;
@@ -336,6 +335,7 @@ QMOE_DEV void dec_topk(const DecodeArgs &a, unsigned ep, int slot, bool publish,
       st_tag(a.tk + (size_t)c * 2 * MAX_TOPK + MAX_TOPK + lane, ep, my_w);
     }
   }
+  return min(max(tk_e[slot], 0), E - 1);
 }
 
 // ---------------------------------------------------------------- gate/up of one tile, one token
@@ -351,6 +351,57 @@ QMOE_DEV void dec_stage_x(const DecodeArgs &a, unsigned ep, char *smem, const De
   }
 }
 
+// ---------------------------------------------------------------- k-steps on the matrix cores
+// A wave's batch of loaded k-steps (codes and scale|bias words, load_batch layout).
+struct DownRegs {
+  qmoe_u32x4 cv[KB_DEC];
+  uint32_t sb[KB_DEC];
+  int nk;
+};
+
+// One k-step (u of the wave's batch d, k-step kb0 + u, activations at column block
+// ((kb0 + u) >> kshift) - g0) of a 32-row tile on the matrix cores.  A operand: lane l gives
+// row l % 16, columns 8 (l / 16) + [0, 8) of each column half, from arow (zero where zero_a);
+// B operand: the k-step's codes after four lane swaps (mfma.h).  Row 0 receives the bias
+// term (b - 128 s) times the group sum of the A rows (hs: 32-column sums).  acc0 / acc1:
+// tile rows 0..15 / 16..31, lane l < 16 holding A rows 0 and 1 of tile row l (+ 16).
+QMOE_DEV void dec_kstep_mf(const DownRegs &d, int u, int nk, int kb0, int g0, int kshift,
+                            const uint16_t *arow, const float *hs, bool zero_a,
+                            qmoe_f32x4 &acc0, qmoe_f32x4 &acc1) {
+  // steps past the wave's count re-read the last one and are scaled by 0
+  const bool valid = u < nk;
+  const int col = (((kb0 + min(u, nk - 1)) >> kshift) - g0) * GROUP;
+  qmoe_u32x4 xa0 = *(const qmoe_u32x4 *)(arow + col);
+  qmoe_u32x4 xa1 = *(const qmoe_u32x4 *)(arow + col + 32);
+  if (zero_a) {
+    xa0 = qmoe_u32x4{0u, 0u, 0u, 0u};
+    xa1 = qmoe_u32x4{0u, 0u, 0u, 0u};
+  }
+  const qmoe_u32x4 cv = d.cv[u];
+  const auto x02 = __builtin_amdgcn_permlane32_swap(cv.x, cv.z, false, false);
+  const auto x13 = __builtin_amdgcn_permlane32_swap(cv.y, cv.w, false, false);
+  const auto y01 = __builtin_amdgcn_permlane16_swap(x02[0], x13[0], false, false);
+  const auto y23 = __builtin_amdgcn_permlane16_swap(x02[1], x13[1], false, false);
+  qmoe_f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
+  t0 = mfma16(xa0, y01[0], t0);
+  t1 = mfma16(xa0, y01[1], t1);
+  t0 = mfma16(xa1, y23[0], t0);
+  t1 = mfma16(xa1, y23[1], t1);
+  // lane l < 16 holds rows 0, 1 of output column l: tile row l (block 0) and 16 + l
+  // (block 1), whose scale|bias word lane l + 16 loaded
+  const uint32_t sb0 = d.sb[u], sb1 = __float_as_uint(xor16(__uint_as_float(sb0)));
+  const float s0 = valid ? bf16lo(sb0) : 0.f, s1 = valid ? bf16lo(sb1) : 0.f;
+  const float c0 = valid ? fmaf(-128.f, bf16lo(sb0), bf16hi(sb0)) : 0.f;
+  const float c1 = valid ? fmaf(-128.f, bf16lo(sb1), bf16hi(sb1)) : 0.f;
+  const float g = hs[col / 32] + hs[col / 32 + 1];
+  acc0[0] = fmaf(s0, t0[0], acc0[0]);
+  acc0[1] = fmaf(s0, t0[1], acc0[1]);
+  acc1[0] = fmaf(s1, t1[0], acc1[0]);
+  acc1[1] = fmaf(s1, t1[1], acc1[1]);
+  acc0[0] = fmaf(c0, g, acc0[0]);
+  acc1[0] = fmaf(c1, g, acc1[0]);
+}
+
 // 16 gate + 16 up rows of store tile `tile` of block `blk` against the staged x (split-K over
 // the four waves); the 16 values silu(g)*u are published (tagged) at h_out[16*tile + r] of
 // each of the H_COPIES copies.
@@ -364,16 +415,23 @@ QMOE_DEV void dec_gate_up(const DecodeArgs &a, const uint8_t *blk, int tile, uin
   float *red = (float *)(smem + L.red);
   const uint8_t *tbase = blk + (size_t)tile * KS * KSTEP_BYTES;
   const int ks0 = (KS * wv) / DEC_W, nk = (KS * (wv + 1)) / DEC_W - ks0;
+  // each batch's k-steps in straight-line chunks of four (steps past the count re-read the
+  // last one and add 0), so that their products overlap
   float acc = 0.f;
   for (int kc = 0; kc < nk; kc += KB_DEC) {
     qmoe_u32x4 cv[KB_DEC];
     uint32_t sb[KB_DEC];
     load_batch<KB_DEC>(tbase, ks0, kc, nk, lane, rr, cv, sb);
+    const int nb = __builtin_amdgcn_readfirstlane(min(KB_DEC, nk - kc));
 #pragma unroll
-    for (int u = 0; u < KB_DEC; ++u)
-      if (kc + u < nk) {
-        const int col = ((ks0 + kc + u) >> a.kshift) * GROUP + half * 32;
-        acc += kstep_bf16(cv[u], sb[u], xl + col, xs[col / 32]);
+    for (int c = 0; c < KB_DEC; c += 4)
+      if (c < nb) {
+#pragma unroll
+        for (int u = c; u < c + 4; ++u) {
+          const int col = ((ks0 + kc + min(u, nb - 1)) >> a.kshift) * GROUP + half * 32;
+          const float r = kstep_bf16(cv[u], sb[u], xl + col, xs[col / 32]);
+          acc += u < nb ? r : 0.f;
+        }
       }
   }
   acc += xor32(acc);
@@ -386,13 +444,6 @@ QMOE_DEV void dec_gate_up(const DecodeArgs &a, const uint8_t *blk, int tile, uin
     st_tag(h_out + (size_t)c * copy_stride + 16 * tile + r, ep, silu(g) * u);
   }
 }
-
-// ---------------------------------------------------------------- down projection pieces
-struct DownRegs {
-  qmoe_u32x4 cv[KB_DEC];
-  uint32_t sb[KB_DEC];
-  int nk;
-};
 
 // This wave's k-steps [kb0, kb0 + nk) (nk <= KB_DEC) of output tile `tile` of the down
 // section of block `blk` (input width K).
@@ -446,43 +497,6 @@ QMOE_DEV void dec_stage_h(const DecodeArgs &a, const uint64_t *src, int n, unsig
 // multi-token kernels (mfma.h).  Per k-step and 16-row block the products of the two column
 // halves are scaled by the row's scale, and (b - 128 s) times the group's sum of hi + lo is
 // added to row 0; rows 0 and 1 added give the 32 sums, which go to red[wave][row].
-QMOE_DEV void dec_down_step(const DownRegs &d, int u, int nk, int kb0, int g0, int kshift,
-                            const uint16_t *arow, const float *hs, bool zero_a,
-                            qmoe_f32x4 &acc0, qmoe_f32x4 &acc1) {
-  // steps past the wave's count re-read the last one and are scaled by 0
-  const bool valid = u < nk;
-  const int col = (((kb0 + min(u, nk - 1)) >> kshift) - g0) * GROUP;
-  qmoe_u32x4 xa0 = *(const qmoe_u32x4 *)(arow + col);
-  qmoe_u32x4 xa1 = *(const qmoe_u32x4 *)(arow + col + 32);
-  if (zero_a) {
-    xa0 = qmoe_u32x4{0u, 0u, 0u, 0u};
-    xa1 = qmoe_u32x4{0u, 0u, 0u, 0u};
-  }
-  const qmoe_u32x4 cv = d.cv[u];
-  const auto x02 = __builtin_amdgcn_permlane32_swap(cv.x, cv.z, false, false);
-  const auto x13 = __builtin_amdgcn_permlane32_swap(cv.y, cv.w, false, false);
-  const auto y01 = __builtin_amdgcn_permlane16_swap(x02[0], x13[0], false, false);
-  const auto y23 = __builtin_amdgcn_permlane16_swap(x02[1], x13[1], false, false);
-  qmoe_f32x4 t0 = {0.f, 0.f, 0.f, 0.f}, t1 = {0.f, 0.f, 0.f, 0.f};
-  t0 = mfma16(xa0, y01[0], t0);
-  t1 = mfma16(xa0, y01[1], t1);
-  t0 = mfma16(xa1, y23[0], t0);
-  t1 = mfma16(xa1, y23[1], t1);
-  // lane l < 16 holds rows 0, 1 of output column l: tile row l (block 0) and 16 + l
-  // (block 1), whose scale|bias word lane l + 16 loaded
-  const uint32_t sb0 = d.sb[u], sb1 = __float_as_uint(xor16(__uint_as_float(sb0)));
-  const float s0 = valid ? bf16lo(sb0) : 0.f, s1 = valid ? bf16lo(sb1) : 0.f;
-  const float c0 = valid ? fmaf(-128.f, bf16lo(sb0), bf16hi(sb0)) : 0.f;
-  const float c1 = valid ? fmaf(-128.f, bf16lo(sb1), bf16hi(sb1)) : 0.f;
-  const float g = hs[col / 32] + hs[col / 32 + 1];
-  acc0[0] = fmaf(s0, t0[0], acc0[0]);
-  acc0[1] = fmaf(s0, t0[1], acc0[1]);
-  acc1[0] = fmaf(s1, t1[0], acc1[0]);
-  acc1[1] = fmaf(s1, t1[1], acc1[1]);
-  acc0[0] = fmaf(c0, g, acc0[0]);
-  acc1[0] = fmaf(c1, g, acc1[0]);
-}
-
 QMOE_DEV void dec_down_dot(const DownRegs &d, int kb0, int g0, int kshift, char *smem,
                            const DecLds &L) {
   const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
@@ -498,11 +512,11 @@ QMOE_DEV void dec_down_dot(const DownRegs &d, int kb0, int g0, int kshift, char 
     // steps' products overlap; the second half only where a wave has more
 #pragma unroll
     for (int u = 0; u < KB_DEC / 2; ++u)
-      dec_down_step(d, u, nk, kb0, g0, kshift, arow, hs, m >= 2, acc0, acc1);
+      dec_kstep_mf(d, u, nk, kb0, g0, kshift, arow, hs, m >= 2, acc0, acc1);
     if (nk > KB_DEC / 2) {
 #pragma unroll
       for (int u = KB_DEC / 2; u < KB_DEC; ++u)
-        dec_down_step(d, u, nk, kb0, g0, kshift, arow, hs, m >= 2, acc0, acc1);
+        dec_kstep_mf(d, u, nk, kb0, g0, kshift, arow, hs, m >= 2, acc0, acc1);
     }
   }
   if (lane < 16) {
@@ -687,9 +701,7 @@ QMOE_DEV void decode_block(const DecodeArgs &a, int b, unsigned ep, char *smem) 
     const int tiles_r = a.I / 16;
     const int slot = b / tiles_r, tile = b % tiles_r;
     dec_stage_x<ST>(a, ep, smem, L);
-    int e;
-    float w;
-    dec_topk(a, ep, slot, b == 0, e, w, smem, L);
+    const int e = dec_topk(a, ep, slot, b == 0, smem, L);
     dec_gate_up(a, a.experts + (size_t)e * a.stride, tile, a.h_r + (size_t)slot * a.I, a.hr_copy, ep,
                 smem, L);
     return;
