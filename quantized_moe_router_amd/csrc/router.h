@@ -418,7 +418,6 @@ QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *sme
   load_rs(0);
   xwait();
   float *z = (float *)smem;                                  // [nt][H]
-  float *fac = z + nt * H;                                   // [TB]
   __shared__ float red[ROUTER_WAVES][TB];
   float ss[TB];
 #pragma unroll
@@ -459,13 +458,15 @@ QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *sme
     if (lane == 0) red[wv][i] = ss[i];
   }
   __syncthreads();
-  if (tid < nt) {
-    float tot = 0.f;
-    for (int w = 0; w < ROUTER_WAVES; ++w) tot += red[w][tid];
-    fac[tid] = a.inv_sqrt_h / sqrtf(tot / (float)H + RMS_EPS);
-  }
-  __syncthreads();
   if (e_first >= a.E) return;
+  // every wave forms the norm factors itself (same sums in the same order)
+  float facv[TB];
+#pragma unroll
+  for (int i = 0; i < TB; ++i) {
+    float tot = 0.f;
+    for (int w = 0; w < ROUTER_WAVES; ++w) tot += red[w][min(i, nt - 1)];
+    facv[i] = a.inv_sqrt_h / sqrtf(tot / (float)H + RMS_EPS);
+  }
   float acc[EPW][TB];
 #pragma unroll
   for (int x = 0; x < EPW; ++x)
@@ -509,7 +510,7 @@ QMOE_DEV void router_logits_block(const RouterArgs &a, int tb, int eb, char *sme
     for (int i = 0; i < TB; ++i) {
       if (i < nt) {
         const float tot = wave_sum(acc[x][i]);
-        float l = fac[i] * tot;
+        float l = facv[i] * tot;
         if (a.lbias) l += lb[x];
         const size_t o = (size_t)(t0 + i) * a.E + e;
         if (e < a.E) {
