@@ -88,17 +88,6 @@ QMOE_DEV float dpp(float v) {
 QMOE_DEV float xor1(float v) { return dpp<0xB1>(v); }   // quad_perm [1, 0, 3, 2]
 QMOE_DEV float xor2(float v) { return dpp<0x4E>(v); }   // quad_perm [2, 3, 0, 1]
 
-// Sum over the 16 lanes of each row, as the xor butterfly 1, 2, 4, 8 adds them: after the
-// quad steps the value is the same in the four lanes of a quad, so the half-row mirror gives
-// the xor-4 partner's value, and after that the row mirror the xor-8 partner's.
-QMOE_DEV float row_sum16(float v) {
-  v += xor1(v);
-  v += xor2(v);
-  v += dpp<0x141>(v);   // row_half_mirror
-  v += dpp<0x140>(v);   // row_mirror
-  return v;
-}
-
 // Sum over the wave, as the xor butterfly 32, 16, 8, 4, 2, 1 adds them (the same bits in
 // every lane): after the xor-32 and xor-16 steps the value repeats every 16 lanes, so the
 // rotation of a row by 8 gives the xor-8 partner's value, and so on down to 1.

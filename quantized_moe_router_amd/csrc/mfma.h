@@ -208,8 +208,9 @@ __global__ void __launch_bounds__(GU_WAVES * WAVE) gu_pf_kernel(FfnArgs a) {
       }
     }
     // group sums: over the 16 lanes of each lane group, then over the waves (LDS permutes
-    // here: the register form of row_sum16 raised this kernel from 113 to 131 VGPRs, one wave
-    // per SIMD less, and this runs once per row block, outside the k-step loop)
+    // here: a register form, quad DPP then the half-row and row mirrors, raised this kernel
+    // from 113 to 131 VGPRs, one wave per SIMD less, and this runs once per row block,
+    // outside the k-step loop)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       hs[i] += __shfl_xor(hs[i], 1, WAVE);
