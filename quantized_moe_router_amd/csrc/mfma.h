@@ -144,6 +144,23 @@ QMOE_DEV void pf_tiles(qmoe_f32x4 (&acc)[NT][2], const uint8_t *const (&tb)[NT],
   if (k0 < nks) pf_batch<NP, NT, KB, true>(acc, tb, k0, nks, ap, grow, gmask, kshift);
 }
 
+// Workgroups (g < ng, b < nb) that share data per g: the shared expert's (weight group, token
+// block) in both kernels below, whose token blocks re-read the group's weights, and the routed
+// down's (slot, output tile group), whose tile groups re-read the slot's h rows.  Workgroups
+// are dispatched round-robin over the 8 XCDs, each with its own L2, so the nb workgroups of
+// one g get the block indices j = 8 (nb (g / 8) + b) + g % 8, which share one residue mod 8
+// (one XCD, whose L2 then serves the re-reads) -- a bijection onto [0, pf_xcd_blocks) once ng
+// is padded to a multiple of 8 (padding workgroups do nothing).
+constexpr int PF_XCDS = 8;
+inline __host__ __device__ int pf_xcd_blocks(int ng, int nb) {
+  return (ng + PF_XCDS - 1) / PF_XCDS * PF_XCDS * nb;
+}
+QMOE_DEV void pf_xcd_block(int j, int nb, int &g, int &b) {
+  const int q = j / PF_XCDS;
+  g = j % PF_XCDS + PF_XCDS * (q / nb);
+  b = q % nb;
+}
+
 // ---------------------------------------------------------------- gate/up + SwiGLU
 // grid: shared workgroups first (h group, block of PF_MT tokens), then routed (slot, h
 // group); a workgroup of GU_WAVES waves owns the four tiles of one 64-column group of h, wave
@@ -156,15 +173,17 @@ __global__ void __launch_bounds__(GU_WAVES * WAVE) gu_pf_kernel(FfnArgs a) {
   __shared__ float gpart[GU_WAVES][PF_MT];
   const int H = a.H, KG = H / GROUP, KS = KG << a.kshift;
   const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE, n = lane % 16, lg = lane / 16;
-  const int grp_s = a.shared ? a.Is / GROUP : 0;
-  const int n_sh = grp_s * ((a.T + PF_MT - 1) / PF_MT);
+  const int grp_s = a.shared ? a.Is / GROUP : 0, ntb = (a.T + PF_MT - 1) / PF_MT;
+  const int n_sh = grp_s ? pf_xcd_blocks(grp_s, ntb) : 0;
   int bid = blockIdx.x;
   SlotRows sr;
   int grp, m0, m1;
   if (bid < n_sh) {
+    int tb;
+    pf_xcd_block(bid, ntb, grp, tb);
+    if (grp >= grp_s) return;
     slot_rows(a, 0, true, sr);
-    grp = bid % grp_s;
-    m0 = (bid / grp_s) * PF_MT;
+    m0 = tb * PF_MT;
     m1 = min(a.T, m0 + PF_MT);
   } else {
     bid -= n_sh;
@@ -243,19 +262,22 @@ __global__ void __launch_bounds__(GU_WAVES * WAVE) gu_pf_kernel(FfnArgs a) {
 __global__ void __launch_bounds__(D_WAVES * WAVE) d_pf_kernel(FfnArgs a) {
   const int H = a.H, tiles = H / TILE_ROWS, tgroups = (tiles + D_WAVES * D_NT - 1) / (D_WAVES * D_NT);
   const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE, n = lane % 16, lg = lane / 16;
-  const int n_sh = a.shared ? tgroups * ((a.T + PF_MT - 1) / PF_MT) : 0;
+  const int ntb = (a.T + PF_MT - 1) / PF_MT;
+  const int n_sh = a.shared ? pf_xcd_blocks(tgroups, ntb) : 0;
   int bid = blockIdx.x;
   SlotRows sr;
   int tg, m0, m1;
   if (bid < n_sh) {
+    int tb;
+    pf_xcd_block(bid, ntb, tg, tb);
+    if (tg >= tgroups) return;
     slot_rows(a, 0, true, sr);
-    tg = bid % tgroups;
-    m0 = (bid / tgroups) * PF_MT;
+    m0 = tb * PF_MT;
     m1 = min(a.T, m0 + PF_MT);
   } else {
-    bid -= n_sh;
-    if (!slot_rows(a, bid / tgroups, false, sr)) return;
-    tg = bid % tgroups;
+    int slot;
+    pf_xcd_block(bid - n_sh, tgroups, slot, tg);
+    if (slot >= a.n_slots || !slot_rows(a, slot, false, sr)) return;
     m0 = 0;
     m1 = sr.m;
   }

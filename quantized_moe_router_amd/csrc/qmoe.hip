@@ -380,8 +380,8 @@ static int launch_d(FfnArgs a, bool with_shared, hipStream_t s) {
 // bracket the gate/up kernel.
 static int launch_pf(const FfnArgs &a, hipStream_t s) {
   int rc;
-  const int n_gu = (a.shared ? (a.Is / GROUP) * ((a.T + PF_MT - 1) / PF_MT) : 0) +
-                   a.n_slots * (a.I / GROUP);
+  const int ntb = (a.T + PF_MT - 1) / PF_MT;
+  const int n_gu = (a.shared ? pf_xcd_blocks(a.Is / GROUP, ntb) : 0) + a.n_slots * (a.I / GROUP);
   if (g_prof_start && (rc = record_event(g_prof_start, s))) return rc;
   if (n_gu > 0) {
     hipLaunchKernelGGL(gu_pf_kernel, dim3(n_gu), dim3(GU_WAVES * WAVE), 0, s, a);
@@ -389,7 +389,7 @@ static int launch_pf(const FfnArgs &a, hipStream_t s) {
   }
   if (g_prof_stop && (rc = record_event(g_prof_stop, s))) return rc;
   const int tgroups = (a.H / TILE_ROWS + D_WAVES * D_NT - 1) / (D_WAVES * D_NT);
-  const int n_d = (a.shared ? tgroups * ((a.T + PF_MT - 1) / PF_MT) : 0) + a.n_slots * tgroups;
+  const int n_d = (a.shared ? pf_xcd_blocks(tgroups, ntb) : 0) + pf_xcd_blocks(a.n_slots, tgroups);
   if (n_d > 0) {
     hipLaunchKernelGGL(d_pf_kernel, dim3(n_d), dim3(D_WAVES * WAVE), 0, s, a);
     QMOE_LAUNCHED();
