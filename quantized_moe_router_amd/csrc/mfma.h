@@ -345,19 +345,20 @@ __global__ void __launch_bounds__(256) gsum_kernel(const uint16_t *x, int n_grou
 
 // sum_j w[j] y[j * H + off .. + 4) over j = 0..k-1 in ascending order (fp32 FMAs); the loads of
 // eight rows are in flight together (a loop of dependent round trips otherwise)
-QMOE_DEV float4 routed_sum4(const float *y, const float *w, int k, int H, size_t off) {
+template <int B>
+QMOE_DEV float4 routed_sum_b(const float *y, const float *w, int k, int H, size_t off) {
   float4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int j0 = 0; j0 < k; j0 += 8) {
-    float4 v[8];
-    float wj[8];
+  for (int j0 = 0; j0 < k; j0 += B) {
+    float4 v[B];
+    float wj[B];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
+    for (int q = 0; q < B; ++q) {
       const int j = min(j0 + q, k - 1);   // rows past k re-read the last one (not used)
       wj[q] = w[j];
       v[q] = *(const float4 *)(y + (size_t)j * H + off);
     }
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
+    for (int q = 0; q < B; ++q)
       if (j0 + q < k) {
         acc.x = fmaf(wj[q], v[q].x, acc.x);
         acc.y = fmaf(wj[q], v[q].y, acc.y);
@@ -366,6 +367,10 @@ QMOE_DEV float4 routed_sum4(const float *y, const float *w, int k, int H, size_t
       }
   }
   return acc;
+}
+// (up to 16 rows' loads in one batch, so that k <= 16 takes one round trip)
+QMOE_DEV float4 routed_sum4(const float *y, const float *w, int k, int H, size_t off) {
+  return k <= 8 ? routed_sum_b<8>(y, w, k, H, off) : routed_sum_b<16>(y, w, k, H, off);
 }
 
 // out[t, :] = bf16( x[t, :] + sum_j w[t,j] y[t*k+j, :] + y_sh[t, :] ) in fp32, j ascending,
@@ -379,12 +384,13 @@ __global__ void __launch_bounds__(256) combine_pf_kernel(const uint16_t *x, cons
   for (size_t o = (size_t)blockIdx.x * blockDim.x + threadIdx.x; o < n4;
        o += (size_t)gridDim.x * blockDim.x) {
     const size_t t = (o * 4) / H, col = (o * 4) % H;
+    // the shared row and the residual loaded first, in flight with the routed rows
+    const float4 vs = y_sh ? *(const float4 *)(y_sh + t * H + col) : float4{0.f, 0.f, 0.f, 0.f};
+    const uint2 xb = *(const uint2 *)(x + t * H + col);
     float4 acc = routed_sum4(y + t * k * H, w + t * k, k, H, col);
     if (y_sh) {
-      const float4 v = *(const float4 *)(y_sh + t * H + col);
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      acc.x += vs.x; acc.y += vs.y; acc.z += vs.z; acc.w += vs.w;
     }
-    const uint2 xb = *(const uint2 *)(x + t * H + col);
     acc.x += bf16lo(xb.x); acc.y += bf16hi(xb.x); acc.z += bf16lo(xb.y); acc.w += bf16hi(xb.y);
     const uint2 ob = {f32_to_bf16_bits(acc.x) | (f32_to_bf16_bits(acc.y) << 16),
                       f32_to_bf16_bits(acc.z) | (f32_to_bf16_bits(acc.w) << 16)};
