@@ -139,37 +139,39 @@ def test_router_zero_input():
     assert np.allclose(w.cpu().numpy(), np.tile(li.pes[:2] / 2, (3, 1)), rtol=1e-6)
 
 
+@pytest.mark.parametrize("T", [1, 3])
 @pytest.mark.parametrize("name", ["tiny", "gemma4_26b_a4b_decode", "qwen3_next_80b_a3b_decode_b1"])
-def test_one_token_exact_ties_take_the_lower_ids(name):
-    """The one-token layer's selection (by rank for up to 128 experts, round by round above)
-    on logits with exact ties: zero input makes every logit its bias (or 0), and a bias drawn
-    from three values puts equal logits on both sides of the k-th place.  The ids must be the
-    oracle's (larger logit first, the lower index first among equal ones) and the weights its
-    softmax times per_expert_scale."""
+def test_exact_ties_take_the_lower_ids(name, T):
+    """The selection on logits with exact ties, in the one-token layer (T = 1: by rank for up to
+    128 experts, round by round above) and in the router kernel of calls of several tokens
+    (T = 3): zero input makes every logit its bias (or 0), and a bias drawn from three values
+    puts equal logits on both sides of the k-th place.  The ids must be the oracle's (larger
+    logit first, the lower index first among equal ones) and the weights its softmax times
+    per_expert_scale."""
     ops = _ops()
     cfg = G.config(name)
     pl, li = layer(name)
     E, k, H = cfg.experts, cfg.top_k, cfg.hidden
     codes, scales, biases, pes, rscale, _ = pl.router.tensors
     bias = (np.random.default_rng(7).integers(0, 3, size=E) * 0.25).astype(np.float32)
-    ws = ops.workspace(pl.dims, 1)
-    x = torch.zeros(1, H, dtype=torch.int16, device=DEV)
+    ws = ops.workspace(pl.dims, T)
+    x = torch.zeros(T, H, dtype=torch.int16, device=DEV)
     for lb in (None, bias):
         router = ops.RouterWeights(codes, scales, biases, pes, rscale,
                                    None if lb is None else torch.from_numpy(lb).to(DEV))
         lw = ops.LayerWeights(pl.dims, router, pl.store, pl.stride, pl.shared)
-        idx = torch.empty(1, k, dtype=torch.int32, device=DEV)
-        w = torch.empty(1, k, dtype=torch.float32, device=DEV)
+        idx = torch.empty(T, k, dtype=torch.int32, device=DEV)
+        w = torch.empty(T, k, dtype=torch.float32, device=DEV)
         ops.layer_forward(lw, x, ws, topk_idx=idx, topk_w=w)
         torch.cuda.synchronize()
-        logits = np.zeros((1, E)) if lb is None else lb.astype(np.float64)[None, :]
+        logits = np.zeros((T, E)) if lb is None else np.tile(lb.astype(np.float64), (T, 1))
         top = O.topk_select(logits, k)
         if lb is not None:      # the case really has ties across the k-th place
             kth = logits[0, top[0, -1]]
             assert (logits[0] == kth).sum() > (logits[0, top[0]] == kth).sum()
-        assert idx.cpu().numpy().tolist() == top.tolist(), f"{name} bias={lb is not None}"
+        assert idx.cpu().numpy().tolist() == top.tolist(), f"{name} T={T} bias={lb is not None}"
         want = O.topk_weights(logits, top, li.pes)
-        assert np.allclose(w.cpu().numpy(), want, rtol=1e-5, atol=0), f"{name} weights"
+        assert np.allclose(w.cpu().numpy(), want, rtol=1e-5, atol=0), f"{name} T={T} weights"
     assert ops.workspace_status(ws) == 0
 
 
