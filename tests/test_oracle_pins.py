@@ -487,13 +487,128 @@ def test_empty_call():
 # ------------------------------------------------------------------ sizes
 
 def test_container_sizes_match_pages():
-    for name, dense, expected, tol in golden_lines("container_sizes.txt"):
+    rows = golden_lines("container_sizes.txt")
+    total, expected = {}, {}
+    for row in rows:
+        if row[0] == "ratio":
+            continue
+        name, dense, exp, tol = row
         cfg = G.config(name)
-        total = cfg.layers * cfg.experts * G.expert_bytes(cfg) + float(dense)
-        assert abs(total / float(expected) - 1) <= float(tol), (name, total)
+        total[name] = cfg.layers * cfg.experts * G.expert_bytes(cfg) + float(dense)
+        expected[name] = float(exp)
+        assert abs(total[name] / expected[name] - 1) <= float(tol), (name, total[name])
+    ratios = [r for r in rows if r[0] == "ratio"]
+    assert ratios
+    for _, num, den, tol in ratios:
+        got = total[num] / total[den]
+        want = expected[num] / expected[den]
+        assert abs(got / want - 1) <= float(tol), (num, den, got, want)
+    # the format's 0.5625 B per weight matters: 0.5 B per weight (codes only) misses the
+    # Gemma install by more than the tolerance
+    cfg = G.config("gemma4_26b_a4b_decode")
+    codes_only = cfg.layers * cfg.experts * 3 * cfg.hidden * cfg.inter * 0.5 + 1.35e9
+    assert abs(codes_only / 14.3e9 - 1) > 0.10
 
 
 def test_silu_orientation_and_swiglu_against_logistic():
     # h = silu(gate) * up: swapping gate and up changes the result (pinned in the fixture)
     s15 = float([p for p in golden_lines("swiglu_identity.txt") if p[:2] == ["logistic", "1.5"]][0][2])
     assert math.isclose(s15, 1 / (1 + math.exp(-1.5)), rel_tol=1e-15)
+
+
+# ------------------------------------------------------------------ router logit bias
+# (optional per-expert bias added to the logits before the top-k and kept in the softmax:
+# the plain linear-layer reading of the Zipf-biased router of the long-prefill workload;
+# the router listing of the TurboFieldfare post, section "TurboFieldfare의 전문가 스트리밍
+# 구조", has no bias term, so the reading is pinned by closed forms here.)
+
+def _bias_only_layer(bias, pes):
+    """Router rows of zero weight (codes 0, s = 1, b = 0): every logit is its bias."""
+    H, E = 64, len(bias)
+    return Layer(np.zeros((E, H), np.uint8), np.full((E, 1), 0x3F80, np.uint16),
+                 np.zeros((E, 1), np.uint16), pes=pes, bias=np.asarray(bias, np.float32))
+
+
+def test_logit_bias_zero_input_closed_form():
+    """x = 0 gives u = 0, so logits == bias exactly.  Biases (0, 1, 1, 2, 0.5), k = 2: the
+    selection is expert 3 (bias 2), then expert 1 (bias 1, lower index of the tie with 2),
+    and the weights are the softmax of (2, 1) -- e/(e+1) and 1/(e+1) -- times the experts'
+    scales.  A flipped sign selects (0, 4); a bias used only for selection gives 1/2, 1/2."""
+    pes = np.array([0.5, 0.75, 1.25, 1.5, 1.0], np.float32)
+    li = _bias_only_layer([0.0, 1.0, 1.0, 2.0, 0.5], pes)
+    x = np.zeros((2, 64), np.uint16)
+    top, w, logits = O.router(x, li, 2)
+    assert np.array_equal(logits, np.tile([0.0, 1.0, 1.0, 2.0, 0.5], (2, 1)))
+    assert top.tolist() == [[3, 1], [3, 1]]
+    e = math.e
+    want = np.array([e / (e + 1) * 1.5, 1 / (e + 1) * 0.75])
+    assert np.allclose(w, np.tile(want, (2, 1)), rtol=1e-15, atol=0)
+    # k = 3 takes the tied expert 2 next; its weight uses the same bias as expert 1
+    top3, w3, _ = O.router(x, li, 3)
+    assert top3[0].tolist() == [3, 1, 2]
+    z = e * e + 2 * e
+    assert np.allclose(w3[0], [e * e / z * 1.5, e / z * 0.75, e / z * 1.25], rtol=1e-15, atol=0)
+
+
+def test_logit_bias_adds_to_projected_logits():
+    """The closed-form router of tests/golden/router_closed_form.txt (case A: logits
+    8/sqrt(1+eps), -8/sqrt(1+eps), 0 for x = 1) with the bias (-8, 8.5, 0.25): the logits are
+    the sums, which reverses the order of experts 0 and 1 and puts expert 2 in between."""
+    want_a = [float(v) for p in golden_lines("router_closed_form.txt") if p[0] == "caseA"
+              for v in p[1:]]
+    li = _router_fixture_layer(None)
+    li.bias = np.array([-8.0, 8.5, 0.25], np.float32)
+    x = np.full((1, 64), 0x3F80, np.uint16)
+    top, w, logits = O.router(x, li, 2)
+    want = np.array(want_a) + np.array([-8.0, 8.5, 0.25])
+    assert np.allclose(logits[0], want, rtol=0, atol=1e-12)
+    assert top[0].tolist() == [1, 2]
+    d = want[1] - want[2]
+    assert np.allclose(w[0], [1 / (1 + math.exp(-d)), 1 / (1 + math.exp(d))], rtol=1e-14, atol=0)
+
+
+def test_logit_bias_none_equals_zero_bias():
+    cfg, li, x = _tiny_layer()
+    base = O.layer_forward(x, li, cfg.top_k)
+    li0 = Layer(li.router_q, li.router_s, li.router_b, li.pes,
+                experts={e: li.expert(e) for e in range(cfg.experts)}, shared=li.shared(),
+                bias=np.zeros(cfg.experts, np.float32))
+    r = O.layer_forward(x, li0, cfg.top_k)
+    assert np.array_equal(r["top"], base["top"]) and np.array_equal(r["out"], base["out"])
+
+
+# ------------------------------------------------------------------ selection override
+# (layer_forward(top_override=...) re-evaluates a near-tied token with another valid
+# selection; the parity tests use it, so it is pinned here.)
+
+def test_top_override_with_own_selection_is_identity():
+    cfg, li, x = _tiny_layer()
+    base = O.layer_forward(x, li, cfg.top_k)
+    again = O.layer_forward(x, li, cfg.top_k, top_override=base["top"])
+    for key in ("logits", "top", "w", "counts", "offsets", "sorted", "active", "y",
+                "y_shared", "out", "out_bf16"):
+        assert np.array_equal(again[key], base[key]), key
+
+
+def test_top_override_alternative_selection():
+    """Another selection: its weights are the softmax of the overriding experts' own logits
+    (times their scales) and its routed rows are those experts' FFN outputs."""
+    cfg, li, x = _tiny_layer()
+    k = cfg.top_k
+    base = O.layer_forward(x, li, k)
+    alt = base["top"].copy()
+    for t in range(x.shape[0]):   # keep the first choice, replace the second by an unchosen expert
+        alt[t, 1] = next(e for e in range(cfg.experts) if e not in base["top"][t])
+    r = O.layer_forward(x, li, k, top_override=alt)
+    assert np.array_equal(r["top"], alt)
+    xf = O.bf16_to_f64(x)
+    for t in range(x.shape[0]):
+        lg = base["logits"][t, alt[t]]
+        p = np.exp(lg - lg.max())
+        p /= p.sum()
+        assert np.allclose(r["w"][t], p * li.pes[alt[t]].astype(np.float64), rtol=1e-14, atol=0)
+        for j in range(k):
+            want = O.expert_ffn(xf[t:t + 1], li.expert(int(alt[t, j])))[0]
+            assert np.allclose(r["y"][t * k + j], want, rtol=1e-12, atol=1e-15)
+    want_out = xf + r["y_shared"] + np.einsum("tk,tkh->th", r["w"], r["y"].reshape(-1, k, cfg.hidden))
+    assert np.allclose(r["out"], want_out, rtol=1e-14, atol=1e-14)
