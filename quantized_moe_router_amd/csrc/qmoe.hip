@@ -150,6 +150,19 @@ WsLayout ws_layout(const qmoe_dims *d, int Tmax) {
   const size_t Tc = std::min<size_t>(T, CHUNK_TOKENS);
   size_t o = 0;
   w.cnt = o; o += COUNTER_BYTES;
+  // The one-token path's tagged hand-off areas come first, at offsets that do not depend on
+  // the token count: a workspace sized for a chunk may serve one-token calls too, and no
+  // multi-token call ever writes into these areas (a stale word there can only be an older
+  // one-token call's, whose tag is an older epoch).
+  w.dec_logits = o; o += (size_t)LOGIT_COPIES * dec_copy_stride(E);
+  w.dec_hr = o; o += (size_t)H_COPIES * dec_copy_stride(k * d->inter);
+  w.dec_hsh = o; o += (size_t)H_COPIES * dec_copy_stride((size_t)d->shared_inter);
+  w.dec_yr = o; o += al((k - 1) * H * 8);
+  w.dec_ysh = o; o += al((size_t)dec_shared_chunks(d) * H * 8);
+  w.dec_nrm = o; o += al((H / TILE_ROWS) * 8);
+  w.dec_tk = o; o += al((size_t)TK_COPIES * 2 * MAX_TOPK * 8);
+  w.dec_x = o; o += 2 * (size_t)X_COPIES * dec_x_copy_bytes((int)H);
+  w.dec_tab = o; o += al((size_t)MAX_STACK * sizeof(DecLayer));
   w.logits = o; o += al(T * E * 4);
   w.tidx = o; o += al(T * k * 4);
   w.tw = o; o += al(T * k * 4);
@@ -169,15 +182,6 @@ WsLayout ws_layout(const qmoe_dims *d, int Tmax) {
   w.gx = o; o += al(T * (H / GROUP) * 4);
   w.ghr = o; o += al(T * k * (size_t)(d->inter / GROUP) * 4);
   w.ghs = o; o += al(T * (size_t)(d->shared_inter / GROUP) * 4);
-  w.dec_logits = o; o += (size_t)LOGIT_COPIES * dec_copy_stride(E);
-  w.dec_hr = o; o += (size_t)H_COPIES * dec_copy_stride(k * d->inter);
-  w.dec_hsh = o; o += (size_t)H_COPIES * dec_copy_stride((size_t)d->shared_inter);
-  w.dec_yr = o; o += al((k - 1) * H * 8);
-  w.dec_ysh = o; o += al((size_t)dec_shared_chunks(d) * H * 8);
-  w.dec_nrm = o; o += al((H / TILE_ROWS) * 8);
-  w.dec_tk = o; o += al((size_t)TK_COPIES * 2 * MAX_TOPK * 8);
-  w.dec_x = o; o += 2 * (size_t)X_COPIES * dec_x_copy_bytes((int)H);
-  w.dec_tab = o; o += al((size_t)MAX_STACK * sizeof(DecLayer));
   w.rpart = o; o += al((size_t)rmf_splits((int)H) * Tc * E * 4);   // router partial tiles
   w.rss = o; o += al((size_t)rmf_splits((int)H) * Tc * 4);         // and sums of x^2
   w.total = o;

@@ -63,3 +63,21 @@ def test_hidden_is_bf16_of_normal():
     x = G.make_hidden(cfg, 0)
     assert x.dtype == np.uint16 and x.shape == (cfg.tokens, cfg.hidden)
     assert not np.array_equal(x, G.make_hidden(cfg, 1))
+
+
+def test_host_c_generator_matches_numpy_recipe():
+    """The C draw + quantiser (workloads/hostgen.py) equals the numpy recipe bit for bit."""
+    from workloads import hostgen as H
+    if H.lib() is None:
+        H.build()
+    for k0, k1, rows, cols, std, bits in [(0, 16, 128, 256, 0.02, 4), (3, 77, 96, 2816, 0.02, 4),
+                                          (5, 1, 128, 2816, 0.02, 8), (1, 9, 256, 128, 0.02, 8),
+                                          (2 ** 32 - 1, 123, 64, 64, 1.0, 4)]:
+        w = G.normal_f32(k0, k1, rows * cols, std).reshape(rows, cols)
+        q, s, b = G.quantize_groups(w, bits)
+        if bits == 4:
+            q = G.pack_nibbles(q)
+        q2, s2, b2 = H.matrix(k0, k1, rows, cols, std, bits)
+        assert np.array_equal(q, q2) and np.array_equal(s, s2) and np.array_equal(b, b2), \
+            (k0, k1, rows, cols, bits)
+        assert np.array_equal(H.normal_f32(k0, k1, rows * cols, std), w.reshape(-1))

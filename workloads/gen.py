@@ -29,6 +29,7 @@ are not on the pages; they are the public model shapes.
 """
 from dataclasses import dataclass, field
 import math
+import os
 from typing import Optional
 
 import numpy as np
@@ -233,6 +234,18 @@ class LayerInputs:
             self._cache[e] = make_expert(self.cfg, self.layer, e)
         return self._cache[e]
 
+    def prefetch(self, experts, workers=None):
+        """Draw the listed experts (not yet drawn) on several threads; the C draw releases
+        the interpreter lock, so they run in parallel."""
+        import concurrent.futures
+        todo = sorted({int(e) for e in experts} - set(self._cache))
+        if not todo:
+            return
+        n = workers or min(16, len(os.sched_getaffinity(0)))
+        with concurrent.futures.ThreadPoolExecutor(max_workers=n) as ex:
+            for e, ew in zip(todo, ex.map(lambda e: make_expert(self.cfg, self.layer, e), todo)):
+                self._cache[e] = ew
+
     def shared(self):
         if "shared" not in self._cache:
             self._cache["shared"] = make_shared(self.cfg, self.layer)
@@ -243,10 +256,26 @@ def layer_key(cfg, layer):
     return (cfg.seed + layer) & 0xFFFFFFFF
 
 
+def _hostgen():
+    """The C implementation of the draw and the quantiser (hostgen.py), or None when it is not
+    built; it returns the same bits as normal_f32 / quantize_groups above."""
+    from . import hostgen
+    return hostgen if hostgen.lib() is not None else None
+
+
+def quantized_matrix(k0, k1, rows, cols, std, bits):
+    """normal_f32 draw of a [rows, cols] matrix, quantised with quantize_groups; codes packed
+    two per byte for 4 bits."""
+    fast = _hostgen()
+    if fast is not None:
+        return fast.matrix(k0, k1, rows, cols, std, bits)
+    w = normal_f32(k0, k1, rows * cols, std).reshape(rows, cols)
+    q, s, b = quantize_groups(w, bits)
+    return (q if bits == 8 else pack_nibbles(q)), s, b
+
+
 def _expert_matrix(cfg, layer, tag, rows, cols):
-    w = normal_f32(layer_key(cfg, layer), tag, rows * cols, cfg.weight_std).reshape(rows, cols)
-    q, s, b = quantize_groups(w, cfg.expert_bits)
-    return (q if cfg.expert_bits == 8 else pack_nibbles(q)), s, b
+    return quantized_matrix(layer_key(cfg, layer), tag, rows, cols, cfg.weight_std, cfg.expert_bits)
 
 
 def _ffn_block(cfg, layer, tags, inter):
@@ -289,8 +318,7 @@ def zipf_bias(cfg, layer, sigma=None):
 
 def make_router(cfg, layer):
     E, H = cfg.experts, cfg.hidden
-    w = normal_f32(layer_key(cfg, layer), Tag.ROUTER, E * H, cfg.weight_std).reshape(E, H)
-    q, s, b = quantize_groups(w, 8)
+    q, s, b = quantized_matrix(layer_key(cfg, layer), Tag.ROUTER, E, H, cfg.weight_std, 8)
     pes = uniform_f32(layer_key(cfg, layer), Tag.PES, E, cfg.pes_lo, cfg.pes_hi)
     bias = zipf_bias(cfg, layer) if cfg.zipf_s else None
     return LayerInputs(cfg, layer, q, s, b, np.ones(H, np.float32), pes, bias)
@@ -309,7 +337,9 @@ def make_hidden(cfg, step, tokens=None, std=None):
     """bf16 bit patterns [T, H] of the hidden states entering the first layer at ``step``."""
     T = cfg.tokens if tokens is None else tokens
     k0 = (cfg.seed + 1_000_003 + step) & 0xFFFFFFFF
-    x = normal_f32(k0, Tag.HIDDEN, T * cfg.hidden, cfg.hidden_std if std is None else std)
+    fast = _hostgen()
+    draw = fast.normal_f32 if fast is not None else normal_f32
+    x = draw(k0, Tag.HIDDEN, T * cfg.hidden, cfg.hidden_std if std is None else std)
     return bf16_bits_from_f32(x).reshape(T, cfg.hidden)
 
 
