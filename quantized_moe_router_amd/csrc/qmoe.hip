@@ -29,7 +29,6 @@ constexpr size_t COUNTER_BYTES = 512 * 1024;
 constexpr int GU_W = 8;     // waves per routed gate/up workgroup (split-K)
 constexpr int D_W = 8;      // waves per down workgroup (split-K)
 constexpr int KB = 12;      // k-steps loaded per batch by a wave
-constexpr int MB_MAX = 8;   // rows (tokens) per activation block
 constexpr int DEC_SYNC_WORD = 32768;       // first word of the one-token decode sync area
 constexpr int MAX_T = 65536;
 
@@ -307,8 +306,6 @@ int record_event(hipEvent_t e, hipStream_t s) {
   return QMOE_OK;
 }
 
-// rows per activation block: one-token calls stage a single row
-inline int mb_for(int T) { return T == 1 ? 1 : MB_MAX; }
 
 static FfnArgs make_ffn_args(const qmoe_layer *L, const uint16_t *x, int T, const int32_t *offsets,
                              const int32_t *sorted, const int32_t *active, const int32_t *n_active,
@@ -352,7 +349,7 @@ static int launch_gu(FfnArgs a, hipStream_t s) {
   const int n = a.n_slots * tiles_r + (sh ? a.Is / 16 : 0);
   if (!sh) a.shared = nullptr;
   if (n == 0) return QMOE_OK;
-  return mb_for(a.T) == 1 ? launch_gu_t<1>(a, n, s) : launch_gu_t<MB_MAX>(a, n, s);
+  return launch_gu_t<1>(a, n, s);
 }
 
 template <int MB>
@@ -376,7 +373,7 @@ static int launch_d(FfnArgs a, bool with_shared, hipStream_t s) {
     const int KSs = a.Is / GROUP;
     Kc = std::max(Kc, GROUP * ((KSs + a.n_sh_chunks - 1) / a.n_sh_chunks));
   }
-  return mb_for(a.T) == 1 ? launch_d_t<1>(a, slots, Kc, s) : launch_d_t<MB_MAX>(a, slots, Kc, s);
+  return launch_d_t<1>(a, slots, Kc, s);
 }
 
 // Matrix-core grouped GEMM (mfma.h): gate/up then down.  Routed rows go to a.y, shared rows
@@ -401,10 +398,11 @@ static int launch_pf(const FfnArgs &a, hipStream_t s) {
   return QMOE_OK;
 }
 
-// Chunks with fewer tokens than this take the VALU kernels (ffn.h): the matrix-core blocks
-// would be mostly padding rows.
+// Chunks with fewer tokens than this take the VALU kernels (ffn.h), which stage one activation
+// row: the matrix-core blocks would be mostly padding rows.
 constexpr int PF_MIN_TOKENS = 2;
 static bool valu_ffn(int T) { return T < PF_MIN_TOKENS; }
+static_assert(PF_MIN_TOKENS == 2, "the VALU launchers are instantiated for one row only");
 
 static int launch_gsum(const uint16_t *x, int T, int H, float *g, hipStream_t s) {
   const int n = T * (H / GROUP);

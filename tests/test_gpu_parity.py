@@ -245,17 +245,31 @@ def _bucket_of(ops, dims, idx):
     return ops.bucket(dims, idx)
 
 
-# T <= 128 takes the matrix-core kernels, T = 200 the VALU ones
-@pytest.mark.parametrize("name,T,sample", [("tiny", 4, None), ("tiny", 37, None), ("tiny", 200, None),
-                                           ("tiny_int8", 1, None), ("tiny_int8", 37, None),
-                                           ("gemma4_26b_a4b_int8_decode", 1, None),
-                                           ("gemma4_26b_a4b_decode", 1, None),
-                                           ("gemma4_26b_a4b_prefill", 128, [0, 77]),
-                                           ("qwen3_next_80b_a3b_decode_b16", 16, [3, 15])])
-def test_expert_ffn_and_combine_parity(name, T, sample):
+def _ffn_ref(li, xf, idx_n, k):
+    """Oracle y [T*k, H] for the GPU's routing (teacher forcing): each expert dequantised
+    once, over every row routed to it."""
+    T, H = xf.shape
+    y = np.zeros((T * k, H))
+    flat = idx_n.reshape(-1)
+    li.prefetch(np.unique(flat))
+    for e in np.unique(flat):
+        ids = np.nonzero(flat == e)[0]
+        y[ids] = O.expert_ffn(xf[ids // k], li.expert(int(e)))
+    return y
+
+
+# Every chunk of two or more tokens takes the matrix-core kernels (T = 200: two chunks,
+# the second of 72 tokens); one token takes the VALU kernels of the standalone FFN call.
+@pytest.mark.parametrize("name,T", [("tiny", 4), ("tiny", 37), ("tiny", 200), ("tiny_int8", 1),
+                                    ("tiny_int8", 37), ("gemma4_26b_a4b_int8_decode", 1),
+                                    ("gemma4_26b_a4b_decode", 1), ("gemma4_26b_a4b_prefill", 128),
+                                    ("qwen3_next_80b_a3b_decode_b16", 16),
+                                    ("qwen3_6_35b_a3b_long_prefill", 128)])
+def test_expert_ffn_and_combine_parity(name, T):
     ops = _ops()
     cfg = G.config(name)
-    pl, li = layer({"gemma4_26b_a4b_prefill": "gemma4_26b_a4b_decode"}.get(name, name))
+    pl, li = layer({"gemma4_26b_a4b_prefill": "gemma4_26b_a4b_decode",
+                    "qwen3_next_80b_a3b_decode_b16": "qwen3_next_80b_a3b_decode_b1"}.get(name, name))
     xb, x = _stacks().hidden(cfg, 1, T)
     ws = ops.workspace(pl.dims, T)
     idx, w = ops.router_topk(pl.dims, pl.router, x, ws)
@@ -264,22 +278,19 @@ def test_expert_ffn_and_combine_parity(name, T, sample):
     out_f32 = torch.empty(T, cfg.hidden, dtype=torch.float32, device=DEV)
     out = ops.combine(pl.dims, x, y, w, y_sh, out_f32=out_f32)
     torch.cuda.synchronize()
+    k = cfg.top_k
     idx_n, w_n = idx.cpu().numpy(), w.cpu().numpy()
     y_n, ysh_n = y.cpu().numpy(), y_sh.cpu().numpy()
     out_n, of_n = np16(out), out_f32.cpu().numpy()
-    toks = range(T) if sample is None else sample
     xf = O.bf16_to_f64(xb)
-    sh = O.expert_ffn(xf[list(toks)], li.shared())
-    flips = 0
-    for n, t in enumerate(toks):
-        # y per assignment, with the GPU's routing (teacher forcing)
-        ys = np.stack([O.expert_ffn(xf[t:t + 1], li.expert(int(e)))[0] for e in idx_n[t]])
-        assert_close_f32(y_n[t * cfg.top_k:(t + 1) * cfg.top_k], ys, f"y token {t}")
-        assert_close_f32(ysh_n[t], sh[n], f"y_shared token {t}")
-        ref = xf[t] + sh[n] + (w_n[t].astype(np.float64)[:, None] * ys).sum(0)
-        assert_close_f32(of_n[t], ref, f"out_f32 token {t}")
-        flips += check_out_bf16(out_n[t], of_n[t], ref, f"out token {t}")
-    print(f"{name}: bf16 1-ulp flips {flips}")
+    ys = _ffn_ref(li, xf, idx_n, k)            # per assignment, with the GPU's routing
+    sh = O.expert_ffn(xf, li.shared())
+    assert_close_f32(y_n, ys, "y")
+    assert_close_f32(ysh_n, sh, "y_shared")
+    ref = xf + sh + np.einsum("tk,tkh->th", w_n.astype(np.float64), ys.reshape(T, k, cfg.hidden))
+    assert_close_f32(of_n, ref, "out_f32")
+    flips = check_out_bf16(out_n, of_n, ref, "out")
+    print(f"{name} T={T}: every token; bf16 1-ulp flips {flips}")
 
 
 # ------------------------------------------------------------------ whole layer
@@ -287,6 +298,8 @@ def test_expert_ffn_and_combine_parity(name, T, sample):
 def _layer_check(cfg, li, xb, out, out_f32, idx, w, toks):
     T = xb.shape[0]
     idx_n = idx.cpu().numpy()
+    top0, _, _ = O.router(xb[list(toks)], li, cfg.top_k)
+    li.prefetch(np.union1d(np.unique(top0), np.unique(idx_n[list(toks)])))
     ref = O.layer_forward(xb[list(toks)], li, cfg.top_k)
     ties, differ = compare_topk(idx_n[list(toks)], w.cpu().numpy()[list(toks)], ref["logits"],
                                 ref["top"], ref["w"])
@@ -304,18 +317,15 @@ def _layer_check(cfg, li, xb, out, out_f32, idx, w, toks):
     return ties, len(differ), flips
 
 
-@pytest.mark.parametrize("name,T,sample", [("tiny", 4, None), ("tiny", 1, None), ("tiny", 64, None),
-                                           ("tiny", 130, [0, 129]),
-                                           ("gemma4_26b_a4b_decode", 1, None),
-                                           ("gemma4_26b_a4b_prefill", 128, [5, 127]),
-                                           ("qwen3_next_80b_a3b_decode_b1", 1, None),
-                                           ("qwen3_next_80b_a3b_decode_b16", 16, [0, 9]),
-                                           ("qwen3_6_35b_a3b_long_prefill", 128, [64]),
-                                           ("tiny_int8", 1, None), ("tiny_int8", 4, None),
-                                           ("tiny_int8", 64, None),
-                                           ("gemma4_26b_a4b_int8_decode", 1, None),
-                                           ("gemma4_26b_a4b_int8_decode", 128, [7, 120])])
-def test_layer_forward_parity(name, T, sample):
+@pytest.mark.parametrize("name,T", [("tiny", 4), ("tiny", 1), ("tiny", 64), ("tiny", 130),
+                                    ("gemma4_26b_a4b_decode", 1), ("gemma4_26b_a4b_prefill", 128),
+                                    ("qwen3_next_80b_a3b_decode_b1", 1),
+                                    ("qwen3_next_80b_a3b_decode_b16", 16),
+                                    ("qwen3_6_35b_a3b_long_prefill", 128),
+                                    ("tiny_int8", 1), ("tiny_int8", 4), ("tiny_int8", 64),
+                                    ("gemma4_26b_a4b_int8_decode", 1),
+                                    ("gemma4_26b_a4b_int8_decode", 128)])
+def test_layer_forward_parity(name, T):
     ops = _ops()
     cfg = G.config(name)
     src = {"gemma4_26b_a4b_prefill": "gemma4_26b_a4b_decode",
@@ -328,9 +338,28 @@ def test_layer_forward_parity(name, T, sample):
     w = torch.empty(T, cfg.top_k, dtype=torch.float32, device=DEV)
     out = ops.layer_forward(pl.weights, x, ws, out_f32=out_f32, topk_idx=idx, topk_w=w)
     torch.cuda.synchronize()
-    toks = range(T) if sample is None else sample
-    ties, nd, flips = _layer_check(cfg, li, xb, out, out_f32, idx, w, toks)
-    print(f"{name} T={T}: near ties {ties}, re-evaluated {nd}, bf16 flips {flips}")
+    ties, nd, flips = _layer_check(cfg, li, xb, out, out_f32, idx, w, range(T))
+    print(f"{name} T={T}: every token; near ties {ties}, re-evaluated {nd}, bf16 flips {flips}")
+
+
+@pytest.mark.parametrize("inter,bits", [(3136, 4), (1600, 8)])
+def test_one_token_layer_too_wide_for_the_single_launch(inter, bits):
+    """One token through a layer whose routed expert is wider than the one-token launch holds
+    (more than 48 k-steps per gate/up row: inter > 3072 for 4-bit codes, > 1536 for 8-bit) takes
+    the VALU kernels of the chunked path; checked against the oracle."""
+    ops = _ops()
+    cfg = G.Config(f"wide_{bits}", 256, 8, 2, inter, 128, layers=1, tokens=1, expert_bits=bits)
+    pl, li = _stacks().build_layer(cfg, 0, DEV)
+    for step in range(3):
+        xb, x = _stacks().hidden(cfg, 60 + step, 1)
+        ws = ops.workspace(pl.dims, 1)
+        out_f32 = torch.empty(1, cfg.hidden, dtype=torch.float32, device=DEV)
+        idx = torch.empty(1, cfg.top_k, dtype=torch.int32, device=DEV)
+        w = torch.empty(1, cfg.top_k, dtype=torch.float32, device=DEV)
+        out = ops.layer_forward(pl.weights, x, ws, out_f32=out_f32, topk_idx=idx, topk_w=w)
+        torch.cuda.synchronize()
+        ties, nd, flips = _layer_check(cfg, li, xb, out, out_f32, idx, w, range(1))
+        print(f"inter {inter} bits {bits} step {step}: near ties {ties}, bf16 flips {flips}")
 
 
 def test_layer_forward_matches_stepwise_and_is_deterministic():
@@ -405,6 +434,30 @@ def test_one_token_calls_repeat_and_report_no_timeout(name):
     check_out_bf16(np16(fresh)[0], o32.cpu().numpy()[0], ref["out"][0], "one-token out")
 
 
+def test_one_token_calls_after_a_chunk_share_the_workspace():
+    """A workspace sized for a 128-token chunk serves chunk calls and one-token calls in turn:
+    the one-token results equal a fresh workspace's bit for bit and the oracle's (the one-token
+    hand-off words sit where no chunk call writes, so a chunk's data never poses as a fresh
+    word)."""
+    ops = _ops()
+    cfg = G.config("gemma4_26b_a4b_decode")
+    pl, li = layer("gemma4_26b_a4b_decode")
+    ws = ops.workspace(pl.dims, 128)
+    xb128, x128 = _stacks().hidden(cfg, 40, 128)
+    xs = [_stacks().hidden(cfg, 41 + j, 1) for j in range(3)]
+    fresh = [ops.layer_forward(pl.weights, x, ops.workspace(pl.dims, 1)) for _, x in xs]
+    o32 = torch.empty(1, cfg.hidden, dtype=torch.float32, device=DEV)
+    for rep in range(3):
+        ops.layer_forward(pl.weights, x128, ws)
+        for j, (_, x) in enumerate(xs):
+            out = ops.layer_forward(pl.weights, x, ws, out_f32=o32)
+            torch.cuda.synchronize()
+            assert torch.equal(out.view(torch.int16), fresh[j].view(torch.int16)), (rep, j)
+    assert ops.workspace_status(ws) == 0
+    ref = O.layer_forward(xs[-1][0], li, cfg.top_k)
+    assert_close_f32(o32.cpu().numpy()[0], ref["out"][0], "one-token out_f32 after chunks")
+
+
 # ------------------------------------------------------------------ post-combine steps (cb2)
 
 class _WithPost:
@@ -431,13 +484,12 @@ def post_layer(name, steps="both"):
     return pl, lw, view
 
 
-@pytest.mark.parametrize("name,T,sample,steps", [
-    ("tiny", 4, None, "both"), ("tiny", 1, None, "both"), ("tiny", 1, None, "scalar"),
-    ("tiny", 64, None, "gain"), ("tiny", 37, None, "scalar"),
-    ("gemma4_26b_a4b_decode", 1, None, "both"), ("gemma4_26b_a4b_decode", 128, [3, 100], "both"),
-    ("qwen3_next_80b_a3b_decode_b1", 1, None, "both"),
-    ("qwen3_6_35b_a3b_long_prefill", 128, [10], "gain")])
-def test_layer_forward_post_parity(name, T, sample, steps):
+@pytest.mark.parametrize("name,T,steps", [
+    ("tiny", 4, "both"), ("tiny", 1, "both"), ("tiny", 1, "scalar"), ("tiny", 64, "gain"),
+    ("tiny", 37, "scalar"), ("gemma4_26b_a4b_decode", 1, "both"),
+    ("gemma4_26b_a4b_decode", 128, "both"), ("qwen3_next_80b_a3b_decode_b1", 1, "both"),
+    ("qwen3_6_35b_a3b_long_prefill", 128, "gain")])
+def test_layer_forward_post_parity(name, T, steps):
     """The layer with cb2's post-combine steps (one-token kernel and chunked path)."""
     ops = _ops()
     cfg = G.config(name)
@@ -450,8 +502,7 @@ def test_layer_forward_post_parity(name, T, sample, steps):
     out = ops.layer_forward(lw, x, ws, out_f32=out_f32, topk_idx=idx, topk_w=w)
     torch.cuda.synchronize()
     assert ops.workspace_status(ws) == 0
-    toks = range(T) if sample is None else sample
-    ties, nd, flips = _layer_check(cfg, view, xb, out, out_f32, idx, w, toks)
+    ties, nd, flips = _layer_check(cfg, view, xb, out, out_f32, idx, w, range(T))
     print(f"{name} T={T} post={steps}: near ties {ties}, re-evaluated {nd}, bf16 flips {flips}")
 
 

@@ -181,16 +181,14 @@ def test_stack_graph_replays_match_eager():
     assert ops.workspace_status(ws) == 0
 
 
-@pytest.mark.parametrize("name,n,post", [("tiny", 5, (2,)), ("gemma4_26b_a4b_decode", 3, ())])
+@pytest.mark.parametrize("name,n,post", [("tiny", 5, (2,)), ("gemma4_26b_a4b_decode", 4, (1, 3)),
+                                         ("qwen3_next_80b_a3b_decode_b1", 3, (0, 1, 2)),
+                                         ("gemma4_26b_a4b_int8_decode", 2, (1,))])
 def test_stack_against_oracle_chain(name, n, post):
-    """Layer by layer against the oracle's own chain (x_{l+1} = bf16 of its layer-l output).
-    While the two chains' inputs are the same bits, every layer meets the layer bar.  Once a
-    bf16 rounding flip (each within the bar) makes them differ, the layers see different
-    inputs, and the synthetic layers amplify the difference (a few flipped elements of x spread
-    through the experts into many elements of the next output); from there on the routing must
-    still agree (or differ only within a logit gap of 1e-3) and the output, corrected by the
-    residual's own share of the input difference, must stay within 2e-3 of the oracle's in
-    row norm."""
+    """Layer by layer against the oracle, teacher-forced: oracle layer l takes the stack's own
+    input to layer l (the bf16 output of its layer l - 1), so every layer is held to the full
+    layer bar -- the top-k bit-exact apart from near ties (oracle gap < 1e-5, counted), the
+    fp32 output element by element within 2e-3 and the bf16 output by the bf16 rule."""
     ops = _ops()
     cfg = G.config(name)
     lws, views = chain(name, n, post)
@@ -199,31 +197,19 @@ def test_stack_against_oracle_chain(name, n, post):
     out, o32, idx, w = run_stack(lws, x, ws)
     torch.cuda.synchronize()
     out_n, o32_n, idx_n, w_n = np16(out), o32.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
-    xo = np.asarray(xb, np.uint16)          # the oracle's input to layer l
     xs = np.asarray(xb, np.uint16)          # the stack's input to layer l
-    same_inputs = 0
+    n_ties = n_differ = flips = 0
     for l in range(n):
-        dx = O.bf16_to_f64(xs) - O.bf16_to_f64(xo)
-        ref = O.layer_forward(xo, views[l], cfg.top_k)
-        alpha = views[l].layer_scalar if views[l].layer_scalar is not None else 1.0
-        if not np.any(dx):
-            same_inputs += 1
-            ties, differ = compare_topk(idx_n[l:l + 1], w_n[l:l + 1], ref["logits"], ref["top"],
-                                        ref["w"])
-            if differ:      # near tie: the oracle re-evaluated with the GPU's valid selection
-                ref = O.layer_forward(xo, views[l], cfg.top_k, top_override=idx_n[l:l + 1])
-            assert_close_f32(o32_n[l], ref["out"][0], f"{name} layer {l} out_f32")
-            check_out_bf16(out_n[l], o32_n[l], ref["out"][0], f"{name} layer {l} out")
-        else:
-            if set(idx_n[l].tolist()) != set(ref["top"][0].tolist()):
-                lg = np.sort(ref["logits"][0])[::-1]
-                assert lg[cfg.top_k - 1] - lg[cfg.top_k] < 1e-3, f"layer {l}: top-k differs"
-                ref = O.layer_forward(xo, views[l], cfg.top_k, top_override=idx_n[l:l + 1])
-            want = ref["out"][0] + alpha * dx[0]
-            err = np.linalg.norm(o32_n[l] - want) / np.linalg.norm(want)
-            assert err <= 2e-3, f"{name} layer {l}: row-norm error {err:.3e}"
-        xo = ref["out_bf16"][0:1].astype(np.uint16)
+        ref = O.layer_forward(xs, views[l], cfg.top_k)
+        ties, differ = compare_topk(idx_n[l:l + 1], w_n[l:l + 1], ref["logits"], ref["top"],
+                                    ref["w"])
+        n_ties += ties
+        if differ:          # near tie: the oracle re-evaluated with the GPU's valid selection
+            n_differ += 1
+            ref = O.layer_forward(xs, views[l], cfg.top_k, top_override=idx_n[l:l + 1])
+        assert_close_f32(o32_n[l], ref["out"][0], f"{name} layer {l} out_f32")
+        flips += check_out_bf16(out_n[l], o32_n[l], ref["out"][0], f"{name} layer {l} out")
         xs = out_n[l:l + 1]
-    print(f"{name} x{n}: {same_inputs} layers with the same input bits as the oracle chain")
-    assert same_inputs >= 1
+    print(f"{name} x{n} teacher-forced: near ties {n_ties}, re-evaluated {n_differ}, "
+          f"bf16 flips {flips}")
     assert ops.workspace_status(ws) == 0
