@@ -50,6 +50,9 @@ def parse():
     p.add_argument("--no-extra", action="store_true",
                    help="skip the post-norm stack and the other workload shapes")
     p.add_argument("--cpu-sample", type=int, default=8, help="token-layers timed on the oracle")
+    p.add_argument("--timeline", action="store_true",
+                   help="only run the one-token stack once with the profiling build's phase "
+                        "timestamps and write profiles/decode_timeline_<workload>.md")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB (reads MIB, writes MIB) a few "
                         "times and exit: the reference kernel for scaling rocprof byte counters")
@@ -227,12 +230,18 @@ def run_decode(args, cfg, layers):
     torch.cuda.synchronize()
     ms_plain = (time.perf_counter() - t2) * 1e3 / args.steps
 
+    status = ops.workspace_status(ws)      # 0: no wait of the timed one-token calls timed out
+    if status != 0:
+        raise RuntimeError(f"workspace status {status} after the timed replays: a one-token "
+                           "call gave up waiting, its results are not valid")
     n_dist = float(np.mean(distinct))
     credited = G.credited_expert_bytes(cfg, n_dist)                   # routed bytes per layer
     all_bytes = credited + G.expert_bytes(cfg, cfg.shared_inter) + G.router_bytes(cfg)
     if T == 1:
+        # credited bytes only: the distinct routed experts' codes, scales and biases (the
+        # shared expert and the router are reported beside, not credited)
         kernel = "decode_layer_kernel (the whole one-token layer in one launch)"
-        kern_bytes = all_bytes
+        kern_bytes = credited
         traffic = stored_traffic(f"decode_layer_kernel_{cfg.name}")
     else:
         kernel = "gu_pf_kernel (routed and shared gate/up + SwiGLU, matrix cores)"
@@ -243,13 +252,74 @@ def run_decode(args, cfg, layers):
     layer_s = ms_step / 1e3 / L
     kern_gbps = kern_bytes / (kern_ms / 1e3) / 1e9
     return dict(
-        ms_step=ms_step, ms_plain=ms_plain, tok_s_layer=tok_s_layer, L=L, T=T,
+        ms_step=ms_step, ms_plain=ms_plain, tok_s_layer=tok_s_layer, L=L, T=T, status=status,
         kern_ms=kern_ms, kern_bytes=kern_bytes, kern_gbps=kern_gbps, kernel=kernel,
         layer_credited_gbps=credited / layer_s / 1e9,
         layer_all_gbps=all_bytes / layer_s / 1e9,
         credited=credited, all_bytes=all_bytes, distinct=n_dist, timing_src=timing_src,
         traffic=traffic,
     )
+
+
+def run_read_ceiling(layers, cfg, reps=5):
+    """The plain streaming read (qmoe_read_blocks) as the achievable-bandwidth reference: the
+    same volume and access shape as one decode layer's routed weights -- the distinct experts a
+    token of each layer selects, whole fixed-stride blocks of the layer's store -- read once per
+    layer of the stack in one graph (HIP event nodes before the first and after the last read,
+    divided by the layer count, as the layer kernel is timed), and a 1 GiB contiguous read."""
+    import numpy as np
+    import torch
+    from quantized_moe_router_amd import ops
+    from workloads import gen as G
+    L = len(layers)
+    nbytes = G.expert_bytes(cfg)
+    nbytes -= nbytes % 16
+    xs = layer_inputs(cfg, 7, L, 1)
+    ws = ops.workspace(layers[0][0].dims, 1)
+    ids = []
+    for l, (pl, _) in enumerate(layers):
+        idx = torch.empty(1, cfg.top_k, dtype=torch.int32, device="cuda")
+        ops.layer_forward(pl.weights, xs[l], ws, topk_idx=idx)
+        ids.append(sorted(set(idx.cpu().numpy().ravel().tolist())))
+    nmax = max(len(i) for i in ids) * ((nbytes + 16383) // 16384)
+    sink = torch.empty(nmax, dtype=torch.int32, device="cuda")
+    ev0, ev1 = ops.Event(), ops.Event()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ev0.record()
+        for (pl, _), i in zip(layers, ids):
+            ops.read_blocks(pl.store, pl.stride, i, nbytes, sink)
+        ev1.record()
+    g.replay()
+    torch.cuda.synchronize()
+    per = []
+    for _ in range(reps):
+        g.replay()
+        torch.cuda.synchronize()
+        per.append(ev0.elapsed_ms(ev1) / L)
+    us = float(np.median(per)) * 1e3
+    moved = float(np.mean([len(i) for i in ids])) * nbytes
+    big = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    big.fill_(1)
+    sink2 = torch.empty((1 << 30) // 16384, dtype=torch.int32, device="cuda")
+    t = []
+    for _ in range(reps + 1):
+        a, b = ops.Event(), ops.Event()
+        a.record()
+        ops.read_blocks(big, 0, [0], 1 << 30, sink2)
+        b.record()
+        torch.cuda.synchronize()
+        t.append(a.elapsed_ms(b))
+    gib_us = float(np.median(t[1:])) * 1e3
+    del big
+    return {"blocks_per_read": round(float(np.mean([len(i) for i in ids])), 2),
+            "bytes_per_read": int(moved), "us_per_read": round(us, 3),
+            "GBps": round(moved / (us * 1e-6) / 1e9, 1),
+            "contiguous_1GiB_GBps": round((1 << 30) / (gib_us * 1e-6) / 1e9, 1),
+            "kernel": "stream_read_kernel (qmoe_read_blocks): 16 KiB per wave, 8 non-temporal "
+                      "16-byte loads in flight per lane",
+            "timing": f"graph of {L} reads (one per layer), HIP event nodes around them, "
+                      f"divided by {L}; the 1 GiB read: HIP events around one launch"}
 
 
 def time_stack(ops, weights, xs, ws, steps):
@@ -455,6 +525,8 @@ def cpu_baseline(cfg, n_samples):
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
         threads = 1
+    host = dict(os_cpu_count=os.cpu_count(), affinity_cores=len(os.sched_getaffinity(0)),
+                blas_threads=int(threads))
     times = []
     for l in range(n_samples):
         x = G.make_hidden(cfg, l)            # each layer gets its own N(0,1) hidden states
@@ -469,14 +541,135 @@ def cpu_baseline(cfg, n_samples):
         assert r["out"].shape == x.shape
     s_per_unit = float(np.median(times))
     return dict(value=cfg.tokens / s_per_unit, unit="tokens/s per MoE layer", cores=int(threads),
-                kind="oracle",
+                kind="oracle", host=host,
                 sample=f"{n_samples} token-layers ({cfg.name}, layers 0..{n_samples - 1}, 1 token "
                        f"each); median {s_per_unit:.3f} s per token-layer; drawing the synthetic "
                        f"experts is excluded")
 
 
+TL_POINTS = 8
+TL_ROLES = {1: ("router", {1: "logits published"}),
+            2: ("shared gate/up", {1: "x staged"}),
+            3: ("routed gate/up", {1: "x staged", 2: "expert known", 3: "weights consumed"}),
+            4: ("shared down", {1: "router seen", 2: "weights in", 3: "h staged"}),
+            5: ("routed down", {1: "top-k known", 2: "weights in", 3: "h staged",
+                                4: "products done", 5: "combine inputs in"})}
+
+
+def run_timeline(args, cfg, layers):
+    """Phase timestamps of the one-token layer (profiling build, QMOE_LIBRARY=timeline): the
+    stack captured in one graph with a timestamp buffer per layer, replayed a few times, then
+    once more into zeroed buffers.  Per role and point: the median and the maximum over the
+    role's workgroups of the time since the layer kernel's first workgroup started, each
+    taken as the median over the layers.  Routed window: from the first routed gate/up
+    workgroup that knows its expert (its weight loads start) to the last routed weight byte in
+    (the last routed gate/up workgroup's weights consumed, or the last routed down
+    workgroup's down weights in); credited routed bytes over that window."""
+    import numpy as np
+    import torch
+    from quantized_moe_router_amd import ops
+    from workloads import gen as G
+    L, T, H = len(layers), 1, cfg.hidden
+    ws = ops.workspace(layers[0][0].dims, T)
+    outs = [torch.empty(T, H, dtype=torch.bfloat16, device="cuda") for _ in range(L)]
+    xs = layer_inputs(cfg, 0, L, T)
+    idx = [torch.empty(T, cfg.top_k, dtype=torch.int32, device="cuda") for _ in range(L)]
+    for l, (pl, _) in enumerate(layers):
+        ops.layer_forward(pl.weights, xs[l], ws, out=outs[l], topk_idx=idx[l])
+    torch.cuda.synchronize()
+    distinct = float(np.mean([len(np.unique(i.cpu().numpy())) for i in idx]))
+    max_blocks = 8192
+    buf = torch.zeros(L, max_blocks * TL_POINTS, dtype=torch.int64, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for l, (pl, _) in enumerate(layers):
+            ops.timeline_set(buf[l])
+            ops.layer_forward(pl.weights, xs[l], ws, out=outs[l])
+        ops.timeline_set(None)
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    buf.zero_()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    status = ops.workspace_status(ws)
+    tl = buf.cpu().numpy().reshape(L, max_blocks, TL_POINTS)
+    per_layer = {}
+    windows, kern = [], []
+    for l in range(L):
+        rows = tl[l]
+        role = rows[:, TL_POINTS - 1]
+        used = role > 0
+        t0 = rows[used, 0].min()
+        us = (rows[:, :TL_POINTS - 1] - t0) / 100.0          # 100 MHz clock -> microseconds
+        kern.append(us[used, 6].max())
+        for r, (name, pts) in TL_ROLES.items():
+            m = role == r
+            if not m.any():
+                continue
+            for p in [0] + sorted(pts) + [6]:
+                mp = m & (rows[:, p] > 0)       # workgroups that record this point
+                if mp.any():
+                    per_layer.setdefault((r, p), []).append((np.median(us[mp, p]), us[mp, p].max(),
+                                                             int(mp.sum())))
+        rg, cd = role == 3, (role == 5) & (rows[:, 2] > 0)
+        start = us[rg, 2].min()
+        end = max(us[rg, 3].max(), us[cd, 2].max() if cd.any() else 0.0)
+        windows.append((start, end))
+    credited = G.credited_expert_bytes(cfg, distinct)
+    w0 = float(np.median([w[0] for w in windows]))
+    w1 = float(np.median([w[1] for w in windows]))
+    win_gbps = credited / ((w1 - w0) * 1e-6) / 1e9
+    lines = []
+    for (r, p), v in sorted(per_layer.items()):
+        name, pts = TL_ROLES[r]
+        label = {0: "start", 6: "end"}.get(p, pts.get(p, str(p)))
+        lines.append((name, label, float(np.median([x[0] for x in v])),
+                      float(np.median([x[1] for x in v])), v[0][2]))
+    return dict(lines=lines, window=(w0, w1), window_gbps=win_gbps, credited=credited,
+                kernel_us=float(np.median(kern)), distinct=distinct, status=status, L=L)
+
+
+def write_timeline(cfg, t, cmd):
+    path = os.path.join(ROOT, "profiles", f"decode_timeline_{cfg.name}.md")
+    w0, w1 = t["window"]
+    with open(path, "w") as f:
+        f.write(f"# Phase timeline of decode_layer_kernel -- {cfg.name} ({t['L']} stacked layers, "
+                "1 token)\n\n")
+        f.write("Profiling build (`libqmoe_timeline.so`: the same sources with QMOE_TIMELINE, thread "
+                "0 of every workgroup recording the 100 MHz device clock at fixed points of its "
+                "role), one graph replay of the stack after three warm-up replays:\n\n")
+        f.write(f"```\n{cmd}\n```\n\n")
+        f.write("Times in microseconds since the layer kernel's first workgroup started; per role "
+                "and point the median and the maximum over the role's workgroups, each the median "
+                "over the layers.\n\n")
+        f.write("| role | workgroups | point | median us | max us |\n|---|---|---|---|---|\n")
+        for name, label, med, mx, n in t["lines"]:
+            f.write(f"| {name} | {n} | {label} | {med:.2f} | {mx:.2f} |\n")
+        f.write(f"\nKernel (first workgroup start to last workgroup end): {t['kernel_us']:.2f} us "
+                "(median over layers; the launch's dispatch before the first workgroup is not "
+                "in it).\n\n")
+        f.write(f"Routed weight window: {w0:.2f} us (the first routed gate/up workgroup knows its "
+                f"expert and starts its weight loads) to {w1:.2f} us (the last routed weight in: "
+                "gate/up weights consumed or routed down weights loaded), "
+                f"{w1 - w0:.2f} us for {t['credited'] / 1e6:.2f} MB of credited routed bytes "
+                f"({t['distinct']:.1f} distinct experts x {G_expert_mb(cfg):.4f} MB): "
+                f"**{t['window_gbps']:.0f} GB/s = {t['window_gbps'] / HBM_PEAK_GBPS:.3f} of "
+                "8 TB/s**.\n\n")
+        f.write(f"Workspace status after the run: {t['status']} (0 = no wait timed out).\n")
+    return path
+
+
+def G_expert_mb(cfg):
+    from workloads import gen as G
+    return G.expert_bytes(cfg) / 1e6
+
+
 def main():
     args = parse()
+    if args.timeline:
+        os.environ["QMOE_LIBRARY"] = "timeline"
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the layer is measured on a "
               f"single MI355X and a multi-GPU figure is not produced.", file=sys.stderr)
@@ -495,10 +688,28 @@ def main():
     n_layers = args.layers or cfg.layers
     log(f"building {cfg.name}: {n_layers} layers")
     layers = build_stack(cfg, n_layers)
+    if args.timeline:
+        if cfg.tokens != 1:
+            sys.exit("--timeline covers the one-token layer")
+        t = run_timeline(args, cfg, layers)
+        path = write_timeline(cfg, t, "python3 bench.py --timeline --workload " + cfg.name +
+                              (f" --layers {n_layers}" if args.layers else ""))
+        log(f"timeline: kernel {t['kernel_us']:.2f} us, routed window {t['window'][0]:.2f}.."
+            f"{t['window'][1]:.2f} us = {t['window_gbps']:.0f} GB/s, status {t['status']}; "
+            f"written to {path}")
+        for name, label, med, mx, n in t["lines"]:
+            log(f"  {name:16s} {label:20s} {med:7.2f} {mx:7.2f}")
+        return
     log("decode timing")
     d = run_decode(args, cfg, layers)
     log(f"decode: {d['ms_step']:.3f} ms/step ({d['ms_plain']:.3f} without events), "
         f"{d['kernel'].split()[0]} {d['kern_ms'] * 1e3:.2f} us = {d['kern_gbps']:.0f} GB/s")
+    ceiling = None
+    if cfg.tokens == 1:
+        log("streaming-read ceiling")
+        ceiling = run_read_ceiling(layers, cfg)
+        log(f"read ceiling: {ceiling['us_per_read']} us per {ceiling['bytes_per_read'] / 1e6:.2f} MB "
+            f"= {ceiling['GBps']} GB/s; 1 GiB contiguous {ceiling['contiguous_1GiB_GBps']} GB/s")
     pf = None
     if not args.no_prefill and cfg.name == "gemma4_26b_a4b_decode":
         log("prefill timing")
@@ -548,8 +759,13 @@ def main():
             "frac": round(d["kern_gbps"] / HBM_PEAK_GBPS, 4),
             "traffic": d["traffic"],
             "bytes_per_launch": int(d["kern_bytes"]),
+            "bytes": "credited: distinct routed experts x (int4 codes + bf16 scale and bias)",
+            "all_bytes_per_launch": int(d["all_bytes"]) if d["T"] == 1 else None,
+            "all_bytes_frac": (round(d["all_bytes"] / (d["kern_ms"] / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)
+                               if d["T"] == 1 else None),
             "avg_launch_us": round(d["kern_ms"] * 1e3, 3),
             "timing": d["timing_src"],
+            "workspace_status": d["status"],
         },
         "layer": {
             "credited_GBps": round(d["layer_credited_gbps"], 1),
@@ -560,6 +776,9 @@ def main():
             "distinct_experts_per_layer": round(d["distinct"], 2),
         },
     }
+    if ceiling:
+        out["read_ceiling"] = ceiling
+        out["roofline"]["frac_of_read_ceiling"] = round(d["kern_gbps"] / ceiling["GBps"], 4)
     if pf:
         out["prefill"] = {
             "workload": "gemma4_26b_a4b_prefill: one 128-token chunk through the same stack (graph replay)",

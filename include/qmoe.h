@@ -337,6 +337,19 @@ int qmoe_event_record(void *event, qmoe_stream_t stream);
 int qmoe_event_elapsed_ms(void *start, void *stop, float *ms_out);
 int qmoe_set_profile_events(void *start, void *stop);
 
+/* ---------------------------------------------------------------- measurement reference */
+
+/* A plain streaming read, the achievable-bandwidth reference against which the layer's weight
+ * streams are measured: reads the first `bytes` bytes of each of the n blocks
+ * base + ids[i] * stride (the access shape of fetching n experts of the fixed-stride store
+ * [SW-mem]) with 16-byte non-temporal loads, each wave a contiguous 16 KiB chunk, and writes one
+ * word per wave to sink (device, at least n * ceil(bytes / 16384) words; its values mean
+ * nothing).  ids: HOST array of n block ids (n <= 64); base device, 16-byte aligned; stride
+ * and bytes multiples of 16.  The caller keeps every block inside its allocation.
+ * Asynchronous on `stream`. */
+int qmoe_read_blocks(const void *base, size_t stride, const int32_t *ids, int32_t n, size_t bytes,
+                     uint32_t *sink, qmoe_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

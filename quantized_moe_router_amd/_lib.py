@@ -6,7 +6,10 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqmoe.so")
+# QMOE_LIBRARY=timeline loads the profiling build (same kernels, plus phase timestamps of the
+# one-token layer, see qmoe_timeline_set); the default is the product library.
+TIMELINE = os.environ.get("QMOE_LIBRARY", "") == "timeline"
+LIB_PATH = os.path.join(_HERE, "libqmoe_timeline.so" if TIMELINE else "libqmoe.so")
 
 QMOE_OK = 0
 ERRORS = {-1: "QMOE_ERR_ARG", -2: "QMOE_ERR_SHAPE", -3: "QMOE_ERR_WORKSPACE",
@@ -19,6 +22,7 @@ EXPORTS = [
     "qmoe_event_create", "qmoe_event_destroy", "qmoe_event_record", "qmoe_event_elapsed_ms",
     "qmoe_set_profile_events", "qmoe_workspace_status", "qmoe_cache_create", "qmoe_cache_destroy",
     "qmoe_cache_plan", "qmoe_cache_stats", "qmoe_layer_forward_tiered", "qmoe_decode_stack",
+    "qmoe_read_blocks",
 ]
 MAX_STACK = 64
 
@@ -92,7 +96,10 @@ def lib():
         "qmoe_layer_forward_tiered": (ctypes.c_int, [ctypes.POINTER(Layer), P, P, I32, P, P, P, P, P,
                                                      SZ, P]),
         "qmoe_decode_stack": (ctypes.c_int, [ctypes.POINTER(Layer), I32, P, P, P, P, P, P, SZ, P]),
+        "qmoe_read_blocks": (ctypes.c_int, [P, SZ, ctypes.POINTER(I32), I32, SZ, P, P]),
     }
+    if TIMELINE:
+        sig["qmoe_timeline_set"] = (ctypes.c_int, [P])
     for name, (res, args) in sig.items():
         f = getattr(L, name)
         f.restype = res

@@ -12,8 +12,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libqmoe.so")
+LIB_TIMELINE = os.path.join(HERE, "libqmoe_timeline.so")   # profiling build (phase timestamps)
 SOURCES = ["qmoe.hip"]
-HEADERS = ["common.h", "store.h", "router.h", "router_mf.h", "ffn.h", "mfma.h", "decode.h"]
+HEADERS = ["common.h", "store.h", "router.h", "router_mf.h", "ffn.h", "mfma.h", "decode.h", "cache.h",
+           "diag.h"]
 
 
 def hipcc():
@@ -36,8 +38,12 @@ def flags():
     ]
 
 
-def build(verbose=False):
-    cmd = [hipcc()] + flags() + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", LIB + ".tmp"]
+def build(verbose=False, timeline=False):
+    """Compile libqmoe.so (or, with timeline, the profiling build libqmoe_timeline.so: the same
+    sources with QMOE_TIMELINE defined)."""
+    out = LIB_TIMELINE if timeline else LIB
+    extra = ["-DQMOE_TIMELINE"] if timeline else []
+    cmd = [hipcc()] + flags() + extra + [os.path.join(CSRC, s) for s in SOURCES] + ["-o", out + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -45,9 +51,10 @@ def build(verbose=False):
                      if "packed-fp32-ops" not in l and "is not a recognized feature" not in l)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + errs)
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, timeline=True))

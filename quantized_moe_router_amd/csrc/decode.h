@@ -46,13 +46,41 @@
 
 namespace qmoe {
 
+// Phase timestamps (only in the library built with QMOE_TIMELINE, for profiling): thread 0 of
+// a workgroup records the device's 100 MHz clock at numbered points of its role into
+// tl[block * TL_POINTS + point], and the role's number at point TL_ROLE.  Points: 0 start;
+// router 1 logits published; shared gate/up 1 x staged; routed gate/up 1 x staged, 2 expert
+// known, 3 weights consumed; shared down 1 router seen, 2 weights in, 3 h staged; routed down
+// 1 top-k known, 2 weights in, 3 h staged, 4 products done, 5 combine inputs in (last slot);
+// every role 6 end.
+constexpr int TL_POINTS = 8, TL_ROLE = 7;
+enum : int { TL_R = 1, TL_SG = 2, TL_RG = 3, TL_SD = 4, TL_RD = 5 };
+#ifdef QMOE_TIMELINE
+#define QMOE_TL(a, point)                                                                  \
+  do {                                                                                     \
+    if (threadIdx.x == 0 && (a).tl) (a).tl[(size_t)blockIdx.x * TL_POINTS + (point)] = wall_clock64(); \
+  } while (0)
+#define QMOE_TL_ROLE(a, role)                                                              \
+  do {                                                                                     \
+    if (threadIdx.x == 0 && (a).tl) (a).tl[(size_t)blockIdx.x * TL_POINTS + TL_ROLE] = (role); \
+  } while (0)
+#else
+#define QMOE_TL(a, point) \
+  do {                    \
+  } while (0)
+#define QMOE_TL_ROLE(a, role) \
+  do {                        \
+  } while (0)
+#endif
+
 // Sync area of the workspace (zero-initialised, one 256-byte line each)
 constexpr int SY_LINE = 64;                    // words per line
 enum : int { SY_EPOCH = 0, SY_STATUS = 1, SY_DONE = 2, SY_LINES = 3 };
 constexpr int MAX_STACK = 64;                  // layers of one chained launch
 constexpr unsigned WAIT_LIMIT = 1u << 20;      // polls: well over a second
 constexpr int DEC_W = 4;                       // waves per workgroup (every role)
-constexpr int KB_DEC = 12;                     // k-steps a wave holds in registers
+constexpr int KB_DEC = 12;                     // k-steps a down wave holds in registers
+constexpr int KB_GU = 12;                      // k-steps a gate/up wave loads per batch
 constexpr int DEC_THREADS = DEC_W * WAVE;
 // Values that many workgroups wait for are published in several copies, each on its own
 // memory pages, and a reader polls one of them, so that polling does not pile onto a few
@@ -99,6 +127,7 @@ struct DecodeArgs {
   uint64_t *xout;               // [X_COPIES] tagged output for the next layer, or null
   size_t x_copy;                // words between x copies
   unsigned *lcnt;               // arrival counter of the combining workgroups (the SY_DONE line)
+  unsigned long long *tl;       // phase timestamps (QMOE_TIMELINE builds), or null
   int advance;                  // this layer's combining workgroups count their arrivals, and
                                 // the last of them advances the epoch (the launch's last layer)
 };
@@ -211,6 +240,7 @@ QMOE_DEV void dec_fetch_x(const DecodeArgs &a, unsigned ep, uint16_t *dst) {
 // ---------------------------------------------------------------- R: router
 template <bool ST>
 QMOE_DEV void dec_router(const DecodeArgs &a, int rb, unsigned ep, char *smem) {
+  QMOE_TL_ROLE(a, TL_R);
   RouterArgs ra;
   ra.x = a.x; ra.rq = a.rq; ra.rs = a.rs; ra.rb = a.rb; ra.rscale = a.rscale; ra.pes = a.pes;
   ra.lbias = a.lbias; ra.T = 1; ra.H = a.H; ra.E = a.E; ra.k = a.k; ra.inv_sqrt_h = a.inv_sqrt_h;
@@ -418,13 +448,13 @@ QMOE_DEV void dec_gate_up(const DecodeArgs &a, const uint8_t *blk, int tile, uin
   // each batch's k-steps in straight-line chunks of four (steps past the count re-read the
   // last one and add 0), so that their products overlap
   float acc = 0.f;
-  for (int kc = 0; kc < nk; kc += KB_DEC) {
-    qmoe_u32x4 cv[KB_DEC];
-    uint32_t sb[KB_DEC];
-    load_batch<KB_DEC>(tbase, ks0, kc, nk, lane, rr, cv, sb);
-    const int nb = __builtin_amdgcn_readfirstlane(min(KB_DEC, nk - kc));
+  for (int kc = 0; kc < nk; kc += KB_GU) {
+    qmoe_u32x4 cv[KB_GU];
+    uint32_t sb[KB_GU];
+    load_batch<KB_GU>(tbase, ks0, kc, nk, lane, rr, cv, sb);
+    const int nb = __builtin_amdgcn_readfirstlane(min(KB_GU, nk - kc));
 #pragma unroll
-    for (int c = 0; c < KB_DEC; c += 4)
+    for (int c = 0; c < KB_GU; c += 4)
       if (c < nb) {
 #pragma unroll
         for (int u = c; u < c + 4; ++u) {
@@ -435,6 +465,7 @@ QMOE_DEV void dec_gate_up(const DecodeArgs &a, const uint8_t *blk, int tile, uin
       }
   }
   acc += xor32(acc);
+  QMOE_TL(a, 3);
   if (half == 0) red[wv * 32 + rr] = acc;
   __syncthreads();
   if (tid < 16 * H_COPIES) {
@@ -538,11 +569,16 @@ QMOE_DEV void dec_shared_down(const DecodeArgs &a, int b, unsigned ep, char *sme
   // once the first router workgroup has published (so that the router's loads go first; the
   // last one's word comes later and then leaves these loads to compete with the routed gate/up
   // stream), load the weights, then wait for h_shared
+  QMOE_TL_ROLE(a, TL_SD);
   wait_tags(a, a.logits + (size_t)(blockIdx.x % LOGIT_COPIES) * a.logit_copy, 1, 1, ep);
+  QMOE_TL(a, 1);
   DownRegs d;
   dec_down_load(a, a.shared, a.Is, tile, kb0 + w0, w1 - w0, d);
+  drain_memory();
+  QMOE_TL(a, 2);
   dec_stage_h(a, a.h_sh + (size_t)(tile % H_COPIES) * a.hsh_copy + (size_t)g0 * GROUP,
               (g1 - g0) * GROUP, ep, smem, L);
+  QMOE_TL(a, 3);
   dec_down_dot(d, kb0 + w0, g0, a.kshift, smem, L);
   __syncthreads();
   if (threadIdx.x < 32) {
@@ -562,6 +598,7 @@ QMOE_DEV void dec_routed_down(const DecodeArgs &a, int b, unsigned ep, char *sme
   // expert and weight of the slot from the top-k the first routed gate/up workgroup published
   // (selected from the same logits by the same code: these workgroups have time to spare and
   // leave the SIMDs to the gate/up workgroups, whose selection is on the critical path)
+  QMOE_TL_ROLE(a, TL_RD);
   int32_t *tk_e = (int32_t *)(smem + L.tks);
   float *tk_w = (float *)(tk_e + MAX_TOPK);
   const uint64_t *tks = a.tk + (size_t)(blockIdx.x % TK_COPIES) * 2 * MAX_TOPK;
@@ -570,6 +607,7 @@ QMOE_DEV void dec_routed_down(const DecodeArgs &a, int b, unsigned ep, char *sme
                 [&](int i, float v) {
                   if (i < a.k) tk_e[i] = __float_as_int(v); else tk_w[i - a.k] = v;
                 });
+  QMOE_TL(a, 1);
   const int e = min(max(tk_e[slot], 0), a.E - 1);
   const float w = tk_w[slot];
   const int KS = (a.I / GROUP) << a.kshift;
@@ -578,9 +616,13 @@ QMOE_DEV void dec_routed_down(const DecodeArgs &a, int b, unsigned ep, char *sme
   DownRegs d;
   dec_down_load(a, a.experts + (size_t)e * a.stride, a.I, min(tile, tiles_d - 1), kb0,
                 tile < tiles_d ? kb1 - kb0 : 0, d);
+  drain_memory();
+  QMOE_TL(a, 2);
   dec_stage_h(a, a.h_r + (size_t)(g % H_COPIES) * a.hr_copy + (size_t)slot * a.I, a.I, ep, smem, L);
+  QMOE_TL(a, 3);
   dec_down_dot(d, kb0, 0, a.kshift, smem, L);
   __syncthreads();
+  QMOE_TL(a, 4);
   // row r of this group (tile r / 32 of the group): the wpt waves of its tile add up
   const float *red = (const float *)(smem + L.red);
   const int row0 = g * TILE_ROWS * tpw;
@@ -595,6 +637,7 @@ QMOE_DEV void dec_routed_down(const DecodeArgs &a, int b, unsigned ep, char *sme
   }
   if (slot < a.k - 1) {
     if (mine) st_tag(a.y_r + (size_t)slot * a.H + row0 + r, ep, yv);
+    QMOE_TL(a, 6);
     return;
   }
   // last slot: combine the rows of this group.  The residual rows, the gain and the layer
@@ -622,6 +665,7 @@ QMOE_DEV void dec_routed_down(const DecodeArgs &a, int b, unsigned ep, char *sme
                                        : a.y_sh + (size_t)(s - (a.k - 1)) * a.H + row0 + rw;
                 },
                 [&](int i, float v) { comb[i] = v; });
+  QMOE_TL(a, 5);
   // Arrival of this combining workgroup, issued now and read at the end.  Once every
   // combining workgroup has its inputs, every workgroup of the launch has published its part
   // and so has read the epoch: the last to arrive may advance it.  (No drain first: the
@@ -681,6 +725,7 @@ QMOE_DEV void dec_routed_down(const DecodeArgs &a, int b, unsigned ep, char *sme
     __hip_atomic_store(a.lcnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     st_sys_u(sy(a, SY_EPOCH), ep);
   }
+  QMOE_TL(a, 6);
 }
 
 // Block b (of one layer) with tag ep.
@@ -688,26 +733,43 @@ template <bool ST>
 QMOE_DEV void decode_block(const DecodeArgs &a, int b, unsigned ep, char *smem) {
   const int Kc_sh = a.shared ? GROUP * ((a.Is / GROUP + a.nc - 1) / a.nc) : 0;
   const DecLds L = dec_lds(a.H, a.E, a.k, a.I, Kc_sh, a.nc, a.wpt);
-  if (b < a.nR) { dec_router<ST>(a, b, ep, smem); return; }
+  QMOE_TL(a, 0);
+  if (b < a.nR) {
+    dec_router<ST>(a, b, ep, smem);
+    QMOE_TL(a, 1);
+    QMOE_TL(a, 6);
+    return;
+  }
   b -= a.nR;
   if (b < a.nSG) {
+    QMOE_TL_ROLE(a, TL_SG);
     dec_stage_x<ST>(a, ep, smem, L);
     __syncthreads();   // (no wait for the router: measured slightly faster than letting it go first)
+    QMOE_TL(a, 1);
     dec_gate_up(a, a.shared, b, a.h_sh, a.hsh_copy, ep, smem, L);
+    QMOE_TL(a, 6);
     return;
   }
   b -= a.nSG;
   if (b < a.nRG) {
+    QMOE_TL_ROLE(a, TL_RG);
     const int tiles_r = a.I / 16;
     const int slot = b / tiles_r, tile = b % tiles_r;
     dec_stage_x<ST>(a, ep, smem, L);
+    QMOE_TL(a, 1);
     const int e = dec_topk(a, ep, slot, b == 0, smem, L);
+    QMOE_TL(a, 2);
     dec_gate_up(a, a.experts + (size_t)e * a.stride, tile, a.h_r + (size_t)slot * a.I, a.hr_copy, ep,
                 smem, L);
+    QMOE_TL(a, 6);
     return;
   }
   b -= a.nRG;
-  if (b < a.nSD) { dec_shared_down(a, b, ep, smem, L); return; }
+  if (b < a.nSD) {
+    dec_shared_down(a, b, ep, smem, L);
+    QMOE_TL(a, 6);
+    return;
+  }
   b -= a.nSD;
   if (b < a.nRD) dec_routed_down<ST>(a, b, ep, smem, L);
 }

@@ -19,6 +19,7 @@
 #include "decode.h"
 #include "router_mf.h"
 #include "cache.h"
+#include "diag.h"
 
 using namespace qmoe;
 
@@ -33,6 +34,9 @@ constexpr int DEC_SYNC_WORD = 32768;       // first word of the one-token decode
 constexpr int MAX_T = 65536;
 
 thread_local std::string g_err;
+#ifdef QMOE_TIMELINE
+thread_local unsigned long long *g_tl = nullptr;   // phase timestamps of the next one-token call
+#endif
 thread_local hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
 
 int fail(int code, const char *fmt, ...) {
@@ -491,6 +495,9 @@ static DecodeArgs make_decode_args(const qmoe_layer *L, const uint16_t *x, uint1
   a.nRD = a.k * ((tiles_d + tpw - 1) / tpw);
   a.lcnt = a.sync + (size_t)SY_DONE * SY_LINE;
   a.advance = 1;
+#ifdef QMOE_TIMELINE
+  a.tl = g_tl;
+#endif
   return a;
 }
 
@@ -1038,6 +1045,44 @@ int qmoe_workspace_status(const void *ws, size_t ws_bytes, int32_t *status_out,
   QMOE_HIP(hipMemcpyAsync(&v, p, sizeof v, hipMemcpyDeviceToHost, (hipStream_t)stream));
   QMOE_HIP(hipStreamSynchronize((hipStream_t)stream));
   *status_out = (int32_t)v;
+  return ok();
+}
+
+#ifdef QMOE_TIMELINE
+// Timeline builds only: device buffer of TL_POINTS 64-bit words per workgroup that the next
+// one-token layer calls on this thread (and the launches captured from them) write their phase
+// timestamps to (NULL: none).
+int qmoe_timeline_set(void *buf) {
+  g_tl = (unsigned long long *)buf;
+  return ok();
+}
+#endif
+
+int qmoe_read_blocks(const void *base, size_t stride, const int32_t *ids, int32_t n, size_t bytes,
+                     uint32_t *sink, qmoe_stream_t stream) {
+  if (!base || !ids || !sink) return fail(QMOE_ERR_ARG, "read_blocks: NULL pointer");
+  if (n < 0 || n > READ_MAX_BLOCKS)
+    return fail(QMOE_ERR_SHAPE, "read_blocks: n must be in [0, %d] (got %d)", READ_MAX_BLOCKS, n);
+  if (bytes % 16 || !aligned(base, 16) || stride % 16)
+    return fail(QMOE_ERR_ARG, "read_blocks: base, stride and bytes must be multiples of 16");
+  if (n == 0 || bytes == 0) return ok();
+  int rc = check_arch();
+  if (rc) return rc;
+  ReadArgs a;
+  memset(&a, 0, sizeof a);
+  a.base = (const uint8_t *)base;
+  a.stride = stride;
+  a.bytes = bytes;
+  a.n = n;
+  for (int i = 0; i < n; ++i) {
+    if (ids[i] < 0) return fail(QMOE_ERR_ARG, "read_blocks: negative block id");
+    a.ids[i] = ids[i];
+  }
+  a.sink = sink;
+  const size_t waves = stream_read_waves(bytes, n);
+  hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0,
+                     (hipStream_t)stream, a);
+  QMOE_LAUNCHED();
   return ok();
 }
 

@@ -288,3 +288,28 @@ def workspace_status(ws):
     v = ctypes.c_int32()
     check(lib().qmoe_workspace_status(_ptr(ws, 1, "ws"), ws.numel(), ctypes.byref(v), _stream()))
     return v.value
+
+
+def timeline_set(buf):
+    """Profiling build only (QMOE_LIBRARY=timeline): device tensor of 8 int64 words per
+    workgroup that the next one-token layer calls on this thread write their phase timestamps
+    to (None: stop)."""
+    L = lib()
+    from . import _lib as _L
+    if not hasattr(L, "qmoe_timeline_set") or not _L.TIMELINE:
+        raise RuntimeError("timeline_set needs the profiling build (QMOE_LIBRARY=timeline)")
+    check(L.qmoe_timeline_set(None if buf is None else ctypes.c_void_p(buf.data_ptr())))
+
+
+def read_blocks(base, stride, ids, nbytes, sink):
+    """Plain streaming read of the first nbytes of blocks base + ids[i] * stride (measurement
+    reference); sink: int32 device tensor of at least len(ids) * ceil(nbytes / 16384) words."""
+    n = len(ids)
+    waves = n * ((nbytes + 16383) // 16384)
+    if sink.numel() < waves or sink.element_size() != 4:
+        raise ValueError("sink too small")
+    if n and (max(ids) + 1) * stride - stride + nbytes > base.numel() * base.element_size():
+        raise ValueError("a block lies outside the buffer")
+    arr = (ctypes.c_int32 * max(n, 1))(*ids)
+    check(lib().qmoe_read_blocks(ctypes.c_void_p(base.data_ptr()), stride, arr, n, nbytes,
+                                 ctypes.c_void_p(sink.data_ptr()), _stream()))
