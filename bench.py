@@ -16,7 +16,11 @@ writing its own output.
 Prints one JSON line with the throughput, the roofline of the dominant kernel (for one token
 the single layer kernel; for more tokens the routed gate/up kernel), timed with HIP events on
 the stream it runs on inside the timed region, and the CPU oracle timed on a bounded sample
-on the host.
+on the host.  Beside the headline it reports every other workload at its configured size
+("configs": the tiny layer, the Gemma-shaped prefill chunk, the 48-layer Qwen3-Next-shaped
+stack at batch 1 and 16, the 40-layer Qwen3.6-shaped stack with one 10,240-token prompt per
+layer and its bucket sizes, int8 experts), each with its dominant kernel's roofline and the
+oracle timed on a bounded sample, and the plain streaming-read reference.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -251,14 +255,155 @@ def run_decode(args, cfg, layers):
     tok_s_layer = T * L / (ms_step / 1e3)
     layer_s = ms_step / 1e3 / L
     kern_gbps = kern_bytes / (kern_ms / 1e3) / 1e9
+    # credited (routed-only) bytes of the dominant kernel
+    kern_credited = credited if T == 1 else n_dist * 2 * G.matrix_bytes(cfg.inter, H)
     return dict(
         ms_step=ms_step, ms_plain=ms_plain, tok_s_layer=tok_s_layer, L=L, T=T, status=status,
         kern_ms=kern_ms, kern_bytes=kern_bytes, kern_gbps=kern_gbps, kernel=kernel,
+        kern_credited=kern_credited,
         layer_credited_gbps=credited / layer_s / 1e9,
         layer_all_gbps=all_bytes / layer_s / 1e9,
         credited=credited, all_bytes=all_bytes, distinct=n_dist, timing_src=timing_src,
-        traffic=traffic,
+        traffic=traffic, buckets=bucket_histogram([i.cpu().numpy() for i in idx], cfg.experts)
+        if T > 1 else None,
     )
+
+
+def bucket_histogram(idx_layers, E, chunk=128):
+    """Bucket sizes of the routing (rows per expert per chunk of at most 128 tokens): the mean
+    and the maximum over chunks of the largest bucket, the mean number of non-empty buckets and
+    the mean rows per non-empty bucket."""
+    import numpy as np
+    mx, ne, rows = [], [], []
+    for idx in idx_layers:
+        for c0 in range(0, idx.shape[0], chunk):
+            cnt = np.bincount(idx[c0:c0 + chunk].ravel(), minlength=E)
+            mx.append(int(cnt.max()))
+            ne.append(int((cnt > 0).sum()))
+            rows.append(float(cnt[cnt > 0].mean()))
+    return {"chunks": len(mx), "max_bucket_mean": round(float(np.mean(mx)), 2),
+            "max_bucket_max": int(np.max(mx)), "nonempty_mean": round(float(np.mean(ne)), 2),
+            "rows_per_nonempty_mean": round(float(np.mean(rows)), 2)}
+
+
+def config_entry(d, cfg, note=None):
+    """One workload's line: throughput per MoE layer and the dominant kernel's roofline."""
+    from workloads import gen as G
+    e = {"workload": f"{cfg.name}: hidden {cfg.hidden}, {cfg.experts} experts top-{cfg.top_k}, "
+                     f"expert inter {cfg.inter}, shared inter {cfg.shared_inter}, "
+                     f"{cfg.expert_bits}-bit experts, {d['L']} stacked layers (of {cfg.layers}), "
+                     f"{d['T']} tokens per call",
+         "tokens_per_s_per_layer": round(d["tok_s_layer"], 1),
+         "us_per_layer_call": round(d["ms_step"] * 1e3 / d["L"], 3),
+         "credited_GBps": round(d["layer_credited_gbps"], 1),
+         "distinct_experts_per_call": round(d["distinct"], 2),
+         "roofline": {"bound": "hbm", "kernel": d["kernel"],
+                      "achieved": round(d["kern_credited"] / (d["kern_ms"] / 1e3) / 1e9, 1),
+                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                      "frac": round(d["kern_credited"] / (d["kern_ms"] / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+                      "bytes": "credited routed bytes of the kernel",
+                      "all_bytes_frac": round((d["all_bytes"] if d["T"] == 1 else d["kern_bytes"])
+                                              / (d["kern_ms"] / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+                      "avg_launch_us": round(d["kern_ms"] * 1e3, 3), "timing": d["timing_src"]}}
+    if d.get("buckets"):
+        e["buckets"] = d["buckets"]
+    if note:
+        e["note"] = note
+    return e
+
+
+def run_long_prefill(args, cfg, layers):
+    """The long prompt of the Zipf-biased Qwen3.6-shaped config: one prompt of cfg.prompt tokens
+    through every layer of the stack, each layer call taking the whole prompt (processed per
+    128-token chunk inside the call), all layers in one graph.  Every layer gets its own N(0,1)
+    prompt states.  The dominant kernel (routed + shared gate/up) is timed with HIP event nodes
+    around it in a graph of one 128-token chunk of each layer's prompt."""
+    import numpy as np
+    import torch
+    from quantized_moe_router_amd import ops
+    from workloads import gen as G
+    import stacks
+    L, P, H, k = len(layers), cfg.prompt, cfg.hidden, cfg.top_k
+    ws = ops.workspace(layers[0][0].dims, min(P, 128))
+    xs = [stacks.hidden(cfg, 500 + l, P)[1] for l in range(L)]
+    out = torch.empty(P, H, dtype=torch.bfloat16, device="cuda")
+    idx = [torch.empty(P, k, dtype=torch.int32, device="cuda") for _ in range(L)]
+    for l, (pl, _) in enumerate(layers):
+        ops.layer_forward(pl.weights, xs[l], ws, out=out, topk_idx=idx[l])
+    torch.cuda.synchronize()
+    idx_n = [i.cpu().numpy() for i in idx]
+    buckets = bucket_histogram(idx_n, cfg.experts)
+    distinct = float(np.mean([len(np.unique(i[c:c + 128])) for i in idx_n for c in range(0, P, 128)]))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for l, (pl, _) in enumerate(layers):
+            ops.layer_forward(pl.weights, xs[l], ws, out=out)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = 2
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    sec = (time.perf_counter() - t0) / reps
+    n_chunks = (P + 127) // 128
+    chunk_layer_s = sec / (L * n_chunks)
+    # the dominant kernel, one chunk per layer (the event pair around layer s's gate/up kernel)
+    evs = [(ops.Event(), ops.Event()) for _ in range(L)]
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2):
+        for l, (pl, _) in enumerate(layers):
+            ops.set_profile_events(*evs[l])
+            ops.layer_forward(pl.weights, xs[l][40 * 128:41 * 128], ws, out=out[:128])
+            ops.set_profile_events(None, None)
+    g2.replay()
+    torch.cuda.synchronize()
+    g2.replay()
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([a.elapsed_ms(b) for a, b in evs]))
+    d40 = float(np.mean([len(np.unique(i[40 * 128:41 * 128])) for i in idx_n]))
+    kern_credited = d40 * 2 * G.matrix_bytes(cfg.inter, H)
+    kern_all = kern_credited + 2 * G.matrix_bytes(cfg.shared_inter, H)
+    credited = G.credited_expert_bytes(cfg, distinct)
+    return {"workload": f"{cfg.name}: hidden {H}, {cfg.experts} experts top-{k} with the Zipf("
+                        f"{cfg.zipf_s}) router bias, expert inter {cfg.inter}, shared inter "
+                        f"{cfg.shared_inter}, {L} stacked layers, one {P}-token prompt per layer "
+                        f"({n_chunks} chunks of 128 tokens per layer call)",
+            "tokens_per_s_per_layer": round(P / (sec / L), 1),
+            "us_per_chunk_layer": round(chunk_layer_s * 1e6, 3),
+            "prompt_ms_all_layers": round(sec * 1e3, 3),
+            "credited_GBps": round(credited / chunk_layer_s / 1e9, 1),
+            "distinct_experts_per_chunk": round(distinct, 2), "buckets": buckets,
+            "roofline": {"bound": "hbm", "kernel": "gu_pf_kernel (routed and shared gate/up + "
+                         "SwiGLU, matrix cores)",
+                         "achieved": round(kern_credited / (kern_ms / 1e3) / 1e9, 1),
+                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(kern_credited / (kern_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "bytes": "credited routed bytes of the kernel",
+                         "all_bytes_frac": round(kern_all / (kern_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+                         "avg_launch_us": round(kern_ms * 1e3, 3),
+                         "timing": f"HIP event nodes around the kernel of chunk 40 of each of the {L} "
+                                   "layers' prompts, one graph"}}
+
+
+def oracle_sample(cfg, samples):
+    """The oracle on the host, timed on `samples` = [(layer, step, tokens)]: median seconds per
+    call (drawing the synthetic experts excluded)."""
+    import numpy as np
+    import oracle as O
+    from workloads import gen as G
+    times = []
+    for layer, step, T in samples:
+        x = G.make_hidden(cfg, step, T)
+        li = G.make_router(cfg, layer)
+        top, _, _ = O.router(x, li, cfg.top_k)
+        li.prefetch(np.unique(top))
+        li.shared()
+        t0 = time.perf_counter()
+        r = O.layer_forward(x, li, cfg.top_k)
+        times.append(time.perf_counter() - t0)
+        assert r["out"].shape == x.shape
+    return float(np.median(times))
 
 
 def run_read_ceiling(layers, cfg, reps=5):
@@ -414,27 +559,61 @@ def run_chain(layers, cfg, steps):
             "outputs_equal_chained_calls": same, "layers": L}
 
 
-def run_other_configs(n_layers, steps):
-    """Per-layer time of the other workload shapes on a short stack of their own layers."""
-    from quantized_moe_router_amd import ops
+def run_other_configs(args):
+    """The other workloads at their configured sizes (each stack built, timed and freed in
+    turn), each with its oracle timed on a bounded sample."""
+    import torch
     from workloads import gen as G
     res = {}
-    for name, src in [("qwen3_next_80b_a3b_decode_b1", None),
-                      ("qwen3_next_80b_a3b_decode_b16", "qwen3_next_80b_a3b_decode_b1"),
-                      ("qwen3_6_35b_a3b_long_prefill", None),
-                      ("gemma4_26b_a4b_int8_decode", None)]:
-        cfg = G.config(name)
-        layers = build_stack(G.config(src or name), n_layers)
-        xs = [x for x in layer_inputs(cfg, 0, n_layers, cfg.tokens)]
-        ws = ops.workspace(layers[0][0].dims, cfg.tokens)
-        sec = time_stack(ops, [pl.weights for pl, _ in layers], xs, ws, steps)
-        res[name] = {"tokens_per_call": cfg.tokens, "us_per_layer_call": round(sec * 1e6, 2),
-                     "tokens_per_s_per_layer": round(cfg.tokens / sec, 1),
-                     "expert_bits": cfg.expert_bits,
-                     "stack": f"{n_layers} layers of this shape (of {cfg.layers})"}
-        del layers, xs, ws
-        import torch
+
+    def cpu(cfg, samples, unit, what):
+        if args.no_cpu_baseline:
+            return None
+        sec = oracle_sample(cfg, samples)
+        return {"value": round(samples[0][2] / sec, 3), "unit": f"tokens/s per MoE layer ({unit})",
+                "s_per_call": round(sec, 4), "kind": "oracle", "sample": what}
+
+    def done(*stacks_):
+        for st in stacks_:
+            del st[:]
         torch.cuda.empty_cache()
+
+    # tiny single layer, 4 tokens (the whole configuration)
+    c1 = G.config("tiny")
+    log("tiny layer")
+    lay = build_stack(c1, 1)
+    res[c1.name] = config_entry(run_decode(args, c1, lay), c1)
+    res[c1.name]["cpu_baseline"] = cpu(c1, [(0, s, 4) for s in range(5)], "4-token call",
+                                       "the 4-token call, 5 inputs, median")
+    done(lay)
+    # Qwen3-Next-shaped stack, 48 layers (43.5 GB), batch 1 and batch 16
+    b1, b16 = G.config("qwen3_next_80b_a3b_decode_b1"), G.config("qwen3_next_80b_a3b_decode_b16")
+    log(f"{b1.name}: building {b1.layers} layers")
+    lay = build_stack(b1, b1.layers)
+    for c, smp, unit, what in [(b1, [(l, l, 1) for l in range(4)], "token-layer",
+                                "layers 0..3, one token each, median"),
+                               (b16, [(0, 0, 16)], "16-token step-layer",
+                                "layer 0, one 16-token step")]:
+        log(f"{c.name} timing")
+        res[c.name] = config_entry(run_decode(args, c, lay), c)
+        res[c.name]["cpu_baseline"] = cpu(c, smp, unit, what)
+    done(lay)
+    # Qwen3.6-shaped long prefill: 40 layers, one 10,240-token prompt per layer
+    c5 = G.config("qwen3_6_35b_a3b_long_prefill")
+    log(f"{c5.name}: building {c5.layers} layers")
+    lay = build_stack(c5, c5.layers)
+    log(f"{c5.name}: {c5.prompt}-token prompt")
+    res[c5.name] = run_long_prefill(args, c5, lay)
+    res[c5.name]["cpu_baseline"] = cpu(c5, [(0, 500, 128)], "128-token chunk-layer",
+                                       "chunk 0 of layer 0's prompt")
+    done(lay)
+    # int8 experts (Gemma-4 shape), a 4-layer stack
+    c8 = G.config("gemma4_26b_a4b_int8_decode")
+    log(f"{c8.name}: 4 layers")
+    lay = build_stack(c8, 4)
+    res[c8.name] = config_entry(run_decode(args, c8, lay), c8,
+                                note="int8 experts, a 4-layer stack of the 30-layer shape")
+    done(lay)
     return res
 
 
@@ -473,46 +652,6 @@ def run_tiered(layers, cfg, slots, steps):
                 copied_MB_per_layer=round(copied / 1e6, 2),
                 host_to_device_GBps=round(copied / sec / 1e9, 1),
                 stack=f"first {len(layers)} layers, 1 token per step, {steps} steps")
-
-
-def run_prefill(layers, cfg_pf, reps=3):
-    """One 128-token chunk per layer through the same stack (prefill shape), graph-replayed."""
-    import numpy as np
-    import torch
-    from quantized_moe_router_amd import ops
-    from workloads import gen as G
-
-    L = len(layers)
-    T, H = cfg_pf.tokens, cfg_pf.hidden
-    dims = layers[0][0].dims
-    ws = ops.workspace(dims, T)
-    outs = [torch.empty(T, H, dtype=torch.bfloat16, device="cuda") for _ in range(L)]
-    xs = [layer_inputs(cfg_pf, 100 + r, L, T) for r in range(reps + 1)]
-    idx = [torch.empty(T, cfg_pf.top_k, dtype=torch.int32, device="cuda") for _ in range(L)]
-    for l, (pl, _) in enumerate(layers):
-        ops.layer_forward(pl.weights, xs[0][l], ws, out=outs[l], topk_idx=idx[l])
-    torch.cuda.synchronize()
-    distinct = [len(np.unique(i.cpu().numpy())) for i in idx]
-    # one graph per input set (the chunk through every layer), replayed as the decode stack is
-    graphs = []
-    for r in range(reps):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for l, (pl, _) in enumerate(layers):
-                ops.layer_forward(pl.weights, xs[r + 1][l], ws, out=outs[l])
-        graphs.append(g)
-    for g in graphs:
-        g.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for g in graphs:
-        g.replay()
-    torch.cuda.synchronize()
-    ms_chunk_stack = (time.perf_counter() - t0) * 1e3 / reps
-    layer_s = ms_chunk_stack / 1e3 / L
-    credited = G.credited_expert_bytes(cfg_pf, float(np.mean(distinct)))
-    return dict(tok_s_layer=T / layer_s, us_per_chunk_layer=layer_s * 1e6,
-                credited_gbps=credited / layer_s / 1e9, distinct_mean=float(np.mean(distinct)))
 
 
 def cpu_baseline(cfg, n_samples):
@@ -710,10 +849,19 @@ def main():
         ceiling = run_read_ceiling(layers, cfg)
         log(f"read ceiling: {ceiling['us_per_read']} us per {ceiling['bytes_per_read'] / 1e6:.2f} MB "
             f"= {ceiling['GBps']} GB/s; 1 GiB contiguous {ceiling['contiguous_1GiB_GBps']} GB/s")
-    pf = None
+    configs = {}
     if not args.no_prefill and cfg.name == "gemma4_26b_a4b_decode":
-        log("prefill timing")
-        pf = run_prefill(layers, G.config("gemma4_26b_a4b_prefill"))
+        log("prefill timing (one 128-token chunk per layer of the same stack)")
+        cfg_pf = G.config("gemma4_26b_a4b_prefill")
+        dp = run_decode(args, cfg_pf, layers)
+        configs[cfg_pf.name] = config_entry(dp, cfg_pf)
+        log(f"prefill: {dp['ms_step'] * 1e3 / dp['L']:.1f} us per chunk-layer, gu_pf_kernel "
+            f"{dp['kern_ms'] * 1e3:.1f} us")
+        if not args.no_cpu_baseline:
+            sec = oracle_sample(cfg_pf, [(0, 100, 128)])
+            configs[cfg_pf.name]["cpu_baseline"] = {
+                "value": round(128 / sec, 3), "unit": "tokens/s per MoE layer (128-token chunk-layer)",
+                "s_per_call": round(sec, 4), "kind": "oracle", "sample": "one 128-token chunk of layer 0"}
     post = other = tiered = chain = None
     if not args.no_extra and cfg.tokens == 1:
         log("post-combine norm stack timing")
@@ -725,12 +873,14 @@ def main():
         if cfg.name == "gemma4_26b_a4b_decode":
             log("tiered residency (16 slots per layer)")
             tiered = run_tiered(layers[:4], cfg, 16, args.steps)
-            log("other workload shapes (4-layer stacks)")
-            other = run_other_configs(4, args.steps)
     cb = None
     if not args.no_cpu_baseline:
         log("cpu oracle timing")
         cb = cpu_baseline(cfg, args.cpu_sample)
+    if not args.no_extra and cfg.name == "gemma4_26b_a4b_decode":
+        del layers
+        torch.cuda.empty_cache()
+        configs.update(run_other_configs(args))
     out = {
         "metric": METRIC,
         "value": round(d["tok_s_layer"], 1),
@@ -779,14 +929,8 @@ def main():
     if ceiling:
         out["read_ceiling"] = ceiling
         out["roofline"]["frac_of_read_ceiling"] = round(d["kern_gbps"] / ceiling["GBps"], 4)
-    if pf:
-        out["prefill"] = {
-            "workload": "gemma4_26b_a4b_prefill: one 128-token chunk through the same stack (graph replay)",
-            "tokens_per_s_per_layer": round(pf["tok_s_layer"], 1),
-            "us_per_chunk_layer": round(pf["us_per_chunk_layer"], 2),
-            "credited_GBps": round(pf["credited_gbps"], 1),
-            "distinct_experts_per_chunk": round(pf["distinct_mean"], 2),
-        }
+    if configs:
+        out["configs"] = configs
     if post:
         out["post_combine_norm"] = {
             "workload": f"{cfg.name} with the post-combine RMS norm (gain) and layer scalar",
@@ -800,8 +944,7 @@ def main():
     if tiered:
         out["tiered_residency"] = dict(tiered, workload=f"{cfg.name}: routed experts in pinned host "
                                        "memory, LFU-with-recency device cache per layer")
-    if other:
-        out["other_workloads"] = other
+
     if cb:
         out["cpu_baseline"] = cb
     print(json.dumps(out), flush=True)
