@@ -247,6 +247,20 @@ int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16
                        float *topk_w_or_null, void *ws, size_t ws_bytes,
                        qmoe_stream_t stream);
 
+/* qmoe_layer_forward without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments, arithmetic and results (bit for bit) as qmoe_layer_forward; the workspace is a
+ * fixed 32 MiB device array inside the library, one per GPU it runs on, held until the process
+ * ends (zero when the library is loaded, left ready for the next call by every call).  Calls no
+ * allocator.  Fails with QMOE_ERR_WORKSPACE, before enqueueing anything, when the shape needs
+ * more scratch than that (qmoe_workspace_bytes(&L->d, min(T, 128)) > 32 MiB; every shape of
+ * this library's configured models needs at most about 18 MiB).  All calls on one GPU share
+ * that GPU's array: calls that overlap on one GPU (different streams or threads, not ordered)
+ * race and must not be issued; calls ordered on one stream are fine. */
+int qmoe_layer_forward_noalloc(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16_t *out,
+                               float *out_f32_or_null, int32_t *topk_idx_or_null,
+                               float *topk_w_or_null, qmoe_stream_t stream);
+
 /* ---------------------------------------------------------------- chained one-token layers */
 
 #define QMOE_MAX_STACK 64

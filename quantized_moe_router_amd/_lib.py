@@ -22,7 +22,7 @@ EXPORTS = [
     "qmoe_event_create", "qmoe_event_destroy", "qmoe_event_record", "qmoe_event_elapsed_ms",
     "qmoe_set_profile_events", "qmoe_workspace_status", "qmoe_cache_create", "qmoe_cache_destroy",
     "qmoe_cache_plan", "qmoe_cache_stats", "qmoe_layer_forward_tiered", "qmoe_decode_stack",
-    "qmoe_read_blocks",
+    "qmoe_read_blocks", "qmoe_layer_forward_noalloc",
 ]
 MAX_STACK = 64
 
@@ -97,6 +97,7 @@ def lib():
                                                      SZ, P]),
         "qmoe_decode_stack": (ctypes.c_int, [ctypes.POINTER(Layer), I32, P, P, P, P, P, P, SZ, P]),
         "qmoe_read_blocks": (ctypes.c_int, [P, SZ, ctypes.POINTER(I32), I32, SZ, P, P]),
+        "qmoe_layer_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(Layer), P, I32, P, P, P, P, P]),
     }
     if TIMELINE:
         sig["qmoe_timeline_set"] = (ctypes.c_int, [P])

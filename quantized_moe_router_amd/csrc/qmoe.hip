@@ -749,17 +749,16 @@ int qmoe_combine_post(const qmoe_dims *d, const uint16_t *x, const float *y, con
   return ok();
 }
 
-int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16_t *out,
+}  // extern "C"
+
+namespace {
+
+// The layer on workspace ws (validated by the caller), per chunk of at most CHUNK_TOKENS tokens.
+int layer_forward_impl(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16_t *out,
                        float *out_f32_or_null, int32_t *topk_idx_or_null, float *topk_w_or_null,
-                       void *ws, size_t ws_bytes, qmoe_stream_t stream) {
-  int rc = check_layer(L);
-  if (rc || (rc = check_T(T))) return rc;
-  if (T == 0) return ok();
-  if (!x || !out) return fail(QMOE_ERR_ARG, "layer_forward: x/out must not be NULL");
-  if (!aligned(x, 16)) return fail(QMOE_ERR_ARG, "x must be 16-byte aligned");
+                       void *ws, qmoe_stream_t stream) {
+  int rc;
   const int Tc_max = std::min<int>(T, CHUNK_TOKENS);
-  if ((rc = check_ws(&L->d, Tc_max, ws, ws_bytes))) return rc;
-  if ((rc = check_arch())) return rc;
   const qmoe_dims *d = &L->d;
   hipStream_t s = (hipStream_t)stream;
   const WsLayout wl = ws_layout(d, Tc_max);
@@ -828,6 +827,79 @@ int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16
     }
   }
   return ok();
+}
+
+// Arguments of a layer call, checked on the host before any device call.
+int check_layer_call(const qmoe_layer *L, const uint16_t *x, int32_t T, const uint16_t *out) {
+  int rc = check_layer(L);
+  if (rc || (rc = check_T(T))) return rc;
+  if (T == 0) return QMOE_OK;
+  if (!x || !out) return fail(QMOE_ERR_ARG, "layer_forward: x/out must not be NULL");
+  if (!aligned(x, 16)) return fail(QMOE_ERR_ARG, "x must be 16-byte aligned");
+  return QMOE_OK;
+}
+
+// ------------------------------------------------------------ allocation-free variant
+// Workspace of qmoe_layer_forward_noalloc: one fixed device array, a copy of which every GPU the
+// library runs on holds until the process ends.  Like every device global without an
+// initialiser it is zero when the code object is loaded, which is the state a new workspace
+// must start in; every call leaves it ready for the next one (counters back at zero, the epoch
+// of the one-token path advanced).  Host code never uses the array's name as an address: the
+// device address comes from hipGetSymbolAddress, once per device.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64] = {};
+
+// The current device's address of `scratch` (looked up on its first use on that device).
+int scratch_address(void **out) {
+  int dev = 0;
+  QMOE_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) return fail(QMOE_ERR_ARCH, "device ordinal %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(QMOE_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return QMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qmoe_layer_forward(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16_t *out,
+                       float *out_f32_or_null, int32_t *topk_idx_or_null, float *topk_w_or_null,
+                       void *ws, size_t ws_bytes, qmoe_stream_t stream) {
+  int rc = check_layer_call(L, x, T, out);
+  if (rc || T == 0) return rc ? rc : ok();
+  if ((rc = check_ws(&L->d, std::min<int>(T, CHUNK_TOKENS), ws, ws_bytes))) return rc;
+  if ((rc = check_arch())) return rc;
+  return layer_forward_impl(L, x, T, out, out_f32_or_null, topk_idx_or_null, topk_w_or_null, ws,
+                            stream);
+}
+
+int qmoe_layer_forward_noalloc(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16_t *out,
+                               float *out_f32_or_null, int32_t *topk_idx_or_null,
+                               float *topk_w_or_null, qmoe_stream_t stream) {
+  int rc = check_layer_call(L, x, T, out);
+  if (rc || T == 0) return rc ? rc : ok();
+  const size_t need = ws_layout(&L->d, std::min<int>(T, CHUNK_TOKENS)).total;
+  if (need > NOALLOC_SCRATCH_BYTES)
+    return fail(QMOE_ERR_WORKSPACE, "layer_forward_noalloc: this shape needs %zu bytes of scratch, "
+                "more than the %zu the library holds per device; use qmoe_layer_forward with a "
+                "workspace", need, NOALLOC_SCRATCH_BYTES);
+  if ((rc = check_arch())) return rc;
+  void *ws = nullptr;
+  if ((rc = scratch_address(&ws))) return rc;
+  return layer_forward_impl(L, x, T, out, out_f32_or_null, topk_idx_or_null, topk_w_or_null, ws,
+                            stream);
 }
 
 int qmoe_cache_create(const qmoe_dims *d, const void *host_store, size_t host_stride,

@@ -184,6 +184,17 @@ def layer_forward(layer, x, ws, out=None, out_f32=None, topk_idx=None, topk_w=No
     return out
 
 
+def layer_forward_noalloc(layer, x, out, out_f32=None, topk_idx=None, topk_w=None):
+    """The layer on the library's own per-device scratch (qmoe_layer_forward_noalloc): no
+    workspace; every output is the caller's, nothing is allocated."""
+    T = x.shape[0]
+    check(lib().qmoe_layer_forward_noalloc(
+        ctypes.byref(layer.struct), _ptr(x, 2, "x"), T, _ptr(out, 2, "out"),
+        _ptr(out_f32, 4, allow_none=True), _ptr(topk_idx, 4, allow_none=True),
+        _ptr(topk_w, 4, allow_none=True), _stream()))
+    return out
+
+
 def decode_stack(layers, x, ws, out=None, out_f32=None, topk_idx=None, topk_w=None):
     """One token through the chained layers in one launch: x [1, H] (or [H]) bf16; returns
     out [n_layers, H] bf16, every layer's output (the last row is the chain's result)."""

@@ -160,3 +160,20 @@ def test_argument_errors_do_not_touch_the_device():
     # events
     assert lib.qmoe_set_profile_events(None, None) == 0       # profiling off
     assert lib.qmoe_event_create(None) == -1
+
+
+def test_noalloc_rejects_a_shape_beyond_its_scratch():
+    """The allocation-free entry point refuses, before any device call, a shape whose workspace
+    would exceed its fixed scratch (here hidden 8192, 1024 experts, top-32, width 4096)."""
+    L = _lib()
+    d = L.make_dims(8192, 1024, 32, 4096, 0)
+    lay = L.Layer()
+    lay.d = d
+    fake = ctypes.c_void_p(1 << 20)       # never dereferenced: the call fails first
+    lay.r = L.Router(fake, fake, fake, None, fake, None)
+    lay.experts = fake
+    lay.expert_stride = L.lib().qmoe_expert_stride(ctypes.byref(d), 4096)
+    rc = L.lib().qmoe_layer_forward_noalloc(ctypes.byref(lay), fake, 128, fake, None, None, None,
+                                            None)
+    assert rc == -3, L.last_error()
+    assert "scratch" in L.last_error()
