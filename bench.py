@@ -940,7 +940,9 @@ def main():
         out["chained_stack"] = dict(chain, workload=f"{cfg.name} with the post-combine norm and "
                                     f"layer scalar: one token through all {chain['layers']} "
                                     "layers, x of each layer the bf16 output of the one before, "
-                                    "in one launch (qmoe_decode_stack)")
+                                    "in one launch (qmoe_decode_stack)",
+                                    mode="non-default: slower on this GPU than the same chain as "
+                                         "graph-replayed one-token calls (chained_layer_calls)")
     if tiered:
         out["tiered_residency"] = dict(tiered, workload=f"{cfg.name}: routed experts in pinned host "
                                        "memory, LFU-with-recency device cache per layer")
