@@ -14,8 +14,10 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libqmoe.so")
 LIB_TIMELINE = os.path.join(HERE, "libqmoe_timeline.so")   # profiling build (phase timestamps)
 SOURCES = ["qmoe.hip"]
-HEADERS = ["common.h", "store.h", "router.h", "router_mf.h", "ffn.h", "mfma.h", "decode.h", "cache.h",
-           "diag.h"]
+HEADERS = ["common.h", "bounds.h", "store.h", "router.h", "router_mf.h", "ffn.h", "mfma.h", "decode.h",
+           "cache.h", "diag.h"]
+HOST_CHECKS_SRC = os.path.join(ROOT, "tests", "csrc", "host_checks.cpp")
+HOST_CHECKS = os.path.join(ROOT, "_build", "host_checks")
 
 
 def hipcc():
@@ -53,6 +55,26 @@ def build(verbose=False, timeline=False):
         raise RuntimeError("hipcc failed:\n" + errs)
     os.replace(out + ".tmp", out)
     return out
+
+
+def build_host_checks(verbose=False):
+    """Compile the CPU debug build of the host code: tests/csrc/host_checks.cpp, which includes
+    the library source, with QMOE_DEBUG_BOUNDS (bounds assertions) and the address and
+    undefined-behaviour sanitizers on the host side.  Returns the executable's path."""
+    os.makedirs(os.path.dirname(HOST_CHECKS), exist_ok=True)
+    cmd = [hipcc(), "-x", "hip", "--offload-arch=gfx950", "-std=c++17", "-O1", "-g",
+           "-DQMOE_DEBUG_BOUNDS",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+           "-I", INCLUDE, "-I", CSRC, HOST_CHECKS_SRC, "-o", HOST_CHECKS + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + r.stdout + r.stderr)
+    os.replace(HOST_CHECKS + ".tmp", HOST_CHECKS)
+    return HOST_CHECKS
 
 
 if __name__ == "__main__":

@@ -15,6 +15,8 @@
 #include <cstdint>
 #include <vector>
 
+#include "bounds.h"
+
 namespace qmoe {
 
 struct CachePlan {
@@ -79,7 +81,42 @@ class ExpertCachePolicy {
     }
     p.slot_of.resize(n);
     for (int i = 0; i < n; ++i) p.slot_of[i] = where_[ids[i]];
+    check(ids, n, p);
     return true;
+  }
+
+  // Invariants after a plan (bounds assertions of the debug build): slots and experts map one
+  // to one, every id of the call has a slot that holds it, and each copy fills a distinct slot
+  // with an expert of the call.
+  void check(const int32_t *ids, int n, const CachePlan &p) const {
+#ifdef QMOE_DEBUG_BOUNDS
+    const int E = (int)where_.size();
+    for (int e = 0; e < E; ++e) {
+      const int s = where_[e];
+      QMOE_BOUNDS(s >= -1 && s < slots());
+      if (s >= 0) QMOE_BOUNDS(slot_expert_[s] == e);
+    }
+    for (int s = 0; s < slots(); ++s) {
+      const int e = slot_expert_[s];
+      QMOE_BOUNDS(e >= -1 && e < E);
+      if (e >= 0) QMOE_BOUNDS(where_[e] == s && count_[s] >= 1 && last_[s] <= tick_);
+    }
+    for (int i = 0; i < n; ++i) {
+      const int s = p.slot_of[i];
+      QMOE_BOUNDS(s >= 0 && s < slots() && slot_expert_[s] == ids[i] && used_[s]);
+    }
+    QMOE_BOUNDS(p.fill_expert.size() == p.fill_slot.size());
+    std::vector<char> filled(slots(), 0);
+    for (size_t j = 0; j < p.fill_slot.size(); ++j) {
+      const int s = p.fill_slot[j];
+      QMOE_BOUNDS(s >= 0 && s < slots() && !filled[s] && slot_expert_[s] == p.fill_expert[j]);
+      filled[s] = 1;
+    }
+#else
+    (void)ids;
+    (void)n;
+    (void)p;
+#endif
   }
 
  private:

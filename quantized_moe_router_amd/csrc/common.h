@@ -3,7 +3,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "bounds.h"
+
 #define QMOE_DEV __device__ __forceinline__
+#define QMOE_HD __host__ __device__ __forceinline__
 
 typedef __bf16 qmoe_bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t qmoe_u32x4 __attribute__((ext_vector_type(4)));
@@ -22,10 +25,10 @@ constexpr int CHUNK_TOKENS = 128;  // layer_forward processes at most this many 
 // ---------------------------------------------------------------- bf16 <-> fp32
 QMOE_DEV float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
 QMOE_DEV float bf16hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
-QMOE_DEV float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+QMOE_HD float bf16_to_f32(uint16_t v) { return __builtin_bit_cast(float, (uint32_t)v << 16); }
 // round to nearest even (finite inputs)
-QMOE_DEV uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
+QMOE_HD uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 

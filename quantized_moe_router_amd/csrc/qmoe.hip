@@ -144,50 +144,70 @@ struct WsLayout {
   size_t cnt, logits, tidx, tw, counts, offsets, sorted, active, nact, slot_tab;
   size_t hr_hi, hr_lo, hs_hi, hs_lo, y, ysh, gx, ghr, ghs, slot_ids;
   size_t dec_logits, dec_hr, dec_hsh, dec_yr, dec_ysh, dec_nrm, dec_tk, dec_x, dec_tab, rpart, rss,
-      total;
+      total = 0;
+  // every region in order, for the bounds checks of the debug build
+  struct Region {
+    const char *name;
+    size_t off, bytes;
+  };
+  static constexpr int MAX_REGIONS = 32;
+  Region reg[MAX_REGIONS];
+  int n_reg = 0;
+  size_t put(const char *name, size_t bytes) {
+    QMOE_BOUNDS(n_reg < MAX_REGIONS && bytes % 256 == 0);
+    reg[n_reg++] = Region{name, total, bytes};
+    total += bytes;
+    return total - bytes;
+  }
+  // bytes of the region that starts at off (empty regions share their offset with the next
+  // one; 0: no region of any size starts there)
+  size_t bytes_at(size_t off) const {
+    size_t b = 0;
+    for (int i = 0; i < n_reg; ++i)
+      if (reg[i].off == off) b += reg[i].bytes;
+    return b;
+  }
 };
 
 WsLayout ws_layout(const qmoe_dims *d, int Tmax) {
   WsLayout w;
   const size_t T = (size_t)Tmax, k = d->top_k, E = d->n_experts, H = d->hidden;
   const size_t Tc = std::min<size_t>(T, CHUNK_TOKENS);
-  size_t o = 0;
-  w.cnt = o; o += COUNTER_BYTES;
+  w.cnt = w.put("cnt", COUNTER_BYTES);
   // The one-token path's tagged hand-off areas come first, at offsets that do not depend on
   // the token count: a workspace sized for a chunk may serve one-token calls too, and no
   // multi-token call ever writes into these areas (a stale word there can only be an older
   // one-token call's, whose tag is an older epoch).
-  w.dec_logits = o; o += (size_t)LOGIT_COPIES * dec_copy_stride(E);
-  w.dec_hr = o; o += (size_t)H_COPIES * dec_copy_stride(k * d->inter);
-  w.dec_hsh = o; o += (size_t)H_COPIES * dec_copy_stride((size_t)d->shared_inter);
-  w.dec_yr = o; o += al((k - 1) * H * 8);
-  w.dec_ysh = o; o += al((size_t)dec_shared_chunks(d) * H * 8);
-  w.dec_nrm = o; o += al((H / TILE_ROWS) * 8);
-  w.dec_tk = o; o += al((size_t)TK_COPIES * 2 * MAX_TOPK * 8);
-  w.dec_x = o; o += 2 * (size_t)X_COPIES * dec_x_copy_bytes((int)H);
-  w.dec_tab = o; o += al((size_t)MAX_STACK * sizeof(DecLayer));
-  w.logits = o; o += al(T * E * 4);
-  w.tidx = o; o += al(T * k * 4);
-  w.tw = o; o += al(T * k * 4);
-  w.counts = o; o += al(E * 4);
-  w.offsets = o; o += al((E + 1) * 4);
-  w.sorted = o; o += al(T * k * 4);
-  w.active = o; o += al(E * 4);
-  w.nact = o; o += al(4);
-  w.slot_tab = o; o += al((size_t)bucket_max_blocks((int)(Tc * k), (int)E) * 16);
-  w.slot_ids = o; o += al(Tc * k * 4);
-  w.hr_hi = o; o += al(T * k * d->inter * 2);
-  w.hr_lo = o; o += al(T * k * d->inter * 2);
-  w.hs_hi = o; o += al(T * (size_t)d->shared_inter * 2);
-  w.hs_lo = o; o += al(T * (size_t)d->shared_inter * 2);
-  w.y = o; o += al(Tc * k * H * 4);
-  w.ysh = o; o += al(Tc * H * 4);
-  w.gx = o; o += al(T * (H / GROUP) * 4);
-  w.ghr = o; o += al(T * k * (size_t)(d->inter / GROUP) * 4);
-  w.ghs = o; o += al(T * (size_t)(d->shared_inter / GROUP) * 4);
-  w.rpart = o; o += al((size_t)rmf_splits((int)H) * Tc * E * 4);   // router partial tiles
-  w.rss = o; o += al((size_t)rmf_splits((int)H) * Tc * 4);         // and sums of x^2
-  w.total = o;
+  w.dec_logits = w.put("dec_logits", (size_t)LOGIT_COPIES * dec_copy_stride(E));
+  w.dec_hr = w.put("dec_hr", (size_t)H_COPIES * dec_copy_stride(k * d->inter));
+  w.dec_hsh = w.put("dec_hsh", (size_t)H_COPIES * dec_copy_stride((size_t)d->shared_inter));
+  w.dec_yr = w.put("dec_yr", al((k - 1) * H * 8));
+  w.dec_ysh = w.put("dec_ysh", al((size_t)dec_shared_chunks(d) * H * 8));
+  w.dec_nrm = w.put("dec_nrm", al((H / TILE_ROWS) * 8));
+  w.dec_tk = w.put("dec_tk", al((size_t)TK_COPIES * 2 * MAX_TOPK * 8));
+  w.dec_x = w.put("dec_x", 2 * (size_t)X_COPIES * dec_x_copy_bytes((int)H));
+  w.dec_tab = w.put("dec_tab", al((size_t)MAX_STACK * sizeof(DecLayer)));
+  w.logits = w.put("logits", al(T * E * 4));
+  w.tidx = w.put("tidx", al(T * k * 4));
+  w.tw = w.put("tw", al(T * k * 4));
+  w.counts = w.put("counts", al(E * 4));
+  w.offsets = w.put("offsets", al((E + 1) * 4));
+  w.sorted = w.put("sorted", al(T * k * 4));
+  w.active = w.put("active", al(E * 4));
+  w.nact = w.put("nact", al(4));
+  w.slot_tab = w.put("slot_tab", al((size_t)bucket_max_blocks((int)(Tc * k), (int)E) * 16));
+  w.slot_ids = w.put("slot_ids", al(Tc * k * 4));
+  w.hr_hi = w.put("hr_hi", al(T * k * d->inter * 2));
+  w.hr_lo = w.put("hr_lo", al(T * k * d->inter * 2));
+  w.hs_hi = w.put("hs_hi", al(T * (size_t)d->shared_inter * 2));
+  w.hs_lo = w.put("hs_lo", al(T * (size_t)d->shared_inter * 2));
+  w.y = w.put("y", al(Tc * k * H * 4));
+  w.ysh = w.put("ysh", al(Tc * H * 4));
+  w.gx = w.put("gx", al(T * (H / GROUP) * 4));
+  w.ghr = w.put("ghr", al(T * k * (size_t)(d->inter / GROUP) * 4));
+  w.ghs = w.put("ghs", al(T * (size_t)(d->shared_inter / GROUP) * 4));
+  w.rpart = w.put("rpart", al((size_t)rmf_splits((int)H) * Tc * E * 4));   // router partial tiles
+  w.rss = w.put("rss", al((size_t)rmf_splits((int)H) * Tc * 4));         // and sums of x^2
   return w;
 }
 
@@ -288,6 +308,7 @@ int launch_router(const RouterArgs &a, size_t smem, void *ws, const WsLayout &wl
 }
 
 static_assert(BUCKET_BLOCK_ROWS == PF_MT, "one matrix-core pass per bucket block");
+static_assert((long)MAX_T * MAX_TOPK <= BUCKET_MAX_N, "bucket scan fields hold every call");
 static_assert((size_t)(DEC_SYNC_WORD + SY_LINES * SY_LINE) * 4 <= COUNTER_BYTES,
               "decode sync area inside the counter area");
 
@@ -495,6 +516,16 @@ static DecodeArgs make_decode_args(const qmoe_layer *L, const uint16_t *x, uint1
   a.nRD = a.k * ((tiles_d + tpw - 1) / tpw);
   a.lcnt = a.sync + (size_t)SY_DONE * SY_LINE;
   a.advance = 1;
+  // every copy of every hand-off area inside its workspace region
+  QMOE_BOUNDS(((size_t)(LOGIT_COPIES - 1) * a.logit_copy + a.E) * 8 <= wl.bytes_at(wl.dec_logits));
+  QMOE_BOUNDS(((size_t)(H_COPIES - 1) * a.hr_copy + (size_t)a.k * a.I) * 8 <= wl.bytes_at(wl.dec_hr));
+  QMOE_BOUNDS(!sh || ((size_t)(H_COPIES - 1) * a.hsh_copy + a.Is) * 8 <= wl.bytes_at(wl.dec_hsh));
+  QMOE_BOUNDS((size_t)(a.k - 1) * a.H * 8 <= wl.bytes_at(wl.dec_yr) || a.k == 1);
+  QMOE_BOUNDS((size_t)a.nc * a.H * 8 <= wl.bytes_at(wl.dec_ysh) || a.nc == 0);
+  QMOE_BOUNDS((size_t)tiles_d * 8 <= wl.bytes_at(wl.dec_nrm));
+  QMOE_BOUNDS((size_t)TK_COPIES * 2 * MAX_TOPK * 8 <= wl.bytes_at(wl.dec_tk));
+  QMOE_BOUNDS((size_t)(DEC_SYNC_WORD + SY_LINES * SY_LINE) * 4 <= wl.bytes_at(wl.cnt));
+  QMOE_BOUNDS(dec_lds_of(d, sh).total <= 160 * 1024);
 #ifdef QMOE_TIMELINE
   a.tl = g_tl;
 #endif
@@ -679,6 +710,7 @@ int qmoe_bucket(const qmoe_dims *d, const int32_t *topk_idx, int32_t T, int32_t 
     return fail(QMOE_ERR_ARG, "bucket: NULL pointer");
   if ((rc = check_arch())) return rc;
   const size_t lds = bucket_lds_bytes(T * d->top_k, d->n_experts);
+  QMOE_BOUNDS((long)T * d->top_k <= BUCKET_MAX_N && lds <= 160 * 1024);
   if ((rc = set_lds(bucket_kernel, lds))) return rc;
   hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(256), lds, (hipStream_t)stream, topk_idx,
                      T * d->top_k, d->n_experts, counts, offsets, sorted, active, n_active);
@@ -791,6 +823,9 @@ int layer_forward_impl(const qmoe_layer *L, const uint16_t *x, int32_t T, uint16
     fa.slot_tab = ra.slot_tab;
     fa.n_slots = bucket_max_blocks(Tc * k, d->n_experts);
     ra.n_slots = fa.n_slots;
+    QMOE_BOUNDS(Tc <= Tc_max && (size_t)fa.n_slots * 16 <= wl.bytes_at(wl.slot_tab));
+    QMOE_BOUNDS((size_t)Tc * k * H * 4 <= wl.bytes_at(wl.y) && (size_t)Tc * k * 4 <= wl.bytes_at(wl.sorted));
+    QMOE_BOUNDS(router_smem(d, Tc) <= 160 * 1024);
     const bool mfma = !valu_ffn(Tc);
     if (mfma) ra.gsum = at<float>(ws, wl.gx);
     if ((rc = launch_router(ra, router_smem(d, Tc), ws, wl, s))) return rc;

@@ -145,8 +145,27 @@ QMOE_DEV float topk_weight(int my_e, float my_l, int k, const float *pes) {
 // expert's first block, else -1}; entries from the number of blocks up to n_slots have zero
 // rows.
 constexpr int BUCKET_BLOCK_ROWS = 16;
+constexpr int BUCKET_MAX_N = 1 << 21;     // assignments of one bucketing call (T x k limits)
 inline __host__ __device__ int bucket_max_blocks(int N, int E) {
   return N / BUCKET_BLOCK_ROWS + (N < E ? N : E);
+}
+// The exclusive scan over experts carries (rows, blocks, active flag) in one 64-bit word:
+// rows in bits 40..63, blocks in bits 20..39, flags in bits 0..19.  Totals stay inside their
+// fields for N <= BUCKET_MAX_N and E <= MAX_EXPERTS (blocks <= N/16 + E < 2^20).
+QMOE_HD long long bucket_scan_word(long long c) {
+  return (c << 40) | (((c + BUCKET_BLOCK_ROWS - 1) / BUCKET_BLOCK_ROWS) << 20) | (c > 0 ? 1 : 0);
+}
+QMOE_HD int bucket_scan_rows(long long v) { return (int)(v >> 40); }
+QMOE_HD int bucket_scan_blocks(long long v) { return (int)((v >> 20) & 0xFFFFF); }
+QMOE_HD int bucket_scan_flags(long long v) { return (int)(v & 0xFFFFF); }
+// Block b of an expert with c rows starting at bucket position pos: {expert, position of the
+// block's first row, rows, the expert's smallest flat id for its first block, else -1}.
+QMOE_HD qmoe_u32x4 bucket_block_entry(int e, int c, int pos, int first_e, int b) {
+  QMOE_BOUNDS(b >= 0 && b * BUCKET_BLOCK_ROWS < c);
+  const int rows = c - b * BUCKET_BLOCK_ROWS;
+  return qmoe_u32x4{(uint32_t)e, (uint32_t)(pos + b * BUCKET_BLOCK_ROWS),
+                    (uint32_t)(rows < BUCKET_BLOCK_ROWS ? rows : BUCKET_BLOCK_ROWS),
+                    b == 0 ? (uint32_t)first_e : 0xFFFFFFFFu};
 }
 
 template <int NT>
@@ -159,10 +178,7 @@ QMOE_DEV void bucket_offsets(int *cnt, const int *first, int E, int32_t *counts,
   const int per = (E + NT - 1) / NT;
   const int e0 = min(E, tid * per), e1 = min(E, e0 + per);
   long long own = 0;
-  for (int e = e0; e < e1; ++e) {
-    const long long c = cnt[e];
-    own += (c << 40) | (((c + BB - 1) / BB) << 20) | (c > 0 ? 1 : 0);
-  }
+  for (int e = e0; e < e1; ++e) own += bucket_scan_word(cnt[e]);
   long long pack = own;
   for (int o = 1; o < WAVE; o <<= 1) {
     const long long up = __shfl_up(pack, o, WAVE);
@@ -177,8 +193,8 @@ QMOE_DEV void bucket_offsets(int *cnt, const int *first, int E, int32_t *counts,
     tot += wtot[w];
   }
   const long long excl = before + pack - own;
-  int run_cnt = (int)(excl >> 40), run_blk = (int)((excl >> 20) & 0xFFFFF),
-      run_act = (int)(excl & 0xFFFFF);
+  int run_cnt = bucket_scan_rows(excl), run_blk = bucket_scan_blocks(excl),
+      run_act = bucket_scan_flags(excl);
   for (int e = e0; e < e1; ++e) {
     const int c = cnt[e];
     counts[e] = c;
@@ -187,18 +203,16 @@ QMOE_DEV void bucket_offsets(int *cnt, const int *first, int E, int32_t *counts,
       active[run_act] = e;
       if (slot_tab)
         for (int b = 0; b * BB < c && run_blk + b < n_slots; ++b)
-          *(qmoe_u32x4 *)(slot_tab + 4 * (run_blk + b)) =
-              qmoe_u32x4{(uint32_t)e, (uint32_t)(run_cnt + b * BB), (uint32_t)min(BB, c - b * BB),
-                         b == 0 ? (uint32_t)first[e] : 0xFFFFFFFFu};
+          *(qmoe_u32x4 *)(slot_tab + 4 * (run_blk + b)) = bucket_block_entry(e, c, run_cnt, first[e], b);
       run_blk += (c + BB - 1) / BB;
       ++run_act;
     }
     cnt[e] = run_cnt;
     run_cnt += c;
   }
-  const int na = (int)(tot & 0xFFFFF), nb = (int)((tot >> 20) & 0xFFFFF);
+  const int na = bucket_scan_flags(tot), nb = bucket_scan_blocks(tot);
   if (tid == NT - 1) {
-    offsets[E] = (int)(tot >> 40);
+    offsets[E] = bucket_scan_rows(tot);
     *n_active = na;
   }
   if (slot_tab)

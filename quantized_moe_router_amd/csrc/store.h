@@ -56,7 +56,7 @@ inline size_t block_stride_bytes(int H, int I, int kshift) {
 }
 
 // nibble slot (0..7) inside a packed word of the element at offset jj (0..7) in the word
-QMOE_DEV int nibble_slot(int jj) { return (jj & 1) * 4 + (jj >> 1); }
+QMOE_HD int nibble_slot(int jj) { return (jj & 1) * 4 + (jj >> 1); }
 
 struct CanonExpert {
   const uint8_t *gq, *uq, *dq;
@@ -73,11 +73,11 @@ struct ChunkPos {
   long kst;          // tile * k-steps per tile + ks
   int chunk, rr, half, row, K, ks, group, plane;
 };
-QMOE_DEV bool chunk_pos(long id, int H, int I, int kshift, ChunkPos &c) {
+QMOE_HD bool chunk_pos(long id, int H, int I, int kshift, ChunkPos &c) {
   const BlockGeom g = block_geom(H, I, kshift);
   const long n_gu = (long)g.gu_tiles * g.gu_ks * 64;
   const long n_all = n_gu + (long)g.d_tiles * g.d_ks * 64;
-  if (id >= n_all) return false;
+  if (id < 0 || id >= n_all) return false;
   c.gu = id < n_gu;
   const long local = c.gu ? id : id - n_gu;
   c.chunk = (int)(local % 64);
@@ -99,32 +99,51 @@ QMOE_DEV bool chunk_pos(long id, int H, int I, int kshift, ChunkPos &c) {
   return true;
 }
 
-// one thread per 16-byte chunk of the block
-__global__ void pack_kernel(CanonExpert c, int H, int I, int kshift, uint8_t *dst) {
+// Element counts of the canonical arrays an index of the chunk map may touch (bounds of the
+// debug build): codes of the matrix the chunk comes from (rows x K, in bytes), and its
+// scale/bias arrays (rows x K/64).
+QMOE_HD size_t canon_code_bytes(const ChunkPos &p, int H, int I, int kshift) {
+  const size_t rows = p.gu ? I : H;
+  return rows * (size_t)(kshift ? p.K : p.K / 2);
+}
+QMOE_HD size_t canon_group_count(const ChunkPos &p, int H, int I) {
+  return (size_t)(p.gu ? I : H) * (p.K / GROUP);
+}
+
+// Packs chunk `id` of the block of one expert: 32 codes into 16 bytes, and for the first
+// half-chunk of a tile row the k-step's scale|bias word.
+QMOE_HD void pack_chunk(const CanonExpert &c, int H, int I, int kshift, uint8_t *dst, long id) {
   ChunkPos p;
-  if (!chunk_pos((long)blockIdx.x * blockDim.x + threadIdx.x, H, I, kshift, p)) return;
+  if (!chunk_pos(id, H, I, kshift, p)) return;
   const BlockGeom g = block_geom(H, I, kshift);
   const bool up = p.gu && p.rr >= 16;
   const uint8_t *q = p.gu ? (up ? c.uq : c.gq) : c.dq;
   const uint16_t *s = p.gu ? (up ? c.us : c.gs) : c.ds;
   const uint16_t *b = p.gu ? (up ? c.ub : c.gb) : c.db;
   const int e0 = p.group * GROUP + p.half * 32;
+  const size_t n_codes = canon_code_bytes(p, H, I, kshift);
   uint32_t w[4] = {0, 0, 0, 0};
   for (int j = 0; j < 32; ++j) {
     uint32_t code;
     if (kshift) {
-      const uint32_t q8 = q[(size_t)p.row * p.K + e0 + j];
+      const size_t at = (size_t)p.row * p.K + e0 + j;
+      QMOE_BOUNDS(at < n_codes);
+      const uint32_t q8 = q[at];
       code = p.plane ? (q8 & 0xFu) : (q8 >> 4);
     } else {
-      const uint8_t *src = q + (size_t)p.row * (p.K / 2) + e0 / 2;
-      code = (src[j >> 1] >> ((j & 1) * 4)) & 0xFu;
+      const size_t at = (size_t)p.row * (p.K / 2) + e0 / 2 + (j >> 1);
+      QMOE_BOUNDS(at < n_codes);
+      code = (q[at] >> ((j & 1) * 4)) & 0xFu;
     }
     w[j >> 3] |= code << (4 * nibble_slot(j & 7));
   }
-  uint8_t *base = dst + (p.gu ? 0 : g.gu_bytes) + (size_t)p.kst * KSTEP_BYTES;
+  const size_t off = (p.gu ? 0 : g.gu_bytes) + (size_t)p.kst * KSTEP_BYTES;
+  QMOE_BOUNDS(off + p.chunk * 16 + 16 <= (p.gu ? g.gu_bytes : g.gu_bytes + g.d_bytes));
+  uint8_t *base = dst + off;
   *(qmoe_u32x4 *)(base + p.chunk * 16) = qmoe_u32x4{w[0], w[1], w[2], w[3]};
   if (p.half == 0) {
     const size_t gi = (size_t)p.row * (p.K / GROUP) + p.group;
+    QMOE_BOUNDS(gi < canon_group_count(p, H, I));
     uint32_t sw = s[gi], bw = b[gi];
     if (kshift && p.plane == 0) sw = f32_to_bf16_bits(bf16_to_f32((uint16_t)sw) * 16.f);  // exact
     if (kshift && p.plane == 1) bw = 0u;
@@ -132,37 +151,50 @@ __global__ void pack_kernel(CanonExpert c, int H, int I, int kshift, uint8_t *ds
   }
 }
 
-__global__ void unpack_kernel(const uint8_t *srcb, int H, int I, int kshift, CanonExpertOut c) {
+// Inverse of pack_chunk: chunk `id` back into the canonical arrays.
+QMOE_HD void unpack_chunk(const uint8_t *srcb, int H, int I, int kshift, const CanonExpertOut &c,
+                          long id) {
   ChunkPos p;
-  if (!chunk_pos((long)blockIdx.x * blockDim.x + threadIdx.x, H, I, kshift, p)) return;
+  if (!chunk_pos(id, H, I, kshift, p)) return;
   const BlockGeom g = block_geom(H, I, kshift);
   const bool up = p.gu && p.rr >= 16;
   uint8_t *q = p.gu ? (up ? c.uq : c.gq) : c.dq;
   uint16_t *s = p.gu ? (up ? c.us : c.gs) : c.ds;
   uint16_t *b = p.gu ? (up ? c.ub : c.gb) : c.db;
-  const uint8_t *base = srcb + (p.gu ? 0 : g.gu_bytes) + (size_t)p.kst * KSTEP_BYTES;
+  const size_t off = (p.gu ? 0 : g.gu_bytes) + (size_t)p.kst * KSTEP_BYTES;
+  QMOE_BOUNDS(off + p.chunk * 16 + 16 <= (p.gu ? g.gu_bytes : g.gu_bytes + g.d_bytes));
+  const uint8_t *base = srcb + off;
   const qmoe_u32x4 v = *(const qmoe_u32x4 *)(base + p.chunk * 16);
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   const int e0 = p.group * GROUP + p.half * 32;
-  auto code_at = [&](int j) { return (w[j >> 3] >> (4 * nibble_slot(j & 7))) & 0xFu; };
+  const size_t n_codes = canon_code_bytes(p, H, I, kshift);
   if (kshift) {
     // the high-nibble k-step writes bits 7..4 of each code, the low one bits 3..0: both
     // k-steps of a group own the same bytes, so the high one writes the whole byte from both
     // (reading the low k-step's chunk, which is the next one)
     if (p.plane == 0) {
+      QMOE_BOUNDS(off + KSTEP_BYTES + p.chunk * 16 + 16 <= g.gu_bytes + g.d_bytes);
       const qmoe_u32x4 v2 = *(const qmoe_u32x4 *)(base + KSTEP_BYTES + p.chunk * 16);
       const uint32_t w2[4] = {v2.x, v2.y, v2.z, v2.w};
-      uint8_t *dq = q + (size_t)p.row * p.K + e0;
+      const size_t at = (size_t)p.row * p.K + e0;
+      QMOE_BOUNDS(at + 32 <= n_codes);
+      uint8_t *dq = q + at;
       for (int j = 0; j < 32; ++j)
-        dq[j] = (uint8_t)((code_at(j) << 4) | ((w2[j >> 3] >> (4 * nibble_slot(j & 7))) & 0xFu));
+        dq[j] = (uint8_t)((((w[j >> 3] >> (4 * nibble_slot(j & 7))) & 0xFu) << 4) |
+                          ((w2[j >> 3] >> (4 * nibble_slot(j & 7))) & 0xFu));
     }
   } else {
-    uint8_t *dq = q + (size_t)p.row * (p.K / 2) + e0 / 2;
-    for (int m = 0; m < 16; ++m) dq[m] = (uint8_t)(code_at(2 * m) | (code_at(2 * m + 1) << 4));
+    const size_t at = (size_t)p.row * (p.K / 2) + e0 / 2;
+    QMOE_BOUNDS(at + 16 <= n_codes);
+    uint8_t *dq = q + at;
+    for (int m = 0; m < 16; ++m)
+      dq[m] = (uint8_t)(((w[(2 * m) >> 3] >> (4 * nibble_slot((2 * m) & 7))) & 0xFu) |
+                        (((w[(2 * m + 1) >> 3] >> (4 * nibble_slot((2 * m + 1) & 7))) & 0xFu) << 4));
   }
   if (p.half == 0) {
     const uint32_t sb = *(const uint32_t *)(base + 1024 + p.rr * 4);
     const size_t gi = (size_t)p.row * (p.K / GROUP) + p.group;
+    QMOE_BOUNDS(gi < canon_group_count(p, H, I));
     if (!kshift) {
       s[gi] = (uint16_t)(sb & 0xFFFFu);
       b[gi] = (uint16_t)(sb >> 16);
@@ -172,6 +204,15 @@ __global__ void unpack_kernel(const uint8_t *srcb, int H, int I, int kshift, Can
       s[gi] = (uint16_t)(sb & 0xFFFFu);
     }
   }
+}
+
+// one thread per 16-byte chunk of the block
+__global__ void pack_kernel(CanonExpert c, int H, int I, int kshift, uint8_t *dst) {
+  pack_chunk(c, H, I, kshift, dst, (long)blockIdx.x * blockDim.x + threadIdx.x);
+}
+
+__global__ void unpack_kernel(const uint8_t *srcb, int H, int I, int kshift, CanonExpertOut c) {
+  unpack_chunk(srcb, H, I, kshift, c, (long)blockIdx.x * blockDim.x + threadIdx.x);
 }
 
 }  // namespace qmoe
