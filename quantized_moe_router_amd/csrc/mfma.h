@@ -59,14 +59,14 @@ QMOE_DEV qmoe_f32x4 mfma16(qmoe_u32x4 a, uint32_t w, qmoe_f32x4 c) {
 }
 
 // One k-step of NT 32-row tiles against the wave's 16 activation rows: acc[j][0] (tile j rows
-// 0..15) and acc[j][1] (rows 16..31).  xa[p][h]: plane p, column half h of the lane's row;
-// sb[j][b]: scale|bias of the lane's column in block b of tile j; g: group sum of the lane's
-// row (used where gmask).
+// 0..15) and acc[j][1] (rows 16..31) += scale * (x . (128 + q)).  xa[p][h]: plane p, column half
+// h of the lane's row; sw[j]: the scale|bias word of tile row lane % 32 (one load per tile),
+// turned by one lane swap into the words of the lane's column in both blocks.  The lanes of
+// group `mine` keep those words in bsel for the bias term of their k-step (pf_bias).
 template <int NP, int NT>
-QMOE_DEV void pf_kstep(qmoe_f32x4 (&acc)[NT][2], const qmoe_u32x4 (&cv)[NT],
-                       const qmoe_u32x4 (&xa)[NP][2], const uint32_t (&sb)[NT][2], float g,
-                       bool gmask) {
-  const float gv = gmask ? g : 0.f;
+QMOE_DEV void pf_kstep(qmoe_f32x4 (&acc)[NT][2], uint32_t (&bsel)[NT][2],
+                       const qmoe_u32x4 (&cv)[NT], const qmoe_u32x4 (&xa)[NP][2],
+                       const uint32_t (&sw)[NT], bool mine) {
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     const auto x02 = __builtin_amdgcn_permlane32_swap(cv[j].x, cv[j].z, false, false);
@@ -81,31 +81,48 @@ QMOE_DEV void pf_kstep(qmoe_f32x4 (&acc)[NT][2], const qmoe_u32x4 (&cv)[NT],
       t0 = mfma16(xa[p][1], y23[0], t0);
       t1 = mfma16(xa[p][1], y23[1], t1);
     }
-    const float sc0 = bf16lo(sb[j][0]), c0 = fmaf(-128.f, sc0, bf16hi(sb[j][0]));
-    const float sc1 = bf16lo(sb[j][1]), c1 = fmaf(-128.f, sc1, bf16hi(sb[j][1]));
+    // lane l loaded the word of tile row l % 32: rows of 16 lanes alternate between block 0
+    // and block 1, and the swap of odd and even rows gives every lane both
+    const auto sb = __builtin_amdgcn_permlane16_swap(sw[j], sw[j], false, false);
+    const float sc0 = bf16lo(sb[0]), sc1 = bf16lo(sb[1]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       acc[j][0][i] = fmaf(sc0, t0[i], acc[j][0][i]);
       acc[j][1][i] = fmaf(sc1, t1[i], acc[j][1][i]);
     }
-    acc[j][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(gv, c0, acc[j][0], 0, 0, 0);
-    acc[j][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(gv, c1, acc[j][1], 0, 0, 0);
+    bsel[j][0] = mine ? sb[0] : bsel[j][0];
+    bsel[j][1] = mine ? sb[1] : bsel[j][1];
+  }
+}
+
+// The bias term of up to four k-steps in one v_mfma_f32_16x16x4_f32 per block: lane group lg
+// supplies, for its k-step of the four, the group sum of its row (A, K entry lg) and
+// (b - 128 s) of its column (B, K entry lg), so acc += sum over the k-steps of g c.  Lane
+// groups without a k-step hold g = 0 and a zero word (c = 0).
+template <int NT>
+QMOE_DEV void pf_bias(qmoe_f32x4 (&acc)[NT][2], uint32_t (&bsel)[NT][2], float g4) {
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const float c = fmaf(-128.f, bf16lo(bsel[j][b]), bf16hi(bsel[j][b]));
+      acc[j][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(g4, c, acc[j][b], 0, 0, 0);
+      bsel[j][b] = 0u;
+    }
   }
 }
 
 // KB consecutive k-steps from ks0 of NT tiles (tile j at tb[j]) (with TAIL only those below
 // nks; the loads past the end re-read the last k-step and are not used), all loads issued
 // before any product.  ap[p]: the lane's row of plane p, offset to its 8-column piece
-// (group g, half h at ap[p] + 64 g + 32 h; k-step ks reads group ks >> kshift); grow: the
-// row's group sums.
+// (group g, half h at ap[p] + 64 g + 32 h; k-step ks reads group ks >> kshift).
 template <int NP, int NT, int KB, bool TAIL>
-QMOE_DEV void pf_batch(qmoe_f32x4 (&acc)[NT][2], const uint8_t *const (&tb)[NT], int ks0, int nks,
-                       const uint16_t *const (&ap)[NP], const float *grow, bool gmask,
-                       int kshift) {
-  const int lane = threadIdx.x % WAVE, n = lane % 16;
+QMOE_DEV void pf_batch(qmoe_f32x4 (&acc)[NT][2], uint32_t (&bsel)[NT][2],
+                       const uint8_t *const (&tb)[NT], int ks0, int nks,
+                       const uint16_t *const (&ap)[NP], int kshift) {
+  const int lane = threadIdx.x % WAVE, lg = lane / 16;
   qmoe_u32x4 cv[KB][NT], xa[KB][NP][2];
-  uint32_t sb[KB][NT][2];
-  float g[KB];
+  uint32_t sw[KB][NT];
 #pragma unroll
   for (int u = 0; u < KB; ++u) {
     const int ks = TAIL ? min(ks0 + u, nks - 1) : ks0 + u;
@@ -113,8 +130,7 @@ QMOE_DEV void pf_batch(qmoe_f32x4 (&acc)[NT][2], const uint8_t *const (&tb)[NT],
     for (int j = 0; j < NT; ++j) {
       const uint8_t *st = tb[j] + (size_t)ks * KSTEP_BYTES;
       cv[u][j] = *(const qmoe_u32x4 *)(st + 16 * lane);
-      sb[u][j][0] = *(const uint32_t *)(st + 1024 + 4 * n);
-      sb[u][j][1] = *(const uint32_t *)(st + 1024 + 64 + 4 * n);
+      sw[u][j] = *(const uint32_t *)(st + 1024 + 4 * (lane % 32));
     }
     const int grp = ks >> kshift;
 #pragma unroll
@@ -122,26 +138,40 @@ QMOE_DEV void pf_batch(qmoe_f32x4 (&acc)[NT][2], const uint8_t *const (&tb)[NT],
       xa[u][p][0] = *(const qmoe_u32x4 *)(ap[p] + GROUP * grp);
       xa[u][p][1] = *(const qmoe_u32x4 *)(ap[p] + GROUP * grp + 32);
     }
-    g[u] = grow[grp];
   }
 #pragma unroll
   for (int u = 0; u < KB; ++u)
-    if (!TAIL || ks0 + u < nks) pf_kstep<NP, NT>(acc, cv[u], xa[u], sb[u], g[u], gmask);
+    if (!TAIL || ks0 + u < nks)
+      pf_kstep<NP, NT>(acc, bsel, cv[u], xa[u], sw[u], ((ks0 + u) & 3) == lg);
 }
 
+// All nks k-steps of NT tiles, four at a time (KB divides 4): the products of each k-step,
+// then the bias term of the four.  grow: the lane's row's group sums.
 template <int NP, int NT, int KB>
 QMOE_DEV void pf_tiles(qmoe_f32x4 (&acc)[NT][2], const uint8_t *const (&tb)[NT], int nks,
-                       const uint16_t *const (&ap)[NP], const float *grow, bool gmask,
-                       int kshift) {
+                       const uint16_t *const (&ap)[NP], const float *grow, int kshift) {
+  static_assert(4 % KB == 0, "k-step batches tile the groups of four");
+  const int lg = (threadIdx.x % WAVE) / 16;
+  uint32_t bsel[NT][2];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     acc[j][0] = qmoe_f32x4{0.f, 0.f, 0.f, 0.f};
     acc[j][1] = qmoe_f32x4{0.f, 0.f, 0.f, 0.f};
+    bsel[j][0] = bsel[j][1] = 0u;
   }
-  int k0 = 0;
-  for (; k0 + KB <= nks; k0 += KB)
-    pf_batch<NP, NT, KB, false>(acc, tb, k0, nks, ap, grow, gmask, kshift);
-  if (k0 < nks) pf_batch<NP, NT, KB, true>(acc, tb, k0, nks, ap, grow, gmask, kshift);
+  for (int k4 = 0; k4 < nks; k4 += 4) {
+    const int kq = k4 + lg;
+    const float g4 = kq < nks ? grow[kq >> kshift] : 0.f;
+    if (k4 + 4 <= nks) {
+#pragma unroll
+      for (int k0 = k4; k0 < k4 + 4; k0 += KB)
+        pf_batch<NP, NT, KB, false>(acc, bsel, tb, k0, nks, ap, kshift);
+    } else {
+      for (int k0 = k4; k0 < nks; k0 += KB)
+        pf_batch<NP, NT, KB, true>(acc, bsel, tb, k0, nks, ap, kshift);
+    }
+    pf_bias<NT>(acc, bsel, g4);
+  }
 }
 
 // Workgroups (g < ng, b < nb) that share data per g: the shared expert's (weight group, token
@@ -208,7 +238,7 @@ __global__ void __launch_bounds__(GU_WAVES * WAVE) gu_pf_kernel(FfnArgs a) {
     const int tok = sr.shared ? p0 + r : flat_of(a, sr, p0 + r) / a.k;
     const uint16_t *const ap[1] = {a.x + (size_t)tok * H + 8 * lg};
     qmoe_f32x4 acc[GU_NT][2];
-    pf_tiles<1, GU_NT, GU_KB>(acc, tb, KS, ap, a.gx + (size_t)tok * KG, lg == 0, a.kshift);
+    pf_tiles<1, GU_NT, GU_KB>(acc, tb, KS, ap, a.gx + (size_t)tok * KG, a.kshift);
     float hs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < GU_NT; ++j) {
@@ -298,7 +328,7 @@ __global__ void __launch_bounds__(D_WAVES * WAVE) d_pf_kernel(FfnArgs a) {
     const size_t pos = (size_t)(pos0 + p0 + min(n, mt - 1));  // padding lanes repeat the last row
     const uint16_t *const ap[2] = {phi + pos * K + 8 * lg, plo + pos * K + 8 * lg};
     qmoe_f32x4 acc[D_NT][2];
-    pf_tiles<2, D_NT, D_KB>(acc, tb, KSd, ap, gh + pos * KGd, lg == 0, a.kshift);
+    pf_tiles<2, D_NT, D_KB>(acc, tb, KSd, ap, gh + pos * KGd, a.kshift);
     int flat = 0;
     if (!sr.shared && lane < mt) flat = flat_of(a, sr, p0 + lane);
 #pragma unroll
