@@ -319,12 +319,17 @@ int qmoe_cache_stats(const qmoe_expert_cache *cache, int64_t *hits_out, int64_t 
 /* The layer with its routed experts streamed through the cache, per chunk of at most 128
  * tokens: router and top-k on the GPU; the ids copied to the host (the one synchronisation of
  * `stream`, where the pages' CPU reads the router's choice); the cache plan; one host-to-device
- * copy per missing expert block; the slot ids copied back; bucketing, expert FFN (routed
- * experts from the slots, shared block from L->shared) and combine (with L's post-combine
- * steps if set) as in qmoe_layer_forward.  L->experts and L->expert_stride are not used.  The
- * chunk's distinct experts must fit in the slots.  Not for use under graph capture.  Results
- * equal qmoe_router_topk -> qmoe_bucket -> qmoe_expert_ffn -> qmoe_combine_post on a resident
- * store bit for bit. */
+ * copy per missing expert block, on two copy streams of the cache's own; the slot ids copied
+ * back; bucketing; the expert FFN of the shared block (L->shared) and of the experts already in
+ * their slots on `stream` while the copies run, then, once the copies have landed, the FFN of
+ * the refilled slots (the pages overlap the expert reads with the shared and cached experts'
+ * work: TurboFieldfare post, section "TurboFieldfare의 전문가 스트리밍 구조"); combine (with
+ * L's post-combine steps if set) as in qmoe_layer_forward.  L->experts and L->expert_stride are
+ * not used.  The chunk's distinct experts must fit in the slots.  The cache's copy streams and
+ * pinned staging are made on the device current at the first forward call; later calls on
+ * another device fail (QMOE_ERR_ARG).  Not for use under graph capture.  Results equal
+ * qmoe_router_topk -> qmoe_bucket -> qmoe_expert_ffn -> qmoe_combine_post on a resident store
+ * bit for bit. */
 int qmoe_layer_forward_tiered(const qmoe_layer *L, qmoe_expert_cache *cache, const uint16_t *x,
                               int32_t T, uint16_t *out, float *out_f32_or_null,
                               int32_t *topk_idx_or_null, float *topk_w_or_null, void *ws,

@@ -10,6 +10,7 @@
 #include <map>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "qmoe.h"
 #include "common.h"
@@ -590,7 +591,12 @@ struct qmoe_expert_cache {
   size_t slot_stride;
   int n_slots;
   qmoe::ExpertCachePolicy policy;
-  int32_t *h_ids = nullptr, *h_slots = nullptr;   // pinned staging, made on first forward call
+  // made on the first forward call, on the device current then: pinned staging for the ids,
+  // the slot ids and the slot lists, and two copy streams (default priority) with an event each
+  int32_t *h_ids = nullptr, *h_slots = nullptr, *h_lists = nullptr;
+  hipStream_t copy_s[2] = {nullptr, nullptr};
+  hipEvent_t copied[2] = {nullptr, nullptr};
+  int device = -1;
   qmoe_expert_cache(const qmoe_dims &dd, const void *hs, size_t hst, void *ds, size_t dst, int n)
       : d(dd), host_store((const uint8_t *)hs), host_stride(hst), slots_mem((uint8_t *)ds),
         slot_stride(dst), n_slots(n), policy(dd.n_experts, n) {}
@@ -957,8 +963,16 @@ int qmoe_cache_create(const qmoe_dims *d, const void *host_store, size_t host_st
 
 int qmoe_cache_destroy(qmoe_expert_cache *cache) {
   if (!cache) return ok();
+  for (int i = 0; i < 2; ++i) {
+    if (cache->copy_s[i]) {
+      (void)hipStreamSynchronize(cache->copy_s[i]);
+      (void)hipStreamDestroy(cache->copy_s[i]);
+    }
+    if (cache->copied[i]) (void)hipEventDestroy(cache->copied[i]);
+  }
   if (cache->h_ids) (void)hipHostFree(cache->h_ids);
   if (cache->h_slots) (void)hipHostFree(cache->h_slots);
+  if (cache->h_lists) (void)hipHostFree(cache->h_lists);
   delete cache;
   return ok();
 }
@@ -1049,9 +1063,20 @@ int qmoe_layer_forward_tiered(const qmoe_layer *L, qmoe_expert_cache *C, const u
   const int Tc_max = std::min<int>(T, CHUNK_TOKENS);
   if ((rc = check_ws(d, Tc_max, ws, ws_bytes))) return rc;
   if ((rc = check_arch())) return rc;
-  if (!C->h_ids) {
+  int dev = 0;
+  QMOE_HIP(hipGetDevice(&dev));
+  if (C->device < 0) {
     QMOE_HIP(hipHostMalloc((void **)&C->h_ids, (size_t)CHUNK_TOKENS * MAX_TOPK * 4));
     QMOE_HIP(hipHostMalloc((void **)&C->h_slots, (size_t)CHUNK_TOKENS * MAX_TOPK * 4));
+    QMOE_HIP(hipHostMalloc((void **)&C->h_lists, (size_t)(C->n_slots + 2) * 4));
+    for (int i = 0; i < 2; ++i) {
+      QMOE_HIP(hipStreamCreateWithFlags(&C->copy_s[i], hipStreamNonBlocking));
+      QMOE_HIP(hipEventCreateWithFlags(&C->copied[i], hipEventDisableTiming));
+    }
+    C->device = dev;
+  } else if (C->device != dev) {
+    return fail(QMOE_ERR_ARG, "cache was first used on device %d, current device is %d", C->device,
+                dev);
   }
   hipStream_t s = (hipStream_t)stream;
   const WsLayout wl = ws_layout(d, Tc_max);
@@ -1073,38 +1098,78 @@ int qmoe_layer_forward_tiered(const qmoe_layer *L, qmoe_expert_cache *C, const u
     if (!C->policy.plan(C->h_ids, N, p))
       return fail(QMOE_ERR_ARG, "a chunk names more distinct experts than the cache's %d slots",
                   C->n_slots);
-    // one copy per missing block, then the slot ids
-    for (size_t j = 0; j < p.fill_slot.size(); ++j)
+    // One copy per missing block, alternating over the two copy streams (the io phase of
+    // TurboFieldfare post, section "TurboFieldfare의 전문가 스트리밍 구조").  The caller's
+    // stream is idle here (synchronised for the ids above), so no earlier kernel still reads a
+    // slot being refilled, and this call's kernels read a refilled slot only after its copy.
+    const int nf = (int)p.fill_slot.size();
+    for (int j = 0; j < nf; ++j)
       QMOE_HIP(hipMemcpyAsync(C->slots_mem + (size_t)p.fill_slot[j] * C->slot_stride,
                               C->host_store + (size_t)p.fill_expert[j] * C->host_stride, blk,
-                              hipMemcpyHostToDevice, s));
+                              hipMemcpyHostToDevice, C->copy_s[j & 1]));
+    for (int i = 0; i < 2 && i < nf; ++i) QMOE_HIP(hipEventRecord(C->copied[i], C->copy_s[i]));
     for (int i = 0; i < N; ++i) C->h_slots[i] = p.slot_of[i];
+    // the call's distinct slots: those it hit first, then those being filled
+    std::vector<char> mark(C->n_slots, 0);   // 1: listed as hit, 2: being filled
+    for (int j = 0; j < nf; ++j) mark[p.fill_slot[j]] = 2;
+    int nh = 0;
+    for (int i = 0; i < N; ++i) {
+      const int sl = p.slot_of[i];
+      if (!mark[sl]) {
+        mark[sl] = 1;
+        C->h_lists[2 + nh++] = sl;
+      }
+    }
+    for (int j = 0; j < nf; ++j) C->h_lists[2 + nh + j] = p.fill_slot[j];
+    C->h_lists[0] = nh;
+    C->h_lists[1] = nf;
     int32_t *slot_ids = at<int32_t>(ws, wl.slot_ids);
     QMOE_HIP(hipMemcpyAsync(slot_ids, C->h_slots, (size_t)N * 4, hipMemcpyHostToDevice, s));
-    // bucketing over the slots, FFN from the slots, combine
+    // bucketing over the slots; its list of active slots is then replaced by the two lists
     int32_t *counts = at<int32_t>(ws, wl.counts), *offsets = at<int32_t>(ws, wl.offsets);
     int32_t *sorted = at<int32_t>(ws, wl.sorted), *active = at<int32_t>(ws, wl.active);
     int32_t *nact = at<int32_t>(ws, wl.nact);
+    QMOE_BOUNDS((size_t)(nh + nf) * 4 <= wl.bytes_at(wl.active) && 8 <= wl.bytes_at(wl.nact));
     const size_t lds = bucket_lds_bytes(N, C->n_slots);
     if ((rc = set_lds(bucket_kernel, lds))) return rc;
     hipLaunchKernelGGL(bucket_kernel, dim3(1), dim3(256), lds, s, (const int32_t *)slot_ids, N,
                        C->n_slots, counts, offsets, sorted, active, nact);
     QMOE_LAUNCHED();
+    QMOE_HIP(hipMemcpyAsync(active, C->h_lists + 2, (size_t)(nh + nf) * 4, hipMemcpyHostToDevice, s));
+    QMOE_HIP(hipMemcpyAsync(nact, C->h_lists, 8, hipMemcpyHostToDevice, s));
+    // the FFN of the shared expert and the hit slots while the copies run, then, once they
+    // have landed, the FFN of the filled slots (the pages overlap the reads with the shared
+    // and cached experts' work); every row's arithmetic is the same as in one launch
     FfnArgs fa = make_ffn_args(L, xc, Tc, offsets, sorted, active, nact, at<float>(ws, wl.y),
                                sh ? at<float>(ws, wl.ysh) : nullptr, ws, Tc_max);
     fa.experts = C->slots_mem;
     fa.stride = C->slot_stride;
     fa.n_experts = C->n_slots;
-    fa.n_slots = std::min(C->n_slots, N);
+    fa.n_slots = nh;
     if (!sh) fa.shared = nullptr;
+    FfnArgs fb = fa;
+    fb.active = active + nh;
+    fb.n_active = nact + 1;
+    fb.n_slots = nf;
+    fb.shared = nullptr;
     uint16_t *oc = out + (size_t)c0 * H;
     float *oc32 = out_f32_or_null ? out_f32_or_null + (size_t)c0 * H : nullptr;
-    if (valu_ffn(Tc)) {
+    const bool valu = valu_ffn(Tc);
+    if (!valu && (rc = launch_gsum(xc, Tc, H, at<float>(ws, wl.gx), s))) return rc;
+    if (valu) {
       if ((rc = launch_gu(fa, s))) return rc;
       if ((rc = launch_d(fa, sh, s))) return rc;
-    } else {
-      if ((rc = launch_gsum(xc, Tc, H, at<float>(ws, wl.gx), s))) return rc;
-      if ((rc = launch_pf(fa, s))) return rc;
+    } else if ((rc = launch_pf(fa, s))) {
+      return rc;
+    }
+    if (nf > 0) {
+      for (int i = 0; i < 2 && i < nf; ++i) QMOE_HIP(hipStreamWaitEvent(s, C->copied[i], 0));
+      if (valu) {
+        if ((rc = launch_gu(fb, s))) return rc;
+        if ((rc = launch_d(fb, false, s))) return rc;
+      } else if ((rc = launch_pf(fb, s))) {
+        return rc;
+      }
     }
     if (post) rc = launch_combine_post(xc, fa.y, w, fa.y_sh, L->post_norm_gain, L->layer_scalar, Tc,
                                        H, k, oc, oc32, s);
