@@ -43,8 +43,8 @@ constexpr int PF_MT = 16;               // activation rows per pass (MFMA rows)
 constexpr int GU_NT = 2;                // gate/up: tiles per wave (a workgroup of 2 waves owns
 constexpr int GU_WAVES = 4 / GU_NT;     //   the 4 tiles of one 64-column group of h)
 constexpr int GU_KB = 2;                //   k-steps per load batch
-constexpr int D_NT = 2;                 // down: tiles per wave
-constexpr int D_WAVES = 4;              //   waves per workgroup
+constexpr int D_NT = 4;                 // down: tiles per wave (the activation rows of a wave serve four tiles)
+constexpr int D_WAVES = 2;              //   waves per workgroup
 constexpr int D_KB = 2;                 //   k-steps per load batch
 
 // B operand: the 8 codes of word w as bf16 (128 + q), element order
