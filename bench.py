@@ -251,7 +251,7 @@ def run_decode(args, cfg, layers):
         kernel = "gu_pf_kernel (routed and shared gate/up + SwiGLU, matrix cores)"
         kern_bytes = (n_dist * 2 * G.matrix_bytes(cfg.inter, H)
                       + 2 * G.matrix_bytes(cfg.shared_inter, H))
-        traffic = None
+        traffic = stored_traffic(f"prefill_kernels_{cfg.name}")
     tok_s_layer = T * L / (ms_step / 1e3)
     layer_s = ms_step / 1e3 / L
     kern_gbps = kern_bytes / (kern_ms / 1e3) / 1e9
@@ -304,7 +304,8 @@ def config_entry(d, cfg, note=None):
                       "bytes": "credited routed bytes of the kernel",
                       "all_bytes_frac": round((d["all_bytes"] if d["T"] == 1 else d["kern_bytes"])
                                               / (d["kern_ms"] / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
-                      "avg_launch_us": round(d["kern_ms"] * 1e3, 3), "timing": d["timing_src"]}}
+                      "avg_launch_us": round(d["kern_ms"] * 1e3, 3), "timing": d["timing_src"],
+                      "traffic": d["traffic"]}}
     if d.get("buckets"):
         e["buckets"] = d["buckets"]
     if note:
@@ -383,7 +384,8 @@ def run_long_prefill(args, cfg, layers):
                          "all_bytes_frac": round(kern_all / (kern_ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
                          "avg_launch_us": round(kern_ms * 1e3, 3),
                          "timing": f"HIP event nodes around the kernel of chunk 40 of each of the {L} "
-                                   "layers' prompts, one graph"}}
+                                   "layers' prompts, one graph",
+                         "traffic": stored_traffic(f"prefill_kernels_{cfg.name}")}}
 
 
 def oracle_sample(cfg, samples):
