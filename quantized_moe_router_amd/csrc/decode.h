@@ -153,7 +153,8 @@ inline __host__ __device__ int dec_tiles_per_wg(int wpt) { return DEC_W / wpt; }
 inline __host__ __device__ DecLds dec_lds(int H, int E, int k, int I, int Kc_sh, int nc, int wpt) {
   DecLds L;
   size_t o = 0;
-  L.tk = o; o = al16(o + (size_t)topk_chunks(E) * WAVE * (topk_chunks(E) <= 2 ? 8 : 4));
+  L.tk = o; o = al16(o + (topk_chunks(E) <= 2 ? (size_t)topk_chunks(E) * WAVE * 8
+                                                : (size_t)topk_chunks(E) * WAVE * 4 + DEC_W * MAX_TOPK * 8));
   L.tks = o; o = al16(o + (size_t)2 * MAX_TOPK * 4);
   L.pes = o; o = al16(o + (size_t)E * 4 + 16);
   L.red = o; o = al16(o + (size_t)DEC_W * 32 * 4);
@@ -291,8 +292,8 @@ QMOE_DEV void dec_rank_select(const uint64_t *key, int k, int32_t *tk_e, float *
 // weight is applied by the routed down workgroups); with publish, the top-k ids and weights
 // are also written out for the routed down workgroups and the caller.  The E logits are
 // fetched (tagged) into LDS; for E <= 128 the whole workgroup ranks them as above, otherwise
-// one wave runs the round-by-round selection in registers (on a SIMD that varies with the
-// block index) and hands the result to the others through LDS.
+// every wave runs the round-by-round selection in registers over a quarter of them and the
+// four lists are merged by rank.
 QMOE_DEV int dec_topk(const DecodeArgs &a, unsigned ep, int slot, bool publish, char *smem,
                       const DecLds &L) {
   const int tid = threadIdx.x, wv = tid / WAVE, lane = tid % WAVE;
@@ -347,13 +348,35 @@ QMOE_DEV int dec_topk(const DecodeArgs &a, unsigned ep, int slot, bool publish, 
       }
     }
     __syncthreads();
-    if (chosen) {
-      topk_select(nch, [&](int c) { return c < nch ? ord[c * WAVE + lane] : 0u; }, k, my_e, my_l);
-      if (lane < k) tk_e[lane] = my_e;
+    // two levels: each wave selects the top-k of its quarter of the chunks (in registers, the
+    // four waves at once), then the k of the union of the four lists by rank.  The union holds
+    // every expert of the overall top-k, and an expert's rank in it is its overall rank.
+    uint64_t *cand = (uint64_t *)(ord + nch * WAVE);   // [DEC_W][k] keys, 0: none
+    const int cpw = (nch + DEC_W - 1) / DEC_W, c0 = wv * cpw;
+    int le;
+    float ll;
+    topk_select(cpw, [&](int c) { return c < cpw && c0 + c < nch ? ord[(c0 + c) * WAVE + lane] : 0u; },
+                k, le, ll);
+    if (lane < k) {
+      // selections past the quarter's expert count took padding or a taken entry: none
+      const int n_sub = min(E, (c0 + cpw) * WAVE) - c0 * WAVE, e = c0 * WAVE + le;
+      cand[wv * k + lane] = lane < n_sub ? (((uint64_t)ord[e] << 32) | (uint32_t)~e) : 0ull;
+    }
+    __syncthreads();
+    if (tid < DEC_W * k) {
+      const uint64_t mine = cand[tid];
+      uint32_t r = 0;
+      for (int j = 0; j < DEC_W * k; ++j) r += cand[j] > mine ? 1u : 0u;
+      if (mine != 0 && r < (uint32_t)k) {
+        tk_e[r] = (int)~(uint32_t)mine;
+        tk_l[r] = topk_ord_logit((uint32_t)(mine >> 32));
+      }
     }
     __syncthreads();
     const int e_out = min(max(tk_e[slot], 0), E - 1);
     if (!publish || !chosen) return e_out;
+    my_e = lane < k ? tk_e[lane] : 0;
+    my_l = lane < k ? tk_l[lane] : 0.f;
   }
   const float my_w = topk_weight(my_e, my_l, k, pes);
   if (lane < k) {

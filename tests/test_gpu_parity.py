@@ -362,6 +362,35 @@ def test_one_token_layer_too_wide_for_the_single_launch(inter, bits):
         print(f"inter {inter} bits {bits} step {step}: near ties {ties}, bf16 flips {flips}")
 
 
+@pytest.mark.parametrize("E,k", [(200, 8), (520, 10), (1024, 32)])
+def test_one_token_top_k_over_many_experts(E, k):
+    """One token through layers of more than 128 experts, where every wave of a gate/up
+    workgroup selects the top-k of a quarter of the experts and the four lists are merged by
+    rank (quarters with fewer than k experts and empty quarters included): against the oracle
+    on random inputs, and a zero input (every logit equal) selecting experts 0..k-1 with
+    weights per_expert_scale / k."""
+    ops = _ops()
+    cfg = G.Config(f"many_{E}", 256, E, k, 128, 128, layers=1, tokens=1)
+    pl, li = _stacks().build_layer(cfg, 0, DEV)
+    ws = ops.workspace(pl.dims, 1)
+    for step in range(3):
+        xb, x = _stacks().hidden(cfg, 70 + step, 1)
+        out_f32 = torch.empty(1, cfg.hidden, dtype=torch.float32, device=DEV)
+        idx = torch.empty(1, k, dtype=torch.int32, device=DEV)
+        w = torch.empty(1, k, dtype=torch.float32, device=DEV)
+        out = ops.layer_forward(pl.weights, x, ws, out_f32=out_f32, topk_idx=idx, topk_w=w)
+        torch.cuda.synchronize()
+        ties, nd, flips = _layer_check(cfg, li, xb, out, out_f32, idx, w, range(1))
+        print(f"E {E} k {k} step {step}: near ties {ties}")
+    x0 = torch.zeros(1, cfg.hidden, dtype=torch.bfloat16, device=DEV)
+    idx = torch.empty(1, k, dtype=torch.int32, device=DEV)
+    w = torch.empty(1, k, dtype=torch.float32, device=DEV)
+    ops.layer_forward(pl.weights, x0, ws, topk_idx=idx, topk_w=w)
+    torch.cuda.synchronize()
+    assert idx.cpu().numpy()[0].tolist() == list(range(k))
+    np.testing.assert_allclose(w.cpu().numpy()[0], li.pes[:k] / k, rtol=1e-6)
+
+
 def test_layer_forward_matches_stepwise_and_is_deterministic():
     ops = _ops()
     cfg = G.config("gemma4_26b_a4b_prefill")
