@@ -394,6 +394,7 @@ static int launch_d_t(const FfnArgs &a, int slots, int Kc, hipStream_t s) {
 static int launch_d(FfnArgs a, bool with_shared, hipStream_t s) {
   if (!with_shared) a.shared = nullptr;
   const int slots = a.n_slots + (with_shared ? a.n_sh_chunks : 0);
+  if (slots == 0) return QMOE_OK;
   int Kc = a.I;
   if (with_shared) {
     const int KSs = a.Is / GROUP;

@@ -636,6 +636,35 @@ def test_tiered_layer_equals_resident_stepwise(name, T, slots, steps):
     print(f"{name} T={T} slots={slots}: hits {model.hits}, misses {model.misses}")
 
 
+@pytest.mark.parametrize("T,steps", [(1, 6), (4, 4)])
+def test_tiered_layer_without_shared_expert(T, steps):
+    """A layer with no shared expert through the tiered mode, including calls whose every
+    expert misses the cache (nothing runs while the copies are in flight): the bits of the
+    resident step-by-step path."""
+    ops = _ops()
+    cfg = G.Config("tiny_no_shared", 256, 16, 2, 128, 0, layers=1, tokens=T)
+    pl, li = _stacks().build_layer(cfg, 0, DEV)
+    host = torch.empty(pl.store.numel(), dtype=torch.uint8, pin_memory=True)
+    host.copy_(pl.store)
+    slot_store = torch.empty(8 * pl.stride, dtype=torch.uint8, device=DEV)
+    cache = ops.ExpertCache(pl.dims, host, pl.stride, slot_store, pl.stride, 8)
+    ws, ws2 = ops.workspace(pl.dims, T), ops.workspace(pl.dims, T)
+    for step in range(steps):
+        xb, x = _stacks().hidden(cfg, 40 + step, T)
+        o32t = torch.empty(T, cfg.hidden, dtype=torch.float32, device=DEV)
+        out_t = ops.layer_forward_tiered(pl.weights, cache, x, ws, out_f32=o32t)
+        idx, w = ops.router_topk(pl.dims, pl.router, x, ws2)
+        counts, offsets, srt, active, n_active = ops.bucket(pl.dims, idx)
+        y, ysh = ops.expert_ffn(pl.weights, x, offsets, srt, active, n_active, ws2)
+        o32r = torch.empty_like(o32t)
+        out_r = ops.combine(pl.dims, x, y, w, ysh, out_f32=o32r)
+        torch.cuda.synchronize()
+        assert torch.equal(out_t.view(torch.int16), out_r.view(torch.int16))
+        assert torch.equal(o32t, o32r)
+    hits, misses = cache.stats()
+    assert misses > 0
+
+
 def test_tiered_layer_with_post_steps_and_too_few_slots():
     ops = _ops()
     cfg = G.config("tiny")
