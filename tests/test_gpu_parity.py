@@ -391,6 +391,27 @@ def test_one_token_top_k_over_many_experts(E, k):
     np.testing.assert_allclose(w.cpu().numpy()[0], li.pes[:k] / k, rtol=1e-6)
 
 
+@pytest.mark.parametrize("T", [37, 130])
+def test_chunked_layer_with_the_most_experts_and_the_largest_top_k(T):
+    """Calls of several tokens at the largest expert count and top-k the library accepts
+    (1024 experts, top-32): the multi-token router's widest register selection, the bucketing
+    of up to 4096 assignments in its general form (more segment x expert cells than the
+    segmented form holds), a slot table of 1280 blocks, and for T = 130 a full chunk followed by
+    a two-token one.  Every token against the oracle."""
+    ops = _ops()
+    cfg = G.Config("many_1024_multi", 256, 1024, 32, 128, 128, layers=1, tokens=T)
+    pl, li = _stacks().build_layer(cfg, 0, DEV)
+    xb, x = _stacks().hidden(cfg, 5, T)
+    ws = ops.workspace(pl.dims, T)
+    out_f32 = torch.empty(T, cfg.hidden, dtype=torch.float32, device=DEV)
+    idx = torch.empty(T, cfg.top_k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, cfg.top_k, dtype=torch.float32, device=DEV)
+    out = ops.layer_forward(pl.weights, x, ws, out_f32=out_f32, topk_idx=idx, topk_w=w)
+    torch.cuda.synchronize()
+    ties, nd, flips = _layer_check(cfg, li, xb, out, out_f32, idx, w, range(T))
+    print(f"E 1024 k 32 T={T}: every token; near ties {ties}, re-evaluated {nd}, bf16 flips {flips}")
+
+
 def test_layer_forward_matches_stepwise_and_is_deterministic():
     ops = _ops()
     cfg = G.config("gemma4_26b_a4b_prefill")
