@@ -412,6 +412,47 @@ def test_chunked_layer_with_the_most_experts_and_the_largest_top_k(T):
     print(f"E 1024 k 32 T={T}: every token; near ties {ties}, re-evaluated {nd}, bf16 flips {flips}")
 
 
+@pytest.mark.parametrize("T", [1, 20])
+def test_layer_at_the_largest_hidden_size(T):
+    """Hidden size 8192, the largest the library accepts: the one-token layer (x staged in LDS,
+    router codes in three batches) and a chunk of 20 tokens (32 router splits, 128 k-steps
+    per gate/up tile), every token against the oracle."""
+    ops = _ops()
+    cfg = G.Config("hidden_8192", 8192, 16, 4, 256, 256, layers=1, tokens=T)
+    pl, li = _stacks().build_layer(cfg, 0, DEV)
+    xb, x = _stacks().hidden(cfg, 9, T)
+    ws = ops.workspace(pl.dims, T)
+    out_f32 = torch.empty(T, cfg.hidden, dtype=torch.float32, device=DEV)
+    idx = torch.empty(T, cfg.top_k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, cfg.top_k, dtype=torch.float32, device=DEV)
+    for _ in range(2):
+        out = ops.layer_forward(pl.weights, x, ws, out_f32=out_f32, topk_idx=idx, topk_w=w)
+        torch.cuda.synchronize()
+        ties, nd, flips = _layer_check(cfg, li, xb, out, out_f32, idx, w, range(T))
+    assert ops.workspace_status(ws) == 0
+    print(f"H 8192 T={T}: every token; near ties {ties}, re-evaluated {nd}, bf16 flips {flips}")
+
+
+@pytest.mark.parametrize("T,bits", [(1, 4), (20, 4), (20, 8)])
+def test_layer_at_the_largest_expert_width(T, bits):
+    """Expert and shared inner width 4096, the largest the library accepts (4- and 8-bit
+    experts): 128 gate/up tiles per expert and 64 (4-bit) or 128 (8-bit) down k-steps per output
+    tile; every token against the oracle."""
+    ops = _ops()
+    cfg = G.Config(f"inter_4096_{bits}", 256, 8, 2, 4096, 4096, layers=1, tokens=T, expert_bits=bits)
+    pl, li = _stacks().build_layer(cfg, 0, DEV)
+    xb, x = _stacks().hidden(cfg, 11, T)
+    ws = ops.workspace(pl.dims, T)
+    out_f32 = torch.empty(T, cfg.hidden, dtype=torch.float32, device=DEV)
+    idx = torch.empty(T, cfg.top_k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, cfg.top_k, dtype=torch.float32, device=DEV)
+    out = ops.layer_forward(pl.weights, x, ws, out_f32=out_f32, topk_idx=idx, topk_w=w)
+    torch.cuda.synchronize()
+    ties, nd, flips = _layer_check(cfg, li, xb, out, out_f32, idx, w, range(T))
+    assert ops.workspace_status(ws) == 0
+    print(f"inter 4096 bits {bits} T={T}: every token; near ties {ties}, bf16 flips {flips}")
+
+
 def test_layer_forward_matches_stepwise_and_is_deterministic():
     ops = _ops()
     cfg = G.config("gemma4_26b_a4b_prefill")
