@@ -453,6 +453,33 @@ def test_layer_at_the_largest_expert_width(T, bits):
     print(f"inter 4096 bits {bits} T={T}: every token; near ties {ties}, bf16 flips {flips}")
 
 
+@pytest.mark.parametrize("E,k,T", [(1, 1, 1), (1, 1, 5), (8, 8, 1), (8, 8, 5), (3, 2, 33)])
+def test_layer_degenerate_routing(E, k, T):
+    """Degenerate routing: a single expert (always selected, weight per_expert_scale[0]), every
+    expert selected (top-k = E: the softmax runs over all logits), and an odd expert count;
+    every token against the oracle."""
+    ops = _ops()
+    cfg = G.Config(f"degenerate_{E}_{k}", 256, E, k, 128, 128, layers=1, tokens=T)
+    pl, li = _stacks().build_layer(cfg, 0, DEV)
+    xb, x = _stacks().hidden(cfg, 13, T)
+    ws = ops.workspace(pl.dims, T)
+    out_f32 = torch.empty(T, cfg.hidden, dtype=torch.float32, device=DEV)
+    idx = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    out = ops.layer_forward(pl.weights, x, ws, out_f32=out_f32, topk_idx=idx, topk_w=w)
+    torch.cuda.synchronize()
+    ties, nd, flips = _layer_check(cfg, li, xb, out, out_f32, idx, w, range(T))
+    assert sorted(set(idx.cpu().numpy().reshape(-1).tolist())) <= list(range(E))
+    if k == E:
+        assert all(sorted(r) == list(range(E)) for r in idx.cpu().numpy().tolist())
+        # the softmax runs over all E logits: the weights over per_expert_scale sum to one
+        ratio = w.cpu().numpy() / li.pes[idx.cpu().numpy()]
+        np.testing.assert_allclose(ratio.sum(axis=1), 1.0, rtol=1e-6)
+    if E == 1:
+        np.testing.assert_array_equal(w.cpu().numpy(), np.full((T, 1), li.pes[0], np.float32))
+    print(f"E {E} k {k} T={T}: near ties {ties}, bf16 flips {flips}")
+
+
 def test_layer_forward_matches_stepwise_and_is_deterministic():
     ops = _ops()
     cfg = G.config("gemma4_26b_a4b_prefill")
