@@ -480,6 +480,28 @@ def test_layer_degenerate_routing(E, k, T):
     print(f"E {E} k {k} T={T}: near ties {ties}, bf16 flips {flips}")
 
 
+@pytest.mark.parametrize("H,E,k,T", [(256, 16, 2, 1), (256, 16, 2, 4), (256, 16, 2, 130),
+                                     (2048, 64, 4, 1), (2048, 64, 4, 40)])
+def test_layer_without_a_shared_expert(H, E, k, T):
+    """A layer with no shared expert (its branch absent, not zero) through the resident path:
+    the one-token layer without its shared roles and the chunked kernels without shared
+    workgroups; every token against the oracle."""
+    ops = _ops()
+    cfg = G.Config(f"no_shared_{H}_{E}", H, E, k, 256 if H > 256 else 128, 0, layers=1, tokens=T)
+    pl, li = _stacks().build_layer(cfg, 0, DEV)
+    assert pl.shared is None
+    xb, x = _stacks().hidden(cfg, 17, T)
+    ws = ops.workspace(pl.dims, T)
+    out_f32 = torch.empty(T, cfg.hidden, dtype=torch.float32, device=DEV)
+    idx = torch.empty(T, k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, k, dtype=torch.float32, device=DEV)
+    out = ops.layer_forward(pl.weights, x, ws, out_f32=out_f32, topk_idx=idx, topk_w=w)
+    torch.cuda.synchronize()
+    ties, nd, flips = _layer_check(cfg, li, xb, out, out_f32, idx, w, range(T))
+    assert ops.workspace_status(ws) == 0
+    print(f"no shared H {H} E {E} T={T}: near ties {ties}, bf16 flips {flips}")
+
+
 def test_layer_forward_matches_stepwise_and_is_deterministic():
     ops = _ops()
     cfg = G.config("gemma4_26b_a4b_prefill")

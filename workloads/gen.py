@@ -247,6 +247,8 @@ class LayerInputs:
                 self._cache[e] = ew
 
     def shared(self):
+        if not self.cfg.shared_inter:   # a layer without a shared expert
+            return None
         if "shared" not in self._cache:
             self._cache["shared"] = make_shared(self.cfg, self.layer)
         return self._cache["shared"]
