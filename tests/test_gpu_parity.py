@@ -1,4 +1,6 @@
 """Parity of the HIP path (through the C ABI) against the fp64 oracle.  Needs an MI355X."""
+import copy
+
 import numpy as np
 import pytest
 import torch
@@ -500,6 +502,34 @@ def test_layer_without_a_shared_expert(H, E, k, T):
     ties, nd, flips = _layer_check(cfg, li, xb, out, out_f32, idx, w, range(T))
     assert ops.workspace_status(ws) == 0
     print(f"no shared H {H} E {E} T={T}: near ties {ties}, bf16 flips {flips}")
+
+
+@pytest.mark.parametrize("name,T", [("gemma4_26b_a4b_decode", 1), ("gemma4_26b_a4b_decode", 20),
+                                    ("tiny", 1), ("tiny", 6)])
+def test_layer_with_a_per_channel_router_scale(name, T):
+    """router_scale as a per-channel vector (every workload uses ones; here U(0.5, 2) per
+    hidden channel, so that a misplaced or transposed scale would change the logits): the
+    one-token layer's router and the matrix-core router of a chunk, every token against the
+    oracle, which reads the same vector."""
+    ops = _ops()
+    cfg = G.config(name)
+    pl, li = layer(name)
+    li2 = copy.copy(li)
+    li2.router_scale = np.random.default_rng(23).uniform(0.5, 2.0, cfg.hidden).astype(np.float32)
+    lw = ops.LayerWeights(pl.dims, _stacks().router_weights(li2, DEV), pl.store, pl.stride,
+                          pl.shared)
+    xb, x = _stacks().hidden(cfg, 19, T)
+    ws = ops.workspace(pl.dims, T)
+    out_f32 = torch.empty(T, cfg.hidden, dtype=torch.float32, device=DEV)
+    idx = torch.empty(T, cfg.top_k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, cfg.top_k, dtype=torch.float32, device=DEV)
+    out = ops.layer_forward(lw, x, ws, out_f32=out_f32, topk_idx=idx, topk_w=w)
+    torch.cuda.synchronize()
+    ties, nd, flips = _layer_check(cfg, li2, xb, out, out_f32, idx, w, range(T))
+    # the scale matters: the oracle's logits with unit scales are far from these
+    l1, l2 = O.router(xb, li, cfg.top_k)[2], O.router(xb, li2, cfg.top_k)[2]
+    assert np.abs(l1 - l2).max() > 1e-2 * np.abs(l2).max()
+    print(f"{name} T={T} per-channel router_scale: near ties {ties}, bf16 flips {flips}")
 
 
 def test_layer_forward_matches_stepwise_and_is_deterministic():
