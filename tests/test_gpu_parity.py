@@ -532,6 +532,32 @@ def test_layer_with_a_per_channel_router_scale(name, T):
     print(f"{name} T={T} per-channel router_scale: near ties {ties}, bf16 flips {flips}")
 
 
+@pytest.mark.parametrize("name,T", [("gemma4_26b_a4b_decode", 1), ("gemma4_26b_a4b_decode", 24),
+                                    ("qwen3_next_80b_a3b_decode_b1", 1)])
+def test_layer_with_outlier_and_tiny_activations(name, T):
+    """Hidden states with a wide dynamic range, as activations with outlier channels have:
+    N(0, 1) values, eight channels scaled by 300, and one in sixteen values scaled by 1e-6.
+    The matrix-core operands stay exact (bf16 x, hi/lo planes of h), so the bar is the same;
+    every token against the oracle."""
+    ops = _ops()
+    cfg = G.config(name)
+    pl, li = layer(name)
+    rng = np.random.default_rng(29)
+    xf = rng.standard_normal((T, cfg.hidden)).astype(np.float32)
+    xf[:, rng.choice(cfg.hidden, 8, replace=False)] *= 300.0
+    xf[rng.random((T, cfg.hidden)) < 1.0 / 16] *= 1e-6
+    xb = G.bf16_bits_from_f32(xf)
+    x = torch.from_numpy(xb.view(np.int16)).to(DEV)
+    ws = ops.workspace(pl.dims, T)
+    out_f32 = torch.empty(T, cfg.hidden, dtype=torch.float32, device=DEV)
+    idx = torch.empty(T, cfg.top_k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, cfg.top_k, dtype=torch.float32, device=DEV)
+    out = ops.layer_forward(pl.weights, x, ws, out_f32=out_f32, topk_idx=idx, topk_w=w)
+    torch.cuda.synchronize()
+    ties, nd, flips = _layer_check(cfg, li, xb, out, out_f32, idx, w, range(T))
+    print(f"{name} T={T} outlier activations: near ties {ties}, bf16 flips {flips}")
+
+
 def test_layer_forward_matches_stepwise_and_is_deterministic():
     ops = _ops()
     cfg = G.config("gemma4_26b_a4b_prefill")
