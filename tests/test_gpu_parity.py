@@ -558,6 +558,47 @@ def test_layer_with_outlier_and_tiny_activations(name, T):
     print(f"{name} T={T} outlier activations: near ties {ties}, bf16 flips {flips}")
 
 
+@pytest.mark.parametrize("T", [1, 20])
+def test_calls_on_side_streams_from_two_threads(T):
+    """The entry points are asynchronous on the caller's stream and reentrant: two host threads,
+    each with its own stream (default priority) and workspace, run the same layer calls
+    concurrently; every output is bit-equal to the same call on the default stream."""
+    import threading
+    ops = _ops()
+    name = "gemma4_26b_a4b_decode"
+    cfg = G.config(name)
+    pl, li = layer(name)
+    xs = [_stacks().hidden(cfg, 40 + i, T)[1] for i in range(4)]
+    ws0 = ops.workspace(pl.dims, T)
+    want = [ops.layer_forward(pl.weights, x, ws0).clone() for x in xs]
+    torch.cuda.synchronize()
+    got = [[None] * len(xs) for _ in range(2)]
+    errors = []
+
+    def worker(j):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                ws = ops.workspace(pl.dims, T)
+                for rep in range(3):
+                    for i, x in enumerate(xs):
+                        got[j][i] = ops.layer_forward(pl.weights, x, ws)
+            s.synchronize()
+        except Exception as e:     # reported in the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(j,)) for j in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for j in range(2):
+        for i in range(len(xs)):
+            assert torch.equal(got[j][i].view(torch.int16), want[i].view(torch.int16)), (j, i)
+
+
 def test_layer_forward_matches_stepwise_and_is_deterministic():
     ops = _ops()
     cfg = G.config("gemma4_26b_a4b_prefill")
