@@ -94,7 +94,7 @@ def record_case(name, n_layers, calls, T):
 
 
 def main():
-    path = sys.argv[1] if len(sys.argv) > 1 else os.path.join("gpurun_out", "parity_record.md")
+    path = sys.argv[1] if len(sys.argv) > 1 else os.path.join("profiles", "parity_record.md")
     torch.cuda.set_device(0)
     rows = []
     for name, nl, calls, T in CASES:
