@@ -599,6 +599,57 @@ def test_calls_on_side_streams_from_two_threads(T):
             assert torch.equal(got[j][i].view(torch.int16), want[i].view(torch.int16)), (j, i)
 
 
+def test_bucket_at_the_largest_call():
+    """The standalone bucketing at the largest call the library accepts: 65,536 tokens of
+    top-32 over 1024 experts (2^21 assignments, the limit of the scan's packed fields), skewed
+    so that some buckets are large; bit-exact against the oracle."""
+    ops = _ops()
+    from quantized_moe_router_amd._lib import make_dims
+    T, k, E = 65536, 32, 1024
+    rng = np.random.default_rng(41)
+    p = 1.0 / np.arange(1, E + 1) ** 1.1
+    p /= p.sum()
+    # distinct experts per token: a random permutation's first k, drawn in a skewed order
+    idx = np.empty((T, k), np.int32)
+    for t0 in range(0, T, 4096):
+        keys = rng.random((4096, E)) ** (1.0 / p[None, :])
+        idx[t0:t0 + 4096] = np.argpartition(-keys, k, axis=1)[:, :k]
+    dims = make_dims(64, E, k, 64, 0)
+    counts, offsets, srt, active, n_active = ops.bucket(dims, torch.from_numpy(idx).to(DEV))
+    c, o, srt_ref, a = O.bucket(idx, E)
+    assert np.array_equal(counts.cpu().numpy(), c)
+    assert np.array_equal(offsets.cpu().numpy(), o)
+    assert np.array_equal(srt.cpu().numpy(), srt_ref)
+    na = int(n_active.cpu().numpy()[0])
+    assert na == len(a) and np.array_equal(active.cpu().numpy()[:na], a)
+
+
+def test_layer_at_the_largest_token_count():
+    """A layer call of 65,536 tokens (512 chunks), the largest the library accepts: 96 tokens
+    spread over the call (first and last chunk included) against the oracle, and the whole
+    output bit-equal to the same tokens run as separate calls of 4,096."""
+    ops = _ops()
+    T = 65536
+    cfg = G.Config("tiny_long", 256, 16, 2, 128, 128, layers=1, tokens=T)
+    pl, li = _stacks().build_layer(cfg, 0, DEV)
+    xb, x = _stacks().hidden(cfg, 43, T)
+    ws = ops.workspace(pl.dims, T)
+    out_f32 = torch.empty(T, cfg.hidden, dtype=torch.float32, device=DEV)
+    idx = torch.empty(T, cfg.top_k, dtype=torch.int32, device=DEV)
+    w = torch.empty(T, cfg.top_k, dtype=torch.float32, device=DEV)
+    out = ops.layer_forward(pl.weights, x, ws, out_f32=out_f32, topk_idx=idx, topk_w=w)
+    torch.cuda.synchronize()
+    assert ops.workspace_status(ws) == 0
+    toks = sorted(set(np.random.default_rng(47).choice(T, 90, replace=False).tolist())
+                  | {0, 1, 127, 128, T - 2, T - 1})
+    ties, nd, flips = _layer_check(cfg, li, xb, out, out_f32, idx, w, toks)
+    ws2 = ops.workspace(pl.dims, 4096)
+    for c0 in range(0, T, 4096):
+        part = ops.layer_forward(pl.weights, x[c0:c0 + 4096], ws2)
+        assert torch.equal(part.view(torch.int16), out[c0:c0 + 4096].view(torch.int16)), c0
+    print(f"T={T}: {len(toks)} tokens against the oracle, near ties {ties}, bf16 flips {flips}")
+
+
 def test_layer_forward_matches_stepwise_and_is_deterministic():
     ops = _ops()
     cfg = G.config("gemma4_26b_a4b_prefill")
