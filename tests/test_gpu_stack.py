@@ -118,7 +118,8 @@ def assert_same(a, b, what):
     ("tiny", 5, (), True), ("tiny", 1, (), True), ("tiny", 6, (1, 2, 5), True),
     ("tiny", 3, (), False), ("tiny_int8", 3, (0,), True),
     ("gemma4_26b_a4b_decode", 4, (), True), ("gemma4_26b_a4b_decode", 3, (0, 2), True),
-    ("qwen3_next_80b_a3b_decode_b1", 3, (), True), ("gemma4_26b_a4b_int8_decode", 2, (), True)])
+    ("qwen3_next_80b_a3b_decode_b1", 3, (), True), ("gemma4_26b_a4b_int8_decode", 2, (), True),
+    ("tiny", 64, tuple(range(64)), True)])
 def test_stack_equals_chained_layer_calls(name, n, post, shared):
     ops = _ops()
     cfg = G.config(name)
@@ -131,6 +132,20 @@ def test_stack_equals_chained_layer_calls(name, n, post, shared):
     torch.cuda.synchronize()
     assert_same(got, ref, f"{name} x{n}")
     assert ops.workspace_status(ws) == 0 and ops.workspace_status(ws2) == 0
+
+
+def test_stack_longer_than_the_table_is_rejected():
+    """A chain of more layers than one launch's table holds (64) is rejected before any launch."""
+    ops = _ops()
+    from quantized_moe_router_amd import QmoeError
+    cfg = G.config("tiny")
+    lws, _ = chain("tiny", 65, tuple(range(65)))
+    _, x = _stacks().hidden(cfg, 34, 1)
+    ws = ops.workspace(lws[0].dims, 1)
+    with pytest.raises(QmoeError):
+        run_stack(lws, x, ws)
+    torch.cuda.synchronize()
+    assert ops.workspace_status(ws) == 0
 
 
 def test_stack_repeats_and_shares_the_workspace_with_layer_calls():
